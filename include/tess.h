@@ -1,0 +1,133 @@
+/* tess.h -- C ABI of libtess.so, the MI355X (gfx950) hot path of the Tessera potential.
+ *
+ * Method: "Ab Initio Accuracy Beyond the Cutoff: Distributed Message-Passing Equivariant
+ * Attention at Tens-of-Millions-of-Atom Scale" (Tessera), abstract: atoms are ordered along
+ * a space-filling curve, a three-level neighbour search with a conservative skin fixes the
+ * pair topology between rebuilds, an equivariant message-passing attention potential gives
+ * the energy, and forces come from back-propagation through the layers.
+ *
+ * Conventions shared by every entry point
+ *  - Units: A, eV, fs, amu. Boxes are orthorhombic and periodic; box[3] is a HOST array.
+ *  - All other array arguments are DEVICE pointers (e.g. torch tensors on cuda:0), owned by
+ *    the caller, row-major, without padding. The library never allocates device memory: the
+ *    caller passes a workspace of at least tess_workspace_bytes() bytes.
+ *  - `hip_stream` is a hipStream_t (NULL = default stream). Work is enqueued on it in order.
+ *  - Return value: a tess_status. Argument, box and workspace errors are detected on the host
+ *    before anything is enqueued. TESS_ERR_HIP reports a failed HIP call (the stream state is
+ *    then undefined).
+ *  - Supported model shapes: channels in {16, 32, 64}, l_max in {1, 2}, n_heads dividing
+ *    channels with channels/n_heads in {16, 32} or n_heads == 1, n_rbf == 8,
+ *    radial_hidden in {32, 64}, n_species <= 16. Others return TESS_ERR_ARG.
+ *  - Limits: n_atoms < 2^27; at most 1024 candidate neighbours per atom.
+ */
+#ifndef TESS_H
+#define TESS_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TESS_OK = 0,
+  TESS_ERR_ARG = -1,       /* bad argument or unsupported model shape */
+  TESS_ERR_BOX = -2,       /* some box edge <= 2 (r_cut + skin) */
+  TESS_ERR_CAPACITY = -3,  /* candidate list longer than edge_cap (see *n_edges) */
+  TESS_ERR_WORKSPACE = -4, /* workspace smaller than tess_workspace_bytes() */
+  TESS_ERR_HIP = -5,       /* a HIP runtime call failed */
+  TESS_ERR_SKIN = -6,      /* an atom moved more than skin/2 since the last rebuild */
+  TESS_ERR_SPECIES = -7,   /* species index outside [0, n_species) */
+  TESS_ERR_ROW = -8        /* an atom has more than 1024 candidate neighbours */
+} tess_status;
+
+/* Model hyper-parameters. Paths P follow from l_max (4 for l_max 1, 11 for l_max 2). */
+typedef struct {
+  int32_t n_species, n_layers, channels, l_max, n_heads, n_rbf, radial_hidden;
+  float r_cut;
+} tess_model_desc;
+
+int32_t tess_abi_version(void);
+const char* tess_status_string(int32_t status);
+
+/* Number of fp32 weights. Blob order (row-major [out][in], y = W x): Emb[S][C]; for each
+ * layer W_q[C][C], W_k[C][C], W1[R][K], W2[P][R], W_lin0[C(1+l_max)][C], then W_lin^l[C][C]
+ * for l = 1..l_max; finally w_E[C]. Returns -1 for an unsupported shape. */
+int64_t tess_weights_count(const tess_model_desc* desc);
+
+/* Workspace bytes for any entry point at this size (desc may be NULL for the neighbour
+ * build alone). */
+int64_t tess_workspace_bytes(const tess_model_desc* desc, int32_t n_atoms, int64_t edge_cap);
+
+/* tess_build_neighbors -- the three-level neighbour search of the Tessera abstract:
+ * (1) wrap every coordinate into the box (fp64, then rounded to fp32) and order the atoms by
+ *     a 30-bit Hilbert key (10 bits per axis, Skilling's transpose form) with a stable
+ *     radix sort; (2) bin the sorted atoms into cells no narrower than r_cut+skin;
+ * (3) keep the pairs with |x_j - x_i + s L|^2 < (r_cut+skin)^2 (fp64, minimum image s),
+ *     rows listing j in ascending order.
+ *  in/out  pos[n][3]     positions; on return wrapped into [0, L] and in sorted order
+ *  in/out  species[n]    permuted to sorted order
+ *  in/out  vel[n][3]     nullable; permuted to sorted order
+ *  out     ref_pos[n][3] nullable; receives a copy of the returned positions
+ *  out     perm[n]       perm[k] = pre-call index of the atom now at slot k
+ *  out     hkey[n]       nullable; Hilbert key of each sorted atom
+ *  out     row_ptr[n+1], col_shift[edge_cap]: CSR; entry = j | code<<27 with
+ *          code = 9(sx+1) + 3(sy+1) + (sz+1) the image shift s in {-1,0,1}^3
+ *  out     rev[edge_cap] nullable; rev[e] = slot of the reverse pair (j <- i, -s)
+ *  out     *n_edges (HOST) number of pairs; on TESS_ERR_CAPACITY the required count
+ * Synchronises the stream once (to read the pair count). On TESS_ERR_CAPACITY / TESS_ERR_ROW
+ * the positions and permutation outputs are valid but col_shift and rev are not. */
+int32_t tess_build_neighbors(int32_t n, const float box[3], float r_cut, float skin,
+                             float* pos, int32_t* species, float* vel, float* ref_pos,
+                             int32_t* perm, uint32_t* hkey, int32_t* row_ptr,
+                             uint32_t* col_shift, int32_t* rev, int64_t edge_cap,
+                             int64_t* n_edges, void* workspace, int64_t ws_bytes,
+                             void* hip_stream);
+
+/* tess_energy_forces -- energy and forces of the equivariant message-passing attention
+ * stack (Tessera title and abstract: equivariant attention, force back-propagation).
+ * Per layer: q/k projections of the scalar channels, per-edge Bessel radial basis with a
+ * cosine envelope and real spherical harmonics (l <= l_max), a radial MLP giving one weight
+ * per coupling path, the coupled value A_e h_j (Gaunt-normalised Clebsch-Gordan paths), a
+ * per-destination softmax over edges inside r_cut weighted by the envelope, sum
+ * aggregation, and a gated residual update. E = sum_i w_E . h_i^(T, l=0); F = -dE/dx.
+ *  in  weights  fp32 blob (tess_weights_count), pos[n][3] in the CSR's atom order,
+ *      species[n], row_ptr/col_shift/rev from tess_build_neighbors (rev may be NULL: it is
+ *      then rebuilt in the workspace), n_edges = row_ptr[n].
+ *  out energy   device double[1]; e_atom device float[n] (nullable);
+ *      forces   device float[n][3] (nullable: energy only, no backward pass).
+ * Fully asynchronous (no host synchronisation). Species outside [0, n_species) give
+ * undefined values; validate species on the host first if they are not trusted. */
+int32_t tess_energy_forces(const tess_model_desc* desc, const float* weights, int32_t n,
+                           const float box[3], const float* pos, const int32_t* species,
+                           const int32_t* row_ptr, const uint32_t* col_shift,
+                           const int32_t* rev, int64_t n_edges, double* energy,
+                           float* e_atom, float* forces, void* workspace, int64_t ws_bytes,
+                           void* hip_stream);
+
+#define TESS_MD_FORCES_VALID 1 /* forces[] already holds F(pos) in the current order */
+
+/* tess_md_steps -- velocity-Verlet MD with a neighbour rebuild every `rebuild_every` steps
+ * (Tessera abstract: a conservative skin keeps the topology between rebuilds). For
+ * s = 0..n_steps-1: if s % rebuild_every == 0, rebuild (pos, vel, species, forces and
+ * perm_accum are permuted to the new order; ref positions reset), computing the forces
+ * first when s == 0 and TESS_MD_FORCES_VALID is not set; then v += dt/2 F/m, x += dt v
+ * (x is not re-wrapped between rebuilds), F = -dE/dx (epot_trace[s] = E), v += dt/2 F/m,
+ * with F/m converted by 9.648533e-3 (eV/A/amu -> A/fs^2).
+ *  in     mass_by_species device float[n_species] (amu), dt_fs, n_steps, rebuild_every
+ *  in/out pos, vel, species, perm_accum[n] (perm_accum[k] = caller id of slot k), forces[n][3]
+ *  out    epot_trace device double[n_steps] (nullable); row_ptr/col_shift/rev as in
+ *         tess_build_neighbors; *n_edges (HOST) pairs of the last rebuild
+ * Synchronises once per rebuild. If an atom moved more than skin/2 from its position at
+ * the last rebuild, the call finishes that interval and returns TESS_ERR_SKIN. */
+int32_t tess_md_steps(const tess_model_desc* desc, const float* weights, int32_t n,
+                      const float box[3], float r_cut, float skin, float* pos, float* vel,
+                      int32_t* species, const float* mass_by_species, float dt_fs,
+                      int32_t n_steps, int32_t rebuild_every, int32_t flags,
+                      int32_t* perm_accum, float* forces, double* epot_trace,
+                      int32_t* row_ptr, uint32_t* col_shift, int32_t* rev, int64_t edge_cap,
+                      int64_t* n_edges, void* workspace, int64_t ws_bytes, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

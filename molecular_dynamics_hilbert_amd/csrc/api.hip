@@ -1,0 +1,223 @@
+// api.hip -- extern "C" entry points of libtess.so (declared in include/tess.h) and the
+// velocity-Verlet kernels of tess_md_steps.
+#include <cmath>
+#include <cstring>
+
+#include "tess_common.h"
+
+namespace tess {
+namespace {
+
+constexpr float kAccelConv = 9.648533e-3f;  // eV/A/amu -> A/fs^2
+
+// First half of a velocity-Verlet step: v += dt/2 F/m; x += dt v; flag |x - x_ref| > skin/2.
+__global__ void k_vv_kick_drift(int32_t n, float dt, const float* __restrict__ F,
+                                const int32_t* __restrict__ species,
+                                const float* __restrict__ mass, float* __restrict__ pos,
+                                float* __restrict__ vel, const float* __restrict__ ref,
+                                float half_skin2, int32_t* __restrict__ flag) {
+  int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float im = kAccelConv / mass[species[i]];
+  float d2 = 0.0f;
+#pragma unroll
+  for (int a = 0; a < 3; a++) {
+    float v = vel[3 * i + a] + 0.5f * dt * F[3 * i + a] * im;
+    float x = pos[3 * i + a] + dt * v;
+    vel[3 * i + a] = v;
+    pos[3 * i + a] = x;
+    float d = x - ref[3 * i + a];
+    d2 += d * d;
+  }
+  if (d2 > half_skin2) atomicOr(flag, 1);
+}
+
+// Second half: v += dt/2 F/m.
+__global__ void k_vv_kick(int32_t n, float dt, const float* __restrict__ F,
+                          const int32_t* __restrict__ species, const float* __restrict__ mass,
+                          float* __restrict__ vel) {
+  int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float im = kAccelConv / mass[species[i]];
+#pragma unroll
+  for (int a = 0; a < 3; a++) vel[3 * i + a] += 0.5f * dt * F[3 * i + a] * im;
+}
+
+inline int32_t gridn(int64_t n, int b) { return (int32_t)((n + b - 1) / b); }
+
+struct Layout {
+  NbrWS nbr;
+  char* ef;
+  int64_t ef_bytes;
+  // tess_md_steps scratch
+  float* ref_pos;
+  int32_t* perm;
+  int32_t* flag;
+  double* epot;
+  int64_t total;
+};
+
+Layout layout(char* base, const tess_model_desc* md, int32_t n, int64_t cap) {
+  Layout L{};
+  Carver cv{base, 0};
+  L.nbr = carve_nbr(cv, n);
+  int64_t nn = n > 0 ? n : 1;
+  L.ref_pos = cv.take<float>(3 * nn);
+  L.perm = cv.take<int32_t>(nn);
+  L.flag = cv.take<int32_t>(64);
+  L.epot = cv.take<double>(4);
+  if (md) {
+    L.ef_bytes = ef_workspace_bytes(*md, n, cap);
+    L.ef = cv.take<char>(L.ef_bytes);
+  }
+  L.total = cv.off + 256;
+  return L;
+}
+
+bool box_ok(const float box[3], float r_cut, float skin) {
+  double rcs = (double)r_cut + (double)skin;
+  for (int a = 0; a < 3; a++)
+    if (!((double)box[a] > 2.0 * rcs) || !std::isfinite(box[a])) return false;
+  return true;
+}
+
+}  // namespace
+}  // namespace tess
+
+using namespace tess;
+
+extern "C" {
+
+int32_t tess_abi_version(void) { return 1; }
+
+const char* tess_status_string(int32_t s) {
+  switch (s) {
+    case TESS_OK: return "ok";
+    case TESS_ERR_ARG: return "invalid argument or unsupported model shape";
+    case TESS_ERR_BOX: return "box edge must exceed 2 (r_cut + skin)";
+    case TESS_ERR_CAPACITY: return "neighbour list longer than edge_cap";
+    case TESS_ERR_WORKSPACE: return "workspace smaller than tess_workspace_bytes()";
+    case TESS_ERR_HIP: return "HIP runtime error";
+    case TESS_ERR_SKIN: return "an atom moved more than skin/2 since the last rebuild";
+    case TESS_ERR_SPECIES: return "species index out of range";
+    case TESS_ERR_ROW: return "an atom has more than 1024 candidate neighbours";
+    default: return "unknown status";
+  }
+}
+
+int64_t tess_weights_count(const tess_model_desc* d) {
+  if (!d || !ef_shape_supported(*d)) return -1;
+  int64_t C = d->channels, R = d->radial_hidden, K = d->n_rbf, Lm = d->l_max;
+  int64_t P = Lm == 1 ? 4 : 11;
+  int64_t per = 2 * C * C + R * K + P * R + C * (1 + Lm) * C + Lm * C * C;
+  return (int64_t)d->n_species * C + d->n_layers * per + C;
+}
+
+int64_t tess_workspace_bytes(const tess_model_desc* d, int32_t n, int64_t edge_cap) {
+  if (n < 0 || edge_cap < 0) return -1;
+  if (d && !ef_shape_supported(*d)) return -1;
+  return layout(nullptr, d, n, edge_cap).total;
+}
+
+int32_t tess_build_neighbors(int32_t n, const float box[3], float r_cut, float skin, float* pos,
+                             int32_t* species, float* vel, float* ref_pos, int32_t* perm,
+                             uint32_t* hkey, int32_t* row_ptr, uint32_t* col_shift, int32_t* rev,
+                             int64_t edge_cap, int64_t* n_edges, void* workspace,
+                             int64_t ws_bytes, void* hip_stream) {
+  if (n < 0 || n >= (1 << 27) || !box || !n_edges || edge_cap < 0 || !(r_cut > 0.0f) ||
+      !(skin >= 0.0f))
+    return TESS_ERR_ARG;
+  if (n > 0 && (!pos || !species || !perm || !row_ptr || (!col_shift && edge_cap > 0)))
+    return TESS_ERR_ARG;
+  if (!box_ok(box, r_cut, skin)) return TESS_ERR_BOX;
+  Layout L = layout(reinterpret_cast<char*>(workspace), nullptr, n, edge_cap);
+  if (!workspace || ws_bytes < L.total) return TESS_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  *n_edges = 0;
+  if (n == 0) {
+    if (row_ptr) TESS_HIP_CHECK(hipMemsetAsync(row_ptr, 0, sizeof(int32_t), st));
+    return TESS_OK;
+  }
+  return build_neighbors_impl(n, box, r_cut, skin, pos, species, vel, ref_pos, nullptr, nullptr,
+                              perm, hkey, row_ptr, col_shift, rev, edge_cap, n_edges, L.nbr, st);
+}
+
+int32_t tess_energy_forces(const tess_model_desc* d, const float* weights, int32_t n,
+                           const float box[3], const float* pos, const int32_t* species,
+                           const int32_t* row_ptr, const uint32_t* col_shift, const int32_t* rev,
+                           int64_t n_edges, double* energy, float* e_atom, float* forces,
+                           void* workspace, int64_t ws_bytes, void* hip_stream) {
+  if (!d || !ef_shape_supported(*d)) return TESS_ERR_ARG;
+  if (n < 0 || n >= (1 << 27) || n_edges < 0 || !box || !energy || !weights) return TESS_ERR_ARG;
+  if (n > 0 && (!pos || !species || !row_ptr || (n_edges > 0 && !col_shift))) return TESS_ERR_ARG;
+  for (int a = 0; a < 3; a++)
+    if (!(box[a] > 0.0f)) return TESS_ERR_BOX;
+  Layout L = layout(reinterpret_cast<char*>(workspace), d, n, n_edges);
+  if (!workspace || ws_bytes < L.total) return TESS_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  if (n == 0) {
+    TESS_HIP_CHECK(hipMemsetAsync(energy, 0, sizeof(double), st));
+    return TESS_OK;
+  }
+  return ef_dispatch(*d, weights, n, box, pos, species, row_ptr, col_shift, rev, n_edges, n_edges,
+                     energy, e_atom, forces, L.ef, L.ef_bytes, st);
+}
+
+int32_t tess_md_steps(const tess_model_desc* d, const float* weights, int32_t n, const float box[3],
+                      float r_cut, float skin, float* pos, float* vel, int32_t* species,
+                      const float* mass_by_species, float dt_fs, int32_t n_steps,
+                      int32_t rebuild_every, int32_t flags, int32_t* perm_accum, float* forces,
+                      double* epot_trace, int32_t* row_ptr, uint32_t* col_shift, int32_t* rev,
+                      int64_t edge_cap, int64_t* n_edges, void* workspace, int64_t ws_bytes,
+                      void* hip_stream) {
+  if (!d || !ef_shape_supported(*d)) return TESS_ERR_ARG;
+  if (n < 1 || n >= (1 << 27) || n_steps < 0 || rebuild_every < 1 || edge_cap < 0 || !box ||
+      !n_edges || !weights || !pos || !vel || !species || !mass_by_species || !perm_accum ||
+      !forces || !row_ptr || !col_shift || !rev || !(dt_fs > 0.0f) || !(r_cut > 0.0f) ||
+      !(skin >= 0.0f) || d->r_cut != r_cut)
+    return TESS_ERR_ARG;
+  if (!box_ok(box, r_cut, skin)) return TESS_ERR_BOX;
+  Layout L = layout(reinterpret_cast<char*>(workspace), d, n, edge_cap);
+  if (!workspace || ws_bytes < L.total) return TESS_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  const float half_skin2 = 0.25f * skin * skin;
+  bool forces_valid = (flags & TESS_MD_FORCES_VALID) != 0;
+  int64_t ne = *n_edges;
+  TESS_HIP_CHECK(hipMemsetAsync(L.flag, 0, sizeof(int32_t), st));
+  for (int32_t s = 0; s < n_steps; s++) {
+    if (s % rebuild_every == 0) {
+      if (s > 0) {
+        int32_t f = 0;
+        TESS_HIP_CHECK(hipMemcpyAsync(&f, L.flag, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+        TESS_HIP_CHECK(hipStreamSynchronize(st));
+        if (f) return TESS_ERR_SKIN;
+      }
+      int32_t rc = build_neighbors_impl(n, box, r_cut, skin, pos, species, vel, L.ref_pos,
+                                        (forces_valid || s > 0) ? forces : nullptr, perm_accum,
+                                        L.perm, nullptr, row_ptr, col_shift, rev, edge_cap, &ne,
+                                        L.nbr, st);
+      *n_edges = ne;
+      if (rc != TESS_OK) return rc;
+      if (s == 0 && !forces_valid) {
+        rc = ef_dispatch(*d, weights, n, box, pos, species, row_ptr, col_shift, rev, ne, edge_cap,
+                         L.epot, nullptr, forces, L.ef, L.ef_bytes, st);
+        if (rc != TESS_OK) return rc;
+      }
+    }
+    k_vv_kick_drift<<<gridn(n, 256), 256, 0, st>>>(n, dt_fs, forces, species, mass_by_species, pos,
+                                                   vel, L.ref_pos, half_skin2, L.flag);
+    TESS_HIP_CHECK(hipGetLastError());
+    int32_t rc = ef_dispatch(*d, weights, n, box, pos, species, row_ptr, col_shift, rev, ne,
+                             edge_cap, epot_trace ? epot_trace + s : L.epot, nullptr, forces, L.ef,
+                             L.ef_bytes, st);
+    if (rc != TESS_OK) return rc;
+    k_vv_kick<<<gridn(n, 256), 256, 0, st>>>(n, dt_fs, forces, species, mass_by_species, vel);
+    TESS_HIP_CHECK(hipGetLastError());
+  }
+  int32_t f = 0;
+  TESS_HIP_CHECK(hipMemcpyAsync(&f, L.flag, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+  TESS_HIP_CHECK(hipStreamSynchronize(st));
+  return f ? TESS_ERR_SKIN : TESS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,1059 @@
+// model.hip -- energy and forces of the equivariant message-passing attention stack on
+// gfx950 (Tessera title and abstract: equivariant attention layers, forces by
+// back-propagation; the backward pass is the per-layer vector-Jacobian-product chain that the
+// REANN-MPI review describes, key_machinery field).
+//
+// Data layout in HBM (fp32): node features [N][D][C] (component-major per node, channels
+// contiguous, so a wave reading one component of one node reads 4C contiguous bytes);
+// q|k per node [N][2C]; per active edge (r < r_cut, destination-major) geometry float4
+// (r_vec, |r|), radial weights w[12], dw/dr[12] and logits s[4] per layer.
+//
+// Kernels per layer (forward): MFMA GEMM q|k; edge_prep (one thread per edge: Bessel basis,
+// radial MLP and its r-derivative, logits); edge_apply (one wave per destination row:
+// softmax statistics, coupling matrices A_e into LDS, then lane = channel accumulates
+// alpha * A_e h_j); MFMA GEMMs of the gated residual update with fused epilogues.
+// Backward: elementwise update adjoint + MFMA GEMMs; edge_grad (one thread per edge:
+// per-head sum over channels of mbar_i (x) h_j contracted through the coupling adjoint, giving
+// the logit adjoint and dE/dr_vec); edge_tapply (one wave per row: h_bar via A^T, k_bar, q_bar);
+// MFMA GEMM for the q/k projections; force assembly through the reverse-edge index.
+#include "tess_common.h"
+
+#include <vector>
+
+namespace tess {
+namespace {
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+constexpr float kPi = 3.14159265358979323846f;
+
+inline int32_t gridn(int64_t n, int b) { return (int32_t)((n + b - 1) / b); }
+
+// ---------------------------------------------------------------------------------------
+// GEMM: Y[r][o] = sum_k X[r][k] * Wt[k][o] (fp32 MFMA 32x32x2), with row maps so that the
+// same kernel reads one irrep block of [N][D][C] features.
+// ---------------------------------------------------------------------------------------
+struct RowMap {
+  int64_t nstride;  // floats between nodes
+  int32_t cstride;  // floats between components of one node
+  int32_t c0;       // first component
+  int32_t rpn;      // rows per node (components of the block)
+};
+__device__ __forceinline__ int64_t row_off(const RowMap& m, int64_t r) {
+  int64_t n = r / m.rpn;
+  int32_t k = (int32_t)(r - n * m.rpn);
+  return n * m.nstride + (int64_t)(m.c0 + k) * m.cstride;
+}
+
+enum { EPI_STORE = 0, EPI_ADD = 1, EPI_UPD0 = 2, EPI_UPDL = 3 };
+
+struct Epi {
+  float* y;           // output (store/add), or pre-activation store for UPD*
+  RowMap ym;
+  const float* hin;   // UPD*: residual input features
+  float* hout;        // UPD*: output features
+  RowMap hm;          // UPD*: map of hin/hout rows
+  const float* gates; // UPDL: [N][C(1+Lm)] pre-activations (gate of degree l at l*C)
+  int32_t gstride, goff, cdim;
+};
+
+template <int EPI>
+__global__ void __launch_bounds__(256) k_gemm(int64_t M, int K, int O, const float* __restrict__ X,
+                                              RowMap xm, const float* __restrict__ Wt, Epi ep) {
+  __shared__ float Xs[64][33];
+  __shared__ float Ws[32][65];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int wr = w >> 1, wc = w & 1;
+  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  const int o0 = blockIdx.y * 64;
+  floatx16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; v++) acc[v] = 0.0f;
+  // per-thread load assignment
+  const int xr = t >> 2, xk = (t & 3) * 8;      // X tile: 64 rows x 32 k
+  const int wk = t >> 3, wo = (t & 7) * 8;      // W tile: 32 k x 64 cols
+  const int64_t xrow = r0 + xr;
+  const bool xrow_ok = xrow < M;
+  const int64_t xbase = xrow_ok ? row_off(xm, xrow) : 0;
+  for (int k0 = 0; k0 < K; k0 += 32) {
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+      int k = k0 + xk + q;
+      Xs[xr][xk + q] = (xrow_ok && k < K) ? X[xbase + k] : 0.0f;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+      int k = k0 + wk, o = o0 + wo + q;
+      Ws[wk][wo + q] = (k < K && o < O) ? Wt[(int64_t)k * O + o] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 32; kk += 2) {
+      float a = Xs[wr * 32 + (lane & 31)][kk + (lane >> 5)];
+      float b = Ws[kk + (lane >> 5)][wc * 32 + (lane & 31)];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int v = 0; v < 16; v++) {
+    int64_t r = r0 + wr * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+    int o = o0 + wc * 32 + (lane & 31);
+    if (r >= M || o >= O) continue;
+    float val = acc[v];
+    if (EPI == EPI_STORE) {
+      ep.y[row_off(ep.ym, r) + o] = val;
+    } else if (EPI == EPI_ADD) {
+      ep.y[row_off(ep.ym, r) + o] += val;
+    } else if (EPI == EPI_UPD0) {
+      ep.y[row_off(ep.ym, r) + o] = val;
+      if (o < ep.cdim) {
+        int64_t hb = row_off(ep.hm, r) + o;
+        ep.hout[hb] = ep.hin[hb] + val * sigmoidf_(val);
+      }
+    } else {  // EPI_UPDL
+      ep.y[row_off(ep.ym, r) + o] = val;
+      int64_t n = r / ep.hm.rpn;
+      float g = ep.gates[n * ep.gstride + ep.goff + o];
+      int64_t hb = row_off(ep.hm, r) + o;
+      ep.hout[hb] = ep.hin[hb] + sigmoidf_(g) * val;
+    }
+  }
+}
+
+template <int EPI>
+hipError_t gemm(hipStream_t st, int64_t M, int K, int O, const float* X, RowMap xm,
+                const float* Wt, const Epi& ep) {
+  if (M <= 0) return hipSuccess;
+  dim3 g((unsigned)((M + 63) / 64), (unsigned)((O + 63) / 64));
+  k_gemm<EPI><<<g, 256, 0, st>>>(M, K, O, X, xm, Wt, ep);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// Weight preparation: transposed copies for the forward GEMMs.
+// ---------------------------------------------------------------------------------------
+__global__ void k_transpose(const float* __restrict__ W, int rows, int cols, float* __restrict__ Wt,
+                            int ldt, int col_off) {
+  int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= (int64_t)rows * cols) return;
+  int r = (int)(k / cols), c = (int)(k % cols);
+  Wt[(int64_t)c * ldt + col_off + r] = W[k];  // Wt[c][col_off + r] = W[r][c]
+}
+
+__global__ void k_embed(int32_t n, int C, int D, const int32_t* __restrict__ species,
+                        const float* __restrict__ emb, float* __restrict__ h) {
+  int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= (int64_t)n * D * C) return;
+  int64_t i = k / (D * C);
+  int rem = (int)(k - i * D * C);
+  int d = rem / C, c = rem % C;
+  h[k] = d == 0 ? emb[species[i] * C + c] : 0.0f;
+}
+
+// ---------------------------------------------------------------------------------------
+// Active-edge list (pairs with r < r_cut), destination-major, with geometry in fp32:
+// r_vec = x_j - x_i + s L. The test is symmetric under (i,j,s) -> (j,i,-s) bit for bit.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ float4 edge_vec(const float* __restrict__ pos, int32_t i, uint32_t c,
+                                           float Lx, float Ly, float Lz, int32_t* j_out) {
+  int32_t j = (int32_t)(c & 0x7FFFFFFu);
+  int code = (int)(c >> 27);
+  float sx = (float)(code / 9 - 1), sy = (float)((code / 3) % 3 - 1), sz = (float)(code % 3 - 1);
+  float rx = (pos[3 * j] - pos[3 * i]) + sx * Lx;
+  float ry = (pos[3 * j + 1] - pos[3 * i + 1]) + sy * Ly;
+  float rz = (pos[3 * j + 2] - pos[3 * i + 2]) + sz * Lz;
+  *j_out = j;
+  return make_float4(rx, ry, rz, __fmul_rn(rx, rx) + __fmul_rn(ry, ry) + __fmul_rn(rz, rz));
+}
+
+__global__ void __launch_bounds__(256) k_active_count(int32_t n, const float* __restrict__ pos,
+                                                      const int32_t* __restrict__ row_ptr,
+                                                      const uint32_t* __restrict__ col, float Lx,
+                                                      float Ly, float Lz, float rc2,
+                                                      int32_t* __restrict__ acnt) {
+  int32_t i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  int lane = threadIdx.x & 63;
+  if (i >= n) return;
+  int cnt = 0;
+  for (int32_t e = row_ptr[i] + lane; e < row_ptr[i + 1]; e += 64) {
+    int32_t j;
+    float4 r = edge_vec(pos, i, col[e], Lx, Ly, Lz, &j);
+    cnt += r.w < rc2;
+  }
+  for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+  if (lane == 0) acnt[i] = cnt;
+}
+
+__global__ void __launch_bounds__(256) k_active_fill(int32_t n, const float* __restrict__ pos,
+                                                     const int32_t* __restrict__ row_ptr,
+                                                     const uint32_t* __restrict__ col, float Lx,
+                                                     float Ly, float Lz, float rc2,
+                                                     const int32_t* __restrict__ arow,
+                                                     int32_t* __restrict__ adst,
+                                                     int32_t* __restrict__ asrc,
+                                                     int32_t* __restrict__ aslot,
+                                                     int32_t* __restrict__ slot2act,
+                                                     float4* __restrict__ ageo) {
+  int32_t i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  int lane = threadIdx.x & 63;
+  if (i >= n) return;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int32_t a0 = arow[i];
+  for (int32_t e0 = row_ptr[i]; e0 < row_ptr[i + 1]; e0 += 64) {
+    int32_t e = e0 + lane;
+    bool ok = e < row_ptr[i + 1];
+    bool act = false;
+    int32_t j = 0;
+    float4 r = make_float4(0, 0, 0, 0);
+    if (ok) {
+      r = edge_vec(pos, i, col[e], Lx, Ly, Lz, &j);
+      act = r.w < rc2;
+    }
+    uint64_t m = __ballot(act);
+    if (act) {
+      int32_t a = a0 + __popcll(m & lt);
+      adst[a] = i;
+      asrc[a] = j;
+      aslot[a] = e;
+      ageo[a] = make_float4(r.x, r.y, r.z, sqrtf(r.w));
+      slot2act[e] = a;
+    } else if (ok) {
+      slot2act[e] = -1;
+    }
+    a0 += __popcll(m);
+  }
+}
+
+__global__ void k_active_rev(const int32_t* __restrict__ arow_n, const int32_t* __restrict__ aslot,
+                             const int32_t* __restrict__ rev, const int32_t* __restrict__ slot2act,
+                             int32_t* __restrict__ arev, int64_t cap) {
+  int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (a >= cap || a >= *arow_n) return;
+  arev[a] = slot2act[rev[aslot[a]]];
+}
+
+// ---------------------------------------------------------------------------------------
+// Radial part: cosine envelope u(r) = (cos(pi r/rc)+1)/2 and Bessel basis
+// b_k = u sqrt(2/rc) sin(k pi r/rc)/r, k = 1..8, with r-derivatives.
+// ---------------------------------------------------------------------------------------
+struct RadialOut {
+  float u, du;
+  float b[8], db[8];
+};
+__device__ __forceinline__ void radial8(float r, float rc, RadialOut& o) {
+  float th = kPi * r / rc;
+  float s1, c1;
+  __sincosf(th, &s1, &c1);
+  o.u = 0.5f * (c1 + 1.0f);
+  o.du = -0.5f * (kPi / rc) * s1;
+  const float pref = sqrtf(2.0f / rc);
+  const float ir = 1.0f / r;
+  float sk = s1, ck = c1;
+#pragma unroll
+  for (int k = 0; k < 8; k++) {
+    float a = (k + 1) * kPi / rc;
+    float B = pref * sk * ir;
+    float dB = pref * (a * ck * ir - sk * ir * ir);
+    o.b[k] = o.u * B;
+    o.db[k] = o.du * B + o.u * dB;
+    float sn = sk * c1 + ck * s1;
+    float cn = ck * c1 - sk * s1;
+    sk = sn;
+    ck = cn;
+  }
+}
+
+// Per active edge and layer: radial weights w_p = W2 SiLU(W1 b), their r-derivative, and the
+// per-head logits s_h = <q_i^h, k_j^h>/sqrt(d).
+template <int LMAX, int C, int H, int R>
+__global__ void __launch_bounds__(256) k_edge_prep(const int32_t* __restrict__ arow_n,
+                                                   const float4* __restrict__ ageo,
+                                                   const int32_t* __restrict__ adst,
+                                                   const int32_t* __restrict__ asrc,
+                                                   const float* __restrict__ W1,
+                                                   const float* __restrict__ W2,
+                                                   const float* __restrict__ qk, float rc,
+                                                   float* __restrict__ ew, float* __restrict__ edw,
+                                                   float4* __restrict__ es, int64_t cap) {
+  constexpr int P = Dims<LMAX>::P;
+  constexpr int dh = C / H;
+  int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (a >= cap || a >= *arow_n) return;
+  float4 g = ageo[a];
+  RadialOut ro;
+  radial8(g.w, rc, ro);
+  float w[P], dw[P];
+#pragma unroll
+  for (int p = 0; p < P; p++) { w[p] = 0.0f; dw[p] = 0.0f; }
+  for (int r = 0; r < R; r++) {
+    float z = 0.0f, zp = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      float wk = W1[r * 8 + k];
+      z += wk * ro.b[k];
+      zp += wk * ro.db[k];
+    }
+    float sg = sigmoidf_(z);
+    float act = z * sg;
+    float dact = sg * (1.0f + z * (1.0f - sg)) * zp;
+#pragma unroll
+    for (int p = 0; p < P; p++) {
+      float w2 = W2[p * R + r];
+      w[p] += w2 * act;
+      dw[p] += w2 * dact;
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < P; p++) {
+    ew[a * 12 + p] = w[p];
+    edw[a * 12 + p] = dw[p];
+  }
+  const float4* qi = reinterpret_cast<const float4*>(qk + (int64_t)adst[a] * 2 * C);
+  const float4* kj = reinterpret_cast<const float4*>(qk + (int64_t)asrc[a] * 2 * C + C);
+  float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int c4 = 0; c4 < C / 4; c4++) {
+    float4 q = qi[c4], k = kj[c4];
+    s[(c4 * 4) / dh] += q.x * k.x + q.y * k.y + q.z * k.z + q.w * k.w;
+  }
+  const float isd = rsqrtf((float)dh);
+  es[a] = make_float4(s[0] * isd, s[1] * isd, s[2] * isd, s[3] * isd);
+}
+
+// ---------------------------------------------------------------------------------------
+// Forward aggregation. One wave per destination row i; 4 rows per 256-thread block.
+//   M_h = max_e s_eh, Z_h = sum_e u_e exp(s_eh - M_h), alpha_eh = u_e exp(s_eh - M_h)/Z_h,
+//   m_i[d3][c] = sum_e alpha_e,h(c) sum_d1 A_e[d3][d1] h_j[d1][c].
+// Edges are processed in chunks of 32: lanes build alpha and A_e (lane = edge) into LDS,
+// then lane = channel accumulates. L0ONLY: only the l = 0 input component is non-zero.
+// ---------------------------------------------------------------------------------------
+constexpr int kChunk = 32;
+
+template <int LMAX, int C, int H, bool L0ONLY>
+__global__ void __launch_bounds__(256) k_edge_apply(int32_t n, const int32_t* __restrict__ arow,
+                                                    const float4* __restrict__ ageo,
+                                                    const int32_t* __restrict__ asrc,
+                                                    const float* __restrict__ ew,
+                                                    const float4* __restrict__ es,
+                                                    const float* __restrict__ h, float rc,
+                                                    float* __restrict__ m,
+                                                    float* __restrict__ MZ) {
+  constexpr int D = Dims<LMAX>::D;
+  constexpr int DD = L0ONLY ? 1 : D;  // input components used
+  constexpr int dh = C / H;
+  __shared__ float sA[4][kChunk][D * DD];
+  __shared__ float sAl[4][kChunk][4];
+  __shared__ int32_t sJ[4][kChunk];
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int32_t i = blockIdx.x * 4 + wv;
+  if (i >= n) return;
+  const int32_t a0 = arow[i], a1 = arow[i + 1];
+  // softmax statistics over the row (lane = edge)
+  float Mh[4], Zh[4];
+#pragma unroll
+  for (int hh = 0; hh < 4; hh++) { Mh[hh] = -INFINITY; Zh[hh] = 0.0f; }
+  for (int32_t a = a0 + lane; a < a1; a += 64) {
+    float4 s = es[a];
+    Mh[0] = fmaxf(Mh[0], s.x);
+    if (H > 1) { Mh[1] = fmaxf(Mh[1], s.y); Mh[2] = fmaxf(Mh[2], s.z); Mh[3] = fmaxf(Mh[3], s.w); }
+  }
+#pragma unroll
+  for (int hh = 0; hh < H; hh++) Mh[hh] = wave_max(Mh[hh]);
+  for (int32_t a = a0 + lane; a < a1; a += 64) {
+    float4 s = es[a];
+    float r = ageo[a].w;
+    float u = 0.5f * (__cosf(kPi * r / rc) + 1.0f);
+    Zh[0] += u * __expf(s.x - Mh[0]);
+    if (H > 1) {
+      Zh[1] += u * __expf(s.y - Mh[1]);
+      Zh[2] += u * __expf(s.z - Mh[2]);
+      Zh[3] += u * __expf(s.w - Mh[3]);
+    }
+  }
+#pragma unroll
+  for (int hh = 0; hh < H; hh++) Zh[hh] = wave_sum(Zh[hh]);
+  if (lane < H) {
+    float mv = a1 > a0 ? Mh[lane] : 0.0f;
+    MZ[(int64_t)i * 2 * H + lane] = mv;
+    MZ[(int64_t)i * 2 * H + H + lane] = Zh[lane];
+  }
+  float acc[D];
+#pragma unroll
+  for (int d = 0; d < D; d++) acc[d] = 0.0f;
+  const int c = lane;
+  const int hc = (c < C ? c : 0) / dh;
+  for (int32_t b = a0; b < a1; b += kChunk) {
+    const int cnt = min(kChunk, a1 - b);
+    if (lane < cnt) {
+      int32_t a = b + lane;
+      float4 g = ageo[a];
+      float4 s = es[a];
+      float u = 0.5f * (__cosf(kPi * g.w / rc) + 1.0f);
+      float sv[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+      for (int hh = 0; hh < 4; hh++)
+        sAl[wv][lane][hh] = (hh < H && Zh[hh] > 0.0f) ? u * __expf(sv[hh] - Mh[hh]) / Zh[hh] : 0.0f;
+      float ir = 1.0f / g.w;
+      float Y[9];
+      sph<LMAX>(g.x * ir, g.y * ir, g.z * ir, Y);
+      float w[Dims<LMAX>::P];
+#pragma unroll
+      for (int p = 0; p < Dims<LMAX>::P; p++) w[p] = ew[(int64_t)a * 12 + p];
+      float A[D * D];
+      coupling_matrix<LMAX>(w, Y, A);
+#pragma unroll
+      for (int d3 = 0; d3 < D; d3++)
+#pragma unroll
+        for (int d1 = 0; d1 < DD; d1++) sA[wv][lane][d3 * DD + d1] = A[d3 * D + d1];
+      sJ[wv][lane] = asrc[a];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    if (c < C) {
+      for (int e = 0; e < cnt; e++) {
+        const float* hj = h + (int64_t)sJ[wv][e] * D * C + c;
+        float hv[DD];
+#pragma unroll
+        for (int d1 = 0; d1 < DD; d1++) hv[d1] = hj[d1 * C];
+        const float al = sAl[wv][e][hc];
+        const float* Ae = sA[wv][e];
+#pragma unroll
+        for (int d3 = 0; d3 < D; d3++) {
+          float t = 0.0f;
+#pragma unroll
+          for (int d1 = 0; d1 < DD; d1++) t += Ae[d3 * DD + d1] * hv[d1];
+          acc[d3] += al * t;
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  }
+  if (c < C) {
+#pragma unroll
+    for (int d = 0; d < D; d++) m[(int64_t)i * D * C + d * C + c] = acc[d];
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Readout E_i = w_E . h_i^(T, 0) and a deterministic fp64 total.
+// ---------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) k_readout(int32_t n, int C, int D, const float* __restrict__ h,
+                                                 const float* __restrict__ wE,
+                                                 float* __restrict__ e_atom,
+                                                 double* __restrict__ part) {
+  __shared__ double sh[256];
+  int32_t i = blockIdx.x * 256 + threadIdx.x;
+  double v = 0.0;
+  if (i < n) {
+    float e = 0.0f;
+    for (int c = 0; c < C; c++) e += wE[c] * h[(int64_t)i * D * C + c];
+    if (e_atom) e_atom[i] = e;
+    v = (double)e;
+  }
+  sh[threadIdx.x] = v;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) sh[threadIdx.x] += sh[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[blockIdx.x] = sh[0];
+}
+
+__global__ void __launch_bounds__(256) k_energy_final(int32_t nb, const double* __restrict__ part,
+                                                      double* __restrict__ energy) {
+  __shared__ double sh[256];
+  double v = 0.0;
+  for (int32_t k = threadIdx.x; k < nb; k += 256) v += part[k];
+  sh[threadIdx.x] = v;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) sh[threadIdx.x] += sh[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) energy[0] = sh[0];
+}
+
+// ---------------------------------------------------------------------------------------
+// Backward: update adjoint (elementwise part). gbar = dE/dh^(t+1).
+//   xcat[n][0:C]      = gbar^0 * SiLU'(y0)
+//   xcat[n][lC:(l+1)C] = sum_m gbar^(l,m) y^(l,m) * sigmoid'(g_l)
+//   ybl[n][l^2+m][c]  = gbar^(l,m) * sigmoid(g_l)
+//   hbar = gbar (residual path), when hbar is not NULL.
+// ---------------------------------------------------------------------------------------
+template <int LMAX>
+__global__ void k_bwd_update(int32_t n, int C, const float* __restrict__ gbar,
+                             const float* __restrict__ yg, const float* __restrict__ yl,
+                             float* __restrict__ xcat, float* __restrict__ ybl,
+                             float* __restrict__ hbar) {
+  constexpr int D = Dims<LMAX>::D;
+  int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= (int64_t)n * C) return;
+  int64_t i = k / C;
+  int c = (int)(k - i * C);
+  const int G = C * (1 + LMAX);
+  const float* gb = gbar + i * D * C + c;
+  float y0 = yg[i * G + c];
+  float sg0 = sigmoidf_(y0);
+  xcat[i * G + c] = gb[0] * sg0 * (1.0f + y0 * (1.0f - sg0));
+#pragma unroll
+  for (int l = 1; l <= LMAX; l++) {
+    float g = yg[i * G + l * C + c];
+    float sg = sigmoidf_(g);
+    float s = 0.0f;
+    for (int mm = 0; mm < 2 * l + 1; mm++) {
+      int d = l * l + mm;
+      float gv = gb[d * C];
+      s += gv * yl[i * D * C + d * C + c];
+      ybl[i * D * C + d * C + c] = gv * sg;
+    }
+    xcat[i * G + l * C + c] = s * sg * (1.0f - sg);
+  }
+  if (hbar) {
+#pragma unroll
+    for (int d = 0; d < D; d++) hbar[i * D * C + d * C + c] = gb[d * C];
+  }
+}
+
+// D_i^h = <mbar_i^h, m_i^h> over the head's channels and all components. Wave per node.
+template <int LMAX, int C, int H>
+__global__ void __launch_bounds__(256) k_dst(int32_t n, const float* __restrict__ mbar,
+                                             const float* __restrict__ m, float* __restrict__ Dst) {
+  constexpr int D = Dims<LMAX>::D;
+  constexpr int dh = C / H;
+  int32_t i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  int lane = threadIdx.x & 63;
+  if (i >= n) return;
+  float v = 0.0f;
+  if (lane < C) {
+#pragma unroll
+    for (int d = 0; d < D; d++)
+      v += mbar[(int64_t)i * D * C + d * C + lane] * m[(int64_t)i * D * C + d * C + lane];
+  }
+#pragma unroll
+  for (int o = 1; o < dh; o <<= 1) v += __shfl_xor(v, o, 64);
+  if (lane < C && (lane % dh) == 0) Dst[(int64_t)i * H + lane / dh] = v;
+}
+
+__global__ void k_gbar_init(int32_t n, int C, int D, const float* __restrict__ wE,
+                            float* __restrict__ gbar) {
+  int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= (int64_t)n * D * C) return;
+  int rem = (int)(k % (D * C));
+  gbar[k] = rem < C ? wE[rem] : 0.0f;
+}
+
+// ---------------------------------------------------------------------------------------
+// Edge gradient, one thread per active edge e = (i <- j), destination-major:
+//   Abar^h = sum_{c in h} mbar_i[:,c] (x) h_j[:,c];  (wbar^h, Ybar^h) = coupling adjoint;
+//   abar_h = <A_e, Abar^h> = w . wbar^h;  sbar_h = alpha_h (abar_h - D_ih);
+//   ubar = sum_h p_h (abar_h - D_ih), p_h = exp(s_h - M_ih)/Z_ih, alpha_h = u p_h;
+//   wbar = sum_h alpha_h wbar^h, Ybar = sum_h alpha_h Ybar^h;
+//   dE/dr = wbar . dw/dr + ubar u'(r);  g = dE/dr n + (I - n n^T) J_Y^T Ybar / r.
+// g (dE/dr_vec) accumulates over layers per edge; sbar is kept for the q/k adjoints.
+// ---------------------------------------------------------------------------------------
+template <int LMAX, int C, int H, bool L0ONLY>
+__global__ void __launch_bounds__(256) k_edge_grad(const int32_t* __restrict__ arow_n,
+                                                   const float4* __restrict__ ageo,
+                                                   const int32_t* __restrict__ adst,
+                                                   const int32_t* __restrict__ asrc,
+                                                   const float* __restrict__ ew,
+                                                   const float* __restrict__ edw,
+                                                   const float4* __restrict__ es,
+                                                   const float* __restrict__ MZ,
+                                                   const float* __restrict__ Dst,
+                                                   const float* __restrict__ mbar,
+                                                   const float* __restrict__ h, float rc,
+                                                   float4* __restrict__ sbar,
+                                                   float* __restrict__ gacc, bool accumulate,
+                                                   int64_t cap) {
+  constexpr int D = Dims<LMAX>::D;
+  constexpr int DD = L0ONLY ? 1 : D;
+  constexpr int P = Dims<LMAX>::P;
+  constexpr int dh = C / H;
+  int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (a >= cap || a >= *arow_n) return;
+  const int32_t i = adst[a], j = asrc[a];
+  float4 g = ageo[a];
+  const float r = g.w, ir = 1.0f / r;
+  const float nx = g.x * ir, ny = g.y * ir, nz = g.z * ir;
+  float th = kPi * r / rc, s1, c1;
+  __sincosf(th, &s1, &c1);
+  const float u = 0.5f * (c1 + 1.0f), du = -0.5f * (kPi / rc) * s1;
+  float Y[9];
+  sph<LMAX>(nx, ny, nz, Y);
+  float w[P];
+#pragma unroll
+  for (int p = 0; p < P; p++) w[p] = ew[a * 12 + p];
+  float4 s4 = es[a];
+  const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+  float wb[P], Yb[9];
+#pragma unroll
+  for (int p = 0; p < P; p++) wb[p] = 0.0f;
+#pragma unroll
+  for (int d = 0; d < 9; d++) Yb[d] = 0.0f;
+  float ubar = 0.0f, sb[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const float* mb_i = mbar + (int64_t)i * D * C;
+  const float* h_j = h + (int64_t)j * D * C;
+#pragma unroll 1
+  for (int hh = 0; hh < H; hh++) {
+    float Ab[D * D];
+#pragma unroll
+    for (int k = 0; k < D * D; k++) Ab[k] = 0.0f;
+#pragma unroll 1
+    for (int c4 = hh * dh; c4 < (hh + 1) * dh; c4 += 4) {
+      float4 mv[D], hv[DD];
+#pragma unroll
+      for (int d = 0; d < D; d++) mv[d] = *reinterpret_cast<const float4*>(mb_i + d * C + c4);
+#pragma unroll
+      for (int d = 0; d < DD; d++) hv[d] = *reinterpret_cast<const float4*>(h_j + d * C + c4);
+#pragma unroll
+      for (int d3 = 0; d3 < D; d3++)
+#pragma unroll
+        for (int d1 = 0; d1 < DD; d1++)
+          Ab[d3 * D + d1] += mv[d3].x * hv[d1].x + mv[d3].y * hv[d1].y + mv[d3].z * hv[d1].z +
+                             mv[d3].w * hv[d1].w;
+    }
+    float wbh[P], Ybh[9];
+    coupling_matrix_vjp<LMAX>(w, Y, Ab, wbh, Ybh);
+    float abar = 0.0f;
+#pragma unroll
+    for (int p = 0; p < P; p++) abar += w[p] * wbh[p];
+    const float Zi = MZ[(int64_t)i * 2 * H + H + hh];
+    const float p_h = Zi > 0.0f ? __expf(sv[hh] - MZ[(int64_t)i * 2 * H + hh]) / Zi : 0.0f;
+    const float al = u * p_h;
+    const float diff = abar - Dst[(int64_t)i * H + hh];
+    sb[hh] = al * diff;
+    ubar += p_h * diff;
+#pragma unroll
+    for (int p = 0; p < P; p++) wb[p] += al * wbh[p];
+#pragma unroll
+    for (int d = 0; d < D; d++) Yb[d] += al * Ybh[d];
+  }
+  float dEdr = ubar * du;
+#pragma unroll
+  for (int p = 0; p < P; p++) dEdr += wb[p] * edw[a * 12 + p];
+  float gy[3];
+  sph_vjp<LMAX>(nx, ny, nz, Yb, gy);
+  const float ng = nx * gy[0] + ny * gy[1] + nz * gy[2];
+  float gx = dEdr * nx + (gy[0] - ng * nx) * ir;
+  float gyv = dEdr * ny + (gy[1] - ng * ny) * ir;
+  float gz = dEdr * nz + (gy[2] - ng * nz) * ir;
+  if (accumulate) {
+    gx += gacc[a * 3]; gyv += gacc[a * 3 + 1]; gz += gacc[a * 3 + 2];
+  }
+  gacc[a * 3] = gx;
+  gacc[a * 3 + 1] = gyv;
+  gacc[a * 3 + 2] = gz;
+  sbar[a] = make_float4(sb[0], sb[1], sb[2], sb[3]);
+}
+
+// ---------------------------------------------------------------------------------------
+// Row-wise adjoints, one wave per atom x (lane = channel). For each active edge a = (x <- y):
+//   source role of x in the forward edge e' = rev(a) = (y <- x):
+//     hbar_x[d1][c] += alpha_e',h(c) sum_d3 A_e'[d3][d1] mbar_y[d3][c],
+//     kbar_x[c]     += sbar_e',h(c) q_y[c] / sqrt(d);
+//   destination role in a itself: qbar_x[c] += sbar_a,h(c) k_y[c] / sqrt(d).
+// A_e' uses the same radial weights as a (same |r|) and Y(-n).
+// ---------------------------------------------------------------------------------------
+template <int LMAX, int C, int H>
+__global__ void __launch_bounds__(256) k_edge_tapply(int32_t n, const int32_t* __restrict__ arow,
+                                                     const float4* __restrict__ ageo,
+                                                     const int32_t* __restrict__ asrc,
+                                                     const int32_t* __restrict__ arev,
+                                                     const float* __restrict__ ew,
+                                                     const float4* __restrict__ es,
+                                                     const float* __restrict__ MZ,
+                                                     const float4* __restrict__ sbar,
+                                                     const float* __restrict__ mbar,
+                                                     const float* __restrict__ qk, float rc,
+                                                     float* __restrict__ hbar,
+                                                     float* __restrict__ qkbar) {
+  constexpr int D = Dims<LMAX>::D;
+  constexpr int dh = C / H;
+  __shared__ float sA[4][kChunk][D * D];
+  __shared__ float sAl[4][kChunk][4];
+  __shared__ float sSs[4][kChunk][4];  // sbar of e' (source role)
+  __shared__ float sSd[4][kChunk][4];  // sbar of a (destination role)
+  __shared__ int32_t sJ[4][kChunk];
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int32_t x = blockIdx.x * 4 + wv;
+  if (x >= n) return;
+  const int32_t a0 = arow[x], a1 = arow[x + 1];
+  const int c = lane;
+  const int hc = (c < C ? c : 0) / dh;
+  float acc[D];
+#pragma unroll
+  for (int d = 0; d < D; d++) acc[d] = 0.0f;
+  float qacc = 0.0f, kacc = 0.0f;
+  for (int32_t b = a0; b < a1; b += kChunk) {
+    const int cnt = min(kChunk, a1 - b);
+    if (lane < cnt) {
+      int32_t a = b + lane;
+      int32_t y = asrc[a];
+      int32_t ep = arev[a];
+      float4 g = ageo[a];
+      float u = 0.5f * (__cosf(kPi * g.w / rc) + 1.0f);
+      float4 s = es[ep];
+      float sv[4] = {s.x, s.y, s.z, s.w};
+      float4 sbs = sbar[ep], sbd = sbar[a];
+      float sbsv[4] = {sbs.x, sbs.y, sbs.z, sbs.w}, sbdv[4] = {sbd.x, sbd.y, sbd.z, sbd.w};
+#pragma unroll
+      for (int hh = 0; hh < 4; hh++) {
+        float Zy = hh < H ? MZ[(int64_t)y * 2 * H + H + hh] : 0.0f;
+        float My = hh < H ? MZ[(int64_t)y * 2 * H + hh] : 0.0f;
+        sAl[wv][lane][hh] = (hh < H && Zy > 0.0f) ? u * __expf(sv[hh] - My) / Zy : 0.0f;
+        sSs[wv][lane][hh] = sbsv[hh];
+        sSd[wv][lane][hh] = sbdv[hh];
+      }
+      float ir = 1.0f / g.w;
+      float Y[9];
+      sph<LMAX>(-g.x * ir, -g.y * ir, -g.z * ir, Y);
+      float w[Dims<LMAX>::P];
+#pragma unroll
+      for (int p = 0; p < Dims<LMAX>::P; p++) w[p] = ew[(int64_t)a * 12 + p];
+      float A[D * D];
+      coupling_matrix<LMAX>(w, Y, A);
+#pragma unroll
+      for (int k = 0; k < D * D; k++) sA[wv][lane][k] = A[k];
+      sJ[wv][lane] = y;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    if (c < C) {
+      for (int e = 0; e < cnt; e++) {
+        const int32_t y = sJ[wv][e];
+        const float* mby = mbar + (int64_t)y * D * C + c;
+        float mv[D];
+#pragma unroll
+        for (int d = 0; d < D; d++) mv[d] = mby[d * C];
+        const float al = sAl[wv][e][hc];
+        const float* Ae = sA[wv][e];
+#pragma unroll
+        for (int d1 = 0; d1 < D; d1++) {
+          float t = 0.0f;
+#pragma unroll
+          for (int d3 = 0; d3 < D; d3++) t += Ae[d3 * D + d1] * mv[d3];
+          acc[d1] += al * t;
+        }
+        kacc += sSs[wv][e][hc] * qk[(int64_t)y * 2 * C + c];
+        qacc += sSd[wv][e][hc] * qk[(int64_t)y * 2 * C + C + c];
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  }
+  if (c < C) {
+#pragma unroll
+    for (int d = 0; d < D; d++) hbar[(int64_t)x * D * C + d * C + c] += acc[d];
+    const float isd = rsqrtf((float)dh);
+    qkbar[(int64_t)x * 2 * C + c] = qacc * isd;
+    qkbar[(int64_t)x * 2 * C + C + c] = kacc * isd;
+  }
+}
+
+// F_x = sum over the active edges a of row x of (g_a - g_rev(a)), g = dE/dr_vec.
+__global__ void k_forces(int32_t n, const int32_t* __restrict__ arow, const int32_t* __restrict__ arev,
+                         const float* __restrict__ gacc, float* __restrict__ F) {
+  int32_t x = blockIdx.x * blockDim.x + threadIdx.x;
+  if (x >= n) return;
+  float f0 = 0.0f, f1 = 0.0f, f2 = 0.0f;
+  for (int32_t a = arow[x]; a < arow[x + 1]; a++) {
+    int32_t b = arev[a];
+    f0 += gacc[a * 3] - gacc[(int64_t)b * 3];
+    f1 += gacc[a * 3 + 1] - gacc[(int64_t)b * 3 + 1];
+    f2 += gacc[a * 3 + 2] - gacc[(int64_t)b * 3 + 2];
+  }
+  F[3 * x] = f0;
+  F[3 * x + 1] = f1;
+  F[3 * x + 2] = f2;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------
+// Workspace of the energy/force pass.
+// ---------------------------------------------------------------------------------------
+struct EFWS {
+  float *WqkT, *W0T, *WlT;  // per layer transposed weights
+  float *h, *qk, *MZ, *m, *yg, *yl;
+  int32_t *arow, *adst, *asrc, *aslot, *slot2act, *arev, *rev_own;
+  float4* ageo;
+  float *ew, *edw;
+  float4* es;
+  float *gbar, *hbar, *mbar, *xcat, *ybl, *qkbar, *Dst, *gacc;
+  float4* sbar;
+  double* epart;
+  int32_t* scan_tmp;
+};
+
+static EFWS carve_ef(Carver& cv, const tess_model_desc& md, int32_t n, int64_t cap) {
+  EFWS w{};
+  const int64_t C = md.channels, Lm = md.l_max, T = md.n_layers, H = md.n_heads;
+  const int64_t D = (Lm + 1) * (Lm + 1);
+  const int64_t nn = n > 0 ? n : 1, ec = cap > 0 ? cap : 1;
+  w.WqkT = cv.take<float>(T * C * 2 * C);
+  w.W0T = cv.take<float>(T * C * C * (1 + Lm));
+  w.WlT = cv.take<float>(T * Lm * C * C + 1);
+  w.h = cv.take<float>((T + 1) * nn * D * C);
+  w.qk = cv.take<float>(T * nn * 2 * C);
+  w.MZ = cv.take<float>(T * nn * 2 * H);
+  w.m = cv.take<float>(T * nn * D * C);
+  w.yg = cv.take<float>(T * nn * C * (1 + Lm));
+  w.yl = cv.take<float>(T * nn * D * C);
+  w.arow = cv.take<int32_t>(nn + 1);
+  w.adst = cv.take<int32_t>(ec);
+  w.asrc = cv.take<int32_t>(ec);
+  w.aslot = cv.take<int32_t>(ec);
+  w.slot2act = cv.take<int32_t>(ec);
+  w.arev = cv.take<int32_t>(ec);
+  w.rev_own = cv.take<int32_t>(ec);
+  w.ageo = cv.take<float4>(ec);
+  w.ew = cv.take<float>(T * ec * 12);
+  w.edw = cv.take<float>(T * ec * 12);
+  w.es = cv.take<float4>(T * ec);
+  w.gbar = cv.take<float>(nn * D * C);
+  w.hbar = cv.take<float>(nn * D * C);
+  w.mbar = cv.take<float>(nn * D * C);
+  w.xcat = cv.take<float>(nn * C * (1 + Lm));
+  w.ybl = cv.take<float>(nn * D * C);
+  w.qkbar = cv.take<float>(nn * 2 * C);
+  w.Dst = cv.take<float>(nn * H);
+  w.gacc = cv.take<float>(ec * 3);
+  w.sbar = cv.take<float4>(ec);
+  w.epart = cv.take<double>(nn / 256 + 2);
+  w.scan_tmp = cv.take<int32_t>(nn / 4096 + 4);
+  return w;
+}
+
+int64_t ef_workspace_bytes(const tess_model_desc& md, int32_t n, int64_t cap) {
+  Carver cv{nullptr, 0};
+  carve_ef(cv, md, n, cap);
+  return cv.off;
+}
+
+namespace {
+
+struct LayerW {
+  const float *Wq, *Wk, *W1, *W2, *W0, *Wl[3];
+};
+
+template <int LMAX, int C, int H, int R>
+int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const float box[3],
+               const float* pos, const int32_t* species, const int32_t* row_ptr,
+               const uint32_t* col_shift, const int32_t* rev_in, int64_t n_edges, int64_t ecap,
+               double* energy, float* e_atom, float* forces, const EFWS& w, hipStream_t st) {
+  constexpr int D = Dims<LMAX>::D;
+  constexpr int P = Dims<LMAX>::P;
+  constexpr int G = C * (1 + LMAX);
+  const int T = md.n_layers, S = md.n_species, K = md.n_rbf;
+  const float rc = md.r_cut;
+  const int64_t cap = n_edges > 0 ? n_edges : 0;  // threads per edge kernel
+  // ecap: edge capacity the workspace was laid out for (strides of per-layer edge arrays)
+  // weight offsets in the blob
+  std::vector<LayerW> lw(T);
+  {
+    int64_t off = (int64_t)S * C;
+    for (int t = 0; t < T; t++) {
+      lw[t].Wq = weights + off; off += C * C;
+      lw[t].Wk = weights + off; off += C * C;
+      lw[t].W1 = weights + off; off += (int64_t)R * K;
+      lw[t].W2 = weights + off; off += (int64_t)P * R;
+      lw[t].W0 = weights + off; off += (int64_t)G * C;
+      for (int l = 1; l <= LMAX; l++) { lw[t].Wl[l] = weights + off; off += C * C; }
+    }
+  }
+  const float* emb = weights;
+  const float* wE = weights + (int64_t)S * C + (int64_t)T * (2 * C * C + R * K + P * R + G * C + LMAX * C * C);
+  // transposed weights
+  for (int t = 0; t < T; t++) {
+    float* qkT = w.WqkT + (int64_t)t * C * 2 * C;
+    k_transpose<<<gridn(C * C, 256), 256, 0, st>>>(lw[t].Wq, C, C, qkT, 2 * C, 0);
+    k_transpose<<<gridn(C * C, 256), 256, 0, st>>>(lw[t].Wk, C, C, qkT, 2 * C, C);
+    k_transpose<<<gridn(G * C, 256), 256, 0, st>>>(lw[t].W0, G, C, w.W0T + (int64_t)t * C * G, G, 0);
+    for (int l = 1; l <= LMAX; l++)
+      k_transpose<<<gridn(C * C, 256), 256, 0, st>>>(
+          lw[t].Wl[l], C, C, w.WlT + ((int64_t)t * LMAX + (l - 1)) * C * C, C, 0);
+  }
+  TESS_HIP_CHECK(hipGetLastError());
+  const int64_t NDC = (int64_t)n * D * C;
+  // embedding
+  k_embed<<<gridn(NDC, 256), 256, 0, st>>>(n, C, D, species, emb, w.h);
+  // active edges
+  const int32_t* rev = rev_in;
+  if (cap > 0) {
+    if (!rev) {
+      // reverse index through a binary search in each row (rows are sorted)
+      TESS_HIP_CHECK(rev_index(n, row_ptr, col_shift, w.rev_own, st));
+      rev = w.rev_own;
+    }
+    k_active_count<<<gridn(n, 4), 256, 0, st>>>(n, pos, row_ptr, col_shift, box[0], box[1], box[2],
+                                                rc * rc, w.arow);
+    TESS_HIP_CHECK(hipMemsetAsync(w.arow + n, 0, sizeof(int32_t), st));
+    TESS_HIP_CHECK(scan_exclusive_i32(w.arow, (int64_t)n + 1, w.scan_tmp, st));
+    k_active_fill<<<gridn(n, 4), 256, 0, st>>>(n, pos, row_ptr, col_shift, box[0], box[1], box[2],
+                                               rc * rc, w.arow, w.adst, w.asrc, w.aslot,
+                                               w.slot2act, w.ageo);
+    k_active_rev<<<gridn(cap, 256), 256, 0, st>>>(w.arow + n, w.aslot, rev, w.slot2act, w.arev, cap);
+    TESS_HIP_CHECK(hipGetLastError());
+  } else {
+    TESS_HIP_CHECK(hipMemsetAsync(w.arow, 0, sizeof(int32_t) * ((size_t)n + 1), st));
+  }
+  const RowMap feat0{(int64_t)D * C, C, 0, 1};
+  // ---------------- forward ----------------
+  for (int t = 0; t < T; t++) {
+    float* ht = w.h + (int64_t)t * NDC;
+    float* hn = w.h + (int64_t)(t + 1) * NDC;
+    float* qk = w.qk + (int64_t)t * n * 2 * C;
+    float* MZ = w.MZ + (int64_t)t * n * 2 * H;
+    float* mt = w.m + (int64_t)t * NDC;
+    float* yg = w.yg + (int64_t)t * n * G;
+    float* yl = w.yl + (int64_t)t * NDC;
+    float* ew = w.ew + (int64_t)t * ecap * 12;
+    float* edw = w.edw + (int64_t)t * ecap * 12;
+    float4* es = w.es + (int64_t)t * ecap;
+    Epi e0{};
+    e0.y = qk;
+    e0.ym = RowMap{2 * C, 0, 0, 1};
+    TESS_HIP_CHECK(gemm<EPI_STORE>(st, n, C, 2 * C, ht, feat0, w.WqkT + (int64_t)t * C * 2 * C, e0));
+    if (cap > 0)
+      k_edge_prep<LMAX, C, H, R><<<gridn(cap, 256), 256, 0, st>>>(
+          w.arow + n, w.ageo, w.adst, w.asrc, lw[t].W1, lw[t].W2, qk, rc, ew, edw, es, cap);
+    if (t == 0)
+      k_edge_apply<LMAX, C, H, true><<<gridn(n, 4), 256, 0, st>>>(n, w.arow, w.ageo, w.asrc, ew,
+                                                                 es, ht, rc, mt, MZ);
+    else
+      k_edge_apply<LMAX, C, H, false><<<gridn(n, 4), 256, 0, st>>>(n, w.arow, w.ageo, w.asrc, ew,
+                                                                  es, ht, rc, mt, MZ);
+    TESS_HIP_CHECK(hipGetLastError());
+    Epi eu{};
+    eu.y = yg;
+    eu.ym = RowMap{G, 0, 0, 1};
+    eu.hin = ht;
+    eu.hout = hn;
+    eu.hm = feat0;
+    eu.cdim = C;
+    TESS_HIP_CHECK(gemm<EPI_UPD0>(st, n, C, G, mt, feat0, w.W0T + (int64_t)t * C * G, eu));
+    for (int l = 1; l <= LMAX; l++) {
+      RowMap ml{(int64_t)D * C, C, l * l, 2 * l + 1};
+      Epi el{};
+      el.y = yl;
+      el.ym = ml;
+      el.hin = ht;
+      el.hout = hn;
+      el.hm = ml;
+      el.gates = yg;
+      el.gstride = G;
+      el.goff = l * C;
+      el.cdim = C;
+      TESS_HIP_CHECK(gemm<EPI_UPDL>(st, (int64_t)n * (2 * l + 1), C, C, mt, ml,
+                                    w.WlT + ((int64_t)t * LMAX + (l - 1)) * C * C, el));
+    }
+  }
+  // readout
+  const float* hT = w.h + (int64_t)T * NDC;
+  int32_t nb = gridn(n, 256);
+  if (nb > 0) k_readout<<<nb, 256, 0, st>>>(n, C, D, hT, wE, e_atom, w.epart);
+  k_energy_final<<<1, 256, 0, st>>>(nb, w.epart, energy);
+  TESS_HIP_CHECK(hipGetLastError());
+  if (!forces) return TESS_OK;
+  // ---------------- backward ----------------
+  float* gbar = w.gbar;
+  float* hbar = w.hbar;
+  k_gbar_init<<<gridn(NDC, 256), 256, 0, st>>>(n, C, D, wE, gbar);
+  for (int t = T - 1; t >= 0; t--) {
+    const float* ht = w.h + (int64_t)t * NDC;
+    const float* qk = w.qk + (int64_t)t * n * 2 * C;
+    const float* MZ = w.MZ + (int64_t)t * n * 2 * H;
+    const float* mt = w.m + (int64_t)t * NDC;
+    const float* yg = w.yg + (int64_t)t * n * G;
+    const float* yl = w.yl + (int64_t)t * NDC;
+    const float* ew = w.ew + (int64_t)t * ecap * 12;
+    const float* edw = w.edw + (int64_t)t * ecap * 12;
+    const float4* es = w.es + (int64_t)t * ecap;
+    k_bwd_update<LMAX><<<gridn((int64_t)n * C, 256), 256, 0, st>>>(n, C, gbar, yg, yl, w.xcat, w.ybl,
+                                                                 t > 0 ? hbar : nullptr);
+    Epi em{};
+    em.y = w.mbar;
+    em.ym = feat0;
+    TESS_HIP_CHECK(gemm<EPI_STORE>(st, n, G, C, w.xcat, RowMap{G, 0, 0, 1}, lw[t].W0, em));
+    for (int l = 1; l <= LMAX; l++) {
+      RowMap ml{(int64_t)D * C, C, l * l, 2 * l + 1};
+      Epi el{};
+      el.y = w.mbar;
+      el.ym = ml;
+      TESS_HIP_CHECK(gemm<EPI_STORE>(st, (int64_t)n * (2 * l + 1), C, C, w.ybl, ml, lw[t].Wl[l], el));
+    }
+    k_dst<LMAX, C, H><<<gridn(n, 4), 256, 0, st>>>(n, w.mbar, mt, w.Dst);
+    if (cap > 0) {
+      if (t == 0)
+        k_edge_grad<LMAX, C, H, true><<<gridn(cap, 256), 256, 0, st>>>(
+            w.arow + n, w.ageo, w.adst, w.asrc, ew, edw, es, MZ, w.Dst, w.mbar, ht, rc, w.sbar,
+            w.gacc, t != T - 1, cap);
+      else
+        k_edge_grad<LMAX, C, H, false><<<gridn(cap, 256), 256, 0, st>>>(
+            w.arow + n, w.ageo, w.adst, w.asrc, ew, edw, es, MZ, w.Dst, w.mbar, ht, rc, w.sbar,
+            w.gacc, t != T - 1, cap);
+    }
+    TESS_HIP_CHECK(hipGetLastError());
+    if (t > 0) {
+      k_edge_tapply<LMAX, C, H><<<gridn(n, 4), 256, 0, st>>>(n, w.arow, w.ageo, w.asrc, w.arev, ew,
+                                                            es, MZ, w.sbar, w.mbar, qk, rc, hbar,
+                                                            w.qkbar);
+      Epi ea{};
+      ea.y = hbar;
+      ea.ym = feat0;
+      TESS_HIP_CHECK(gemm<EPI_ADD>(st, n, 2 * C, C, w.qkbar, RowMap{2 * C, 0, 0, 1}, lw[t].Wq, ea));
+      float* tmp = gbar;
+      gbar = hbar;
+      hbar = tmp;
+    }
+  }
+  if (cap > 0) {
+    k_forces<<<gridn(n, 256), 256, 0, st>>>(n, w.arow, w.arev, w.gacc, forces);
+  } else if (n > 0) {
+    TESS_HIP_CHECK(hipMemsetAsync(forces, 0, sizeof(float) * 3 * (size_t)n, st));
+  }
+  TESS_HIP_CHECK(hipGetLastError());
+  return TESS_OK;
+}
+
+}  // namespace
+
+bool ef_shape_supported(const tess_model_desc& md) {
+  if (md.n_rbf != 8 || md.n_layers < 1 || md.n_layers > 16 || md.n_species < 1 ||
+      md.n_species > 16 || !(md.r_cut > 0.0f))
+    return false;
+  const int l = md.l_max, c = md.channels, h = md.n_heads, r = md.radial_hidden;
+  return (l == 1 && c == 16 && h == 1 && r == 32) || (l == 2 && c == 32 && h == 4 && r == 32) ||
+         (l == 2 && c == 64 && h == 4 && r == 64) || (l == 2 && c == 16 && h == 4 && r == 32) ||
+         (l == 1 && c == 32 && h == 4 && r == 32);
+}
+
+int32_t ef_dispatch(const tess_model_desc& md, const float* weights, int32_t n, const float box[3],
+                    const float* pos, const int32_t* species, const int32_t* row_ptr,
+                    const uint32_t* col_shift, const int32_t* rev, int64_t n_edges,
+                    int64_t ecap, double* energy, float* e_atom, float* forces, char* ws,
+                    int64_t ws_bytes, hipStream_t st) {
+  Carver cv{ws, 0};
+  EFWS w = carve_ef(cv, md, n, ecap);
+  if (cv.off > ws_bytes) return TESS_ERR_WORKSPACE;
+  const int l = md.l_max, c = md.channels, h = md.n_heads, r = md.radial_hidden;
+#define TESS_EF_CASE(L_, C_, H_, R_)                                                          \
+  if (l == L_ && c == C_ && h == H_ && r == R_)                                               \
+    return ef_run<L_, C_, H_, R_>(md, weights, n, box, pos, species, row_ptr, col_shift, rev, \
+                                  n_edges, ecap, energy, e_atom, forces, w, st);
+  TESS_EF_CASE(1, 16, 1, 32)
+  TESS_EF_CASE(2, 32, 4, 32)
+  TESS_EF_CASE(2, 64, 4, 64)
+  TESS_EF_CASE(2, 16, 4, 32)
+  TESS_EF_CASE(1, 32, 4, 32)
+#undef TESS_EF_CASE
+  return TESS_ERR_ARG;
+}
+
+}  // namespace tess

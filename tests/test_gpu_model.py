@@ -1,0 +1,170 @@
+"""GPU parity of tess_energy_forces against the fp64 oracle.
+
+Bar: |dE|/|E| <= 1e-5 and |dF| <= 1e-4 (1 + |F|) eV/A per component (fp32 path vs fp64
+oracle on the same fp32 positions). water648 and salt4k compare every atom with the oracle run
+live; salt60k and capsid39k compare against stored oracle values (total E, 1024 sampled atoms);
+salt500k compares per-atom energies and forces of sampled atoms computed by the oracle on
+clusters that contain their whole receptive field, plus net force and symmetry properties."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from molecular_dynamics_hilbert_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+WEIGHT_SEED = {"water648": 2001, "salt4k": 2002, "salt60k": 2003, "capsid39k": 2004,
+               "salt500k": 2005}
+
+
+@pytest.fixture(scope="module")
+def T():
+    import torch
+    assert torch.cuda.is_available()
+    from molecular_dynamics_hilbert_amd import tess
+    tess.lib()
+    return tess
+
+
+def _run(T, wl, w, forces=True):
+    import torch
+    s = T.System(wl, w)
+    s.rebuild()
+    s.energy_forces(forces=forces)
+    torch.cuda.synchronize()
+    return dict(energy=float(s.energy.cpu()[0]), e_atom=s.e_atom.cpu().numpy().astype(np.float64),
+                forces=s.forces.cpu().numpy().astype(np.float64), perm=s.perm.cpu().numpy(),
+                sys=s)
+
+
+def _assert_ef(E, F, Eref, Fref, tag=""):
+    rel = abs(E - Eref) / abs(Eref)
+    dF = np.abs(F - Fref)
+    print("%s |dE|/|E|=%.2e max|dF|=%.2e max|F|=%.3f" % (tag, rel, dF.max(), np.abs(Fref).max()),
+          flush=True)
+    assert rel <= 1e-5, (E, Eref)
+    assert np.all(dF <= 1e-4 * (1 + np.abs(Fref))), dF.max()
+
+
+@pytest.mark.parametrize("wname", ["water648", "salt4k"])
+def test_energy_forces_full_oracle(T, oracle_mod, wname):
+    wl = W.load(wname)
+    w = W.make_weights(wl.model, WEIGHT_SEED[wname])
+    g = _run(T, wl, w)
+    nb = oracle_mod.build_neighbors(wl.box, wl.pos, wl.species, wl.model.r_cut, wl.skin)
+    ref = oracle_mod.energy_forces(wl.model, w, wl.box, nb["pos"].astype(np.float64),
+                                   nb["species"], nb["row_ptr"], nb["col_shift"])
+    _assert_ef(g["energy"], g["forces"], ref["energy"], ref["forces"], wname)
+    assert np.all(np.abs(g["e_atom"] - ref["e_atom"]) <= 1e-5 * (1 + np.abs(ref["e_atom"])))
+    assert abs(g["e_atom"].sum() - g["energy"]) <= 1e-6 * abs(g["energy"])
+
+
+def _golden(name):
+    path = os.path.join(GOLDEN, name + ".json")
+    if not os.path.exists(path):
+        pytest.skip("no stored oracle values for %s (run tests/golden/make_golden.py)" % name)
+    with open(path) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("wname", ["salt60k", "capsid39k"])
+def test_energy_forces_stored_oracle(T, wname):
+    from tests.golden.make_golden import digest
+    gold = _golden(wname)
+    wl = W.load(wname)
+    w = W.make_weights(wl.model, gold["weight_seed"])
+    assert digest(wl, w) == gold["digest"], "input generator changed since the values were stored"
+    g = _run(T, wl, w)
+    inv = np.empty(wl.n, np.int64)
+    inv[g["perm"]] = np.arange(wl.n)
+    slots = inv[np.array(gold["sample_ids"])]
+    _assert_ef(g["energy"], g["forces"][slots], gold["energy"], np.array(gold["forces"]), wname)
+    ea = np.array(gold["e_atom"])
+    assert np.all(np.abs(g["e_atom"][slots] - ea) <= 1e-5 * (1 + np.abs(ea)))
+    assert np.abs(g["forces"].sum(0)).max() <= 1e-4 * max(1.0, np.abs(g["forces"]).max()) * 10
+
+
+def test_energy_forces_salt500k_clusters(T):
+    from tests.golden.make_golden import digest
+    gold = _golden("salt500k")
+    wl = W.load("salt500k")
+    w = W.make_weights(wl.model, gold["weight_seed"])
+    assert digest(wl, w) == gold["digest"]
+    g = _run(T, wl, w)
+    inv = np.empty(wl.n, np.int64)
+    inv[g["perm"]] = np.arange(wl.n)
+    ea = np.array(gold["e_atom"])
+    got = g["e_atom"][inv[np.array(gold["e_ids"])]]
+    print("salt500k max|de_atom| %.2e" % np.abs(got - ea).max(), flush=True)
+    assert np.all(np.abs(got - ea) <= 1e-5 * (1 + np.abs(ea)))
+    fr = np.array(gold["forces"])
+    gf = g["forces"][inv[np.array(gold["f_ids"])]]
+    print("salt500k max|dF| %.2e" % np.abs(gf - fr).max(), flush=True)
+    assert np.all(np.abs(gf - fr) <= 1e-4 * (1 + np.abs(fr)))
+    # properties at full size: translation invariance (net force), per-atom sum
+    F = g["forces"]
+    assert np.abs(F.sum(0)).max() <= 1e-3
+    assert abs(g["e_atom"].sum() - g["energy"]) <= 1e-6 * abs(g["energy"])
+
+
+def test_repeatable_and_energy_only(T):
+    wl = W.load("salt4k")
+    w = W.make_weights(wl.model, 2002)
+    a = _run(T, wl, w)
+    b = _run(T, wl, w)
+    assert a["energy"] == b["energy"]
+    assert np.array_equal(a["forces"], b["forces"])
+    c = _run(T, wl, w, forces=False)
+    assert c["energy"] == a["energy"]
+
+
+def test_skin_edges_contribute_nothing(T):
+    """Pairs with r_c <= r < r_c+skin carry exactly zero: E and F from a skin-0 list equal
+    those from the skin-1 list bit for bit (same active edges in the same order)."""
+    wl = W.load("salt4k")
+    w = W.make_weights(wl.model, 2002)
+    a = _run(T, wl, w)
+    wl0 = W.Workload(wl.name, wl.box, wl.pos, wl.species, wl.species_names, wl.model, skin=0.0)
+    b = _run(T, wl0, w)
+    assert b["sys"].n_edges < a["sys"].n_edges
+    assert a["energy"] == b["energy"]
+    assert np.array_equal(a["forces"], b["forces"])
+
+
+def test_rotation_equivariance_isolated_cluster(T):
+    from scipy.spatial.transform import Rotation
+    wl = W.load("water648")
+    w = W.make_weights(wl.model, 2001)
+    L = 50.0
+    pos = wl.pos.astype(np.float64) - wl.pos.mean(0) + L / 2
+    base = W.Workload(wl.name, np.full(3, L, np.float32), pos.astype(np.float32), wl.species,
+                      wl.species_names, wl.model)
+    a = _run(T, base, w)
+    Fa = np.empty((wl.n, 3)); Fa[a["perm"]] = a["forces"]
+    R = Rotation.random(random_state=5).as_matrix()
+    pr = ((pos - L / 2) @ R.T + L / 2).astype(np.float32)
+    rot = W.Workload(wl.name, base.box, pr, wl.species, wl.species_names, wl.model)
+    b = _run(T, rot, w)
+    Fb = np.empty((wl.n, 3)); Fb[b["perm"]] = b["forces"]
+    assert abs(a["energy"] - b["energy"]) <= 1e-5 * abs(a["energy"])
+    assert np.abs(Fb - Fa @ R.T).max() <= 1e-4 * (1 + np.abs(Fa).max())
+
+
+def test_no_pairs_within_cutoff(T, oracle_mod):
+    """Atoms further apart than r_c + skin: only the embedding and the empty-message update
+    remain; compared with the oracle."""
+    wl = W.load("water648")
+    pos = np.array([[5, 5, 5], [15, 5, 5], [5, 15, 5], [5, 5, 15.0]], np.float32)
+    sp = np.array([0, 1, 1, 0], np.int32)
+    small = W.Workload("tiny", np.full(3, 30.0, np.float32), pos, sp, wl.species_names, wl.model)
+    w = W.make_weights(wl.model, 2001)
+    g = _run(T, small, w)
+    assert g["sys"].n_edges == 0
+    nb = oracle_mod.build_neighbors(small.box, pos, sp, 5.75, 1.0)
+    ref = oracle_mod.energy_forces(wl.model, w, small.box, nb["pos"].astype(np.float64),
+                                   nb["species"], nb["row_ptr"], nb["col_shift"])
+    assert abs(g["energy"] - ref["energy"]) <= 1e-5 * abs(ref["energy"])
+    assert np.all(g["forces"] == 0.0)

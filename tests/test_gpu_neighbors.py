@@ -1,0 +1,155 @@
+"""GPU parity of the rebuild (tess_build_neighbors) against the fp64 oracle: Hilbert keys,
+stable order, wrapped positions and the CSR bit for bit (pairs the oracle flags within 1e-5 A
+of r_c+skin excepted), reverse index validity, edge cases and error paths."""
+import numpy as np
+import pytest
+
+from molecular_dynamics_hilbert_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+RC, SKIN = 5.75, 1.0
+
+
+@pytest.fixture(scope="module")
+def T():
+    import torch
+    assert torch.cuda.is_available()
+    from molecular_dynamics_hilbert_amd import tess
+    tess.lib()
+    return tess
+
+
+def _gpu_rebuild(T, box, pos, species, vel=None, cap=None, rc=RC, skin=SKIN):
+    import torch
+    n = pos.shape[0]
+    dev = "cuda"
+    p = torch.from_numpy(np.ascontiguousarray(pos, np.float32)).to(dev)
+    s = torch.from_numpy(np.ascontiguousarray(species, np.int32)).to(dev)
+    v = None if vel is None else torch.from_numpy(np.ascontiguousarray(vel, np.float32)).to(dev)
+    ref = torch.empty_like(p)
+    perm = torch.empty(n, dtype=torch.int32, device=dev)
+    hkey = torch.empty(n, dtype=torch.int32, device=dev)
+    row_ptr = torch.empty(n + 1, dtype=torch.int32, device=dev)
+    if cap is None:
+        cap = 400 * max(n, 1)
+    col = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    rev = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    ws = T.workspace(None, n, cap)
+    st, ne = T.build_neighbors(box, rc, skin, p, s, perm, row_ptr, col, ws, vel=v, ref_pos=ref,
+                               hkey=hkey, rev=rev, check=False)
+    torch.cuda.synchronize()
+    out = dict(status=st, n_edges=ne, pos=p.cpu().numpy(), species=s.cpu().numpy(),
+               perm=perm.cpu().numpy(), hkey=hkey.cpu().numpy().view(np.uint32),
+               row_ptr=row_ptr.cpu().numpy(), col=col[:ne].cpu().numpy().view(np.uint32),
+               rev=rev[:ne].cpu().numpy(), ref=ref.cpu().numpy())
+    if v is not None:
+        out["vel"] = v.cpu().numpy()
+    return out
+
+
+def _strip_flagged(row_ptr, col, flagged):
+    """Remove flagged (i, j) pairs from a CSR (both directions)."""
+    keep_rows, keep_cols = [0], []
+    for i in range(len(row_ptr) - 1):
+        seg = col[row_ptr[i]:row_ptr[i + 1]]
+        js = (seg & 0x7FFFFFF).astype(np.int64)
+        mask = np.array([(min(i, j), max(i, j)) not in flagged for j in js], dtype=bool)
+        keep_cols.append(seg[mask])
+        keep_rows.append(keep_rows[-1] + int(mask.sum()))
+    return np.array(keep_rows), np.concatenate(keep_cols) if keep_cols else np.zeros(0, np.uint32)
+
+
+def _check_against_oracle(oracle_mod, box, pos, species, g, vel=None):
+    ref = oracle_mod.build_neighbors(box, pos, species, RC, SKIN)
+    wpos, keys = oracle_mod.wrap_keys(box, pos)
+    assert g["status"] == 0
+    assert np.array_equal(g["perm"], ref["perm"]), "stable Hilbert order"
+    assert np.array_equal(g["hkey"], ref["keys"]), "Hilbert keys"
+    assert np.array_equal(g["pos"], ref["pos"]), "wrapped positions"
+    assert np.array_equal(g["ref"], ref["pos"])
+    assert np.array_equal(g["species"], ref["species"])
+    if vel is not None:
+        assert np.array_equal(g["vel"], np.asarray(vel, np.float32)[ref["perm"]])
+    fi, fj = oracle_mod.flagged_pairs(box, ref["pos"], RC, SKIN, 1e-5)
+    flagged = {(min(a, b), max(a, b)) for a, b in zip(fi.tolist(), fj.tolist())}
+    if flagged:
+        r1, c1 = _strip_flagged(ref["row_ptr"], ref["col_shift"], flagged)
+        r2, c2 = _strip_flagged(g["row_ptr"], g["col"], flagged)
+    else:
+        r1, c1, r2, c2 = ref["row_ptr"], ref["col_shift"], g["row_ptr"], g["col"]
+    assert np.array_equal(r1, r2), "row pointers"
+    assert np.array_equal(c1, c2), "CSR entries"
+    # reverse index: (i <- j, s) maps to (j <- i, -s)
+    rp, col, rev = g["row_ptr"], g["col"], g["rev"]
+    rows = np.repeat(np.arange(len(rp) - 1), np.diff(rp))
+    assert np.all((col[rev] & 0x7FFFFFF) == rows)
+    assert np.all((col[rev] >> 27) == 26 - (col >> 27))
+    assert np.all(rev[rev] == np.arange(len(rev)))
+    return ref
+
+
+@pytest.mark.parametrize("wname", ["water648", "salt4k", "salt60k", "capsid39k", "salt500k"])
+def test_rebuild_matches_oracle(T, oracle_mod, wname):
+    wl = W.load(wname)
+    vel = W.maxwell_velocities(wl.species, wl.masses(), 300.0, 3000)
+    g = _gpu_rebuild(T, wl.box, wl.pos, wl.species, vel=vel)
+    print(wname, "pairs", g["n_edges"], flush=True)
+    _check_against_oracle(oracle_mod, wl.box, wl.pos, wl.species, g, vel=vel)
+
+
+@pytest.mark.parametrize("seed,n,L", [(10, 60, 13.6), (11, 150, 13.6), (12, 200, 20.5),
+                                      (13, 300, 27.1), (14, 40, 14.0), (15, 3000, 30.0)])
+def test_rebuild_tiny_and_ragged_boxes(T, oracle_mod, seed, n, L):
+    box, pos, sp = W.random_small_box(n, L, seed)
+    g = _gpu_rebuild(T, box, pos, sp)
+    _check_against_oracle(oracle_mod, box, pos, sp, g)
+
+
+def test_rebuild_repeatable_bit_for_bit(T):
+    wl = W.load("salt60k")
+    a = _gpu_rebuild(T, wl.box, wl.pos, wl.species)
+    b = _gpu_rebuild(T, wl.box, wl.pos, wl.species)
+    for k in ("perm", "hkey", "row_ptr", "col", "rev", "pos"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_rebuild_is_idempotent(T):
+    """Rebuilding already sorted, wrapped positions keeps the order (stable sort)."""
+    wl = W.load("salt4k")
+    a = _gpu_rebuild(T, wl.box, wl.pos, wl.species)
+    b = _gpu_rebuild(T, wl.box, a["pos"], a["species"])
+    assert np.array_equal(b["perm"], np.arange(wl.n))
+    assert np.array_equal(a["col"], b["col"])
+
+
+def test_edge_cases_empty_single_isolated(T, oracle_mod):
+    box = np.full(3, 40.0, np.float32)
+    g = _gpu_rebuild(T, box, np.zeros((0, 3), np.float32), np.zeros(0, np.int32), cap=16)
+    assert g["status"] == 0 and g["n_edges"] == 0 and g["row_ptr"][0] == 0
+    g = _gpu_rebuild(T, box, np.array([[1.0, 2.0, 3.0]], np.float32), np.zeros(1, np.int32), cap=16)
+    assert g["status"] == 0 and g["n_edges"] == 0 and list(g["row_ptr"]) == [0, 0]
+    # two atoms across the periodic boundary, and one pair exactly representable
+    pos = np.array([[0.1, 20.0, 20.0], [39.8, 20.0, 20.0], [10.0, 10.0, 10.0], [15.0, 10.0, 10.0]],
+                   np.float32)
+    g = _gpu_rebuild(T, box, pos, np.zeros(4, np.int32), cap=16)
+    _check_against_oracle(oracle_mod, box, pos, np.zeros(4, np.int32), g)
+    assert g["n_edges"] == 4
+
+
+def test_errors_capacity_box_row(T, oracle_mod):
+    wl = W.load("water648")
+    ref = oracle_mod.build_neighbors(wl.box, wl.pos, wl.species, RC, SKIN)
+    need = int(ref["row_ptr"][-1])
+    g = _gpu_rebuild(T, wl.box, wl.pos, wl.species, cap=need - 1)
+    assert g["status"] == T.ERR_CAPACITY and g["n_edges"] == need
+    assert np.array_equal(g["perm"], ref["perm"])  # ordering outputs stay valid
+    g = _gpu_rebuild(T, wl.box, wl.pos, wl.species, cap=need)
+    assert g["status"] == 0
+    small = np.full(3, 13.4, np.float32)
+    g = _gpu_rebuild(T, small, wl.pos[:50] % 13.4, wl.species[:50])
+    assert g["status"] == T.ERR_BOX
+    # far too dense: some atom has more than 1024 candidates
+    box, pos, sp = W.random_small_box(2600, 14.0, 3)
+    g = _gpu_rebuild(T, box, pos, sp, cap=4000000)
+    assert g["status"] == T.ERR_ROW

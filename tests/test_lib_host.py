@@ -1,0 +1,63 @@
+"""Host-side checks of libtess.so that need no GPU: it loads next to torch on one HIP runtime,
+exports every function include/tess.h declares, and rejects bad arguments, unsupported shapes,
+small boxes and small workspaces before enqueueing anything."""
+import ctypes as C
+import re
+
+import numpy as np
+import pytest
+
+from molecular_dynamics_hilbert_amd import workloads as W
+
+
+@pytest.fixture(scope="module")
+def T():
+    from molecular_dynamics_hilbert_amd import tess
+    tess.lib()
+    return tess
+
+
+def test_exports_every_declared_function(T):
+    names = T.header_functions()
+    assert {"tess_build_neighbors", "tess_energy_forces", "tess_md_steps"} <= set(names)
+    for nm in names:
+        assert hasattr(T.lib(), nm), nm
+
+
+def test_single_hip_runtime(T):
+    maps = open("/proc/self/maps").read()
+    paths = set(re.findall(r"(\S*libamdhip64\S*)", maps))
+    assert len(paths) == 1, paths
+
+
+def test_counts_and_status(T):
+    assert T.lib().tess_abi_version() == 1
+    for wl in (W.water648(), W.salt4k()):
+        assert T.weights_count(wl.model) == W.weight_count(wl.model)
+    assert T.weights_count(W.big_model()) == W.weight_count(W.big_model())
+    bad = W.ModelSpec(n_species=2, n_layers=1, channels=24, l_max=1, n_heads=1)
+    assert T.weights_count(bad) == -1
+    assert T.workspace_bytes(W.big_model(), 1000, 200000) > T.workspace_bytes(W.big_model(), 1000, 100000)
+    assert T.status_string(T.ERR_CAPACITY).startswith("neighbour list")
+
+
+def test_host_side_rejections(T):
+    L = T.lib()
+    fake = C.c_void_p(0x1000)  # never dereferenced: every call below fails host-side
+    ne = C.c_int64(0)
+    small = (C.c_float * 3)(13.0, 13.0, 13.0)
+    ok_box = (C.c_float * 3)(30.0, 30.0, 30.0)
+    assert L.tess_build_neighbors(10, small, 5.75, 1.0, fake, fake, None, None, fake, None, fake,
+                                  fake, None, 100, C.byref(ne), fake, 1 << 30, None) == T.ERR_BOX
+    assert L.tess_build_neighbors(10, ok_box, 5.75, 1.0, fake, fake, None, None, fake, None, fake,
+                                  fake, None, 100, C.byref(ne), fake, 16, None) == T.ERR_WORKSPACE
+    assert L.tess_build_neighbors(-1, ok_box, 5.75, 1.0, fake, fake, None, None, fake, None, fake,
+                                  fake, None, 100, C.byref(ne), fake, 1 << 30, None) == T.ERR_ARG
+    bad = T.desc(W.ModelSpec(n_species=2, n_layers=1, channels=24, l_max=1, n_heads=1))
+    e = L.tess_energy_forces(C.byref(bad), fake, 10, ok_box, fake, fake, fake, fake, None, 10,
+                             fake, None, None, fake, 1 << 40, None)
+    assert e == T.ERR_ARG
+    good = T.desc(W.water648().model)
+    e = L.tess_energy_forces(C.byref(good), fake, 10, ok_box, fake, fake, fake, fake, None, 10,
+                             fake, None, None, fake, 8, None)
+    assert e == T.ERR_WORKSPACE
