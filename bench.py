@@ -1,0 +1,214 @@
+"""Benchmark of the Tessera hot path on one MI355X.
+
+A step is one velocity-Verlet MD step of the whole path: energy + forces of the 4-layer
+l_max=2 model and the integrator, with the neighbour rebuild (Hilbert sort, cells, r_c+skin
+candidate list) every 20 steps, as tess_md_steps runs it. The workload is salt60k: 60,000
+atoms at 0.1 atoms/A^3 (one GPU's share of 30.7M atoms over 512 ranks), synthetic seeded
+positions and random-init weights. The timed call runs --steps MD steps from device-resident
+inputs.
+
+Output: one JSON line with the throughput (atom-steps/s), the rebuild and E+F times, the
+roofline position of the dominant kernel (HIP events around its launches, on the stream the
+library launches it on), and the fp64 oracle timed on the host cores on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "atom-steps/s (E+F, 4-layer l<=2) at 60K atoms on 1 GPU; neighbor rebuild ms"
+PEAK_FP32_VECTOR_TFLOPS = 157.3  # MI355X fp32 vector, 256 CUs x 2.4 GHz (packed issue)
+PEAK_HBM_GBS = 8000.0
+
+
+def edge_kernel_flops(spec, n_active: int) -> dict:
+    """Algorithmic fp32 flops (FMA = 2) of the edge kernels over one E+F pass, counting only
+    the defining contractions (lower-order per-edge terms are left out):
+      edge_apply : sum_e alpha A_e h_j  -> C*D*D MAC per edge (layer 0: C*D, only l=0 inputs)
+      edge_grad  : Abar^h = sum_c mbar (x) h_j -> C*D*D MAC per edge (layer 0: C*D)
+      edge_tapply: A_e^T mbar -> C*D*D MAC per edge (layers 1..T-1)
+      edge_prep  : radial MLP and its r-derivative 2*(K*R + P*R) MAC + logits C MAC per edge"""
+    C, T, K, R = spec.channels, spec.n_layers, spec.n_rbf, spec.radial_hidden
+    D = (spec.l_max + 1) ** 2
+    P = spec.n_paths
+    full, l0 = C * D * D, C * D
+    return {
+        "edge_apply": 2.0 * n_active * (l0 + (T - 1) * full),
+        "edge_grad": 2.0 * n_active * (l0 + (T - 1) * full),
+        "edge_tapply": 2.0 * n_active * (T - 1) * full,
+        "edge_prep": 2.0 * n_active * T * (2 * (K * R + P * R) + C),
+    }
+
+
+def cpu_baseline(n_sample: int = 8000) -> dict:
+    """The fp64 oracle on the host cores: one rebuild + one E+F on a bounded sample."""
+    import oracle
+    from molecular_dynamics_hilbert_amd import workloads as W
+    wl = W.salt_box(n_sample, 1103, W.big_model(), "salt%dk" % (n_sample // 1000))
+    w = W.make_weights(wl.model, 2003)
+    oracle.build()
+    t0 = time.perf_counter()
+    nb = oracle.build_neighbors(wl.box, wl.pos, wl.species, wl.model.r_cut, wl.skin)
+    t1 = time.perf_counter()
+    oracle.energy_forces(wl.model, w, wl.box, nb["pos"].astype(np.float64), nb["species"],
+                         nb["row_ptr"], nb["col_shift"])
+    t2 = time.perf_counter()
+    t_rb, t_ef = t1 - t0, t2 - t1
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": n_sample / (t_ef + t_rb / 20.0), "unit": "atom-steps/s", "cores": cores,
+            "kind": "oracle",
+            "sample": ("%d atoms at the salt60k density and species mix (periodic box %.2f A), "
+                       "same 4-layer 64-channel l_max=2 model; one rebuild (%.2f s) + one E+F "
+                       "(%.2f s) in fp64; atom-steps/s = N / (t_EF + t_rebuild/20)"
+                       % (n_sample, float(wl.box[0]), t_rb, t_ef))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="salt60k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (sharding is "
+              "described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from molecular_dynamics_hilbert_amd import tess as T
+    from molecular_dynamics_hilbert_amd import workloads as W
+
+    dev = "cuda"
+    wl = W.load(args.workload)
+    seed = {"salt60k": 2003, "capsid39k": 2004, "salt500k": 2005}.get(args.workload, 2003)
+    w = W.make_weights(wl.model, seed)
+    vel0 = W.maxwell_velocities(wl.species, wl.masses(), 300.0, 3003)
+    s = T.System(wl, w, vel=None)
+    vel = torch.from_numpy(vel0).to(dev)
+    masses = torch.from_numpy(wl.masses().astype(np.float32)).to(dev)
+    pa = torch.arange(wl.n, dtype=torch.int32, device=dev)
+    ep = torch.zeros(max(args.steps, args.warmup, 1), dtype=torch.float64, device=dev)
+    every = wl.rebuild_every
+
+    skin_flags = [0]
+
+    def md(nsteps, valid):
+        """Run nsteps as whole rebuild intervals (one tess_md_steps call per interval, each
+        starting with a rebuild). Random weights bind nothing, so at 300 K the fastest H atoms
+        can pass skin/2 inside an interval; the library then reports TESS_ERR_SKIN after
+        finishing it. Such intervals are counted, not aborted."""
+        done = 0
+        while done < nsteps:
+            k = min(every, nsteps - done)
+            st, _ = T.md_steps(s.spec, s.weights, s.box, s.r_cut, s.skin, s.pos, vel, s.species,
+                               masses, wl.dt_fs, k, every, pa, s.forces, s.row_ptr, s.col_shift,
+                               s.rev, s.ws, epot_trace=ep, forces_valid=valid or done > 0,
+                               check=False)
+            if st == T.ERR_SKIN:
+                skin_flags[0] += 1
+            elif st != T.OK:
+                raise T.TessError(st, "tess_md_steps")
+            done += k
+
+    # warmup (first call computes the initial forces)
+    md(max(args.warmup, 1), False)
+    torch.cuda.synchronize()
+    skin_flags[0] = 0
+    # timed region: exactly `steps` MD steps, inputs resident in HBM
+    T.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    md(args.steps, True)
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t0
+    kern = {k: T.timing_read(k) for k in ("edge_prep", "edge_apply", "edge_grad", "edge_tapply",
+                                          "node_gemm", "radix_scatter", "nbr_count", "nbr_fill")}
+    T.timing_enable(False)
+    value = wl.n * args.steps / t_total
+    ms_per_step = 1e3 * t_total / args.steps
+
+    # separate timings: rebuild alone and E+F alone (median of 5, HIP events on the stream)
+    st = torch.cuda.current_stream()
+    s.vel = None
+    rb, ef = [], []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        s.rebuild()  # synchronises once inside (pair count)
+        b.record(st)
+        torch.cuda.synchronize()
+        rb.append(a.elapsed_time(b))
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        s.energy_forces()
+        b.record(st)
+        torch.cuda.synchronize()
+        ef.append(a.elapsed_time(b))
+    # pairs inside r_cut (the edges the model works on), counted on the host from the CSR
+    rp = s.row_ptr.cpu().numpy()
+    n_cand = int(rp[-1])
+    n_active = _count_active(s, n_cand)
+
+    flops = edge_kernel_flops(wl.model, n_active)
+    ef_calls = args.steps  # E+F passes inside the timed region (forces were valid on entry)
+    rows = {}
+    for k, (ms, cnt) in kern.items():
+        if cnt:
+            rows[k] = {"launches": cnt, "avg_ms": ms / cnt, "total_ms": ms}
+    dom = max(("edge_apply", "edge_grad", "edge_tapply", "edge_prep"),
+              key=lambda k: kern[k][0])
+    dom_ms, dom_cnt = kern[dom]
+    dom_flops = flops[dom] * ef_calls
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else 0.0
+    roofline = {"kernel": dom, "bound": "alu", "achieved": round(achieved, 3),
+                "peak": PEAK_FP32_VECTOR_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_FP32_VECTOR_TFLOPS, 4), "traffic": None,
+                "avg_launch_ms": dom_ms / max(dom_cnt, 1), "launches": dom_cnt,
+                "flops_per_ef_pass": flops[dom]}
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "atom-steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "n_atoms": wl.n, "box_A": float(wl.box[0]),
+                   "layers": wl.model.n_layers, "channels": wl.model.channels,
+                   "l_max": wl.model.l_max, "heads": wl.model.n_heads,
+                   "rebuild_every": every, "dt_fs": wl.dt_fs, "pairs_r_c_plus_skin": n_cand,
+                   "pairs_r_c": n_active, "skin_flagged_intervals": skin_flags[0]},
+        "rebuild_ms": round(statistics.median(rb), 4),
+        "ef_ms": round(statistics.median(ef), 4),
+        "roofline": roofline,
+        "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in rows.items()},
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def _count_active(s, n_cand: int) -> int:
+    """Pairs with r < r_cut, counted from the device CSR with fp32 geometry (as the library)."""
+    pos = s.pos.cpu().numpy()
+    rp = s.row_ptr.cpu().numpy()
+    col = s.col_shift[:n_cand].cpu().numpy().view(np.uint32)
+    i = np.repeat(np.arange(s.n), np.diff(rp))
+    j = (col & 0x7FFFFFF).astype(np.int64)
+    code = (col >> 27).astype(np.int64)
+    sh = np.stack([code // 9 - 1, (code // 3) % 3 - 1, code % 3 - 1], 1).astype(np.float32)
+    r = (pos[j] - pos[i]) + sh * np.asarray(s.box, np.float32)
+    return int(((r * r).sum(1) < np.float32(s.r_cut) ** 2).sum())
+
+
+if __name__ == "__main__":
+    main()

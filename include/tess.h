@@ -15,9 +15,9 @@
  *  - Return value: a tess_status. Argument, box and workspace errors are detected on the host
  *    before anything is enqueued. TESS_ERR_HIP reports a failed HIP call (the stream state is
  *    then undefined).
- *  - Supported model shapes: channels in {16, 32, 64}, l_max in {1, 2}, n_heads dividing
- *    channels with channels/n_heads in {16, 32} or n_heads == 1, n_rbf == 8,
- *    radial_hidden in {32, 64}, n_species <= 16. Others return TESS_ERR_ARG.
+ *  - Supported model shapes (kernels are compiled per shape): n_rbf == 8, n_species <= 16,
+ *    n_layers <= 16 and (l_max, channels, n_heads, radial_hidden) one of (1, 16, 1, 32),
+ *    (1, 32, 4, 32), (2, 16, 4, 32), (2, 32, 4, 32), (2, 64, 4, 64). Others: TESS_ERR_ARG.
  *  - Limits: n_atoms < 2^27; at most 1024 candidate neighbours per atom.
  */
 #ifndef TESS_H
@@ -126,6 +126,16 @@ int32_t tess_md_steps(const tess_model_desc* desc, const float* weights, int32_t
                       int32_t* perm_accum, float* forces, double* epot_trace,
                       int32_t* row_ptr, uint32_t* col_shift, int32_t* rev, int64_t edge_cap,
                       int64_t* n_edges, void* workspace, int64_t ws_bytes, void* hip_stream);
+
+/* Optional kernel timing for benchmarks (not part of the method). tess_timing_enable(1)
+ * clears the counters and, until tess_timing_enable(0), records a pair of HIP events on the
+ * launching stream around each launch of the instrumented kernels ("edge_prep",
+ * "edge_apply", "edge_grad", "edge_tapply", "node_gemm", "radix_scatter", "nbr_count",
+ * "nbr_fill"). tess_timing_read waits for those events and returns the summed milliseconds
+ * and the launch count of one kernel. Host memory only; not thread-safe across concurrent
+ * calls on several streams. */
+int32_t tess_timing_enable(int32_t on);
+int32_t tess_timing_read(const char* kernel, double* total_ms, int64_t* launches);
 
 #ifdef __cplusplus
 }

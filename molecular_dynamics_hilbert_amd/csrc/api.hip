@@ -3,9 +3,47 @@
 #include <cmath>
 #include <cstring>
 
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
 #include "tess_common.h"
 
 namespace tess {
+
+// ---- optional per-kernel timing --------------------------------------------------------
+namespace {
+struct TimingState {
+  std::mutex mu;
+  bool on = false;
+  std::map<std::string, std::vector<std::pair<hipEvent_t, hipEvent_t>>> ev;
+  std::map<std::string, hipEvent_t> open;
+};
+TimingState& timing() {
+  static TimingState t;
+  return t;
+}
+}  // namespace
+
+bool timing_on() { return timing().on; }
+
+void timing_mark(const char* name, hipStream_t st, bool begin) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  hipEvent_t e;
+  if (hipEventCreate(&e) != hipSuccess) return;
+  hipEventRecord(e, st);
+  if (begin) {
+    t.open[name] = e;
+  } else {
+    auto it = t.open.find(name);
+    if (it == t.open.end()) { hipEventDestroy(e); return; }
+    t.ev[name].push_back({it->second, e});
+    t.open.erase(it);
+  }
+}
+
 namespace {
 
 constexpr float kAccelConv = 9.648533e-3f;  // eV/A/amu -> A/fs^2
@@ -89,6 +127,36 @@ using namespace tess;
 extern "C" {
 
 int32_t tess_abi_version(void) { return 1; }
+
+int32_t tess_timing_enable(int32_t on) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  for (auto& kv : t.ev)
+    for (auto& pr : kv.second) { hipEventDestroy(pr.first); hipEventDestroy(pr.second); }
+  t.ev.clear();
+  for (auto& kv : t.open) hipEventDestroy(kv.second);
+  t.open.clear();
+  t.on = on != 0;
+  return TESS_OK;
+}
+
+int32_t tess_timing_read(const char* kernel, double* total_ms, int64_t* launches) {
+  if (!kernel || !total_ms || !launches) return TESS_ERR_ARG;
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  *total_ms = 0.0;
+  *launches = 0;
+  auto it = t.ev.find(kernel);
+  if (it == t.ev.end()) return TESS_OK;
+  for (auto& pr : it->second) {
+    if (hipEventSynchronize(pr.second) != hipSuccess) return TESS_ERR_HIP;
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, pr.first, pr.second) != hipSuccess) return TESS_ERR_HIP;
+    *total_ms += ms;
+    *launches += 1;
+  }
+  return TESS_OK;
+}
 
 const char* tess_status_string(int32_t s) {
   switch (s) {

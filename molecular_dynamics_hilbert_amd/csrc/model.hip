@@ -125,7 +125,7 @@ hipError_t gemm(hipStream_t st, int64_t M, int K, int O, const float* X, RowMap 
                 const float* Wt, const Epi& ep) {
   if (M <= 0) return hipSuccess;
   dim3 g((unsigned)((M + 63) / 64), (unsigned)((O + 63) / 64));
-  k_gemm<EPI><<<g, 256, 0, st>>>(M, K, O, X, xm, Wt, ep);
+  TESS_TIMED("node_gemm", st, k_gemm<EPI><<<g, 256, 0, st>>>(M, K, O, X, xm, Wt, ep));
   return hipGetLastError();
 }
 
@@ -921,14 +921,18 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     e0.ym = RowMap{2 * C, 0, 0, 1};
     TESS_HIP_CHECK(gemm<EPI_STORE>(st, n, C, 2 * C, ht, feat0, w.WqkT + (int64_t)t * C * 2 * C, e0));
     if (cap > 0)
-      k_edge_prep<LMAX, C, H, R><<<gridn(cap, 256), 256, 0, st>>>(
-          w.arow + n, w.ageo, w.adst, w.asrc, lw[t].W1, lw[t].W2, qk, rc, ew, edw, es, cap);
+      TESS_TIMED("edge_prep", st,
+                 k_edge_prep<LMAX, C, H, R><<<gridn(cap, 256), 256, 0, st>>>(
+                     w.arow + n, w.ageo, w.adst, w.asrc, lw[t].W1, lw[t].W2, qk, rc, ew, edw, es,
+                     cap));
     if (t == 0)
-      k_edge_apply<LMAX, C, H, true><<<gridn(n, 4), 256, 0, st>>>(n, w.arow, w.ageo, w.asrc, ew,
-                                                                 es, ht, rc, mt, MZ);
+      TESS_TIMED("edge_apply", st,
+                 k_edge_apply<LMAX, C, H, true><<<gridn(n, 4), 256, 0, st>>>(
+                     n, w.arow, w.ageo, w.asrc, ew, es, ht, rc, mt, MZ));
     else
-      k_edge_apply<LMAX, C, H, false><<<gridn(n, 4), 256, 0, st>>>(n, w.arow, w.ageo, w.asrc, ew,
-                                                                  es, ht, rc, mt, MZ);
+      TESS_TIMED("edge_apply", st,
+                 k_edge_apply<LMAX, C, H, false><<<gridn(n, 4), 256, 0, st>>>(
+                     n, w.arow, w.ageo, w.asrc, ew, es, ht, rc, mt, MZ));
     TESS_HIP_CHECK(hipGetLastError());
     Epi eu{};
     eu.y = yg;
@@ -991,19 +995,22 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     k_dst<LMAX, C, H><<<gridn(n, 4), 256, 0, st>>>(n, w.mbar, mt, w.Dst);
     if (cap > 0) {
       if (t == 0)
-        k_edge_grad<LMAX, C, H, true><<<gridn(cap, 256), 256, 0, st>>>(
-            w.arow + n, w.ageo, w.adst, w.asrc, ew, edw, es, MZ, w.Dst, w.mbar, ht, rc, w.sbar,
-            w.gacc, t != T - 1, cap);
+        TESS_TIMED("edge_grad", st,
+                   k_edge_grad<LMAX, C, H, true><<<gridn(cap, 256), 256, 0, st>>>(
+                       w.arow + n, w.ageo, w.adst, w.asrc, ew, edw, es, MZ, w.Dst, w.mbar, ht, rc,
+                       w.sbar, w.gacc, t != T - 1, cap));
       else
-        k_edge_grad<LMAX, C, H, false><<<gridn(cap, 256), 256, 0, st>>>(
-            w.arow + n, w.ageo, w.adst, w.asrc, ew, edw, es, MZ, w.Dst, w.mbar, ht, rc, w.sbar,
-            w.gacc, t != T - 1, cap);
+        TESS_TIMED("edge_grad", st,
+                   k_edge_grad<LMAX, C, H, false><<<gridn(cap, 256), 256, 0, st>>>(
+                       w.arow + n, w.ageo, w.adst, w.asrc, ew, edw, es, MZ, w.Dst, w.mbar, ht, rc,
+                       w.sbar, w.gacc, t != T - 1, cap));
     }
     TESS_HIP_CHECK(hipGetLastError());
     if (t > 0) {
-      k_edge_tapply<LMAX, C, H><<<gridn(n, 4), 256, 0, st>>>(n, w.arow, w.ageo, w.asrc, w.arev, ew,
-                                                            es, MZ, w.sbar, w.mbar, qk, rc, hbar,
-                                                            w.qkbar);
+      TESS_TIMED("edge_tapply", st,
+                 k_edge_tapply<LMAX, C, H><<<gridn(n, 4), 256, 0, st>>>(
+                     n, w.arow, w.ageo, w.asrc, w.arev, ew, es, MZ, w.sbar, w.mbar, qk, rc, hbar,
+                     w.qkbar));
       Epi ea{};
       ea.y = hbar;
       ea.ym = feat0;

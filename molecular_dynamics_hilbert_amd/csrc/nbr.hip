@@ -480,8 +480,9 @@ int32_t build_neighbors_impl(int32_t n, const float box[3], float r_cut, float s
     int shift = 8 * pass;
     k_radix_hist<<<nblk, 256, 0, st>>>(ws.key[cur], n, shift, ws.hist, nblk);
     TESS_HIP_CHECK(scan_exclusive_i32(ws.hist, (int64_t)256 * nblk, ws.scan_tmp, st));
-    k_radix_scatter<<<nblk, 256, 0, st>>>(ws.key[cur], ws.idx[cur], ws.key[cur ^ 1],
-                                          ws.idx[cur ^ 1], n, shift, ws.hist, nblk);
+    TESS_TIMED("radix_scatter", st,
+               k_radix_scatter<<<nblk, 256, 0, st>>>(ws.key[cur], ws.idx[cur], ws.key[cur ^ 1],
+                                                     ws.idx[cur ^ 1], n, shift, ws.hist, nblk));
     TESS_HIP_CHECK(hipGetLastError());
     cur ^= 1;
   }
@@ -515,8 +516,9 @@ int32_t build_neighbors_impl(int32_t n, const float box[3], float r_cut, float s
   TESS_HIP_CHECK(hipGetLastError());
   // 4. pairs: count, scan, check, fill
   TESS_HIP_CHECK(hipMemsetAsync(row_ptr + n, 0, sizeof(int32_t), st));
-  k_pairs<false><<<n, 64, 0, st>>>(n, g, rcs2, pos, ws.cell_id, ws.cell_start, ws.cell_atoms,
-                                   row_ptr, nullptr, ws.misc);
+  TESS_TIMED("nbr_count", st,
+             k_pairs<false><<<n, 64, 0, st>>>(n, g, rcs2, pos, ws.cell_id, ws.cell_start,
+                                              ws.cell_atoms, row_ptr, nullptr, ws.misc));
   TESS_HIP_CHECK(hipGetLastError());
   TESS_HIP_CHECK(scan_exclusive_i32(row_ptr, (int64_t)n + 1, ws.scan_tmp, st));
   int32_t host[2] = {0, 0};
@@ -526,8 +528,9 @@ int32_t build_neighbors_impl(int32_t n, const float box[3], float r_cut, float s
   *n_edges = host[0];
   if (host[1] > kMaxRow) return TESS_ERR_ROW;
   if ((int64_t)host[0] > edge_cap) return TESS_ERR_CAPACITY;
-  k_pairs<true><<<n, 64, 0, st>>>(n, g, rcs2, pos, ws.cell_id, ws.cell_start, ws.cell_atoms,
-                                  row_ptr, col_shift, ws.misc);
+  TESS_TIMED("nbr_fill", st,
+             k_pairs<true><<<n, 64, 0, st>>>(n, g, rcs2, pos, ws.cell_id, ws.cell_start,
+                                             ws.cell_atoms, row_ptr, col_shift, ws.misc));
   TESS_HIP_CHECK(hipGetLastError());
   if (rev) {
     k_rev<<<grid(n, 4), 256, 0, st>>>(n, row_ptr, col_shift, rev);

@@ -291,3 +291,20 @@ int32_t ef_dispatch(const tess_model_desc& md, const float* weights, int32_t n, 
     hipError_t _e = (expr);                        \
     if (_e != hipSuccess) return TESS_ERR_HIP;     \
   } while (0)
+
+// Optional per-kernel timing (tess_timing_enable / tess_timing_read): HIP events recorded on
+// the launching stream around each instrumented launch.
+namespace tess {
+bool timing_on();
+void timing_mark(const char* name, hipStream_t st, bool begin);
+}  // namespace tess
+#define TESS_TIMED(name, st, ...)            \
+  do {                                       \
+    if (tess::timing_on()) {                 \
+      tess::timing_mark(name, st, true);     \
+      __VA_ARGS__;                           \
+      tess::timing_mark(name, st, false);    \
+    } else {                                 \
+      __VA_ARGS__;                           \
+    }                                        \
+  } while (0)

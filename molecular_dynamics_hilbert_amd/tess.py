@@ -60,8 +60,26 @@ def lib() -> C.CDLL:
         L.tess_md_steps.restype = i32
         L.tess_md_steps.argtypes = [p, p, i32, p, f32, f32, p, p, p, p, f32, i32, i32, i32, p, p,
                                     p, p, p, p, i64, p, p, i64, p]
+        L.tess_timing_enable.restype = i32
+        L.tess_timing_enable.argtypes = [i32]
+        L.tess_timing_read.restype = i32
+        L.tess_timing_read.argtypes = [C.c_char_p, p, p]
         _lib = L
     return _lib
+
+
+def timing_enable(on: bool) -> None:
+    lib().tess_timing_enable(1 if on else 0)
+
+
+def timing_read(kernel: str):
+    """(total_ms, launches) of an instrumented kernel since timing_enable(True)."""
+    ms = C.c_double(0.0)
+    cnt = C.c_int64(0)
+    st = lib().tess_timing_read(kernel.encode(), C.byref(ms), C.byref(cnt))
+    if st != OK:
+        raise TessError(st, "tess_timing_read")
+    return ms.value, cnt.value
 
 
 def header_functions() -> list:
