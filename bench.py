@@ -79,6 +79,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="salt60k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the benchmark, copy this many MiB device-to-device once (a plain "
+                         "copy kernel of known size, to scale HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (sharding is "
@@ -195,6 +198,13 @@ def main():
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(),
     }
     print(json.dumps(out), flush=True)
+    if args.copy_calibration_mib > 0:
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
 
 
 def _count_active(s, n_cand: int) -> int:

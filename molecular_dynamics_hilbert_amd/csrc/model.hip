@@ -277,7 +277,10 @@ __global__ void __launch_bounds__(256) k_edge_prep(const int32_t* __restrict__ a
                                                    float4* __restrict__ es, int64_t cap) {
   constexpr int P = Dims<LMAX>::P;
   constexpr int dh = C / H;
-  int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  // only the first ceil(n_active/256) blocks work; spread them evenly over the XCDs
+  const uint32_t nb_act = (uint32_t)((*arow_n + blockDim.x - 1) / blockDim.x);
+  if (blockIdx.x >= nb_act) return;
+  int64_t a = (int64_t)xcd_block(blockIdx.x, nb_act) * blockDim.x + threadIdx.x;
   if (a >= cap || a >= *arow_n) return;
   float4 g = ageo[a];
   RadialOut ro;
@@ -345,7 +348,7 @@ __global__ void __launch_bounds__(256) k_edge_apply(int32_t n, const int32_t* __
   __shared__ float sAl[4][kChunk][4];
   __shared__ int32_t sJ[4][kChunk];
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int32_t i = blockIdx.x * 4 + wv;
+  const int32_t i = xcd_block(blockIdx.x, gridDim.x) * 4 + wv;
   if (i >= n) return;
   const int32_t a0 = arow[i], a1 = arow[i + 1];
   // softmax statistics over the row (lane = edge)
@@ -573,7 +576,10 @@ __global__ void __launch_bounds__(256) k_edge_grad(const int32_t* __restrict__ a
   constexpr int DD = L0ONLY ? 1 : D;
   constexpr int P = Dims<LMAX>::P;
   constexpr int dh = C / H;
-  int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  // only the first ceil(n_active/256) blocks work; spread them evenly over the XCDs
+  const uint32_t nb_act = (uint32_t)((*arow_n + blockDim.x - 1) / blockDim.x);
+  if (blockIdx.x >= nb_act) return;
+  int64_t a = (int64_t)xcd_block(blockIdx.x, nb_act) * blockDim.x + threadIdx.x;
   if (a >= cap || a >= *arow_n) return;
   const int32_t i = adst[a], j = asrc[a];
   float4 g = ageo[a];
@@ -679,7 +685,7 @@ __global__ void __launch_bounds__(256) k_edge_tapply(int32_t n, const int32_t* _
   __shared__ float sSd[4][kChunk][4];  // sbar of a (destination role)
   __shared__ int32_t sJ[4][kChunk];
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int32_t x = blockIdx.x * 4 + wv;
+  const int32_t x = xcd_block(blockIdx.x, gridDim.x) * 4 + wv;
   if (x >= n) return;
   const int32_t a0 = arow[x], a1 = arow[x + 1];
   const int c = lane;

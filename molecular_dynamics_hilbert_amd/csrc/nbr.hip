@@ -291,10 +291,7 @@ __global__ void __launch_bounds__(64) k_pairs(int32_t n, CellGrid g, double rcs2
     count += __popcll(m);
   }
   if (!FILL) {
-    if (lane == 0) {
-      row_ptr[i] = count;
-      atomicMax(&misc[0], count);
-    }
+    if (lane == 0) row_ptr[i] = count;
     return;
   }
   if (count > kMaxRow) return;  // rejected on the host before this pass runs
@@ -319,6 +316,18 @@ __global__ void __launch_bounds__(64) k_pairs(int32_t n, CellGrid g, double rcs2
     uint32_t e = buf[k];
     col_shift[o + k] = (e >> 5) | ((e & 31u) << 27);
   }
+}
+
+// Longest row of a scanned CSR: block maxima, one atomic per block.
+__global__ void __launch_bounds__(256) k_max_row(int32_t n, const int32_t* __restrict__ row_ptr,
+                                                 int32_t* __restrict__ out) {
+  int32_t i = blockIdx.x * 256 + threadIdx.x;
+  int v = i < n ? row_ptr[i + 1] - row_ptr[i] : 0;
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+  __shared__ int32_t sh[4];
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) atomicMax(out, max(max(sh[0], sh[1]), max(sh[2], sh[3])));
 }
 
 // rev[e] for every pair of row i: position of (j <- i, 26 - code) in row j (rows are sorted
@@ -521,6 +530,8 @@ int32_t build_neighbors_impl(int32_t n, const float box[3], float r_cut, float s
                                               ws.cell_atoms, row_ptr, nullptr, ws.misc));
   TESS_HIP_CHECK(hipGetLastError());
   TESS_HIP_CHECK(scan_exclusive_i32(row_ptr, (int64_t)n + 1, ws.scan_tmp, st));
+  k_max_row<<<grid(n, 256), 256, 0, st>>>(n, row_ptr, ws.misc);
+  TESS_HIP_CHECK(hipGetLastError());
   int32_t host[2] = {0, 0};
   TESS_HIP_CHECK(hipMemcpyAsync(&host[0], row_ptr + n, sizeof(int32_t), hipMemcpyDeviceToHost, st));
   TESS_HIP_CHECK(hipMemcpyAsync(&host[1], ws.misc, sizeof(int32_t), hipMemcpyDeviceToHost, st));

@@ -209,6 +209,14 @@ __device__ __forceinline__ void coupling_matrix_vjp(const float* w, const float*
 }
 
 // ---- small device helpers ----------------------------------------------------------
+// Workgroups are dealt round-robin over the 8 XCDs (each with its own L2). Renumber them so
+// that XCD x works through one contiguous range of logical blocks: with Hilbert-ordered
+// atoms, neighbouring rows then share their gathered feature rows in that XCD's L2.
+__device__ __forceinline__ uint32_t xcd_block(uint32_t b, uint32_t nb) {
+  const uint32_t per = nb >> 3, rem = nb & 7u, x = b & 7u, idx = b >> 3;
+  return x < rem ? x * (per + 1) + idx : rem * (per + 1) + (x - rem) * per + idx;
+}
+
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
 __device__ __forceinline__ float wave_sum(float v) {

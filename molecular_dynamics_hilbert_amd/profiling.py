@@ -1,0 +1,95 @@
+"""Summaries of rocprofv3 CSV output (kernel statistics and FETCH_SIZE / WRITE_SIZE counters)
+for the profiles/ folder.
+
+HBM bytes of a kernel are taken from the TCC counters FETCH_SIZE and WRITE_SIZE (KiB per
+dispatch), each scaled by the ratio between the known byte count of a plain device copy and
+what the same counter reads for that copy in the same run.
+
+usage:
+  python -m molecular_dynamics_hilbert_amd.profiling stats <run_kernel_stats.csv>
+  python -m molecular_dynamics_hilbert_amd.profiling traffic <fetch.csv> <write.csv> <kernel>
+         <copy_MiB> <out.json>
+"""
+from __future__ import annotations
+
+import csv
+import hashlib
+import json
+import os
+import re
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def short_name(name: str) -> str:
+    n = re.sub(r"\(anonymous namespace\)::", "", name)
+    n = re.sub(r"^void ", "", n)
+    n = n.split("(")[0]
+    return n.replace("tess::", "")
+
+
+def kernel_stats_md(path: str, top: int = 20) -> str:
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    out = ["| kernel | calls | avg us | min us | max us | share % |", "|---|---:|---:|---:|---:|---:|"]
+    for r in rows[:top]:
+        out.append("| %s | %s | %.1f | %.1f | %.1f | %.2f |" % (
+            short_name(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3,
+            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    return "\n".join(out)
+
+
+def _counter_rows(path: str, counter: str):
+    return [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+
+
+def _per_dispatch(rows):
+    """Counter values summed per dispatch (a counter may be reported per XCD/instance)."""
+    acc = {}
+    for r in rows:
+        k = (r["Dispatch_Id"], r["Kernel_Name"])
+        acc[k] = acc.get(k, 0.0) + float(r["Counter_Value"])
+    return acc
+
+
+def traffic(fetch_csv: str, write_csv: str, kernel: str, copy_mib: int) -> dict:
+    """Bytes per launch of `kernel` (substring of the demangled name), scaled by the copy."""
+    res = {}
+    for label, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        d = _per_dispatch(_counter_rows(path, counter))
+        copies = [v for (i, n), v in d.items() if "copyBuffer" in n or "copy" in n.lower()]
+        copy_kib = max(copies) if copies else None
+        scale = (copy_mib * 1024.0) / copy_kib if copy_kib else 1.0
+        vals = [v for (i, n), v in d.items() if kernel in n]
+        res[label] = {"kib_per_launch_raw": sum(vals) / max(len(vals), 1), "launches": len(vals),
+                      "copy_kib_raw": copy_kib, "copy_scale": scale,
+                      "bytes_per_launch": 1024.0 * scale * sum(vals) / max(len(vals), 1)}
+    res["kernel"] = kernel
+    res["bytes_per_launch"] = res["fetch"]["bytes_per_launch"] + res["write"]["bytes_per_launch"]
+    return res
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(HERE, "csrc"))):
+        with open(os.path.join(HERE, "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def main(argv):
+    if argv[0] == "stats":
+        print(kernel_stats_md(argv[1]))
+    elif argv[0] == "traffic":
+        t = traffic(argv[1], argv[2], argv[3], int(argv[4]))
+        t["source_digest"] = source_digest()
+        with open(argv[5], "w") as f:
+            json.dump(t, f, indent=1)
+        print(json.dumps(t, indent=1))
+    else:
+        raise SystemExit(__doc__)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])
