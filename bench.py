@@ -178,7 +178,8 @@ def main():
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else 0.0
     roofline = {"kernel": dom, "bound": "alu", "achieved": round(achieved, 3),
                 "peak": PEAK_FP32_VECTOR_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_FP32_VECTOR_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_FP32_VECTOR_TFLOPS, 4),
+                "traffic": _traffic(dom, args.workload),
                 "avg_launch_ms": dom_ms / max(dom_cnt, 1), "launches": dom_cnt,
                 "flops_per_ef_pass": flops[dom]}
     out = {
@@ -205,6 +206,21 @@ def main():
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
+
+
+def _traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
+    (profiles/traffic_<kernel>_<workload>.json), or None when there is none or the kernel
+    sources changed since the counters were taken."""
+    from molecular_dynamics_hilbert_amd import profiling
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_digest") != profiling.source_digest():
+        return None
+    return round(t["bytes_per_launch"], 1)
 
 
 def _count_active(s, n_cand: int) -> int:

@@ -78,9 +78,55 @@ def source_digest() -> str:
     return h.hexdigest()
 
 
+def write_summaries(stats_csv: str, fetch_csv: str, write_csv: str, kernel_key: str,
+                    kernel_name: str, workload: str, copy_mib: int, commands: list,
+                    out_dir: str) -> None:
+    """profiles/<kernel>_<workload>.md (kernel statistics + counter traffic) and
+    profiles/traffic_<kernel>_<workload>.json (bytes per launch, source digest)."""
+    t = traffic(fetch_csv, write_csv, kernel_name, copy_mib)
+    t["source_digest"] = source_digest()
+    t["workload"] = workload
+    with open(os.path.join(out_dir, "traffic_%s_%s.json" % (kernel_key, workload)), "w") as f:
+        json.dump(t, f, indent=1)
+    md = ["# %s at %s: rocprofv3 summary" % (kernel_key, workload), "",
+          "Commands (run from the repository root):", ""]
+    md += ["    " + c for c in commands]
+    md += ["", "## Kernel statistics (--kernel-trace --stats)", "", kernel_stats_md(stats_csv), "",
+           "## HBM traffic of %s (FETCH_SIZE / WRITE_SIZE, copy-calibrated)" % kernel_key, "",
+           "| counter | raw KiB/launch | copy raw KiB (%d MiB copy) | scale | bytes/launch |" % copy_mib,
+           "|---|---:|---:|---:|---:|"]
+    for lab, cnt in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        r = t[lab]
+        md.append("| %s | %.1f | %.1f | %.4f | %.4g |" % (cnt, r["kib_per_launch_raw"],
+                                                        r["copy_kib_raw"] or 0, r["copy_scale"],
+                                                        r["bytes_per_launch"]))
+    rows = [r for r in csv.DictReader(open(stats_csv)) if kernel_name in r["Name"]]
+    calls = sum(int(r["Calls"]) for r in rows)
+    tot = sum(float(r["TotalDurationNs"]) for r in rows)
+    md += ["", "All launches matching `%s` (every layer): %d calls, average %.1f us." % (
+        kernel_name, calls, tot / max(calls, 1) / 1e3)]
+    md += ["", "Launches counted: %d. Source digest: %s." % (t["fetch"]["launches"],
+                                                             t["source_digest"])]
+    with open(os.path.join(out_dir, "%s_%s.md" % (kernel_key, workload)), "w") as f:
+        f.write("\n".join(md) + "\n")
+
+
 def main(argv):
     if argv[0] == "stats":
         print(kernel_stats_md(argv[1]))
+    elif argv[0] == "summarize":
+        # summarize <prof_dir> <pmc_fetch_dir> <pmc_write_dir> <kernel_key> <kernel_name> <workload> <copy_mib>
+        d, f, w, key, name, wl, mib = argv[1:8]
+        cmds = ["rocprofv3 --kernel-trace --stats -f csv -d %s -o run -- python bench.py --steps 20 "
+                "--warmup 20 --no-cpu-baseline" % d,
+                "rocprofv3 --pmc FETCH_SIZE -f csv -d %s -o run -- python bench.py --steps 1 "
+                "--warmup 1 --no-cpu-baseline --copy-calibration-mib %s" % (f, mib),
+                "rocprofv3 --pmc WRITE_SIZE -f csv -d %s -o run -- python bench.py --steps 1 "
+                "--warmup 1 --no-cpu-baseline --copy-calibration-mib %s" % (w, mib)]
+        write_summaries(os.path.join(d, "run_kernel_stats.csv"),
+                        os.path.join(f, "run_counter_collection.csv"),
+                        os.path.join(w, "run_counter_collection.csv"), key, name, wl, int(mib),
+                        cmds, os.path.join(os.path.dirname(HERE), "profiles"))
     elif argv[0] == "traffic":
         t = traffic(argv[1], argv[2], argv[3], int(argv[4]))
         t["source_digest"] = source_digest()
