@@ -324,119 +324,228 @@ __global__ void __launch_bounds__(256) k_edge_prep(const int32_t* __restrict__ a
 }
 
 // ---------------------------------------------------------------------------------------
-// Forward aggregation. One wave per destination row i; 4 rows per 256-thread block.
-//   M_h = max_e s_eh, Z_h = sum_e u_e exp(s_eh - M_h), alpha_eh = u_e exp(s_eh - M_h)/Z_h,
-//   m_i[d3][c] = sum_e alpha_e,h(c) sum_d1 A_e[d3][d1] h_j[d1][c].
-// Edges are processed in chunks of 32: lanes build alpha and A_e (lane = edge) into LDS,
-// then lane = channel accumulates. L0ONLY: only the l = 0 input component is non-zero.
+// Edge contraction on the matrix cores, one wave per row (4 rows per 256-thread block).
+//
+//   forward (TRANS = false), row = destination i, edges a = (i <- j):
+//     M_h = max_a s_ah, Z_h = sum_a u_a exp(s_ah - M_h), alpha_ah = u_a exp(s_ah - M_h)/Z_h,
+//     m_i[d3][c] = sum_a alpha_a,h(c) sum_d1 A_a[d3][d1] h_j[d1][c];
+//   adjoint (TRANS = true), row = x, edges a = (x <- y) with forward edge e' = rev(a) = (y <- x):
+//     hbar_x[d1][c] += alpha_e',h(c) sum_d3 A_e'[d3][d1] mbar_y[d3][c]   (A_e' uses Y(-n_a)),
+//     kbar_x[c] += sbar_e',h(c) q_y[c] / sqrt(d),  qbar_x[c] += sbar_a,h(c) k_y[c] / sqrt(d).
+//
+// Per edge the channel sum is a 16x16x4 fp32 MFMA per 16-channel tile and 4-component step:
+// A-operand (16 channels x 4 input components) = alpha * gathered features, B-operand
+// (4 input x 16 output components) = the edge's coupling matrix, read from LDS. Tile t holds
+// channels (C/16)*n + t, n = 0..15, so each lane loads its C/16 channels with one vector load
+// and stores C/16 contiguous channels at the end. Chunks of 32 edges: lanes first build
+// alpha and A_e (lane = edge) into LDS.
+// L0ONLY: only the l = 0 input component is non-zero (first layer).
 // ---------------------------------------------------------------------------------------
 constexpr int kChunk = 32;
 
-template <int LMAX, int C, int H, bool L0ONLY>
-__global__ void __launch_bounds__(256) k_edge_apply(int32_t n, const int32_t* __restrict__ arow,
-                                                    const float4* __restrict__ ageo,
-                                                    const int32_t* __restrict__ asrc,
-                                                    const float* __restrict__ ew,
-                                                    const float4* __restrict__ es,
-                                                    const float* __restrict__ h, float rc,
-                                                    float* __restrict__ m,
-                                                    float* __restrict__ MZ) {
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+template <int NT>
+struct VecT;
+template <> struct VecT<1> { typedef float T; };
+template <> struct VecT<2> { typedef float2 T; };
+template <> struct VecT<4> { typedef float4 T; };
+
+template <int NT>
+__device__ __forceinline__ void load_vec(const float* p, float* v) {
+  if constexpr (NT == 4) {
+    float4 x = *reinterpret_cast<const float4*>(p);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  } else if constexpr (NT == 2) {
+    float2 x = *reinterpret_cast<const float2*>(p);
+    v[0] = x.x; v[1] = x.y;
+  } else {
+    v[0] = p[0];
+  }
+}
+
+template <int LMAX, int C, int H, bool L0ONLY, bool TRANS>
+__global__ void __launch_bounds__(256) k_edge_contract(
+    int32_t n, const int32_t* __restrict__ arow, const float4* __restrict__ ageo,
+    const int32_t* __restrict__ asrc, const int32_t* __restrict__ arev,
+    const float* __restrict__ ew, const float4* __restrict__ es, const float* __restrict__ X,
+    float rc, float* __restrict__ out, float* __restrict__ MZ, const float4* __restrict__ sbar,
+    const float* __restrict__ qk, float* __restrict__ qkbar) {
   constexpr int D = Dims<LMAX>::D;
-  constexpr int DD = L0ONLY ? 1 : D;  // input components used
+  constexpr int DI = L0ONLY ? 1 : D;          // input components that can be non-zero
+  constexpr int KS = (DI + 3) / 4;            // 4-component MFMA steps
+  constexpr int NT = C / 16;                  // 16-channel tiles
   constexpr int dh = C / H;
-  __shared__ float sA[4][kChunk][D * DD];
+  static_assert(C % 16 == 0 && dh % NT == 0, "unsupported channel/head split");
+  __shared__ float sA[4][kChunk][D * D];
   __shared__ float sAl[4][kChunk][4];
+  __shared__ float sSs[4][TRANS ? kChunk : 1][4];
+  __shared__ float sSd[4][TRANS ? kChunk : 1][4];
   __shared__ int32_t sJ[4][kChunk];
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int32_t i = xcd_block(blockIdx.x, gridDim.x) * 4 + wv;
-  if (i >= n) return;
-  const int32_t a0 = arow[i], a1 = arow[i + 1];
-  // softmax statistics over the row (lane = edge)
-  float Mh[4], Zh[4];
+  const int g = lane >> 4, nn = lane & 15;  // MFMA lane coordinates
+  const int32_t x = xcd_block(blockIdx.x, gridDim.x) * 4 + wv;
+  if (x >= n) return;
+  const int32_t a0 = arow[x], a1 = arow[x + 1];
+  float Mh[4] = {0.0f, 0.0f, 0.0f, 0.0f}, Zh[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (!TRANS) {
+    // softmax statistics over the row (lane = edge)
 #pragma unroll
-  for (int hh = 0; hh < 4; hh++) { Mh[hh] = -INFINITY; Zh[hh] = 0.0f; }
-  for (int32_t a = a0 + lane; a < a1; a += 64) {
-    float4 s = es[a];
-    Mh[0] = fmaxf(Mh[0], s.x);
-    if (H > 1) { Mh[1] = fmaxf(Mh[1], s.y); Mh[2] = fmaxf(Mh[2], s.z); Mh[3] = fmaxf(Mh[3], s.w); }
-  }
+    for (int hh = 0; hh < 4; hh++) Mh[hh] = -INFINITY;
+    for (int32_t a = a0 + lane; a < a1; a += 64) {
+      float4 sv = es[a];
+      Mh[0] = fmaxf(Mh[0], sv.x);
+      if (H > 1) { Mh[1] = fmaxf(Mh[1], sv.y); Mh[2] = fmaxf(Mh[2], sv.z); Mh[3] = fmaxf(Mh[3], sv.w); }
+    }
 #pragma unroll
-  for (int hh = 0; hh < H; hh++) Mh[hh] = wave_max(Mh[hh]);
-  for (int32_t a = a0 + lane; a < a1; a += 64) {
-    float4 s = es[a];
-    float r = ageo[a].w;
-    float u = 0.5f * (__cosf(kPi * r / rc) + 1.0f);
-    Zh[0] += u * __expf(s.x - Mh[0]);
-    if (H > 1) {
-      Zh[1] += u * __expf(s.y - Mh[1]);
-      Zh[2] += u * __expf(s.z - Mh[2]);
-      Zh[3] += u * __expf(s.w - Mh[3]);
+    for (int hh = 0; hh < H; hh++) Mh[hh] = wave_max(Mh[hh]);
+    for (int32_t a = a0 + lane; a < a1; a += 64) {
+      float4 sv = es[a];
+      float u = 0.5f * (__cosf(kPi * ageo[a].w / rc) + 1.0f);
+      Zh[0] += u * __expf(sv.x - Mh[0]);
+      if (H > 1) {
+        Zh[1] += u * __expf(sv.y - Mh[1]);
+        Zh[2] += u * __expf(sv.z - Mh[2]);
+        Zh[3] += u * __expf(sv.w - Mh[3]);
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < H; hh++) Zh[hh] = wave_sum(Zh[hh]);
+    if (lane < H) {
+      MZ[(int64_t)x * 2 * H + lane] = a1 > a0 ? Mh[lane] : 0.0f;
+      MZ[(int64_t)x * 2 * H + H + lane] = Zh[lane];
     }
   }
+  floatx4 acc[NT];
 #pragma unroll
-  for (int hh = 0; hh < H; hh++) Zh[hh] = wave_sum(Zh[hh]);
-  if (lane < H) {
-    float mv = a1 > a0 ? Mh[lane] : 0.0f;
-    MZ[(int64_t)i * 2 * H + lane] = mv;
-    MZ[(int64_t)i * 2 * H + H + lane] = Zh[lane];
-  }
-  float acc[D];
-#pragma unroll
-  for (int d = 0; d < D; d++) acc[d] = 0.0f;
-  const int c = lane;
-  const int hc = (c < C ? c : 0) / dh;
+  for (int t = 0; t < NT; t++) acc[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  const int hl = (NT * nn) / dh;  // head of this lane's A-operand channels
+  float qacc = 0.0f, kacc = 0.0f;
+  const int hc = (lane < C ? lane : 0) / dh;  // head of channel `lane` (q/k adjoints)
   for (int32_t b = a0; b < a1; b += kChunk) {
     const int cnt = min(kChunk, a1 - b);
     if (lane < cnt) {
-      int32_t a = b + lane;
-      float4 g = ageo[a];
-      float4 s = es[a];
-      float u = 0.5f * (__cosf(kPi * g.w / rc) + 1.0f);
-      float sv[4] = {s.x, s.y, s.z, s.w};
+      const int32_t a = b + lane;
+      const int32_t y = asrc[a];
+      float4 geo = ageo[a];
+      float u = 0.5f * (__cosf(kPi * geo.w / rc) + 1.0f);
+      float sv[4];
+      if (!TRANS) {
+        float4 s4 = es[a];
+        sv[0] = s4.x; sv[1] = s4.y; sv[2] = s4.z; sv[3] = s4.w;
 #pragma unroll
-      for (int hh = 0; hh < 4; hh++)
-        sAl[wv][lane][hh] = (hh < H && Zh[hh] > 0.0f) ? u * __expf(sv[hh] - Mh[hh]) / Zh[hh] : 0.0f;
-      float ir = 1.0f / g.w;
+        for (int hh = 0; hh < 4; hh++)
+          sAl[wv][lane][hh] = (hh < H && Zh[hh] > 0.0f) ? u * __expf(sv[hh] - Mh[hh]) / Zh[hh] : 0.0f;
+      } else {
+        const int32_t ep = arev[a];
+        float4 s4 = es[ep];
+        sv[0] = s4.x; sv[1] = s4.y; sv[2] = s4.z; sv[3] = s4.w;
+        float4 sbs = sbar[ep], sbd = sbar[a];
+        const float sbsv[4] = {sbs.x, sbs.y, sbs.z, sbs.w}, sbdv[4] = {sbd.x, sbd.y, sbd.z, sbd.w};
+#pragma unroll
+        for (int hh = 0; hh < 4; hh++) {
+          float Zy = hh < H ? MZ[(int64_t)y * 2 * H + H + hh] : 0.0f;
+          float My = hh < H ? MZ[(int64_t)y * 2 * H + hh] : 0.0f;
+          sAl[wv][lane][hh] = (hh < H && Zy > 0.0f) ? u * __expf(sv[hh] - My) / Zy : 0.0f;
+          sSs[wv][TRANS ? lane : 0][hh] = sbsv[hh];
+          sSd[wv][TRANS ? lane : 0][hh] = sbdv[hh];
+        }
+      }
+      const float ir = 1.0f / geo.w;
+      const float sg = TRANS ? -1.0f : 1.0f;
       float Y[9];
-      sph<LMAX>(g.x * ir, g.y * ir, g.z * ir, Y);
+      sph<LMAX>(sg * geo.x * ir, sg * geo.y * ir, sg * geo.z * ir, Y);
       float w[Dims<LMAX>::P];
 #pragma unroll
       for (int p = 0; p < Dims<LMAX>::P; p++) w[p] = ew[(int64_t)a * 12 + p];
       float A[D * D];
       coupling_matrix<LMAX>(w, Y, A);
+      // row o of the LDS copy lists the coupling of output component o to every input
+      // component: A itself (forward) or its transpose (adjoint)
 #pragma unroll
-      for (int d3 = 0; d3 < D; d3++)
+      for (int o = 0; o < D; o++)
 #pragma unroll
-        for (int d1 = 0; d1 < DD; d1++) sA[wv][lane][d3 * DD + d1] = A[d3 * D + d1];
-      sJ[wv][lane] = asrc[a];
+        for (int k = 0; k < D; k++) sA[wv][lane][o * D + k] = TRANS ? A[k * D + o] : A[o * D + k];
+      sJ[wv][lane] = y;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    if (c < C) {
-      for (int e = 0; e < cnt; e++) {
-        const float* hj = h + (int64_t)sJ[wv][e] * D * C + c;
-        float hv[DD];
+    // Groups of 4 edges: lane group g takes edge 4E + g; MFMA step k contracts input
+    // component k of those 4 edges. A lane fetches its edge's DI feature slices and DI
+    // coupling values per group; the next group is fetched before this group's MFMAs.
+    const int ngroups = (cnt + 3) >> 2;
+    float xv[DI][NT], bv[DI], al;
+    auto fetch = [&](int E, float (*xo)[NT], float* bo, float& ao) {
+      const int e = 4 * E + g;
+      if (e < cnt) {
+        ao = sAl[wv][e][hl];
+        const float* Xy = X + (int64_t)sJ[wv][e] * D * C + NT * nn;
 #pragma unroll
-        for (int d1 = 0; d1 < DD; d1++) hv[d1] = hj[d1 * C];
-        const float al = sAl[wv][e][hc];
-        const float* Ae = sA[wv][e];
+        for (int k = 0; k < DI; k++) load_vec<NT>(Xy + k * C, xo[k]);
+        const float* Ae = sA[wv][e] + (nn < D ? nn : 0) * D;
 #pragma unroll
-        for (int d3 = 0; d3 < D; d3++) {
-          float t = 0.0f;
+        for (int k = 0; k < DI; k++) bo[k] = nn < D ? Ae[k] : 0.0f;
+      } else {
+        ao = 0.0f;
 #pragma unroll
-          for (int d1 = 0; d1 < DD; d1++) t += Ae[d3 * DD + d1] * hv[d1];
-          acc[d3] += al * t;
+        for (int k = 0; k < DI; k++) {
+          bo[k] = 0.0f;
+#pragma unroll
+          for (int t = 0; t < NT; t++) xo[k][t] = 0.0f;
         }
+      }
+    };
+    fetch(0, xv, bv, al);
+    for (int E = 0; E < ngroups; E++) {
+      float xn[DI][NT], bn[DI], an;
+      fetch(E + 1, xn, bn, an);
+#pragma unroll
+      for (int k = 0; k < DI; k++)
+#pragma unroll
+        for (int t = 0; t < NT; t++)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(al * xv[k][t], bv[k], acc[t], 0, 0, 0);
+#pragma unroll
+      for (int k = 0; k < DI; k++) {
+        bv[k] = bn[k];
+#pragma unroll
+        for (int t = 0; t < NT; t++) xv[k][t] = xn[k][t];
+      }
+      al = an;
+    }
+    if (TRANS && lane < C) {
+      for (int e = 0; e < cnt; e++) {
+        const int32_t y = sJ[wv][e];
+        kacc += sSs[wv][TRANS ? e : 0][hc] * qk[(int64_t)y * 2 * C + lane];
+        qacc += sSd[wv][TRANS ? e : 0][hc] * qk[(int64_t)y * 2 * C + C + lane];
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   }
-  if (c < C) {
+  // lane (g, nn) holds output component nn for channels NT*(4g + r) + t, r = 0..3
+  if (nn < D) {
+    float* o = out + (int64_t)x * D * C + nn * C;
 #pragma unroll
-    for (int d = 0; d < D; d++) m[(int64_t)i * D * C + d * C + c] = acc[d];
+    for (int r = 0; r < 4; r++) {
+      float v[NT];
+#pragma unroll
+      for (int t = 0; t < NT; t++) v[t] = acc[t][r];
+      float* dst = o + NT * (4 * g + r);
+      if (!TRANS) {
+#pragma unroll
+        for (int t = 0; t < NT; t++) dst[t] = v[t];
+      } else {
+#pragma unroll
+        for (int t = 0; t < NT; t++) dst[t] += v[t];
+      }
+    }
+  }
+  if (TRANS && lane < C) {
+    const float isd = rsqrtf((float)dh);
+    qkbar[(int64_t)x * 2 * C + lane] = qacc * isd;
+    qkbar[(int64_t)x * 2 * C + C + lane] = kacc * isd;
   }
 }
 
@@ -656,112 +765,6 @@ __global__ void __launch_bounds__(256) k_edge_grad(const int32_t* __restrict__ a
   sbar[a] = make_float4(sb[0], sb[1], sb[2], sb[3]);
 }
 
-// ---------------------------------------------------------------------------------------
-// Row-wise adjoints, one wave per atom x (lane = channel). For each active edge a = (x <- y):
-//   source role of x in the forward edge e' = rev(a) = (y <- x):
-//     hbar_x[d1][c] += alpha_e',h(c) sum_d3 A_e'[d3][d1] mbar_y[d3][c],
-//     kbar_x[c]     += sbar_e',h(c) q_y[c] / sqrt(d);
-//   destination role in a itself: qbar_x[c] += sbar_a,h(c) k_y[c] / sqrt(d).
-// A_e' uses the same radial weights as a (same |r|) and Y(-n).
-// ---------------------------------------------------------------------------------------
-template <int LMAX, int C, int H>
-__global__ void __launch_bounds__(256) k_edge_tapply(int32_t n, const int32_t* __restrict__ arow,
-                                                     const float4* __restrict__ ageo,
-                                                     const int32_t* __restrict__ asrc,
-                                                     const int32_t* __restrict__ arev,
-                                                     const float* __restrict__ ew,
-                                                     const float4* __restrict__ es,
-                                                     const float* __restrict__ MZ,
-                                                     const float4* __restrict__ sbar,
-                                                     const float* __restrict__ mbar,
-                                                     const float* __restrict__ qk, float rc,
-                                                     float* __restrict__ hbar,
-                                                     float* __restrict__ qkbar) {
-  constexpr int D = Dims<LMAX>::D;
-  constexpr int dh = C / H;
-  __shared__ float sA[4][kChunk][D * D];
-  __shared__ float sAl[4][kChunk][4];
-  __shared__ float sSs[4][kChunk][4];  // sbar of e' (source role)
-  __shared__ float sSd[4][kChunk][4];  // sbar of a (destination role)
-  __shared__ int32_t sJ[4][kChunk];
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int32_t x = xcd_block(blockIdx.x, gridDim.x) * 4 + wv;
-  if (x >= n) return;
-  const int32_t a0 = arow[x], a1 = arow[x + 1];
-  const int c = lane;
-  const int hc = (c < C ? c : 0) / dh;
-  float acc[D];
-#pragma unroll
-  for (int d = 0; d < D; d++) acc[d] = 0.0f;
-  float qacc = 0.0f, kacc = 0.0f;
-  for (int32_t b = a0; b < a1; b += kChunk) {
-    const int cnt = min(kChunk, a1 - b);
-    if (lane < cnt) {
-      int32_t a = b + lane;
-      int32_t y = asrc[a];
-      int32_t ep = arev[a];
-      float4 g = ageo[a];
-      float u = 0.5f * (__cosf(kPi * g.w / rc) + 1.0f);
-      float4 s = es[ep];
-      float sv[4] = {s.x, s.y, s.z, s.w};
-      float4 sbs = sbar[ep], sbd = sbar[a];
-      float sbsv[4] = {sbs.x, sbs.y, sbs.z, sbs.w}, sbdv[4] = {sbd.x, sbd.y, sbd.z, sbd.w};
-#pragma unroll
-      for (int hh = 0; hh < 4; hh++) {
-        float Zy = hh < H ? MZ[(int64_t)y * 2 * H + H + hh] : 0.0f;
-        float My = hh < H ? MZ[(int64_t)y * 2 * H + hh] : 0.0f;
-        sAl[wv][lane][hh] = (hh < H && Zy > 0.0f) ? u * __expf(sv[hh] - My) / Zy : 0.0f;
-        sSs[wv][lane][hh] = sbsv[hh];
-        sSd[wv][lane][hh] = sbdv[hh];
-      }
-      float ir = 1.0f / g.w;
-      float Y[9];
-      sph<LMAX>(-g.x * ir, -g.y * ir, -g.z * ir, Y);
-      float w[Dims<LMAX>::P];
-#pragma unroll
-      for (int p = 0; p < Dims<LMAX>::P; p++) w[p] = ew[(int64_t)a * 12 + p];
-      float A[D * D];
-      coupling_matrix<LMAX>(w, Y, A);
-#pragma unroll
-      for (int k = 0; k < D * D; k++) sA[wv][lane][k] = A[k];
-      sJ[wv][lane] = y;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    if (c < C) {
-      for (int e = 0; e < cnt; e++) {
-        const int32_t y = sJ[wv][e];
-        const float* mby = mbar + (int64_t)y * D * C + c;
-        float mv[D];
-#pragma unroll
-        for (int d = 0; d < D; d++) mv[d] = mby[d * C];
-        const float al = sAl[wv][e][hc];
-        const float* Ae = sA[wv][e];
-#pragma unroll
-        for (int d1 = 0; d1 < D; d1++) {
-          float t = 0.0f;
-#pragma unroll
-          for (int d3 = 0; d3 < D; d3++) t += Ae[d3 * D + d1] * mv[d3];
-          acc[d1] += al * t;
-        }
-        kacc += sSs[wv][e][hc] * qk[(int64_t)y * 2 * C + c];
-        qacc += sSd[wv][e][hc] * qk[(int64_t)y * 2 * C + C + c];
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  }
-  if (c < C) {
-#pragma unroll
-    for (int d = 0; d < D; d++) hbar[(int64_t)x * D * C + d * C + c] += acc[d];
-    const float isd = rsqrtf((float)dh);
-    qkbar[(int64_t)x * 2 * C + c] = qacc * isd;
-    qkbar[(int64_t)x * 2 * C + C + c] = kacc * isd;
-  }
-}
-
 // F_x = sum over the active edges a of row x of (g_a - g_rev(a)), g = dE/dr_vec.
 __global__ void k_forces(int32_t n, const int32_t* __restrict__ arow, const int32_t* __restrict__ arev,
                          const float* __restrict__ gacc, float* __restrict__ F) {
@@ -933,12 +936,14 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
                      cap));
     if (t == 0)
       TESS_TIMED("edge_apply", st,
-                 k_edge_apply<LMAX, C, H, true><<<gridn(n, 4), 256, 0, st>>>(
-                     n, w.arow, w.ageo, w.asrc, ew, es, ht, rc, mt, MZ));
+                 k_edge_contract<LMAX, C, H, true, false><<<gridn(n, 4), 256, 0, st>>>(
+                     n, w.arow, w.ageo, w.asrc, w.arev, ew, es, ht, rc, mt, MZ, nullptr, nullptr,
+                     nullptr));
     else
       TESS_TIMED("edge_apply", st,
-                 k_edge_apply<LMAX, C, H, false><<<gridn(n, 4), 256, 0, st>>>(
-                     n, w.arow, w.ageo, w.asrc, ew, es, ht, rc, mt, MZ));
+                 k_edge_contract<LMAX, C, H, false, false><<<gridn(n, 4), 256, 0, st>>>(
+                     n, w.arow, w.ageo, w.asrc, w.arev, ew, es, ht, rc, mt, MZ, nullptr, nullptr,
+                     nullptr));
     TESS_HIP_CHECK(hipGetLastError());
     Epi eu{};
     eu.y = yg;
@@ -1014,9 +1019,9 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     TESS_HIP_CHECK(hipGetLastError());
     if (t > 0) {
       TESS_TIMED("edge_tapply", st,
-                 k_edge_tapply<LMAX, C, H><<<gridn(n, 4), 256, 0, st>>>(
-                     n, w.arow, w.ageo, w.asrc, w.arev, ew, es, MZ, w.sbar, w.mbar, qk, rc, hbar,
-                     w.qkbar));
+                 k_edge_contract<LMAX, C, H, false, true><<<gridn(n, 4), 256, 0, st>>>(
+                     n, w.arow, w.ageo, w.asrc, w.arev, ew, es, w.mbar, rc, hbar,
+                     const_cast<float*>(MZ), w.sbar, qk, w.qkbar));
       Epi ea{};
       ea.y = hbar;
       ea.ym = feat0;
