@@ -56,66 +56,76 @@ struct Epi {
   int32_t gstride, goff, cdim;
 };
 
-template <int EPI>
-__global__ void __launch_bounds__(256) k_gemm(int64_t M, int K, int O, const float* __restrict__ X,
+// Block tile 128 rows x 64 columns, 4 waves of 32 x 64 (two 32x32 MFMA tiles each). The
+// block's K x 64 slice of Wt is staged in LDS once. Each lane loads its row of X with float4
+// loads: lanes 0-31 take k = 8s..8s+3 and lanes 32-63 k = 8s+4..8s+7, so MFMA step (s, q)
+// pairs k = 8s+q (first half-wave) with k = 8s+4+q (second half-wave), and the B operand
+// uses the same pairing. K must be a multiple of 8 and at most kGemmMaxK.
+constexpr int kGemmMaxK = 192;
+
+template <int EPI, int K>
+__global__ void __launch_bounds__(256) k_gemm(int64_t M, int O, const float* __restrict__ X,
                                               RowMap xm, const float* __restrict__ Wt, Epi ep) {
-  __shared__ float Xs[64][33];
-  __shared__ float Ws[32][65];
+  __shared__ float Ws[K][64 + 1];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int wr = w >> 1, wc = w & 1;
-  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  const int64_t r0 = (int64_t)blockIdx.x * 128 + w * 32;
   const int o0 = blockIdx.y * 64;
-  floatx16 acc;
+  for (int k = t; k < K * 64; k += 256) {
+    const int kk = k >> 6, oo = k & 63;
+    Ws[kk][oo] = (o0 + oo < O) ? Wt[(int64_t)kk * O + o0 + oo] : 0.0f;
+  }
+  const int64_t row = r0 + (lane & 31);
+  const bool row_ok = row < M;
+  const int kh = (lane >> 5) * 4;
+  float4 xa[K / 8];
+  if (row_ok) {
+    const float* xr = X + row_off(xm, row);
 #pragma unroll
-  for (int v = 0; v < 16; v++) acc[v] = 0.0f;
-  // per-thread load assignment
-  const int xr = t >> 2, xk = (t & 3) * 8;      // X tile: 64 rows x 32 k
-  const int wk = t >> 3, wo = (t & 7) * 8;      // W tile: 32 k x 64 cols
-  const int64_t xrow = r0 + xr;
-  const bool xrow_ok = xrow < M;
-  const int64_t xbase = xrow_ok ? row_off(xm, xrow) : 0;
-  for (int k0 = 0; k0 < K; k0 += 32) {
+    for (int s8 = 0; s8 < K / 8; s8++) xa[s8] = *reinterpret_cast<const float4*>(xr + 8 * s8 + kh);
+  } else {
 #pragma unroll
-    for (int q = 0; q < 8; q++) {
-      int k = k0 + xk + q;
-      Xs[xr][xk + q] = (xrow_ok && k < K) ? X[xbase + k] : 0.0f;
+    for (int s8 = 0; s8 < K / 8; s8++) xa[s8] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  }
+  __syncthreads();
+  floatx16 acc0, acc1;
+#pragma unroll
+  for (int v = 0; v < 16; v++) { acc0[v] = 0.0f; acc1[v] = 0.0f; }
+  const int col = lane & 31;
+#pragma unroll
+  for (int s8 = 0; s8 < K / 8; s8++) {
+    const float av[4] = {xa[s8].x, xa[s8].y, xa[s8].z, xa[s8].w};
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const int k = 8 * s8 + q + kh;
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av[q], Ws[k][col], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av[q], Ws[k][32 + col], acc1, 0, 0, 0);
     }
-#pragma unroll
-    for (int q = 0; q < 8; q++) {
-      int k = k0 + wk, o = o0 + wo + q;
-      Ws[wk][wo + q] = (k < K && o < O) ? Wt[(int64_t)k * O + o] : 0.0f;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 32; kk += 2) {
-      float a = Xs[wr * 32 + (lane & 31)][kk + (lane >> 5)];
-      float b = Ws[kk + (lane >> 5)][wc * 32 + (lane & 31)];
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
-    }
-    __syncthreads();
   }
 #pragma unroll
-  for (int v = 0; v < 16; v++) {
-    int64_t r = r0 + wr * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-    int o = o0 + wc * 32 + (lane & 31);
-    if (r >= M || o >= O) continue;
-    float val = acc[v];
-    if (EPI == EPI_STORE) {
-      ep.y[row_off(ep.ym, r) + o] = val;
-    } else if (EPI == EPI_ADD) {
-      ep.y[row_off(ep.ym, r) + o] += val;
-    } else if (EPI == EPI_UPD0) {
-      ep.y[row_off(ep.ym, r) + o] = val;
-      if (o < ep.cdim) {
-        int64_t hb = row_off(ep.hm, r) + o;
-        ep.hout[hb] = ep.hin[hb] + val * sigmoidf_(val);
+  for (int nt = 0; nt < 2; nt++) {
+#pragma unroll
+    for (int v = 0; v < 16; v++) {
+      const int64_t r = r0 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+      const int o = o0 + 32 * nt + col;
+      if (r >= M || o >= O) continue;
+      const float val = nt == 0 ? acc0[v] : acc1[v];
+      if (EPI == EPI_STORE) {
+        ep.y[row_off(ep.ym, r) + o] = val;
+      } else if (EPI == EPI_ADD) {
+        ep.y[row_off(ep.ym, r) + o] += val;
+      } else if (EPI == EPI_UPD0) {
+        ep.y[row_off(ep.ym, r) + o] = val;
+        if (o < ep.cdim) {
+          const int64_t hb = row_off(ep.hm, r) + o;
+          ep.hout[hb] = ep.hin[hb] + val * sigmoidf_(val);
+        }
+      } else {  // EPI_UPDL
+        ep.y[row_off(ep.ym, r) + o] = val;
+        const int64_t nd = r / ep.hm.rpn;
+        const float g = ep.gates[nd * ep.gstride + ep.goff + o];
+        const int64_t hb = row_off(ep.hm, r) + o;
+        ep.hout[hb] = ep.hin[hb] + sigmoidf_(g) * val;
       }
-    } else {  // EPI_UPDL
-      ep.y[row_off(ep.ym, r) + o] = val;
-      int64_t n = r / ep.hm.rpn;
-      float g = ep.gates[n * ep.gstride + ep.goff + o];
-      int64_t hb = row_off(ep.hm, r) + o;
-      ep.hout[hb] = ep.hin[hb] + sigmoidf_(g) * val;
     }
   }
 }
@@ -124,8 +134,17 @@ template <int EPI>
 hipError_t gemm(hipStream_t st, int64_t M, int K, int O, const float* X, RowMap xm,
                 const float* Wt, const Epi& ep) {
   if (M <= 0) return hipSuccess;
-  dim3 g((unsigned)((M + 63) / 64), (unsigned)((O + 63) / 64));
-  TESS_TIMED("node_gemm", st, k_gemm<EPI><<<g, 256, 0, st>>>(M, K, O, X, xm, Wt, ep));
+  dim3 g((unsigned)((M + 127) / 128), (unsigned)((O + 63) / 64));
+  switch (K) {
+    case 16: TESS_TIMED("node_gemm", st, k_gemm<EPI, 16><<<g, 256, 0, st>>>(M, O, X, xm, Wt, ep)); break;
+    case 32: TESS_TIMED("node_gemm", st, k_gemm<EPI, 32><<<g, 256, 0, st>>>(M, O, X, xm, Wt, ep)); break;
+    case 48: TESS_TIMED("node_gemm", st, k_gemm<EPI, 48><<<g, 256, 0, st>>>(M, O, X, xm, Wt, ep)); break;
+    case 64: TESS_TIMED("node_gemm", st, k_gemm<EPI, 64><<<g, 256, 0, st>>>(M, O, X, xm, Wt, ep)); break;
+    case 96: TESS_TIMED("node_gemm", st, k_gemm<EPI, 96><<<g, 256, 0, st>>>(M, O, X, xm, Wt, ep)); break;
+    case 128: TESS_TIMED("node_gemm", st, k_gemm<EPI, 128><<<g, 256, 0, st>>>(M, O, X, xm, Wt, ep)); break;
+    case 192: TESS_TIMED("node_gemm", st, k_gemm<EPI, 192><<<g, 256, 0, st>>>(M, O, X, xm, Wt, ep)); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -666,6 +685,8 @@ __global__ void k_gbar_init(int32_t n, int C, int D, const float* __restrict__ w
 //   dE/dr = wbar . dw/dr + ubar u'(r);  g = dE/dr n + (I - n n^T) J_Y^T Ybar / r.
 // g (dE/dr_vec) accumulates over layers per edge; sbar is kept for the q/k adjoints.
 // ---------------------------------------------------------------------------------------
+constexpr int kGradRows = 8;  // destination rows of m_bar staged in LDS per block
+
 template <int LMAX, int C, int H, bool L0ONLY>
 __global__ void __launch_bounds__(256) k_edge_grad(const int32_t* __restrict__ arow_n,
                                                    const float4* __restrict__ ageo,
@@ -685,11 +706,23 @@ __global__ void __launch_bounds__(256) k_edge_grad(const int32_t* __restrict__ a
   constexpr int DD = L0ONLY ? 1 : D;
   constexpr int P = Dims<LMAX>::P;
   constexpr int dh = C / H;
-  // only the first ceil(n_active/256) blocks work; spread them evenly over the XCDs
-  const uint32_t nb_act = (uint32_t)((*arow_n + blockDim.x - 1) / blockDim.x);
-  if (blockIdx.x >= nb_act) return;
-  int64_t a = (int64_t)xcd_block(blockIdx.x, nb_act) * blockDim.x + threadIdx.x;
-  if (a >= cap || a >= *arow_n) return;
+  __shared__ float4 smb[kGradRows * D * C / 4];
+  const int64_t n_act = *arow_n;
+  const uint32_t nb_act = (uint32_t)((n_act + blockDim.x - 1) / blockDim.x);
+  if (blockIdx.x >= nb_act) return;  // whole block idle
+  const int64_t a_base = (int64_t)xcd_block(blockIdx.x, nb_act) * blockDim.x;
+  const int64_t a = a_base + threadIdx.x;
+  const bool active = a < n_act && a < cap;
+  // stage the m_bar rows of this block's first destinations (edges are destination-major)
+  const int32_t i_first = adst[a_base];
+  const int32_t i_last = adst[min(a_base + (int64_t)blockDim.x, n_act) - 1];
+  const int nst = min(i_last - i_first + 1, kGradRows);
+  {
+    const float4* src = reinterpret_cast<const float4*>(mbar + (int64_t)i_first * D * C);
+    for (int k = threadIdx.x; k < nst * D * C / 4; k += blockDim.x) smb[k] = src[k];
+  }
+  __syncthreads();
+  if (!active) return;
   const int32_t i = adst[a], j = asrc[a];
   float4 g = ageo[a];
   const float r = g.w, ir = 1.0f / r;
@@ -710,27 +743,43 @@ __global__ void __launch_bounds__(256) k_edge_grad(const int32_t* __restrict__ a
 #pragma unroll
   for (int d = 0; d < 9; d++) Yb[d] = 0.0f;
   float ubar = 0.0f, sb[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  const float* mb_i = mbar + (int64_t)i * D * C;
+  const int ri = i - i_first;
   const float* h_j = h + (int64_t)j * D * C;
+  // Abar^h = sum_{c in head} m_bar_i[:,c] (x) h_j[:,c]; m_bar_i comes from LDS when this
+  // wave's rows are all staged (the usual case, decided wave-uniformly), else from memory.
+  const bool all_staged = __ballot(ri >= nst) == 0ull;
+  auto outer = [&](auto mrow, int hh, float* Ab) {
+#pragma unroll 1
+    for (int c4 = hh * dh; c4 < (hh + 1) * dh; c4 += 4) {
+      float4 hv[DD];
+#pragma unroll
+      for (int d = 0; d < DD; d++) hv[d] = *reinterpret_cast<const float4*>(h_j + d * C + c4);
+#pragma unroll
+      for (int d3 = 0; d3 < D; d3++) {
+        const float4 mv = mrow(d3 * C + c4);
+#pragma unroll
+        for (int d1 = 0; d1 < DD; d1++) {
+          float acc = Ab[d3 * D + d1];
+          acc = __builtin_fmaf(mv.x, hv[d1].x, acc);
+          acc = __builtin_fmaf(mv.y, hv[d1].y, acc);
+          acc = __builtin_fmaf(mv.z, hv[d1].z, acc);
+          acc = __builtin_fmaf(mv.w, hv[d1].w, acc);
+          Ab[d3 * D + d1] = acc;
+        }
+      }
+    }
+  };
+  const float* mb_g = mbar + (int64_t)i * D * C;
+  const int lbase = ri * (D * C / 4);
 #pragma unroll 1
   for (int hh = 0; hh < H; hh++) {
     float Ab[D * D];
 #pragma unroll
     for (int k = 0; k < D * D; k++) Ab[k] = 0.0f;
-#pragma unroll 1
-    for (int c4 = hh * dh; c4 < (hh + 1) * dh; c4 += 4) {
-      float4 mv[D], hv[DD];
-#pragma unroll
-      for (int d = 0; d < D; d++) mv[d] = *reinterpret_cast<const float4*>(mb_i + d * C + c4);
-#pragma unroll
-      for (int d = 0; d < DD; d++) hv[d] = *reinterpret_cast<const float4*>(h_j + d * C + c4);
-#pragma unroll
-      for (int d3 = 0; d3 < D; d3++)
-#pragma unroll
-        for (int d1 = 0; d1 < DD; d1++)
-          Ab[d3 * D + d1] += mv[d3].x * hv[d1].x + mv[d3].y * hv[d1].y + mv[d3].z * hv[d1].z +
-                             mv[d3].w * hv[d1].w;
-    }
+    if (all_staged)
+      outer([&](int off) { return smb[lbase + (off >> 2)]; }, hh, Ab);
+    else
+      outer([&](int off) { return *reinterpret_cast<const float4*>(mb_g + off); }, hh, Ab);
     float wbh[P], Ybh[9];
     coupling_matrix_vjp<LMAX>(w, Y, Ab, wbh, Ybh);
     float abar = 0.0f;
@@ -763,6 +812,207 @@ __global__ void __launch_bounds__(256) k_edge_grad(const int32_t* __restrict__ a
   gacc[a * 3 + 1] = gyv;
   gacc[a * 3 + 2] = gz;
   sbar[a] = make_float4(sb[0], sb[1], sb[2], sb[3]);
+}
+
+// ---------------------------------------------------------------------------------------
+// Edge gradient on the matrix cores (C = 64, 4 heads of 16 channels), one wave per
+// destination row i (4 rows per 256-thread block). Per edge e = (i <- j):
+//   Abar^h[d3][d1] = sum_{c in h} mbar_i[d3][c] h_j[d1][c]   -- 4 MFMA 16x16x4 per head;
+// the K index runs over the head's channels, permuted as c = 16h + 4g + q so that lane group
+// g reads 4 consecutive channels. A-operand = mbar_i (fixed for the row, kept in
+// registers), B-operand = h_j (gathered, one float4 per head per lane, fetched one edge
+// ahead). Lane (g, n) ends with Abar^h[4g + r][n], r = 0..3.
+//   abar_h = <A_e, Abar^h> (cross-lane sum); Abar = sum_h alpha_h Abar^h goes to LDS;
+// after each chunk of 16 edges, lanes take one edge each for the coupling adjoint, the radial
+// and geometric chain and the outputs, exactly as in the per-edge kernel above.
+// ---------------------------------------------------------------------------------------
+constexpr int kGChunk = 16;
+constexpr bool kUseGradMfma = false;  // VALU per-edge kernel is faster on gfx950 at C = 64
+
+// Row sum over the 16 lanes of each DPP row (quad swaps, half-row and row mirrors).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF,
+                                                             0xF, true));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_mov<0x141>(v);  // row_half_mirror
+  v += dpp_mov<0x140>(v);  // row_mirror
+  return v;
+}
+
+// Sums four per-lane values over the 64 lanes of a wave; the total of value h ends in every
+// lane of row h (lanes 16h .. 16h+15).
+__device__ __forceinline__ float wave_sum4_rows(const float* p, int lane) {
+  const bool hi32 = lane >= 32, hi16 = (lane & 16) != 0;
+  const float send0 = hi32 ? p[0] : p[2], send1 = hi32 ? p[1] : p[3];
+  const float keep0 = hi32 ? p[2] : p[0], keep1 = hi32 ? p[3] : p[1];
+  const float k0 = keep0 + __shfl_xor(send0, 32, 64);
+  const float k1 = keep1 + __shfl_xor(send1, 32, 64);
+  const float v = (hi16 ? k1 : k0) + __shfl_xor(hi16 ? k0 : k1, 16, 64);
+  return row16_sum(v);
+}
+
+template <int LMAX>
+__global__ void __launch_bounds__(256) k_edge_grad_mfma(
+    int32_t n, const int32_t* __restrict__ arow, const float4* __restrict__ ageo,
+    const int32_t* __restrict__ asrc, const float* __restrict__ ew,
+    const float* __restrict__ edw, const float4* __restrict__ es, const float* __restrict__ MZ,
+    const float* __restrict__ Dst, const float* __restrict__ mbar, const float* __restrict__ h,
+    float rc, float4* __restrict__ sbar, float* __restrict__ gacc, bool accumulate) {
+  constexpr int C = 64, H = 4;
+  constexpr int D = Dims<LMAX>::D;
+  constexpr int P = Dims<LMAX>::P;
+  __shared__ float sA[4][kGChunk][D * D];   // coupling matrices A_e
+  __shared__ float sAb[4][kGChunk][D * D];  // Abar = sum_h alpha_h Abar^h
+  __shared__ float sAl[4][kGChunk][4];      // alpha_h
+  __shared__ float sAa[4][kGChunk][4];      // abar_h
+  __shared__ int32_t sJ[4][kGChunk];
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 4, nn = lane & 15;
+  const int32_t i = xcd_block(blockIdx.x, gridDim.x) * 4 + wv;
+  if (i >= n) return;
+  const int32_t a0 = arow[i], a1 = arow[i + 1];
+  // row constants
+  float Mh[4], Zh[4], Dh[4];
+#pragma unroll
+  for (int hh = 0; hh < H; hh++) {
+    Mh[hh] = MZ[(int64_t)i * 2 * H + hh];
+    Zh[hh] = MZ[(int64_t)i * 2 * H + H + hh];
+    Dh[hh] = Dst[(int64_t)i * H + hh];
+  }
+  // A-operand: mbar_i[nn][16h + 4g + q], q = 0..3
+  float4 am[H];
+#pragma unroll
+  for (int hh = 0; hh < H; hh++)
+    am[hh] = nn < D ? *reinterpret_cast<const float4*>(mbar + (int64_t)i * D * C +
+                                                       (nn < D ? nn : 0) * C + 16 * hh + 4 * g)
+                    : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int32_t b = a0; b < a1; b += kGChunk) {
+    const int cnt = min(kGChunk, a1 - b);
+    if (lane < cnt) {
+      const int32_t a = b + lane;
+      float4 geo = ageo[a];
+      const float u = 0.5f * (__cosf(kPi * geo.w / rc) + 1.0f);
+      float4 s4 = es[a];
+      const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+      for (int hh = 0; hh < 4; hh++)
+        sAl[wv][lane][hh] = Zh[hh] > 0.0f ? u * __expf(sv[hh] - Mh[hh]) / Zh[hh] : 0.0f;
+      const float ir = 1.0f / geo.w;
+      float Y[9];
+      sph<LMAX>(geo.x * ir, geo.y * ir, geo.z * ir, Y);
+      float w[P];
+#pragma unroll
+      for (int p = 0; p < P; p++) w[p] = ew[(int64_t)a * 12 + p];
+      float A[D * D];
+      coupling_matrix<LMAX>(w, Y, A);
+#pragma unroll
+      for (int k = 0; k < D * D; k++) sA[wv][lane][k] = A[k];
+      sJ[wv][lane] = asrc[a];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    // B-operands of edge e: h_j[nn][16h + 4g .. +3]
+    auto fetch = [&](int e, float4* bo) {
+      const bool ok = e < cnt && nn < D;
+      const float* hj = h + (int64_t)sJ[wv][ok ? e : 0] * D * C + (nn < D ? nn : 0) * C + 4 * g;
+#pragma unroll
+      for (int hh = 0; hh < H; hh++)
+        bo[hh] = ok ? *reinterpret_cast<const float4*>(hj + 16 * hh) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    };
+    float4 bh[H];
+    fetch(0, bh);
+    for (int e = 0; e < cnt; e++) {
+      float4 bn[H];
+      fetch(e + 1, bn);
+      floatx4 acc[H];
+#pragma unroll
+      for (int hh = 0; hh < H; hh++) {
+        acc[hh] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        acc[hh] = __builtin_amdgcn_mfma_f32_16x16x4f32(am[hh].x, bh[hh].x, acc[hh], 0, 0, 0);
+        acc[hh] = __builtin_amdgcn_mfma_f32_16x16x4f32(am[hh].y, bh[hh].y, acc[hh], 0, 0, 0);
+        acc[hh] = __builtin_amdgcn_mfma_f32_16x16x4f32(am[hh].z, bh[hh].z, acc[hh], 0, 0, 0);
+        acc[hh] = __builtin_amdgcn_mfma_f32_16x16x4f32(am[hh].w, bh[hh].w, acc[hh], 0, 0, 0);
+      }
+      // lane (g, nn) holds Abar^h[4g + r][nn]
+      float ae[4];
+#pragma unroll
+      for (int r = 0; r < 4; r++)
+        ae[r] = (4 * g + r < D && nn < D) ? sA[wv][e][min(4 * g + r, D - 1) * D + min(nn, D - 1)] : 0.0f;
+      float part[H];
+#pragma unroll
+      for (int hh = 0; hh < H; hh++)
+        part[hh] = ae[0] * acc[hh][0] + ae[1] * acc[hh][1] + ae[2] * acc[hh][2] + ae[3] * acc[hh][3];
+      const float abar_row = wave_sum4_rows(part, lane);  // abar of head (lane / 16)
+      const float al0 = sAl[wv][e][0], al1 = sAl[wv][e][1], al2 = sAl[wv][e][2], al3 = sAl[wv][e][3];
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        if (4 * g + r < D && nn < D)
+          sAb[wv][e][(4 * g + r) * D + nn] =
+              al0 * acc[0][r] + al1 * acc[1][r] + al2 * acc[2][r] + al3 * acc[3][r];
+      }
+      if (nn == 0) sAa[wv][e][g] = abar_row;
+#pragma unroll
+      for (int hh = 0; hh < H; hh++) bh[hh] = bn[hh];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    // per-edge epilogue (lane = edge)
+    if (lane < cnt) {
+      const int32_t a = b + lane;
+      float4 geo = ageo[a];
+      const float r = geo.w, ir = 1.0f / r;
+      const float nx = geo.x * ir, ny = geo.y * ir, nz = geo.z * ir;
+      float s1, c1;
+      __sincosf(kPi * r / rc, &s1, &c1);
+      const float u = 0.5f * (c1 + 1.0f), du = -0.5f * (kPi / rc) * s1;
+      float Y[9];
+      sph<LMAX>(nx, ny, nz, Y);
+      float w[P];
+#pragma unroll
+      for (int p = 0; p < P; p++) w[p] = ew[(int64_t)a * 12 + p];
+      float Ab[D * D];
+#pragma unroll
+      for (int k = 0; k < D * D; k++) Ab[k] = sAb[wv][lane][k];
+      float wb[P], Yb[9];
+      coupling_matrix_vjp<LMAX>(w, Y, Ab, wb, Yb);
+      float4 s4 = es[a];
+      const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+      float ubar = 0.0f, sb[4];
+#pragma unroll
+      for (int hh = 0; hh < H; hh++) {
+        const float p_h = Zh[hh] > 0.0f ? __expf(sv[hh] - Mh[hh]) / Zh[hh] : 0.0f;
+        const float al = u * p_h;
+        const float diff = sAa[wv][lane][hh] - Dh[hh];
+        sb[hh] = al * diff;
+        ubar += p_h * diff;
+      }
+      float dEdr = ubar * du;
+#pragma unroll
+      for (int p = 0; p < P; p++) dEdr += wb[p] * edw[(int64_t)a * 12 + p];
+      float gy[3];
+      sph_vjp<LMAX>(nx, ny, nz, Yb, gy);
+      const float ng = nx * gy[0] + ny * gy[1] + nz * gy[2];
+      float gx = dEdr * nx + (gy[0] - ng * nx) * ir;
+      float gyv = dEdr * ny + (gy[1] - ng * ny) * ir;
+      float gz = dEdr * nz + (gy[2] - ng * nz) * ir;
+      if (accumulate) {
+        gx += gacc[(int64_t)a * 3]; gyv += gacc[(int64_t)a * 3 + 1]; gz += gacc[(int64_t)a * 3 + 2];
+      }
+      gacc[(int64_t)a * 3] = gx;
+      gacc[(int64_t)a * 3 + 1] = gyv;
+      gacc[(int64_t)a * 3 + 2] = gz;
+      sbar[a] = make_float4(sb[0], sb[1], sb[2], sb[3]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  }
 }
 
 // F_x = sum over the active edges a of row x of (g_a - g_rev(a)), g = dE/dr_vec.
@@ -1010,6 +1260,11 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
                    k_edge_grad<LMAX, C, H, true><<<gridn(cap, 256), 256, 0, st>>>(
                        w.arow + n, w.ageo, w.adst, w.asrc, ew, edw, es, MZ, w.Dst, w.mbar, ht, rc,
                        w.sbar, w.gacc, t != T - 1, cap));
+      else if constexpr (C == 64 && H == 4 && kUseGradMfma)
+        TESS_TIMED("edge_grad", st,
+                   k_edge_grad_mfma<LMAX><<<gridn(n, 4), 256, 0, st>>>(
+                       n, w.arow, w.ageo, w.asrc, ew, edw, es, MZ, w.Dst, w.mbar, ht, rc, w.sbar,
+                       w.gacc, t != T - 1));
       else
         TESS_TIMED("edge_grad", st,
                    k_edge_grad<LMAX, C, H, false><<<gridn(cap, 256), 256, 0, st>>>(
