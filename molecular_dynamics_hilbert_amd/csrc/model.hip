@@ -677,18 +677,125 @@ __global__ void k_gbar_init(int32_t n, int C, int D, const float* __restrict__ w
 }
 
 // ---------------------------------------------------------------------------------------
-// Edge gradient, one thread per active edge e = (i <- j), destination-major:
+// Edge gradient for active edge e = (i <- j), destination-major. One lane per (edge, head):
 //   Abar^h = sum_{c in h} mbar_i[:,c] (x) h_j[:,c];  (wbar^h, Ybar^h) = coupling adjoint;
 //   abar_h = <A_e, Abar^h> = w . wbar^h;  sbar_h = alpha_h (abar_h - D_ih);
 //   ubar = sum_h p_h (abar_h - D_ih), p_h = exp(s_h - M_ih)/Z_ih, alpha_h = u p_h;
-//   wbar = sum_h alpha_h wbar^h, Ybar = sum_h alpha_h Ybar^h;
+//   wbar = sum_h alpha_h wbar^h, Ybar = sum_h alpha_h Ybar^h  (sums over the edge's lanes);
 //   dE/dr = wbar . dw/dr + ubar u'(r);  g = dE/dr n + (I - n n^T) J_Y^T Ybar / r.
 // g (dE/dr_vec) accumulates over layers per edge; sbar is kept for the q/k adjoints.
+// Each lane reads the head's contiguous channel slice of a feature row of h_j with back-to-back
+// 16-byte loads, so the H lanes of an edge together read whole rows; m_bar rows of the
+// block's destinations are staged in LDS.
 // ---------------------------------------------------------------------------------------
-constexpr int kGradRows = 8;  // destination rows of m_bar staged in LDS per block
+constexpr int kGradRows = 8;  // destination rows of m_bar staged in LDS at a time
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF,
+                                                            0xF, false));
+}
+// Sum over the 4 lanes of a quad (quad_perm [1,0,3,2] then [2,3,0,1]); every lane gets it.
+__device__ __forceinline__ float quad_sum(float v) {
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  return v;
+}
+
+// Rows d1 = L1^2 + S0 .. L1^2 + S0 + NR - 1 (sender degree L1) of one head's gradient:
+// Abar[d3][m1] = sum_{c in head} mbar_i[d3][c] h_j[d1][c] for every output component d3 (all of
+// a row's head channels loaded at once), then the part of the coupling adjoint that these
+// columns feed (the adjoint is a sum over (d3, d1) entries, so it splits by column):
+//   t^p[m2] = sum_{m1 in rows, m3} C^p[m1][m2][m3] Abar[(l3,m3)][m1],  wbar^p = t^p . Y_l2;
+//   abar += w_p wbar^p;  wb[p] += alpha wbar^p;  Yb[l2^2+m2] += alpha w_p t^p[m2].
+template <int LMAX, int C, int DH, int L1, int S0, int NR, class MRow>
+__device__ __forceinline__ void grad_rows(MRow mrow, const float* __restrict__ h_j, int c0,
+                                          const float* w, const float* Y, float al,
+                                          float& abar, float* wb, float* Yb) {
+  constexpr int D = Dims<LMAX>::D, B0 = L1 * L1 + S0, NC = DH / 4;
+  constexpr const CGTable& T = cg_table<LMAX>();
+  float4 hv[NR][NC];
+#pragma unroll
+  for (int m = 0; m < NR; m++)
+#pragma unroll
+    for (int t = 0; t < NC; t++)
+      hv[m][t] = *reinterpret_cast<const float4*>(h_j + (B0 + m) * C + c0 + 4 * t);
+  float Ab[D * NR];
+  float4 mv[NC], mn[NC];
+#pragma unroll
+  for (int t = 0; t < NC; t++) mv[t] = mrow(c0 + 4 * t);
+#pragma unroll
+  for (int d3 = 0; d3 < D; d3++) {
+    if (d3 + 1 < D) {
+#pragma unroll
+      for (int t = 0; t < NC; t++) mn[t] = mrow((d3 + 1) * C + c0 + 4 * t);
+    }
+#pragma unroll
+    for (int m = 0; m < NR; m++) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int t = 0; t < NC; t++) {
+        acc = __builtin_fmaf(mv[t].x, hv[m][t].x, acc);
+        acc = __builtin_fmaf(mv[t].y, hv[m][t].y, acc);
+        acc = __builtin_fmaf(mv[t].z, hv[m][t].z, acc);
+        acc = __builtin_fmaf(mv[t].w, hv[m][t].w, acc);
+      }
+      Ab[d3 * NR + m] = acc;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < NC; t++) mv[t] = mn[t];
+  }
+#pragma unroll
+  for (int p = 0; p < Dims<LMAX>::P; p++) {
+    if (T.l1[p] != L1) continue;
+    const float alw = al * w[p];
+    float wbh = 0.0f;
+    bool touched = false;
+#pragma unroll
+    for (int m2 = 0; m2 < 5; m2++) {
+      if (m2 >= 2 * T.l2[p] + 1) continue;
+      float tpm = 0.0f;
+      bool any = false;
+#pragma unroll
+      for (int m = 0; m < NR; m++)
+#pragma unroll
+        for (int m3 = 0; m3 < 5; m3++) {
+          if (m3 < 2 * T.l3[p] + 1 && T.v[p][S0 + m][m2][m3] != 0.0) {
+            tpm += (float)T.v[p][S0 + m][m2][m3] * Ab[(T.l3[p] * T.l3[p] + m3) * NR + m];
+            any = true;
+          }
+        }
+      if (any) {
+        wbh += tpm * Y[T.l2[p] * T.l2[p] + m2];
+        Yb[T.l2[p] * T.l2[p] + m2] += alw * tpm;
+        touched = true;
+      }
+    }
+    if (touched) {
+      abar += w[p] * wbh;
+      wb[p] += al * wbh;
+    }
+  }
+}
+
+// All rows of sender degree L1, at most 3 rows at a time.
+template <int LMAX, int C, int DH, int L1, class MRow>
+__device__ __forceinline__ void grad_block(MRow mrow, const float* __restrict__ h_j, int c0,
+                                           const float* w, const float* Y, float al,
+                                           float& abar, float* wb, float* Yb) {
+  if constexpr (L1 == 0) {
+    grad_rows<LMAX, C, DH, 0, 0, 1>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
+  } else if constexpr (L1 == 1) {
+    grad_rows<LMAX, C, DH, 1, 0, 3>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
+  } else {
+    grad_rows<LMAX, C, DH, 2, 0, 3>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
+    grad_rows<LMAX, C, DH, 2, 3, 2>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
+  }
+}
 
 template <int LMAX, int C, int H, bool L0ONLY>
-__global__ void __launch_bounds__(256) k_edge_grad(const int32_t* __restrict__ arow_n,
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) k_edge_grad(const int32_t* __restrict__ arow_n,
                                                    const float4* __restrict__ ageo,
                                                    const int32_t* __restrict__ adst,
                                                    const int32_t* __restrict__ asrc,
@@ -702,299 +809,81 @@ __global__ void __launch_bounds__(256) k_edge_grad(const int32_t* __restrict__ a
                                                    float4* __restrict__ sbar,
                                                    float* __restrict__ gacc, bool accumulate,
                                                    int64_t cap) {
+  static_assert(H == 1 || H == 4, "one lane or a quad of lanes per edge");
   constexpr int D = Dims<LMAX>::D;
-  constexpr int DD = L0ONLY ? 1 : D;
   constexpr int P = Dims<LMAX>::P;
   constexpr int dh = C / H;
+  constexpr int EPB = 256 / H;  // edges per block
   __shared__ float4 smb[kGradRows * D * C / 4];
   const int64_t n_act = *arow_n;
-  const uint32_t nb_act = (uint32_t)((n_act + blockDim.x - 1) / blockDim.x);
+  const uint32_t nb_act = (uint32_t)((n_act + EPB - 1) / EPB);
   if (blockIdx.x >= nb_act) return;  // whole block idle
-  const int64_t a_base = (int64_t)xcd_block(blockIdx.x, nb_act) * blockDim.x;
-  const int64_t a = a_base + threadIdx.x;
+  const int64_t a_base = (int64_t)xcd_block(blockIdx.x, nb_act) * EPB;
+  const int hh = (int)threadIdx.x % H;
+  const int64_t a = a_base + threadIdx.x / H;
   const bool active = a < n_act && a < cap;
-  // stage the m_bar rows of this block's first destinations (edges are destination-major)
+  // The block's destinations (edges are destination-major) are staged in LDS kGradRows
+  // m_bar rows at a time; each edge is processed in the batch that holds its row.
   const int32_t i_first = adst[a_base];
-  const int32_t i_last = adst[min(a_base + (int64_t)blockDim.x, n_act) - 1];
-  const int nst = min(i_last - i_first + 1, kGradRows);
-  {
-    const float4* src = reinterpret_cast<const float4*>(mbar + (int64_t)i_first * D * C);
-    for (int k = threadIdx.x; k < nst * D * C / 4; k += blockDim.x) smb[k] = src[k];
-  }
-  __syncthreads();
-  if (!active) return;
-  const int32_t i = adst[a], j = asrc[a];
-  float4 g = ageo[a];
-  const float r = g.w, ir = 1.0f / r;
-  const float nx = g.x * ir, ny = g.y * ir, nz = g.z * ir;
-  float th = kPi * r / rc, s1, c1;
-  __sincosf(th, &s1, &c1);
-  const float u = 0.5f * (c1 + 1.0f), du = -0.5f * (kPi / rc) * s1;
-  float Y[9];
-  sph<LMAX>(nx, ny, nz, Y);
-  float w[P];
-#pragma unroll
-  for (int p = 0; p < P; p++) w[p] = ew[a * 12 + p];
-  float4 s4 = es[a];
-  const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
-  float wb[P], Yb[9];
-#pragma unroll
-  for (int p = 0; p < P; p++) wb[p] = 0.0f;
-#pragma unroll
-  for (int d = 0; d < 9; d++) Yb[d] = 0.0f;
-  float ubar = 0.0f, sb[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  const int ri = i - i_first;
-  const float* h_j = h + (int64_t)j * D * C;
-  // Abar^h = sum_{c in head} m_bar_i[:,c] (x) h_j[:,c]; m_bar_i comes from LDS when this
-  // wave's rows are all staged (the usual case, decided wave-uniformly), else from memory.
-  const bool all_staged = __ballot(ri >= nst) == 0ull;
-  auto outer = [&](auto mrow, int hh, float* Ab) {
-#pragma unroll 1
-    for (int c4 = hh * dh; c4 < (hh + 1) * dh; c4 += 4) {
-      float4 hv[DD];
-#pragma unroll
-      for (int d = 0; d < DD; d++) hv[d] = *reinterpret_cast<const float4*>(h_j + d * C + c4);
-#pragma unroll
-      for (int d3 = 0; d3 < D; d3++) {
-        const float4 mv = mrow(d3 * C + c4);
-#pragma unroll
-        for (int d1 = 0; d1 < DD; d1++) {
-          float acc = Ab[d3 * D + d1];
-          acc = __builtin_fmaf(mv.x, hv[d1].x, acc);
-          acc = __builtin_fmaf(mv.y, hv[d1].y, acc);
-          acc = __builtin_fmaf(mv.z, hv[d1].z, acc);
-          acc = __builtin_fmaf(mv.w, hv[d1].w, acc);
-          Ab[d3 * D + d1] = acc;
-        }
-      }
+  const int32_t nrows = adst[min(a_base + (int64_t)EPB, n_act) - 1] - i_first + 1;
+  const int ri = active ? adst[a] - i_first : -1;
+  for (int b0 = 0; b0 < nrows; b0 += kGradRows) {
+    const int nst = min(nrows - b0, kGradRows);
+    if (b0 > 0) __syncthreads();
+    {
+      const float4* src = reinterpret_cast<const float4*>(mbar + (int64_t)(i_first + b0) * D * C);
+      for (int k = threadIdx.x; k < nst * D * C / 4; k += blockDim.x) smb[k] = src[k];
     }
-  };
-  const float* mb_g = mbar + (int64_t)i * D * C;
-  const int lbase = ri * (D * C / 4);
-#pragma unroll 1
-  for (int hh = 0; hh < H; hh++) {
-    float Ab[D * D];
+    __syncthreads();
+    if (ri < b0 || ri >= b0 + nst) continue;
+    const int32_t i = i_first + ri, j = asrc[a];
+    float4 g = ageo[a];
+    const float r = g.w, ir = 1.0f / r;
+    const float nx = g.x * ir, ny = g.y * ir, nz = g.z * ir;
+    float th = kPi * r / rc, s1, c1;
+    __sincosf(th, &s1, &c1);
+    const float u = 0.5f * (c1 + 1.0f), du = -0.5f * (kPi / rc) * s1;
+    float Y[9];
+    sph<LMAX>(nx, ny, nz, Y);
+    float w[P];
 #pragma unroll
-    for (int k = 0; k < D * D; k++) Ab[k] = 0.0f;
-    if (all_staged)
-      outer([&](int off) { return smb[lbase + (off >> 2)]; }, hh, Ab);
-    else
-      outer([&](int off) { return *reinterpret_cast<const float4*>(mb_g + off); }, hh, Ab);
-    float wbh[P], Ybh[9];
-    coupling_matrix_vjp<LMAX>(w, Y, Ab, wbh, Ybh);
-    float abar = 0.0f;
+    for (int p = 0; p < P; p++) w[p] = ew[a * 12 + p];
+    const float sv = reinterpret_cast<const float*>(es)[a * 4 + hh];
+    float wb[P], Yb[9];
 #pragma unroll
-    for (int p = 0; p < P; p++) abar += w[p] * wbh[p];
+    for (int p = 0; p < P; p++) wb[p] = 0.0f;
+#pragma unroll
+    for (int d = 0; d < 9; d++) Yb[d] = 0.0f;
+    const float* h_j = h + (int64_t)j * D * C;
+    const int lbase = (ri - b0) * (D * C / 4);
+    auto mrow = [&](int off) { return smb[lbase + (off >> 2)]; };
     const float Zi = MZ[(int64_t)i * 2 * H + H + hh];
-    const float p_h = Zi > 0.0f ? __expf(sv[hh] - MZ[(int64_t)i * 2 * H + hh]) / Zi : 0.0f;
+    const float p_h = Zi > 0.0f ? __expf(sv - MZ[(int64_t)i * 2 * H + hh]) / Zi : 0.0f;
     const float al = u * p_h;
+    float abar = 0.0f;
+    const int c0 = hh * dh;
+    grad_block<LMAX, C, dh, 0>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
+    if constexpr (!L0ONLY) {
+      grad_block<LMAX, C, dh, 1>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
+      if constexpr (LMAX >= 2) grad_block<LMAX, C, dh, 2>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
+    }
     const float diff = abar - Dst[(int64_t)i * H + hh];
-    sb[hh] = al * diff;
-    ubar += p_h * diff;
+    const float sb = al * diff;
+    float ubar = p_h * diff;
+    if constexpr (H == 4) {  // sums over the heads of this edge
 #pragma unroll
-    for (int p = 0; p < P; p++) wb[p] += al * wbh[p];
+      for (int p = 0; p < P; p++) wb[p] = quad_sum(wb[p]);
 #pragma unroll
-    for (int d = 0; d < D; d++) Yb[d] += al * Ybh[d];
-  }
-  float dEdr = ubar * du;
-#pragma unroll
-  for (int p = 0; p < P; p++) dEdr += wb[p] * edw[a * 12 + p];
-  float gy[3];
-  sph_vjp<LMAX>(nx, ny, nz, Yb, gy);
-  const float ng = nx * gy[0] + ny * gy[1] + nz * gy[2];
-  float gx = dEdr * nx + (gy[0] - ng * nx) * ir;
-  float gyv = dEdr * ny + (gy[1] - ng * ny) * ir;
-  float gz = dEdr * nz + (gy[2] - ng * nz) * ir;
-  if (accumulate) {
-    gx += gacc[a * 3]; gyv += gacc[a * 3 + 1]; gz += gacc[a * 3 + 2];
-  }
-  gacc[a * 3] = gx;
-  gacc[a * 3 + 1] = gyv;
-  gacc[a * 3 + 2] = gz;
-  sbar[a] = make_float4(sb[0], sb[1], sb[2], sb[3]);
-}
-
-// ---------------------------------------------------------------------------------------
-// Edge gradient on the matrix cores (C = 64, 4 heads of 16 channels), one wave per
-// destination row i (4 rows per 256-thread block). Per edge e = (i <- j):
-//   Abar^h[d3][d1] = sum_{c in h} mbar_i[d3][c] h_j[d1][c]   -- 4 MFMA 16x16x4 per head;
-// the K index runs over the head's channels, permuted as c = 16h + 4g + q so that lane group
-// g reads 4 consecutive channels. A-operand = mbar_i (fixed for the row, kept in
-// registers), B-operand = h_j (gathered, one float4 per head per lane, fetched one edge
-// ahead). Lane (g, n) ends with Abar^h[4g + r][n], r = 0..3.
-//   abar_h = <A_e, Abar^h> (cross-lane sum); Abar = sum_h alpha_h Abar^h goes to LDS;
-// after each chunk of 16 edges, lanes take one edge each for the coupling adjoint, the radial
-// and geometric chain and the outputs, exactly as in the per-edge kernel above.
-// ---------------------------------------------------------------------------------------
-constexpr int kGChunk = 16;
-constexpr bool kUseGradMfma = false;  // VALU per-edge kernel is faster on gfx950 at C = 64
-
-// Row sum over the 16 lanes of each DPP row (quad swaps, half-row and row mirrors).
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF,
-                                                             0xF, true));
-}
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
-  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
-  v += dpp_mov<0x141>(v);  // row_half_mirror
-  v += dpp_mov<0x140>(v);  // row_mirror
-  return v;
-}
-
-// Sums four per-lane values over the 64 lanes of a wave; the total of value h ends in every
-// lane of row h (lanes 16h .. 16h+15).
-__device__ __forceinline__ float wave_sum4_rows(const float* p, int lane) {
-  const bool hi32 = lane >= 32, hi16 = (lane & 16) != 0;
-  const float send0 = hi32 ? p[0] : p[2], send1 = hi32 ? p[1] : p[3];
-  const float keep0 = hi32 ? p[2] : p[0], keep1 = hi32 ? p[3] : p[1];
-  const float k0 = keep0 + __shfl_xor(send0, 32, 64);
-  const float k1 = keep1 + __shfl_xor(send1, 32, 64);
-  const float v = (hi16 ? k1 : k0) + __shfl_xor(hi16 ? k0 : k1, 16, 64);
-  return row16_sum(v);
-}
-
-template <int LMAX>
-__global__ void __launch_bounds__(256) k_edge_grad_mfma(
-    int32_t n, const int32_t* __restrict__ arow, const float4* __restrict__ ageo,
-    const int32_t* __restrict__ asrc, const float* __restrict__ ew,
-    const float* __restrict__ edw, const float4* __restrict__ es, const float* __restrict__ MZ,
-    const float* __restrict__ Dst, const float* __restrict__ mbar, const float* __restrict__ h,
-    float rc, float4* __restrict__ sbar, float* __restrict__ gacc, bool accumulate) {
-  constexpr int C = 64, H = 4;
-  constexpr int D = Dims<LMAX>::D;
-  constexpr int P = Dims<LMAX>::P;
-  __shared__ float sA[4][kGChunk][D * D];   // coupling matrices A_e
-  __shared__ float sAb[4][kGChunk][D * D];  // Abar = sum_h alpha_h Abar^h
-  __shared__ float sAl[4][kGChunk][4];      // alpha_h
-  __shared__ float sAa[4][kGChunk][4];      // abar_h
-  __shared__ int32_t sJ[4][kGChunk];
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g = lane >> 4, nn = lane & 15;
-  const int32_t i = xcd_block(blockIdx.x, gridDim.x) * 4 + wv;
-  if (i >= n) return;
-  const int32_t a0 = arow[i], a1 = arow[i + 1];
-  // row constants
-  float Mh[4], Zh[4], Dh[4];
-#pragma unroll
-  for (int hh = 0; hh < H; hh++) {
-    Mh[hh] = MZ[(int64_t)i * 2 * H + hh];
-    Zh[hh] = MZ[(int64_t)i * 2 * H + H + hh];
-    Dh[hh] = Dst[(int64_t)i * H + hh];
-  }
-  // A-operand: mbar_i[nn][16h + 4g + q], q = 0..3
-  float4 am[H];
-#pragma unroll
-  for (int hh = 0; hh < H; hh++)
-    am[hh] = nn < D ? *reinterpret_cast<const float4*>(mbar + (int64_t)i * D * C +
-                                                       (nn < D ? nn : 0) * C + 16 * hh + 4 * g)
-                    : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  for (int32_t b = a0; b < a1; b += kGChunk) {
-    const int cnt = min(kGChunk, a1 - b);
-    if (lane < cnt) {
-      const int32_t a = b + lane;
-      float4 geo = ageo[a];
-      const float u = 0.5f * (__cosf(kPi * geo.w / rc) + 1.0f);
-      float4 s4 = es[a];
-      const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-      for (int hh = 0; hh < 4; hh++)
-        sAl[wv][lane][hh] = Zh[hh] > 0.0f ? u * __expf(sv[hh] - Mh[hh]) / Zh[hh] : 0.0f;
-      const float ir = 1.0f / geo.w;
-      float Y[9];
-      sph<LMAX>(geo.x * ir, geo.y * ir, geo.z * ir, Y);
-      float w[P];
-#pragma unroll
-      for (int p = 0; p < P; p++) w[p] = ew[(int64_t)a * 12 + p];
-      float A[D * D];
-      coupling_matrix<LMAX>(w, Y, A);
-#pragma unroll
-      for (int k = 0; k < D * D; k++) sA[wv][lane][k] = A[k];
-      sJ[wv][lane] = asrc[a];
+      for (int d = 0; d < 9; d++) Yb[d] = quad_sum(Yb[d]);
+      ubar = quad_sum(ubar);
+      reinterpret_cast<float*>(sbar)[a * 4 + hh] = sb;
+    } else {
+      sbar[a] = make_float4(sb, 0.0f, 0.0f, 0.0f);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    // B-operands of edge e: h_j[nn][16h + 4g .. +3]
-    auto fetch = [&](int e, float4* bo) {
-      const bool ok = e < cnt && nn < D;
-      const float* hj = h + (int64_t)sJ[wv][ok ? e : 0] * D * C + (nn < D ? nn : 0) * C + 4 * g;
-#pragma unroll
-      for (int hh = 0; hh < H; hh++)
-        bo[hh] = ok ? *reinterpret_cast<const float4*>(hj + 16 * hh) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    };
-    float4 bh[H];
-    fetch(0, bh);
-    for (int e = 0; e < cnt; e++) {
-      float4 bn[H];
-      fetch(e + 1, bn);
-      floatx4 acc[H];
-#pragma unroll
-      for (int hh = 0; hh < H; hh++) {
-        acc[hh] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-        acc[hh] = __builtin_amdgcn_mfma_f32_16x16x4f32(am[hh].x, bh[hh].x, acc[hh], 0, 0, 0);
-        acc[hh] = __builtin_amdgcn_mfma_f32_16x16x4f32(am[hh].y, bh[hh].y, acc[hh], 0, 0, 0);
-        acc[hh] = __builtin_amdgcn_mfma_f32_16x16x4f32(am[hh].z, bh[hh].z, acc[hh], 0, 0, 0);
-        acc[hh] = __builtin_amdgcn_mfma_f32_16x16x4f32(am[hh].w, bh[hh].w, acc[hh], 0, 0, 0);
-      }
-      // lane (g, nn) holds Abar^h[4g + r][nn]
-      float ae[4];
-#pragma unroll
-      for (int r = 0; r < 4; r++)
-        ae[r] = (4 * g + r < D && nn < D) ? sA[wv][e][min(4 * g + r, D - 1) * D + min(nn, D - 1)] : 0.0f;
-      float part[H];
-#pragma unroll
-      for (int hh = 0; hh < H; hh++)
-        part[hh] = ae[0] * acc[hh][0] + ae[1] * acc[hh][1] + ae[2] * acc[hh][2] + ae[3] * acc[hh][3];
-      const float abar_row = wave_sum4_rows(part, lane);  // abar of head (lane / 16)
-      const float al0 = sAl[wv][e][0], al1 = sAl[wv][e][1], al2 = sAl[wv][e][2], al3 = sAl[wv][e][3];
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        if (4 * g + r < D && nn < D)
-          sAb[wv][e][(4 * g + r) * D + nn] =
-              al0 * acc[0][r] + al1 * acc[1][r] + al2 * acc[2][r] + al3 * acc[3][r];
-      }
-      if (nn == 0) sAa[wv][e][g] = abar_row;
-#pragma unroll
-      for (int hh = 0; hh < H; hh++) bh[hh] = bn[hh];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    // per-edge epilogue (lane = edge)
-    if (lane < cnt) {
-      const int32_t a = b + lane;
-      float4 geo = ageo[a];
-      const float r = geo.w, ir = 1.0f / r;
-      const float nx = geo.x * ir, ny = geo.y * ir, nz = geo.z * ir;
-      float s1, c1;
-      __sincosf(kPi * r / rc, &s1, &c1);
-      const float u = 0.5f * (c1 + 1.0f), du = -0.5f * (kPi / rc) * s1;
-      float Y[9];
-      sph<LMAX>(nx, ny, nz, Y);
-      float w[P];
-#pragma unroll
-      for (int p = 0; p < P; p++) w[p] = ew[(int64_t)a * 12 + p];
-      float Ab[D * D];
-#pragma unroll
-      for (int k = 0; k < D * D; k++) Ab[k] = sAb[wv][lane][k];
-      float wb[P], Yb[9];
-      coupling_matrix_vjp<LMAX>(w, Y, Ab, wb, Yb);
-      float4 s4 = es[a];
-      const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
-      float ubar = 0.0f, sb[4];
-#pragma unroll
-      for (int hh = 0; hh < H; hh++) {
-        const float p_h = Zh[hh] > 0.0f ? __expf(sv[hh] - Mh[hh]) / Zh[hh] : 0.0f;
-        const float al = u * p_h;
-        const float diff = sAa[wv][lane][hh] - Dh[hh];
-        sb[hh] = al * diff;
-        ubar += p_h * diff;
-      }
+    if (hh == 0) {
       float dEdr = ubar * du;
 #pragma unroll
-      for (int p = 0; p < P; p++) dEdr += wb[p] * edw[(int64_t)a * 12 + p];
+      for (int p = 0; p < P; p++) dEdr += wb[p] * edw[a * 12 + p];
       float gy[3];
       sph_vjp<LMAX>(nx, ny, nz, Yb, gy);
       const float ng = nx * gy[0] + ny * gy[1] + nz * gy[2];
@@ -1002,20 +891,15 @@ __global__ void __launch_bounds__(256) k_edge_grad_mfma(
       float gyv = dEdr * ny + (gy[1] - ng * ny) * ir;
       float gz = dEdr * nz + (gy[2] - ng * nz) * ir;
       if (accumulate) {
-        gx += gacc[(int64_t)a * 3]; gyv += gacc[(int64_t)a * 3 + 1]; gz += gacc[(int64_t)a * 3 + 2];
+        gx += gacc[a * 3]; gyv += gacc[a * 3 + 1]; gz += gacc[a * 3 + 2];
       }
-      gacc[(int64_t)a * 3] = gx;
-      gacc[(int64_t)a * 3 + 1] = gyv;
-      gacc[(int64_t)a * 3 + 2] = gz;
-      sbar[a] = make_float4(sb[0], sb[1], sb[2], sb[3]);
+      gacc[a * 3] = gx;
+      gacc[a * 3 + 1] = gyv;
+      gacc[a * 3 + 2] = gz;
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   }
 }
 
-// F_x = sum over the active edges a of row x of (g_a - g_rev(a)), g = dE/dr_vec.
 __global__ void k_forces(int32_t n, const int32_t* __restrict__ arow, const int32_t* __restrict__ arev,
                          const float* __restrict__ gacc, float* __restrict__ F) {
   int32_t x = blockIdx.x * blockDim.x + threadIdx.x;
@@ -1255,19 +1139,15 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     }
     k_dst<LMAX, C, H><<<gridn(n, 4), 256, 0, st>>>(n, w.mbar, mt, w.Dst);
     if (cap > 0) {
+      const int32_t gb = gridn(cap, 256 / H);
       if (t == 0)
         TESS_TIMED("edge_grad", st,
-                   k_edge_grad<LMAX, C, H, true><<<gridn(cap, 256), 256, 0, st>>>(
+                   k_edge_grad<LMAX, C, H, true><<<gb, 256, 0, st>>>(
                        w.arow + n, w.ageo, w.adst, w.asrc, ew, edw, es, MZ, w.Dst, w.mbar, ht, rc,
                        w.sbar, w.gacc, t != T - 1, cap));
-      else if constexpr (C == 64 && H == 4 && kUseGradMfma)
-        TESS_TIMED("edge_grad", st,
-                   k_edge_grad_mfma<LMAX><<<gridn(n, 4), 256, 0, st>>>(
-                       n, w.arow, w.ageo, w.asrc, ew, edw, es, MZ, w.Dst, w.mbar, ht, rc, w.sbar,
-                       w.gacc, t != T - 1));
       else
         TESS_TIMED("edge_grad", st,
-                   k_edge_grad<LMAX, C, H, false><<<gridn(cap, 256), 256, 0, st>>>(
+                   k_edge_grad<LMAX, C, H, false><<<gb, 256, 0, st>>>(
                        w.arow + n, w.ageo, w.adst, w.asrc, ew, edw, es, MZ, w.Dst, w.mbar, ht, rc,
                        w.sbar, w.gacc, t != T - 1, cap));
     }
