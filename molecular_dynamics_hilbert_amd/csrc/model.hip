@@ -9,13 +9,14 @@
 // (r_vec, |r|), radial weights w[12], dw/dr[12] and logits s[4] per layer.
 //
 // Kernels per layer (forward): MFMA GEMM q|k; edge_prep (one thread per edge: Bessel basis,
-// radial MLP and its r-derivative, logits); edge_apply (one wave per destination row:
-// softmax statistics, coupling matrices A_e into LDS, then lane = channel accumulates
-// alpha * A_e h_j); MFMA GEMMs of the gated residual update with fused epilogues.
-// Backward: elementwise update adjoint + MFMA GEMMs; edge_grad (one thread per edge:
-// per-head sum over channels of mbar_i (x) h_j contracted through the coupling adjoint, giving
-// the logit adjoint and dE/dr_vec); edge_tapply (one wave per row: h_bar via A^T, k_bar, q_bar);
-// MFMA GEMM for the q/k projections; force assembly through the reverse-edge index.
+// radial MLP and its r-derivative, logits); edge contraction (one wave per destination row:
+// softmax statistics, coupling matrices A_e into LDS, then alpha * A_e h_j summed over the
+// row's edges on 4x4x1 MFMA blocks); MFMA GEMMs of the gated residual update with fused
+// epilogues. Backward: elementwise update adjoint + MFMA GEMMs; edge_grad (one lane per edge
+// and head: per-head sum over channels of mbar_i (x) h_j contracted through the coupling
+// adjoint, giving the logit adjoint and dE/dr_vec); the transposed edge contraction (one wave
+// per row: h_bar via A^T, k_bar, q_bar); MFMA GEMM for the q/k projections; force assembly
+// through the reverse-edge index.
 #include "tess_common.h"
 
 #include <vector>
@@ -352,39 +353,24 @@ __global__ void __launch_bounds__(256) k_edge_prep(const int32_t* __restrict__ a
 //     hbar_x[d1][c] += alpha_e',h(c) sum_d3 A_e'[d3][d1] mbar_y[d3][c]   (A_e' uses Y(-n_a)),
 //     kbar_x[c] += sbar_e',h(c) q_y[c] / sqrt(d),  qbar_x[c] += sbar_a,h(c) k_y[c] / sqrt(d).
 //
-// Per edge the channel sum is a 16x16x4 fp32 MFMA per 16-channel tile and 4-component step:
-// A-operand (16 channels x 4 input components) = alpha * gathered features, B-operand
-// (4 input x 16 output components) = the edge's coupling matrix, read from LDS. Tile t holds
-// channels (C/16)*n + t, n = 0..15, so each lane loads its C/16 channels with one vector load
-// and stores C/16 contiguous channels at the end. Chunks of 32 edges: lanes first build
-// alpha and A_e (lane = edge) into LDS.
+// Chunks of 32 edges: lanes first build alpha and A_e (lane = edge) into LDS. The channel sums
+// then run on 4x4x1 MFMA blocks (v_mfma_f32_4x4x1f32: 16 independent 4x4 outer products per
+// instruction; block b takes its A column from lanes 4b..4b+3 and its B row from the same
+// lanes, and lane 4b+j ends with D_b[r][j] in register r). Lane = (edge q of a group of
+// 64/(C/4) edges, channel quad m): it loads 4 consecutive channels of one input component
+// with one 16-byte load, and for s = 0..3 feeds channel 4m+s as its A value; its B value is
+// the coupling from that input component to output component 4g+(lane&3) of the same edge.
+// Blocks of different edges add into separate accumulators that are summed over the group's
+// edges once per row. Output components 0..7 use the matrix cores (two groups of four),
+// component 8 (l = 2, m = 2) is a vector FMA.
 // L0ONLY: only the l = 0 input component is non-zero (first layer).
 // ---------------------------------------------------------------------------------------
 constexpr int kChunk = 32;
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-template <int NT>
-struct VecT;
-template <> struct VecT<1> { typedef float T; };
-template <> struct VecT<2> { typedef float2 T; };
-template <> struct VecT<4> { typedef float4 T; };
-
-template <int NT>
-__device__ __forceinline__ void load_vec(const float* p, float* v) {
-  if constexpr (NT == 4) {
-    float4 x = *reinterpret_cast<const float4*>(p);
-    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
-  } else if constexpr (NT == 2) {
-    float2 x = *reinterpret_cast<const float2*>(p);
-    v[0] = x.x; v[1] = x.y;
-  } else {
-    v[0] = p[0];
-  }
-}
-
 template <int LMAX, int C, int H, bool L0ONLY, bool TRANS>
-__global__ void __launch_bounds__(256) k_edge_contract(
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) k_edge_contract(
     int32_t n, const int32_t* __restrict__ arow, const float4* __restrict__ ageo,
     const int32_t* __restrict__ asrc, const int32_t* __restrict__ arev,
     const float* __restrict__ ew, const float4* __restrict__ es, const float* __restrict__ X,
@@ -392,17 +378,19 @@ __global__ void __launch_bounds__(256) k_edge_contract(
     const float* __restrict__ qk, float* __restrict__ qkbar) {
   constexpr int D = Dims<LMAX>::D;
   constexpr int DI = L0ONLY ? 1 : D;          // input components that can be non-zero
-  constexpr int KS = (DI + 3) / 4;            // 4-component MFMA steps
-  constexpr int NT = C / 16;                  // 16-channel tiles
+  constexpr int CQ = C / 4;                   // channel quads
+  constexpr int EPG = 64 / CQ;                // edges per group
+  constexpr int NDG = LMAX == 2 ? 2 : 1;      // groups of 4 output components on MFMA
+  constexpr bool VC8 = LMAX == 2;             // output component 8 on the VALU
   constexpr int dh = C / H;
-  static_assert(C % 16 == 0 && dh % NT == 0, "unsupported channel/head split");
+  static_assert(C % 16 == 0 && C <= 64 && dh % 4 == 0, "unsupported channel/head split");
   __shared__ float sA[4][kChunk][D * D];
   __shared__ float sAl[4][kChunk][4];
   __shared__ float sSs[4][TRANS ? kChunk : 1][4];
   __shared__ float sSd[4][TRANS ? kChunk : 1][4];
   __shared__ int32_t sJ[4][kChunk];
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g = lane >> 4, nn = lane & 15;  // MFMA lane coordinates
+  const int q = lane / CQ, m = lane % CQ, jj = lane & 3;
   const int32_t x = xcd_block(blockIdx.x, gridDim.x) * 4 + wv;
   if (x >= n) return;
   const int32_t a0 = arow[x], a1 = arow[x + 1];
@@ -435,10 +423,13 @@ __global__ void __launch_bounds__(256) k_edge_contract(
       MZ[(int64_t)x * 2 * H + H + lane] = Zh[lane];
     }
   }
-  floatx4 acc[NT];
+  floatx4 acc[4][NDG];
 #pragma unroll
-  for (int t = 0; t < NT; t++) acc[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-  const int hl = (NT * nn) / dh;  // head of this lane's A-operand channels
+  for (int t = 0; t < 4; t++)
+#pragma unroll
+    for (int d = 0; d < NDG; d++) acc[t][d] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  float4 acc8 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  const int hl = (4 * m) / dh;  // head of this lane's channels
   float qacc = 0.0f, kacc = 0.0f;
   const int hc = (lane < C ? lane : 0) / dh;  // head of channel `lane` (q/k adjoints)
   for (int32_t b = a0; b < a1; b += kChunk) {
@@ -490,47 +481,50 @@ __global__ void __launch_bounds__(256) k_edge_contract(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    // Groups of 4 edges: lane group g takes edge 4E + g; MFMA step k contracts input
-    // component k of those 4 edges. A lane fetches its edge's DI feature slices and DI
-    // coupling values per group; the next group is fetched before this group's MFMAs.
-    const int ngroups = (cnt + 3) >> 2;
-    float xv[DI][NT], bv[DI], al;
-    auto fetch = [&](int E, float (*xo)[NT], float* bo, float& ao) {
-      const int e = 4 * E + g;
-      if (e < cnt) {
-        ao = sAl[wv][e][hl];
-        const float* Xy = X + (int64_t)sJ[wv][e] * D * C + NT * nn;
+    // Groups of EPG edges; past the chunk's end a lane re-reads the last edge with alpha = 0.
+    // Two register sets of features alternate so that the next group is in flight during this
+    // group's MFMAs.
+    const int ngroups = (cnt + EPG - 1) / EPG;
+    auto fetch = [&](int E, float4* xo, float& ao, int& eo) {
+      const int e0 = E * EPG + q;
+      const int e = e0 < cnt ? e0 : cnt - 1;
+      ao = e0 < cnt ? sAl[wv][e][hl] : 0.0f;
+      eo = e;
+      const float* Xy = X + (int64_t)sJ[wv][e] * D * C + 4 * m;
 #pragma unroll
-        for (int k = 0; k < DI; k++) load_vec<NT>(Xy + k * C, xo[k]);
-        const float* Ae = sA[wv][e] + (nn < D ? nn : 0) * D;
+      for (int k = 0; k < DI; k++) xo[k] = *reinterpret_cast<const float4*>(Xy + k * C);
+    };
+    auto mma = [&](const float4* xi, float ai, int e) {
+      const float* Ae = sA[wv][e];
 #pragma unroll
-        for (int k = 0; k < DI; k++) bo[k] = nn < D ? Ae[k] : 0.0f;
-      } else {
-        ao = 0.0f;
+      for (int k = 0; k < DI; k++) {
+        const float xs[4] = {ai * xi[k].x, ai * xi[k].y, ai * xi[k].z, ai * xi[k].w};
 #pragma unroll
-        for (int k = 0; k < DI; k++) {
-          bo[k] = 0.0f;
+        for (int d = 0; d < NDG; d++) {
+          const float bk = Ae[(4 * d + jj) * D + k];
 #pragma unroll
-          for (int t = 0; t < NT; t++) xo[k][t] = 0.0f;
+          for (int t = 0; t < 4; t++)
+            acc[t][d] = __builtin_amdgcn_mfma_f32_4x4x1f32(xs[t], bk, acc[t][d], 0, 0, 0);
+        }
+        if constexpr (VC8) {
+          const float b8 = Ae[8 * D + k];
+          acc8.x = __builtin_fmaf(b8, xs[0], acc8.x);
+          acc8.y = __builtin_fmaf(b8, xs[1], acc8.y);
+          acc8.z = __builtin_fmaf(b8, xs[2], acc8.z);
+          acc8.w = __builtin_fmaf(b8, xs[3], acc8.w);
         }
       }
     };
-    fetch(0, xv, bv, al);
-    for (int E = 0; E < ngroups; E++) {
-      float xn[DI][NT], bn[DI], an;
-      fetch(E + 1, xn, bn, an);
-#pragma unroll
-      for (int k = 0; k < DI; k++)
-#pragma unroll
-        for (int t = 0; t < NT; t++)
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(al * xv[k][t], bv[k], acc[t], 0, 0, 0);
-#pragma unroll
-      for (int k = 0; k < DI; k++) {
-        bv[k] = bn[k];
-#pragma unroll
-        for (int t = 0; t < NT; t++) xv[k][t] = xn[k][t];
-      }
-      al = an;
+    float4 xa[DI], xb[DI];
+    float ala, alb;
+    int ea, eb;
+    fetch(0, xa, ala, ea);
+    for (int E = 0; E < ngroups; E += 2) {
+      fetch(E + 1, xb, alb, eb);
+      mma(xa, ala, ea);
+      if (E + 1 >= ngroups) break;
+      fetch(E + 2, xa, ala, ea);
+      mma(xb, alb, eb);
     }
     if (TRANS && lane < C) {
       for (int e = 0; e < cnt; e++) {
@@ -543,22 +537,47 @@ __global__ void __launch_bounds__(256) k_edge_contract(
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   }
-  // lane (g, nn) holds output component nn for channels NT*(4g + r) + t, r = 0..3
-  if (nn < D) {
-    float* o = out + (int64_t)x * D * C + nn * C;
+  // sum over the edge slots q of a group (lanes CQ apart)
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-      float v[NT];
+  for (int o = CQ; o < 64; o <<= 1) {
 #pragma unroll
-      for (int t = 0; t < NT; t++) v[t] = acc[t][r];
-      float* dst = o + NT * (4 * g + r);
-      if (!TRANS) {
+    for (int t = 0; t < 4; t++)
 #pragma unroll
-        for (int t = 0; t < NT; t++) dst[t] = v[t];
-      } else {
+      for (int d = 0; d < NDG; d++)
 #pragma unroll
-        for (int t = 0; t < NT; t++) dst[t] += v[t];
+        for (int r = 0; r < 4; r++) acc[t][d][r] += __shfl_xor(acc[t][d][r], o, 64);
+    if constexpr (VC8) {
+      acc8.x += __shfl_xor(acc8.x, o, 64);
+      acc8.y += __shfl_xor(acc8.y, o, 64);
+      acc8.z += __shfl_xor(acc8.z, o, 64);
+      acc8.w += __shfl_xor(acc8.w, o, 64);
+    }
+  }
+  if (lane < CQ) {
+    // lane 4bb + jj holds, for tile t and register r, channel 16 bb + 4 r + t of output
+    // component 4 d + jj
+    const int bb = lane >> 2;
+    float* o = out + (int64_t)x * D * C;
+#pragma unroll
+    for (int d = 0; d < NDG; d++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        float4* dst = reinterpret_cast<float4*>(o + (4 * d + jj) * C + 16 * bb + 4 * r);
+        float4 v = make_float4(acc[0][d][r], acc[1][d][r], acc[2][d][r], acc[3][d][r]);
+        if (TRANS) {
+          float4 pv = *dst;
+          v.x += pv.x; v.y += pv.y; v.z += pv.z; v.w += pv.w;
+        }
+        *dst = v;
       }
+    if constexpr (VC8) {
+      float4* dst = reinterpret_cast<float4*>(o + 8 * C + 4 * m);
+      float4 v = acc8;
+      if (TRANS) {
+        float4 pv = *dst;
+        v.x += pv.x; v.y += pv.y; v.z += pv.z; v.w += pv.w;
+      }
+      *dst = v;
     }
   }
   if (TRANS && lane < C) {

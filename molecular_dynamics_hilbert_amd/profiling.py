@@ -54,14 +54,15 @@ def _per_dispatch(rows):
 
 
 def traffic(fetch_csv: str, write_csv: str, kernel: str, copy_mib: int) -> dict:
-    """Bytes per launch of `kernel` (substring of the demangled name), scaled by the copy."""
+    """Bytes per launch of `kernel` (regular expression searched in the demangled name),
+    scaled by the copy."""
     res = {}
     for label, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
         d = _per_dispatch(_counter_rows(path, counter))
         copies = [v for (i, n), v in d.items() if "copyBuffer" in n or "copy" in n.lower()]
         copy_kib = max(copies) if copies else None
         scale = (copy_mib * 1024.0) / copy_kib if copy_kib else 1.0
-        vals = [v for (i, n), v in d.items() if kernel in n]
+        vals = [v for (i, n), v in d.items() if re.search(kernel, n)]
         res[label] = {"kib_per_launch_raw": sum(vals) / max(len(vals), 1), "launches": len(vals),
                       "copy_kib_raw": copy_kib, "copy_scale": scale,
                       "bytes_per_launch": 1024.0 * scale * sum(vals) / max(len(vals), 1)}
@@ -100,7 +101,7 @@ def write_summaries(stats_csv: str, fetch_csv: str, write_csv: str, kernel_key: 
         md.append("| %s | %.1f | %.1f | %.4f | %.4g |" % (cnt, r["kib_per_launch_raw"],
                                                         r["copy_kib_raw"] or 0, r["copy_scale"],
                                                         r["bytes_per_launch"]))
-    rows = [r for r in csv.DictReader(open(stats_csv)) if kernel_name in r["Name"]]
+    rows = [r for r in csv.DictReader(open(stats_csv)) if re.search(kernel_name, r["Name"])]
     calls = sum(int(r["Calls"]) for r in rows)
     tot = sum(float(r["TotalDurationNs"]) for r in rows)
     md += ["", "All launches matching `%s` (every layer): %d calls, average %.1f us." % (
