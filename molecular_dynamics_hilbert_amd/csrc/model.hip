@@ -25,6 +25,7 @@ namespace tess {
 namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 constexpr float kPi = 3.14159265358979323846f;
 
 inline int32_t gridn(int64_t n, int b) { return (int32_t)((n + b - 1) / b); }
@@ -366,8 +367,6 @@ __global__ void __launch_bounds__(256) k_edge_prep(const int32_t* __restrict__ a
 // L0ONLY: only the l = 0 input component is non-zero (first layer).
 // ---------------------------------------------------------------------------------------
 constexpr int kChunk = 32;
-
-typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 template <int LMAX, int C, int H, bool L0ONLY, bool TRANS>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) k_edge_contract(

@@ -217,7 +217,10 @@ __device__ __forceinline__ uint32_t xcd_block(uint32_t b, uint32_t nb) {
   return x < rem ? x * (per + 1) + idx : rem * (per + 1) + (x - rem) * per + idx;
 }
 
-__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// Logistic function with the hardware reciprocal (about 1 ulp).
+__device__ __forceinline__ float sigmoidf_(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
