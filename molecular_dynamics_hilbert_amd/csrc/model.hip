@@ -63,6 +63,27 @@ struct Epi {
 // loads: lanes 0-31 take k = 8s..8s+3 and lanes 32-63 k = 8s+4..8s+7, so MFMA step (s, q)
 // pairs k = 8s+q (first half-wave) with k = 8s+4+q (second half-wave), and the B operand
 // uses the same pairing. K must be a multiple of 8 and at most kGemmMaxK.
+// Offsets of output row v of a lane (row r0 + 8(v/4) + 4(lane/32) + v%4) in y, h and the
+// gates; rows past M are clamped (and flagged) so that loads stay in bounds. One 32-bit
+// division by the rows-per-node count (row maps of y and h share it).
+struct EpiRow {
+  int64_t yb, hb, gb;
+  bool ok;
+};
+__device__ __forceinline__ EpiRow epi_row(const Epi& ep, int64_t r0, int v, int lane, int64_t M) {
+  const int64_t r = r0 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+  EpiRow e;
+  e.ok = r < M;
+  const uint32_t rr = (uint32_t)(e.ok ? r : M - 1);
+  const uint32_t rpn = (uint32_t)ep.ym.rpn;
+  const uint32_t nd = rr / rpn;
+  const int32_t kc = (int32_t)(rr - nd * rpn);
+  e.yb = (int64_t)nd * ep.ym.nstride + (int64_t)(ep.ym.c0 + kc) * ep.ym.cstride;
+  e.hb = (int64_t)nd * ep.hm.nstride + (int64_t)(ep.hm.c0 + kc) * ep.hm.cstride;
+  e.gb = (int64_t)nd * ep.gstride + ep.goff;
+  return e;
+}
+
 constexpr int kGemmMaxK = 192;
 
 template <int EPI, int K>
@@ -88,11 +109,35 @@ __global__ void __launch_bounds__(256) k_gemm(int64_t M, int O, const float* __r
 #pragma unroll
     for (int s8 = 0; s8 < K / 8; s8++) xa[s8] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   }
+  // epilogue inputs of this lane's 32 elements (rows r0 + 8(v/4) + 4 half + v%4, columns
+  // o0 + col and o0 + 32 + col), requested before the MFMA loop
+  const int col = lane & 31;
+  bool ook[2], hok[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; nt++) {
+    ook[nt] = o0 + 32 * nt + col < O;
+    hok[nt] = ook[nt] && (EPI != EPI_UPD0 || o0 + 32 * nt + col < ep.cdim);
+  }
+  float in0[16][2], in1[16][2];
+#pragma unroll
+  for (int v = 0; v < 16; v++) {
+    const EpiRow er = epi_row(ep, r0, v, lane, M);
+#pragma unroll
+    for (int nt = 0; nt < 2; nt++) {
+      // unconditional loads from clamped columns (a load under a branch would be waited for
+      // inside the branch); values of columns outside the output are never used
+      const int o = o0 + 32 * nt + col;
+      in0[v][nt] = 0.0f;
+      in1[v][nt] = 0.0f;
+      if (EPI == EPI_ADD) in0[v][nt] = ep.y[er.yb + (ook[nt] ? o : 0)];
+      if (EPI == EPI_UPD0 || EPI == EPI_UPDL) in0[v][nt] = ep.hin[er.hb + (hok[nt] ? o : 0)];
+      if (EPI == EPI_UPDL) in1[v][nt] = ep.gates[er.gb + (ook[nt] ? o : 0)];
+    }
+  }
   __syncthreads();
   floatx16 acc0, acc1;
 #pragma unroll
   for (int v = 0; v < 16; v++) { acc0[v] = 0.0f; acc1[v] = 0.0f; }
-  const int col = lane & 31;
 #pragma unroll
   for (int s8 = 0; s8 < K / 8; s8++) {
     const float av[4] = {xa[s8].x, xa[s8].y, xa[s8].z, xa[s8].w};
@@ -103,30 +148,29 @@ __global__ void __launch_bounds__(256) k_gemm(int64_t M, int O, const float* __r
       acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av[q], Ws[k][32 + col], acc1, 0, 0, 0);
     }
   }
+  // Epilogue: the inputs loaded before the MFMA loop, then one store per element. The row
+  // offsets are recomputed here rather than kept live across the MFMA loop (the empty asm
+  // hides r0 from common-subexpression elimination).
+  int64_t r0s = r0;
+  asm volatile("" : "+v"(r0s));
 #pragma unroll
-  for (int nt = 0; nt < 2; nt++) {
+  for (int v = 0; v < 16; v++) {
+    const EpiRow er = epi_row(ep, r0s, v, lane, M);
 #pragma unroll
-    for (int v = 0; v < 16; v++) {
-      const int64_t r = r0 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+    for (int nt = 0; nt < 2; nt++) {
       const int o = o0 + 32 * nt + col;
-      if (r >= M || o >= O) continue;
       const float val = nt == 0 ? acc0[v] : acc1[v];
+      if (!er.ok || !ook[nt]) continue;
       if (EPI == EPI_STORE) {
-        ep.y[row_off(ep.ym, r) + o] = val;
+        ep.y[er.yb + o] = val;
       } else if (EPI == EPI_ADD) {
-        ep.y[row_off(ep.ym, r) + o] += val;
+        ep.y[er.yb + o] = in0[v][nt] + val;
       } else if (EPI == EPI_UPD0) {
-        ep.y[row_off(ep.ym, r) + o] = val;
-        if (o < ep.cdim) {
-          const int64_t hb = row_off(ep.hm, r) + o;
-          ep.hout[hb] = ep.hin[hb] + val * sigmoidf_(val);
-        }
+        ep.y[er.yb + o] = val;
+        if (hok[nt]) ep.hout[er.hb + o] = in0[v][nt] + val * sigmoidf_(val);
       } else {  // EPI_UPDL
-        ep.y[row_off(ep.ym, r) + o] = val;
-        const int64_t nd = r / ep.hm.rpn;
-        const float g = ep.gates[nd * ep.gstride + ep.goff + o];
-        const int64_t hb = row_off(ep.hm, r) + o;
-        ep.hout[hb] = ep.hin[hb] + sigmoidf_(g) * val;
+        ep.y[er.yb + o] = val;
+        ep.hout[er.hb + o] = in0[v][nt] + sigmoidf_(in1[v][nt]) * val;
       }
     }
   }
