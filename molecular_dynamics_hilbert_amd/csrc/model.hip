@@ -398,22 +398,21 @@ __global__ void __launch_bounds__(256) k_edge_prep(const int32_t* __restrict__ a
 //     hbar_x[d1][c] += alpha_e',h(c) sum_d3 A_e'[d3][d1] mbar_y[d3][c]   (A_e' uses Y(-n_a)),
 //     kbar_x[c] += sbar_e',h(c) q_y[c] / sqrt(d),  qbar_x[c] += sbar_a,h(c) k_y[c] / sqrt(d).
 //
-// Chunks of 32 edges: lanes first build alpha and A_e (lane = edge) into LDS. The channel sums
-// then run on 4x4x1 MFMA blocks (v_mfma_f32_4x4x1f32: 16 independent 4x4 outer products per
-// instruction; block b takes its A column from lanes 4b..4b+3 and its B row from the same
-// lanes, and lane 4b+j ends with D_b[r][j] in register r). Lane = (edge q of a group of
-// 64/(C/4) edges, channel quad m): it loads 4 consecutive channels of one input component
-// with one 16-byte load, and for s = 0..3 feeds channel 4m+s as its A value; its B value is
-// the coupling from that input component to output component 4g+(lane&3) of the same edge.
-// Blocks of different edges add into separate accumulators that are summed over the group's
-// edges once per row. Output components 0..7 use the matrix cores (two groups of four),
-// component 8 (l = 2, m = 2) is a vector FMA.
+// Chunks of 32 (adjoint: 24) edges: lanes first build alpha and A_e (lane = edge) into
+// LDS. The channel sums then run on 4x4x1 MFMA blocks (v_mfma_f32_4x4x1f32: 16 independent
+// 4x4 outer products per instruction; block b takes its A column from lanes 4b..4b+3 and
+// its B row from the same lanes, and lane 4b+j ends with D_b[r][j] in register r). Lane =
+// (edge q of a group of 64/(C/4) edges, channel quad m): it loads 4 consecutive channels of
+// one input component with one 16-byte load, and for s = 0..3 feeds channel 4m+s as its A
+// value; its B value is the coupling from that input component to output component
+// 4g+(lane&3) of the same edge. Blocks of different edges add into separate accumulators
+// that are summed over the group's edges once per row. Output components 0..7 use the
+// matrix cores (two groups of four), component 8 (l = 2, m = 2) is a vector FMA.
 // L0ONLY: only the l = 0 input component is non-zero (first layer).
 // ---------------------------------------------------------------------------------------
-constexpr int kChunk = 32;
 
 template <int LMAX, int C, int H, bool L0ONLY, bool TRANS>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) k_edge_contract(
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS ? 4 : 3, 8))) k_edge_contract(
     int32_t n, const int32_t* __restrict__ arow, const float4* __restrict__ ageo,
     const int32_t* __restrict__ asrc, const int32_t* __restrict__ arev,
     const float* __restrict__ ew, const float4* __restrict__ es, const float* __restrict__ X,
@@ -427,6 +426,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
   constexpr bool VC8 = LMAX == 2;             // output component 8 on the VALU
   constexpr int dh = C / H;
   static_assert(C % 16 == 0 && C <= 64 && dh % 4 == 0, "unsupported channel/head split");
+  // edges per chunk (the adjoint keeps less in registers and runs 4 waves per SIMD)
+  constexpr int kChunk = TRANS ? 24 : 32;
   __shared__ float sA[4][kChunk][D * D];
   __shared__ float sAl[4][kChunk][4];
   __shared__ float sSs[4][TRANS ? kChunk : 1][4];
