@@ -538,20 +538,39 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
 #pragma unroll
       for (int k = 0; k < DI; k++) xo[k] = *reinterpret_cast<const float4*>(Xy + k * C);
     };
+    // alpha depends on (edge, head of the channel). When a head spans 16 channels, the four
+    // rows of an MFMA block (channels 16(b%4)+4i+s) share one head, which is also the head of
+    // the lane supplying the block's B value, so alpha scales B; otherwise it scales A.
+    constexpr bool AL_ON_B = dh % 16 == 0;
     auto mma = [&](const float4* xi, float ai, int e) {
       const float* Ae = sA[wv][e];
+      // the forward reads the group's coupling values from LDS before its MFMAs; the adjoint
+      // (at 4 waves per SIMD) has no registers to spare for that and reads them per step
+      float bv[DI][NDG], b8v[DI];
 #pragma unroll
       for (int k = 0; k < DI; k++) {
-        const float xs[4] = {ai * xi[k].x, ai * xi[k].y, ai * xi[k].z, ai * xi[k].w};
+#pragma unroll
+        for (int d = 0; d < NDG; d++) bv[k][d] = TRANS ? 0.0f : Ae[(4 * d + jj) * D + k];
+        b8v[k] = (VC8 && !TRANS) ? Ae[8 * D + k] : 0.0f;
+      }
+#pragma unroll
+      for (int k = 0; k < DI; k++) {
+        if constexpr (TRANS) {
+#pragma unroll
+          for (int d = 0; d < NDG; d++) bv[k][d] = Ae[(4 * d + jj) * D + k];
+          if constexpr (VC8) b8v[k] = Ae[8 * D + k];
+        }
+        const float sa = AL_ON_B ? 1.0f : ai;
+        const float xs[4] = {sa * xi[k].x, sa * xi[k].y, sa * xi[k].z, sa * xi[k].w};
 #pragma unroll
         for (int d = 0; d < NDG; d++) {
-          const float bk = Ae[(4 * d + jj) * D + k];
+          const float bk = AL_ON_B ? ai * bv[k][d] : bv[k][d];
 #pragma unroll
           for (int t = 0; t < 4; t++)
             acc[t][d] = __builtin_amdgcn_mfma_f32_4x4x1f32(xs[t], bk, acc[t][d], 0, 0, 0);
         }
         if constexpr (VC8) {
-          const float b8 = Ae[8 * D + k];
+          const float b8 = AL_ON_B ? ai * b8v[k] : b8v[k];
           acc8.x = __builtin_fmaf(b8, xs[0], acc8.x);
           acc8.y = __builtin_fmaf(b8, xs[1], acc8.y);
           acc8.z = __builtin_fmaf(b8, xs[2], acc8.z);
