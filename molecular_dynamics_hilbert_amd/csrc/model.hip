@@ -195,14 +195,34 @@ hipError_t gemm(hipStream_t st, int64_t M, int K, int O, const float* X, RowMap 
 }
 
 // ---------------------------------------------------------------------------------------
-// Weight preparation: transposed copies for the forward GEMMs.
+// Weight preparation: transposed copies for the forward GEMMs, every layer in one launch
+// (blockIdx.y = layer). Per layer of the blob (row-major [out][in]): W_q, W_k, W1, W2, W_lin0,
+// W_lin^l; written as [W_q^T | W_k^T] ([C][2C]), W_lin0^T ([C][G]) and W_lin^l^T ([C][C]).
 // ---------------------------------------------------------------------------------------
-__global__ void k_transpose(const float* __restrict__ W, int rows, int cols, float* __restrict__ Wt,
-                            int ldt, int col_off) {
-  int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (k >= (int64_t)rows * cols) return;
-  int r = (int)(k / cols), c = (int)(k % cols);
-  Wt[(int64_t)c * ldt + col_off + r] = W[k];  // Wt[c][col_off + r] = W[r][c]
+template <int LMAX, int C, int R>
+__global__ void k_prep_weights(const float* __restrict__ weights, int S, int K,
+                               float* __restrict__ WqkT, float* __restrict__ W0T,
+                               float* __restrict__ WlT) {
+  constexpr int P = Dims<LMAX>::P;
+  constexpr int G = C * (1 + LMAX);
+  constexpr int NEL = 2 * C * C + G * C + LMAX * C * C;
+  const int t = blockIdx.y;
+  const int k = blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= NEL) return;
+  const int64_t stride = 2 * C * C + (int64_t)R * K + P * R + G * C + LMAX * C * C;
+  const float* lb = weights + (int64_t)S * C + t * stride;
+  const float* lin = lb + 2 * C * C + (int64_t)R * K + P * R;  // W_lin0, then W_lin^l
+  if (k < 2 * C * C) {
+    const int which = k / (C * C), kk = k % (C * C), r = kk / C, c = kk % C;
+    WqkT[(int64_t)t * C * 2 * C + c * 2 * C + which * C + r] = lb[k];
+  } else if (k < 2 * C * C + G * C) {
+    const int kk = k - 2 * C * C, r = kk / C, c = kk % C;
+    W0T[(int64_t)t * C * G + c * G + r] = lin[kk];
+  } else {
+    const int kk = k - 2 * C * C - G * C, l1 = kk / (C * C), k2 = kk % (C * C), r = k2 / C,
+              c = k2 % C;
+    WlT[((int64_t)t * LMAX + l1) * C * C + c * C + r] = lin[G * C + kk];
+  }
 }
 
 __global__ void k_embed(int32_t n, int C, int D, const int32_t* __restrict__ species,
@@ -416,8 +436,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
     int32_t n, const int32_t* __restrict__ arow, const float4* __restrict__ ageo,
     const int32_t* __restrict__ asrc, const int32_t* __restrict__ arev,
     const float* __restrict__ ew, const float4* __restrict__ es, const float* __restrict__ X,
-    float rc, float* __restrict__ out, float* __restrict__ MZ, const float4* __restrict__ sbar,
-    const float* __restrict__ qk, float* __restrict__ qkbar) {
+    float rc, float* __restrict__ out, const float* __restrict__ base, float* __restrict__ MZ,
+    const float4* __restrict__ sbar, const float* __restrict__ qk, float* __restrict__ qkbar) {
   constexpr int D = Dims<LMAX>::D;
   constexpr int DI = L0ONLY ? 1 : D;          // input components that can be non-zero
   constexpr int CQ = C / 4;                   // channel quads
@@ -619,28 +639,30 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
   if (lane < CQ) {
     // lane 4bb + jj holds, for tile t and register r, channel 16 bb + 4 r + t of output
     // component 4 d + jj
+    // the adjoint adds the residual path: out = base + contribution (every component of
+    // every row is written)
     const int bb = lane >> 2;
-    float* o = out + (int64_t)x * D * C;
+    const int64_t ro = (int64_t)x * D * C;
 #pragma unroll
     for (int d = 0; d < NDG; d++)
 #pragma unroll
       for (int r = 0; r < 4; r++) {
-        float4* dst = reinterpret_cast<float4*>(o + (4 * d + jj) * C + 16 * bb + 4 * r);
+        const int64_t off = ro + (4 * d + jj) * C + 16 * bb + 4 * r;
         float4 v = make_float4(acc[0][d][r], acc[1][d][r], acc[2][d][r], acc[3][d][r]);
         if (TRANS) {
-          float4 pv = *dst;
+          const float4 pv = *reinterpret_cast<const float4*>(base + off);
           v.x += pv.x; v.y += pv.y; v.z += pv.z; v.w += pv.w;
         }
-        *dst = v;
+        *reinterpret_cast<float4*>(out + off) = v;
       }
     if constexpr (VC8) {
-      float4* dst = reinterpret_cast<float4*>(o + 8 * C + 4 * m);
+      const int64_t off = ro + 8 * C + 4 * m;
       float4 v = acc8;
       if (TRANS) {
-        float4 pv = *dst;
+        const float4 pv = *reinterpret_cast<const float4*>(base + off);
         v.x += pv.x; v.y += pv.y; v.z += pv.z; v.w += pv.w;
       }
-      *dst = v;
+      *reinterpret_cast<float4*>(out + off) = v;
     }
   }
   if (TRANS && lane < C) {
@@ -694,13 +716,12 @@ __global__ void __launch_bounds__(256) k_energy_final(int32_t nb, const double* 
 //   xcat[n][0:C]      = gbar^0 * SiLU'(y0)
 //   xcat[n][lC:(l+1)C] = sum_m gbar^(l,m) y^(l,m) * sigmoid'(g_l)
 //   ybl[n][l^2+m][c]  = gbar^(l,m) * sigmoid(g_l)
-//   hbar = gbar (residual path), when hbar is not NULL.
+// (the residual path hbar = gbar + ... is added by the transposed edge contraction)
 // ---------------------------------------------------------------------------------------
 template <int LMAX>
 __global__ void k_bwd_update(int32_t n, int C, const float* __restrict__ gbar,
                              const float* __restrict__ yg, const float* __restrict__ yl,
-                             float* __restrict__ xcat, float* __restrict__ ybl,
-                             float* __restrict__ hbar) {
+                             float* __restrict__ xcat, float* __restrict__ ybl) {
   constexpr int D = Dims<LMAX>::D;
   int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (k >= (int64_t)n * C) return;
@@ -723,10 +744,6 @@ __global__ void k_bwd_update(int32_t n, int C, const float* __restrict__ gbar,
       ybl[i * D * C + d * C + c] = gv * sg;
     }
     xcat[i * G + l * C + c] = s * sg * (1.0f - sg);
-  }
-  if (hbar) {
-#pragma unroll
-    for (int d = 0; d < D; d++) hbar[i * D * C + d * C + c] = gb[d * C];
   }
 }
 
@@ -1095,14 +1112,10 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
   const float* emb = weights;
   const float* wE = weights + (int64_t)S * C + (int64_t)T * (2 * C * C + R * K + P * R + G * C + LMAX * C * C);
   // transposed weights
-  for (int t = 0; t < T; t++) {
-    float* qkT = w.WqkT + (int64_t)t * C * 2 * C;
-    k_transpose<<<gridn(C * C, 256), 256, 0, st>>>(lw[t].Wq, C, C, qkT, 2 * C, 0);
-    k_transpose<<<gridn(C * C, 256), 256, 0, st>>>(lw[t].Wk, C, C, qkT, 2 * C, C);
-    k_transpose<<<gridn(G * C, 256), 256, 0, st>>>(lw[t].W0, G, C, w.W0T + (int64_t)t * C * G, G, 0);
-    for (int l = 1; l <= LMAX; l++)
-      k_transpose<<<gridn(C * C, 256), 256, 0, st>>>(
-          lw[t].Wl[l], C, C, w.WlT + ((int64_t)t * LMAX + (l - 1)) * C * C, C, 0);
+  {
+    constexpr int NEL = 2 * C * C + G * C + LMAX * C * C;
+    k_prep_weights<LMAX, C, R><<<dim3(gridn(NEL, 256), T), 256, 0, st>>>(weights, S, K, w.WqkT,
+                                                                         w.W0T, w.WlT);
   }
   TESS_HIP_CHECK(hipGetLastError());
   const int64_t NDC = (int64_t)n * D * C;
@@ -1153,13 +1166,13 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     if (t == 0)
       TESS_TIMED("edge_apply", st,
                  k_edge_contract<LMAX, C, H, true, false><<<gridn(n, 4), 256, 0, st>>>(
-                     n, w.arow, w.ageo, w.asrc, w.arev, ew, es, ht, rc, mt, MZ, nullptr, nullptr,
-                     nullptr));
+                     n, w.arow, w.ageo, w.asrc, w.arev, ew, es, ht, rc, mt, nullptr, MZ, nullptr,
+                     nullptr, nullptr));
     else
       TESS_TIMED("edge_apply", st,
                  k_edge_contract<LMAX, C, H, false, false><<<gridn(n, 4), 256, 0, st>>>(
-                     n, w.arow, w.ageo, w.asrc, w.arev, ew, es, ht, rc, mt, MZ, nullptr, nullptr,
-                     nullptr));
+                     n, w.arow, w.ageo, w.asrc, w.arev, ew, es, ht, rc, mt, nullptr, MZ, nullptr,
+                     nullptr, nullptr));
     TESS_HIP_CHECK(hipGetLastError());
     Epi eu{};
     eu.y = yg;
@@ -1206,8 +1219,8 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     const float* ew = w.ew + (int64_t)t * ecap * 12;
     const float* edw = w.edw + (int64_t)t * ecap * 12;
     const float4* es = w.es + (int64_t)t * ecap;
-    k_bwd_update<LMAX><<<gridn((int64_t)n * C, 256), 256, 0, st>>>(n, C, gbar, yg, yl, w.xcat, w.ybl,
-                                                                 t > 0 ? hbar : nullptr);
+    k_bwd_update<LMAX><<<gridn((int64_t)n * C, 256), 256, 0, st>>>(n, C, gbar, yg, yl, w.xcat,
+                                                                 w.ybl);
     Epi em{};
     em.y = w.mbar;
     em.ym = feat0;
@@ -1237,7 +1250,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     if (t > 0) {
       TESS_TIMED("edge_tapply", st,
                  k_edge_contract<LMAX, C, H, false, true><<<gridn(n, 4), 256, 0, st>>>(
-                     n, w.arow, w.ageo, w.asrc, w.arev, ew, es, w.mbar, rc, hbar,
+                     n, w.arow, w.ageo, w.asrc, w.arev, ew, es, w.mbar, rc, hbar, gbar,
                      const_cast<float*>(MZ), w.sbar, qk, w.qkbar));
       Epi ea{};
       ea.y = hbar;
