@@ -79,6 +79,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="salt60k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-large", action="store_true",
+                    help="skip the 500,000-atom rebuild and E+F timing")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the benchmark, copy this many MiB device-to-device once (a plain "
                          "copy kernel of known size, to scale HBM counters)")
@@ -196,6 +198,7 @@ def main():
         "ef_ms": round(statistics.median(ef), 4),
         "roofline": roofline,
         "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in rows.items()},
+        "large_system": None if args.no_large else large_system(),
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(),
     }
     print(json.dumps(out), flush=True)
@@ -206,6 +209,39 @@ def main():
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
+
+
+def large_system(name: str = "salt500k") -> dict:
+    """Rebuild and E+F of the 500,000-atom box (edge 171 A, 4-layer model): medians of 5
+    rebuilds and 3 E+F passes after one of each untimed, HIP events on the stream."""
+    import torch
+
+    from molecular_dynamics_hilbert_amd import tess as T
+    from molecular_dynamics_hilbert_amd import workloads as W
+    wl = W.load(name)
+    s = T.System(wl, W.make_weights(wl.model, 2005))
+    st = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        out = []
+        for _ in range(reps + 1):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            fn()
+            b.record(st)
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b))
+        return statistics.median(out[1:])
+
+    rb = timed(s.rebuild, 5)
+    ef = timed(s.energy_forces, 3)
+    n_cand = s.n_edges
+    res = {"workload": name, "n_atoms": wl.n, "box_A": float(wl.box[0]),
+           "pairs_r_c_plus_skin": n_cand, "rebuild_ms": round(rb, 4), "ef_ms": round(ef, 3),
+           "ef_atom_steps_per_s": round(wl.n / (ef * 1e-3), 1)}
+    del s
+    torch.cuda.empty_cache()
+    return res
 
 
 def _traffic(kernel: str, workload: str):

@@ -432,7 +432,7 @@ __global__ void __launch_bounds__(256) k_edge_prep(const int32_t* __restrict__ a
 // ---------------------------------------------------------------------------------------
 
 template <int LMAX, int C, int H, bool L0ONLY, bool TRANS>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS ? 4 : 3, 8))) k_edge_contract(
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS ? 4 : (L0ONLY ? 4 : 3), 8))) k_edge_contract(
     int32_t n, const int32_t* __restrict__ arow, const float4* __restrict__ ageo,
     const int32_t* __restrict__ asrc, const int32_t* __restrict__ arev,
     const float* __restrict__ ew, const float4* __restrict__ es, const float* __restrict__ X,
@@ -448,7 +448,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
   static_assert(C % 16 == 0 && C <= 64 && dh % 4 == 0, "unsupported channel/head split");
   // edges per chunk (the adjoint keeps less in registers and runs 4 waves per SIMD)
   constexpr int kChunk = TRANS ? 24 : 32;
-  __shared__ float sA[4][kChunk][D * D];
+  __shared__ float sA[4][kChunk][D * DI];
   __shared__ float sAl[4][kChunk][4];
   __shared__ float sSs[4][TRANS ? kChunk : 1][4];
   __shared__ float sSd[4][TRANS ? kChunk : 1][4];
@@ -535,11 +535,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
       float A[D * D];
       coupling_matrix<LMAX>(w, Y, A);
       // row o of the LDS copy lists the coupling of output component o to every input
-      // component: A itself (forward) or its transpose (adjoint)
+      // component that can be non-zero: A itself (forward) or its transpose (adjoint); the
+      // entries that are never stored are never computed
 #pragma unroll
       for (int o = 0; o < D; o++)
 #pragma unroll
-        for (int k = 0; k < D; k++) sA[wv][lane][o * D + k] = TRANS ? A[k * D + o] : A[o * D + k];
+        for (int k = 0; k < DI; k++) sA[wv][lane][o * DI + k] = TRANS ? A[k * D + o] : A[o * D + k];
       sJ[wv][lane] = y;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -570,15 +571,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
 #pragma unroll
       for (int k = 0; k < DI; k++) {
 #pragma unroll
-        for (int d = 0; d < NDG; d++) bv[k][d] = TRANS ? 0.0f : Ae[(4 * d + jj) * D + k];
-        b8v[k] = (VC8 && !TRANS) ? Ae[8 * D + k] : 0.0f;
+        for (int d = 0; d < NDG; d++) bv[k][d] = TRANS ? 0.0f : Ae[(4 * d + jj) * DI + k];
+        b8v[k] = (VC8 && !TRANS) ? Ae[8 * DI + k] : 0.0f;
       }
 #pragma unroll
       for (int k = 0; k < DI; k++) {
         if constexpr (TRANS) {
 #pragma unroll
-          for (int d = 0; d < NDG; d++) bv[k][d] = Ae[(4 * d + jj) * D + k];
-          if constexpr (VC8) b8v[k] = Ae[8 * D + k];
+          for (int d = 0; d < NDG; d++) bv[k][d] = Ae[(4 * d + jj) * DI + k];
+          if constexpr (VC8) b8v[k] = Ae[8 * DI + k];
         }
         const float sa = AL_ON_B ? 1.0f : ai;
         const float xs[4] = {sa * xi[k].x, sa * xi[k].y, sa * xi[k].z, sa * xi[k].w};
