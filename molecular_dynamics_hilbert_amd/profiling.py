@@ -119,11 +119,11 @@ def main(argv):
         # summarize <prof_dir> <pmc_fetch_dir> <pmc_write_dir> <kernel_key> <kernel_name> <workload> <copy_mib>
         d, f, w, key, name, wl, mib = argv[1:8]
         cmds = ["rocprofv3 --kernel-trace --stats -f csv -d %s -o run -- python bench.py --steps 20 "
-                "--warmup 20 --no-cpu-baseline" % d,
+                "--warmup 20 --no-cpu-baseline --no-large" % d,
                 "rocprofv3 --pmc FETCH_SIZE -f csv -d %s -o run -- python bench.py --steps 1 "
-                "--warmup 1 --no-cpu-baseline --copy-calibration-mib %s" % (f, mib),
+                "--warmup 1 --no-cpu-baseline --no-large --copy-calibration-mib %s" % (f, mib),
                 "rocprofv3 --pmc WRITE_SIZE -f csv -d %s -o run -- python bench.py --steps 1 "
-                "--warmup 1 --no-cpu-baseline --copy-calibration-mib %s" % (w, mib)]
+                "--warmup 1 --no-cpu-baseline --no-large --copy-calibration-mib %s" % (w, mib)]
         write_summaries(os.path.join(d, "run_kernel_stats.csv"),
                         os.path.join(f, "run_counter_collection.csv"),
                         os.path.join(w, "run_counter_collection.csv"), key, name, wl, int(mib),
