@@ -231,11 +231,12 @@ __global__ void __launch_bounds__(64) k_pairs(int32_t n, CellGrid g, double rcs2
                                               int32_t* __restrict__ row_ptr,
                                               uint32_t* __restrict__ col_shift,
                                               int32_t* __restrict__ misc) {
-  __shared__ int32_t vcell[27], vcode[27], vpre[28];
+  __shared__ int32_t vstart[27], vcode[27], vpre[28];
   __shared__ uint32_t buf[FILL ? kMaxRow : 1];
   const int32_t i = blockIdx.x;
   const int lane = threadIdx.x;
   const double xi0 = (double)pos[3 * i], xi1 = (double)pos[3 * i + 1], xi2 = (double)pos[3 * i + 2];
+  int32_t csize = 0;
   if (lane < 27) {
     int c = cell_id[i];
     int cz = c % g.nc[2], cy = (c / g.nc[2]) % g.nc[1], cx = c / (g.nc[1] * g.nc[2]);
@@ -248,31 +249,50 @@ __global__ void __launch_bounds__(64) k_pairs(int32_t n, CellGrid g, double rcs2
       else if (cc[a] >= g.nc[a]) { cc[a] -= g.nc[a]; s[a] = 1; }
     }
     int cell = (cc[0] * g.nc[1] + cc[1]) * g.nc[2] + cc[2];
-    vcell[lane] = cell;
+    const int32_t c0 = cell_start[cell];
+    vstart[lane] = c0;
     vcode[lane] = 9 * (s[0] + 1) + 3 * (s[1] + 1) + (s[2] + 1);
-    vpre[lane + 1] = cell_start[cell + 1] - cell_start[cell];
+    csize = cell_start[cell + 1] - c0;
   }
-  if (lane == 0) vpre[0] = 0;
-  __syncthreads();
-  if (lane == 0)
-    for (int v = 0; v < 27; v++) vpre[v + 1] += vpre[v];
+  // inclusive prefix of the 27 cell sizes across lanes (wave scan), vpre[v] = start of cell v
+  {
+    int32_t inc = csize;
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+      const int32_t y = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += y;
+    }
+    if (lane < 27) vpre[lane + 1] = inc;
+    if (lane == 0) vpre[0] = 0;
+  }
   __syncthreads();
   const int total = vpre[27];
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int count = 0;
-  for (int q0 = 0; q0 < total; q0 += 64) {
-    int q = q0 + lane;
-    bool pass = false;
-    uint32_t entry = 0;
-    if (q < total) {
+  // Candidates q0 + lane and q0 + 64 + lane are tested together (two independent load
+  // chains per lane); their ballots are consumed in candidate order.
+  for (int q0 = 0; q0 < total; q0 += 128) {
+    bool pass[2] = {false, false};
+    uint32_t entry[2] = {0u, 0u};
+    int32_t jv[2];
+    int vv[2];
+    bool ok[2];
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      const int q = q0 + 64 * h + lane;
+      ok[h] = q < total;
       int lo = 0, hi = 27;  // find v with vpre[v] <= q < vpre[v+1]
       while (hi - lo > 1) {
         int mid = (lo + hi) >> 1;
         if (vpre[mid] <= q) lo = mid; else hi = mid;
       }
-      int v = lo;
-      int32_t j = cell_atoms[cell_start[vcell[v]] + (q - vpre[v])];
-      int code = vcode[v];
+      vv[h] = lo;
+      jv[h] = ok[h] ? cell_atoms[vstart[lo] + (q - vpre[lo])] : i;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      const int32_t j = jv[h];
+      const int code = vcode[vv[h]];
       double s0 = (double)(code / 9 - 1), s1 = (double)((code / 3) % 3 - 1),
              s2 = (double)(code % 3 - 1);
       double r0 = ((double)pos[3 * j] - xi0) + s0 * g.L[0];
@@ -280,21 +300,47 @@ __global__ void __launch_bounds__(64) k_pairs(int32_t n, CellGrid g, double rcs2
       double r2 = ((double)pos[3 * j + 2] - xi2) + s2 * g.L[2];
       double rr = r0 * r0 + r1 * r1;
       rr = rr + r2 * r2;
-      pass = (rr < rcs2) && !(j == i && code == 13);
-      entry = ((uint32_t)j << 5) | (uint32_t)code;
+      pass[h] = ok[h] && (rr < rcs2) && !(j == i && code == 13);
+      entry[h] = ((uint32_t)j << 5) | (uint32_t)code;
     }
-    uint64_t m = __ballot(pass);
-    if (FILL) {
-      int slot = count + __popcll(m & lt);
-      if (pass && slot < kMaxRow) buf[slot] = entry;
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      uint64_t m = __ballot(pass[h]);
+      if (FILL) {
+        int slot = count + __popcll(m & lt);
+        if (pass[h] && slot < kMaxRow) buf[slot] = entry[h];
+      }
+      count += __popcll(m);
     }
-    count += __popcll(m);
   }
   if (!FILL) {
     if (lane == 0) row_ptr[i] = count;
     return;
   }
   if (count > kMaxRow) return;  // rejected on the host before this pass runs
+  int64_t o = row_ptr[i];
+  __syncthreads();
+  if (count <= 256) {
+    // rank sort: keys within a row are distinct, so an entry's position is the number of
+    // smaller keys (the wave reads every key once, a broadcast LDS read per key)
+    uint32_t mine[4];
+    int rank[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      mine[u] = lane + 64 * u < count ? buf[lane + 64 * u] : 0xFFFFFFFFu;
+      rank[u] = 0;
+    }
+    for (int k = 0; k < count; k++) {
+      const uint32_t y = buf[k];
+#pragma unroll
+      for (int u = 0; u < 4; u++) rank[u] += y < mine[u] ? 1 : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; u++)
+      if (lane + 64 * u < count)
+        col_shift[o + rank[u]] = (mine[u] >> 5) | ((mine[u] & 31u) << 27);
+    return;
+  }
   int p2 = 1;
   while (p2 < count) p2 <<= 1;
   for (int k = count + lane; k < p2; k += 64) buf[k] = 0xFFFFFFFFu;
@@ -311,7 +357,6 @@ __global__ void __launch_bounds__(64) k_pairs(int32_t n, CellGrid g, double rcs2
       __syncthreads();
     }
   }
-  int64_t o = row_ptr[i];
   for (int k = lane; k < count; k += 64) {
     uint32_t e = buf[k];
     col_shift[o + k] = (e >> 5) | ((e & 31u) << 27);
@@ -339,18 +384,35 @@ __global__ void __launch_bounds__(256) k_rev(int32_t n, const int32_t* __restric
   int lane = threadIdx.x & 63;
   if (i >= n) return;
   int32_t b = row_ptr[i], e_end = row_ptr[i + 1];
-  for (int32_t e = b + lane; e < e_end; e += 64) {
-    uint32_t c = col[e];
-    int32_t j = (int32_t)(c & 0x7FFFFFFu);
-    uint32_t want = ((uint32_t)i << 5) | (26u - (c >> 27));
-    int32_t lo = row_ptr[j], hi = row_ptr[j + 1];
-    while (lo < hi) {
-      int32_t mid = (lo + hi) >> 1;
-      uint32_t cm = col[mid];
-      uint32_t km = ((cm & 0x7FFFFFFu) << 5) | (cm >> 27);
-      if (km < want) lo = mid + 1; else hi = mid;
+  // two entries per lane, their binary searches interleaved (independent load chains)
+  for (int32_t e0 = b + lane; e0 < e_end; e0 += 128) {
+    int32_t lo[2], hi[2];
+    uint32_t want[2];
+    bool ok[2];
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      const int32_t e = e0 + 64 * h;
+      ok[h] = e < e_end;
+      const uint32_t c = col[ok[h] ? e : e0];
+      const int32_t j = (int32_t)(c & 0x7FFFFFFu);
+      want[h] = ((uint32_t)i << 5) | (26u - (c >> 27));
+      lo[h] = ok[h] ? row_ptr[j] : 0;
+      hi[h] = ok[h] ? row_ptr[j + 1] : 0;
     }
-    rev[e] = lo;
+    while (lo[0] < hi[0] || lo[1] < hi[1]) {
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        if (lo[h] < hi[h]) {
+          const int32_t mid = (lo[h] + hi[h]) >> 1;
+          const uint32_t cm = col[mid];
+          const uint32_t km = ((cm & 0x7FFFFFFu) << 5) | (cm >> 27);
+          if (km < want[h]) lo[h] = mid + 1; else hi[h] = mid;
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; h++)
+      if (ok[h]) rev[e0 + 64 * h] = lo[h];
   }
 }
 
