@@ -496,16 +496,33 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
   const int hl = (4 * m) / dh;  // head of this lane's channels
   float qacc = 0.0f, kacc = 0.0f;
   const int hc = (lane < C ? lane : 0) / dh;  // head of channel `lane` (q/k adjoints)
+  // Per-edge inputs of a chunk's prologue (lane = edge). The forward requests those of the
+  // next chunk before the current chunk's MFMA groups, so their latency is hidden.
+  constexpr int PP = Dims<LMAX>::P;
+  int32_t pf_y = 0;
+  float4 pf_geo = make_float4(0.0f, 0.0f, 0.0f, 1.0f), pf_s4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  float pf_w[PP];
+  auto prefetch = [&](int32_t bb) {
+    const int32_t a = bb + lane;
+    if (!TRANS && bb < a1 && lane < min(kChunk, a1 - bb)) {
+      pf_y = asrc[a];
+      pf_geo = ageo[a];
+      pf_s4 = es[a];
+#pragma unroll
+      for (int p = 0; p < PP; p++) pf_w[p] = ew[(int64_t)a * 12 + p];
+    }
+  };
+  prefetch(a0);
   for (int32_t b = a0; b < a1; b += kChunk) {
     const int cnt = min(kChunk, a1 - b);
     if (lane < cnt) {
       const int32_t a = b + lane;
-      const int32_t y = asrc[a];
-      float4 geo = ageo[a];
+      const int32_t y = TRANS ? asrc[a] : pf_y;
+      float4 geo = TRANS ? ageo[a] : pf_geo;
       float u = 0.5f * (__cosf(kPi * geo.w / rc) + 1.0f);
       float sv[4];
       if (!TRANS) {
-        float4 s4 = es[a];
+        float4 s4 = pf_s4;
         sv[0] = s4.x; sv[1] = s4.y; sv[2] = s4.z; sv[3] = s4.w;
 #pragma unroll
         for (int hh = 0; hh < 4; hh++)
@@ -531,7 +548,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
       sph<LMAX>(sg * geo.x * ir, sg * geo.y * ir, sg * geo.z * ir, Y);
       float w[Dims<LMAX>::P];
 #pragma unroll
-      for (int p = 0; p < Dims<LMAX>::P; p++) w[p] = ew[(int64_t)a * 12 + p];
+      for (int p = 0; p < Dims<LMAX>::P; p++) w[p] = TRANS ? ew[(int64_t)a * 12 + p] : pf_w[p];
       float A[D * D];
       coupling_matrix<LMAX>(w, Y, A);
       // row o of the LDS copy lists the coupling of output component o to every input
@@ -546,6 +563,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    prefetch(b + kChunk);
     // Groups of EPG edges; past the chunk's end a lane re-reads the last edge with alpha = 0.
     // Two register sets of features alternate so that the next group is in flight during this
     // group's MFMAs.
@@ -565,18 +583,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
     constexpr bool AL_ON_B = dh % 16 == 0;
     auto mma = [&](const float4* xi, float ai, int e) {
       const float* Ae = sA[wv][e];
-      // the forward reads the group's coupling values from LDS before its MFMAs; the adjoint
-      // (at 4 waves per SIMD) has no registers to spare for that and reads them per step
       float bv[DI][NDG], b8v[DI];
 #pragma unroll
       for (int k = 0; k < DI; k++) {
 #pragma unroll
-        for (int d = 0; d < NDG; d++) bv[k][d] = TRANS ? 0.0f : Ae[(4 * d + jj) * DI + k];
-        b8v[k] = (VC8 && !TRANS) ? Ae[8 * DI + k] : 0.0f;
+        for (int d = 0; d < NDG; d++) bv[k][d] = 0.0f;
+        b8v[k] = 0.0f;
       }
 #pragma unroll
       for (int k = 0; k < DI; k++) {
-        if constexpr (TRANS) {
+        {
 #pragma unroll
           for (int d = 0; d < NDG; d++) bv[k][d] = Ae[(4 * d + jj) * DI + k];
           if constexpr (VC8) b8v[k] = Ae[8 * DI + k];
