@@ -51,7 +51,7 @@ enum { EPI_STORE = 0, EPI_ADD = 1, EPI_UPD0 = 2, EPI_UPDL = 3 };
 struct Epi {
   float* y;           // output (store/add), or pre-activation store for UPD*
   RowMap ym;
-  const float* hin;   // UPD*: residual input features
+  const float* hin;   // UPD*: residual input features (UPDL: NULL means zero)
   float* hout;        // UPD*: output features
   RowMap hm;          // UPD*: map of hin/hout rows
   const float* gates; // UPDL: [N][C(1+Lm)] pre-activations (gate of degree l at l*C)
@@ -130,7 +130,8 @@ __global__ void __launch_bounds__(256) k_gemm(int64_t M, int O, const float* __r
       in0[v][nt] = 0.0f;
       in1[v][nt] = 0.0f;
       if (EPI == EPI_ADD) in0[v][nt] = ep.y[er.yb + (ook[nt] ? o : 0)];
-      if (EPI == EPI_UPD0 || EPI == EPI_UPDL) in0[v][nt] = ep.hin[er.hb + (hok[nt] ? o : 0)];
+      if (EPI == EPI_UPD0 || EPI == EPI_UPDL)  // a NULL residual input reads as zero
+        in0[v][nt] = ep.hin ? ep.hin[er.hb + (hok[nt] ? o : 0)] : 0.0f;
       if (EPI == EPI_UPDL) in1[v][nt] = ep.gates[er.gb + (ook[nt] ? o : 0)];
     }
   }
@@ -225,14 +226,15 @@ __global__ void k_prep_weights(const float* __restrict__ weights, int S, int K,
   }
 }
 
+// h^0: the species embedding in the l = 0 component. The l >= 1 components of h^0 are zero
+// and never read (layer 0 contracts only l = 0 inputs and its gated update starts from zero).
 __global__ void k_embed(int32_t n, int C, int D, const int32_t* __restrict__ species,
                         const float* __restrict__ emb, float* __restrict__ h) {
   int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (k >= (int64_t)n * D * C) return;
-  int64_t i = k / (D * C);
-  int rem = (int)(k - i * D * C);
-  int d = rem / C, c = rem % C;
-  h[k] = d == 0 ? emb[species[i] * C + c] : 0.0f;
+  if (k >= (int64_t)n * C) return;
+  int64_t i = k / C;
+  int c = (int)(k - i * C);
+  h[i * D * C + c] = emb[species[i] * C + c];
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1016,20 +1018,30 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
   }
 }
 
-__global__ void k_forces(int32_t n, const int32_t* __restrict__ arow, const int32_t* __restrict__ arev,
-                         const float* __restrict__ gacc, float* __restrict__ F) {
-  int32_t x = blockIdx.x * blockDim.x + threadIdx.x;
+// F_x = sum over the row's active edges a of (g_a - g_rev(a)); one wave per row, lanes over
+// edges, a fixed-order wave sum (deterministic).
+__global__ void __launch_bounds__(256) k_forces(int32_t n, const int32_t* __restrict__ arow,
+                                                const int32_t* __restrict__ arev,
+                                                const float* __restrict__ gacc,
+                                                float* __restrict__ F) {
+  const int32_t x = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   if (x >= n) return;
   float f0 = 0.0f, f1 = 0.0f, f2 = 0.0f;
-  for (int32_t a = arow[x]; a < arow[x + 1]; a++) {
-    int32_t b = arev[a];
-    f0 += gacc[a * 3] - gacc[(int64_t)b * 3];
-    f1 += gacc[a * 3 + 1] - gacc[(int64_t)b * 3 + 1];
-    f2 += gacc[a * 3 + 2] - gacc[(int64_t)b * 3 + 2];
+  for (int32_t a = arow[x] + lane; a < arow[x + 1]; a += 64) {
+    const int32_t b = arev[a];
+    f0 += gacc[(int64_t)a * 3] - gacc[(int64_t)b * 3];
+    f1 += gacc[(int64_t)a * 3 + 1] - gacc[(int64_t)b * 3 + 1];
+    f2 += gacc[(int64_t)a * 3 + 2] - gacc[(int64_t)b * 3 + 2];
   }
-  F[3 * x] = f0;
-  F[3 * x + 1] = f1;
-  F[3 * x + 2] = f2;
+  f0 = wave_sum(f0);
+  f1 = wave_sum(f1);
+  f2 = wave_sum(f2);
+  if (lane == 0) {
+    F[3 * (int64_t)x] = f0;
+    F[3 * (int64_t)x + 1] = f1;
+    F[3 * (int64_t)x + 2] = f2;
+  }
 }
 
 }  // namespace
@@ -1137,7 +1149,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
   TESS_HIP_CHECK(hipGetLastError());
   const int64_t NDC = (int64_t)n * D * C;
   // embedding
-  k_embed<<<gridn(NDC, 256), 256, 0, st>>>(n, C, D, species, emb, w.h);
+  k_embed<<<gridn((int64_t)n * C, 256), 256, 0, st>>>(n, C, D, species, emb, w.h);
   // active edges
   const int32_t* rev = rev_in;
   if (cap > 0) {
@@ -1204,7 +1216,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
       Epi el{};
       el.y = yl;
       el.ym = ml;
-      el.hin = ht;
+      el.hin = t == 0 ? nullptr : ht;  // h^0 has no l >= 1 components
       el.hout = hn;
       el.hm = ml;
       el.gates = yg;
@@ -1279,7 +1291,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     }
   }
   if (cap > 0) {
-    k_forces<<<gridn(n, 256), 256, 0, st>>>(n, w.arow, w.arev, w.gacc, forces);
+    k_forces<<<gridn(n, 4), 256, 0, st>>>(n, w.arow, w.arev, w.gacc, forces);
   } else if (n > 0) {
     TESS_HIP_CHECK(hipMemsetAsync(forces, 0, sizeof(float) * 3 * (size_t)n, st));
   }
