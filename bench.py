@@ -81,6 +81,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-large", action="store_true",
                     help="skip the 500,000-atom rebuild and E+F timing")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each rebuild interval from a captured HIP graph "
+                         "(TESS_MD_GRAPH); per-kernel timing then comes from a second, eager "
+                         "pass of the same length")
+    ap.add_argument("--no-hooks", action="store_true",
+                    help="time the MD steps without the per-kernel HIP events (A/B of their "
+                         "cost); per-kernel timing then comes from a second pass")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the benchmark, copy this many MiB device-to-device once (a plain "
                          "copy kernel of known size, to scale HBM counters)")
@@ -90,6 +97,15 @@ def main():
               "described in DESIGN.md); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    import torch
+
+    # all work on one created stream (default priority): HIP graphs cannot be captured on the
+    # NULL stream, and eager and graph runs then share the same stream setup
+    with torch.cuda.stream(torch.cuda.Stream()):
+        run(args)
+
+
+def run(args):
     import torch
 
     from molecular_dynamics_hilbert_amd import tess as T
@@ -109,7 +125,7 @@ def main():
 
     skin_flags = [0]
 
-    def md(nsteps, valid):
+    def md(nsteps, valid, graph=False):
         """Run nsteps as whole rebuild intervals (one tess_md_steps call per interval, each
         starting with a rebuild). Random weights bind nothing, so at 300 K the fastest H atoms
         can pass skin/2 inside an interval; the library then reports TESS_ERR_SKIN after
@@ -120,27 +136,46 @@ def main():
             st, _ = T.md_steps(s.spec, s.weights, s.box, s.r_cut, s.skin, s.pos, vel, s.species,
                                masses, wl.dt_fs, k, every, pa, s.forces, s.row_ptr, s.col_shift,
                                s.rev, s.ws, epot_trace=ep, forces_valid=valid or done > 0,
-                               check=False)
+                               graph=graph, check=False)
             if st == T.ERR_SKIN:
                 skin_flags[0] += 1
             elif st != T.OK:
                 raise T.TessError(st, "tess_md_steps")
             done += k
 
-    # warmup (first call computes the initial forces)
-    md(max(args.warmup, 1), False)
+    # warmup (first call computes the initial forces; with --graph it also captures the graph)
+    md(max(args.warmup, 1), False, args.graph)
     torch.cuda.synchronize()
     skin_flags[0] = 0
-    # timed region: exactly `steps` MD steps, inputs resident in HBM
+    names = ("edge_prep", "edge_apply", "edge_grad", "edge_tapply", "node_gemm", "radix_scatter",
+             "nbr_count", "nbr_fill")
+    # profile pass (same length): HIP events around every instrumented kernel, giving the
+    # per-kernel times and the dominant edge kernel
     T.timing_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     md(args.steps, True)
     torch.cuda.synchronize()
-    t_total = time.perf_counter() - t0
-    kern = {k: T.timing_read(k) for k in ("edge_prep", "edge_apply", "edge_grad", "edge_tapply",
-                                          "node_gemm", "radix_scatter", "nbr_count", "nbr_fill")}
+    kern = {k: T.timing_read(k) for k in names}
     T.timing_enable(False)
+    dom = max(("edge_apply", "edge_grad", "edge_tapply", "edge_prep"), key=lambda k: kern[k][0])
+    skin_flags[0] = 0
+    # timed region: exactly `steps` MD steps, inputs resident in HBM. Only the dominant kernel
+    # carries HIP events in it (its roofline numbers come from this region); --graph and
+    # --no-hooks time a region without any events and take the dominant kernel's times from
+    # the profile pass
+    hooks_in_region = not (args.graph or args.no_hooks)
+    if hooks_in_region:
+        T.timing_only(dom)
+        T.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    md(args.steps, True, args.graph)
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t0
+    skin_timed = skin_flags[0]
+    if hooks_in_region:
+        kern[dom] = T.timing_read(dom)
+        T.timing_enable(False)
+        T.timing_only(None)
     value = wl.n * args.steps / t_total
     ms_per_step = 1e3 * t_total / args.steps
 
@@ -173,8 +208,6 @@ def main():
     for k, (ms, cnt) in kern.items():
         if cnt:
             rows[k] = {"launches": cnt, "avg_ms": ms / cnt, "total_ms": ms}
-    dom = max(("edge_apply", "edge_grad", "edge_tapply", "edge_prep"),
-              key=lambda k: kern[k][0])
     dom_ms, dom_cnt = kern[dom]
     dom_flops = flops[dom] * ef_calls
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12 if dom_ms > 0 else 0.0
@@ -193,7 +226,9 @@ def main():
                    "layers": wl.model.n_layers, "channels": wl.model.channels,
                    "l_max": wl.model.l_max, "heads": wl.model.n_heads,
                    "rebuild_every": every, "dt_fs": wl.dt_fs, "pairs_r_c_plus_skin": n_cand,
-                   "pairs_r_c": n_active, "skin_flagged_intervals": skin_flags[0]},
+                   "pairs_r_c": n_active, "skin_flagged_intervals": skin_timed,
+                   "launch": "hip_graph" if args.graph else "eager",
+                   "kernel_events_in_timed_region": dom if hooks_in_region else None},
         "rebuild_ms": round(statistics.median(rb), 4),
         "ef_ms": round(statistics.median(ef), 4),
         "roofline": roofline,

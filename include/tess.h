@@ -105,6 +105,7 @@ int32_t tess_energy_forces(const tess_model_desc* desc, const float* weights, in
                            void* hip_stream);
 
 #define TESS_MD_FORCES_VALID 1 /* forces[] already holds F(pos) in the current order */
+#define TESS_MD_GRAPH 2        /* replay each interval's steps from a captured HIP graph */
 
 /* tess_md_steps -- velocity-Verlet MD with a neighbour rebuild every `rebuild_every` steps
  * (Tessera abstract: a conservative skin keeps the topology between rebuilds). For
@@ -118,7 +119,13 @@ int32_t tess_energy_forces(const tess_model_desc* desc, const float* weights, in
  *  out    epot_trace device double[n_steps] (nullable); row_ptr/col_shift/rev as in
  *         tess_build_neighbors; *n_edges (HOST) pairs of the last rebuild
  * Synchronises once per rebuild. If an atom moved more than skin/2 from its position at
- * the last rebuild, the call finishes that interval and returns TESS_ERR_SKIN. */
+ * the last rebuild, the call finishes that interval and returns TESS_ERR_SKIN.
+ * flags: TESS_MD_FORCES_VALID; TESS_MD_GRAPH captures the steps of a rebuild interval into a
+ * HIP graph once and replays it for later intervals and calls with identical arguments
+ * (pointers, sizes, step count, dt, box, model); results are identical to eager launches.
+ * It is ignored on the NULL stream and while kernel timing is enabled. One graph is cached
+ * per process (a call with other arguments re-captures it); calls that use the flag must not
+ * run concurrently from several threads. Other flag bits: TESS_ERR_ARG. */
 int32_t tess_md_steps(const tess_model_desc* desc, const float* weights, int32_t n,
                       const float box[3], float r_cut, float skin, float* pos, float* vel,
                       int32_t* species, const float* mass_by_species, float dt_fs,
@@ -136,6 +143,9 @@ int32_t tess_md_steps(const tess_model_desc* desc, const float* weights, int32_t
  * calls on several streams. */
 int32_t tess_timing_enable(int32_t on);
 int32_t tess_timing_read(const char* kernel, double* total_ms, int64_t* launches);
+/* Restrict the timing events to one instrumented kernel (NULL or "" = all of them); an event
+ * pair costs a little GPU time, so a benchmark can time only the kernel it reports. */
+int32_t tess_timing_only(const char* kernel);
 
 #ifdef __cplusplus
 }

@@ -19,6 +19,7 @@ struct TimingState {
   bool on = false;
   std::map<std::string, std::vector<std::pair<hipEvent_t, hipEvent_t>>> ev;
   std::map<std::string, hipEvent_t> open;
+  std::string only;  // when not empty, only this kernel is timed
 };
 TimingState& timing() {
   static TimingState t;
@@ -27,6 +28,13 @@ TimingState& timing() {
 }  // namespace
 
 bool timing_on() { return timing().on; }
+
+bool timing_wants(const char* name) {
+  TimingState& t = timing();
+  if (!t.on) return false;
+  std::lock_guard<std::mutex> g(t.mu);
+  return t.only.empty() || t.only == name;
+}
 
 void timing_mark(const char* name, hipStream_t st, bool begin) {
   TimingState& t = timing();
@@ -124,6 +132,77 @@ bool box_ok(const float box[3], float r_cut, float skin) {
 
 using namespace tess;
 
+// ---- graph replay of a rebuild interval (TESS_MD_GRAPH) ----------------------------------
+// The k velocity-Verlet steps between two rebuilds are captured once into a HIP graph and
+// replayed for every later interval with the same arguments (pointers, sizes, step count,
+// time step, box, model). One cached graph per process; a different key re-captures it.
+namespace {
+struct GraphKey {
+  const void* p[14];
+  int64_t i[6];
+  float f[5];
+  bool operator==(const GraphKey& o) const { return std::memcmp(this, &o, sizeof(*this)) == 0; }
+};
+struct GraphCache {
+  std::mutex mu;
+  bool valid = false;
+  GraphKey key;
+  hipGraphExec_t exec = nullptr;
+};
+GraphCache& graph_cache() {
+  static GraphCache c;
+  return c;
+}
+
+template <class StepFn>
+int32_t md_interval_graph(const tess_model_desc* d, const float* weights, int32_t n,
+                          const float box[3], float* pos, float* vel, int32_t* species,
+                          const float* mass, float dt, float* forces, double* epot0,
+                          int32_t* row_ptr, uint32_t* col_shift, int32_t* rev, int64_t edge_cap,
+                          void* ws, int32_t k, hipStream_t st, StepFn step, bool* done) {
+  GraphKey key;
+  std::memset(&key, 0, sizeof(key));
+  // the model description and the box are host arrays: their values are part of the key
+  const void* ps[14] = {weights, pos, vel, species, mass, forces, epot0, row_ptr, col_shift,
+                        rev, ws, nullptr, nullptr, nullptr};
+  for (int a = 0; a < 14; a++) key.p[a] = ps[a];
+  key.i[0] = n; key.i[1] = edge_cap; key.i[2] = k;
+  key.i[3] = d->n_species; key.i[4] = d->n_layers;
+  key.i[5] = ((int64_t)d->channels << 40) | ((int64_t)d->radial_hidden << 24) |
+             ((int64_t)d->n_rbf << 16) | ((int64_t)d->l_max << 8) | d->n_heads;
+  key.f[0] = dt; key.f[1] = box[0]; key.f[2] = box[1]; key.f[3] = box[2]; key.f[4] = d->r_cut;
+  GraphCache& c = graph_cache();
+  std::lock_guard<std::mutex> g(c.mu);
+  if (!(c.valid && c.key == key)) {
+    if (c.valid) {
+      hipGraphExecDestroy(c.exec);
+      c.valid = false;
+    }
+    if (hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+      (void)hipGetLastError();
+      return TESS_OK;  // not capturable: the caller runs the steps eagerly
+    }
+    int32_t rc = TESS_OK;
+    for (int32_t j = 0; j < k && rc == TESS_OK; j++) rc = step(j);
+    hipGraph_t graph = nullptr;
+    const hipError_t ec = hipStreamEndCapture(st, &graph);
+    if (rc != TESS_OK || ec != hipSuccess || !graph) {
+      if (graph) hipGraphDestroy(graph);
+      (void)hipGetLastError();
+      return rc != TESS_OK ? rc : TESS_ERR_HIP;
+    }
+    const hipError_t ei = hipGraphInstantiate(&c.exec, graph, nullptr, nullptr, 0);
+    hipGraphDestroy(graph);
+    if (ei != hipSuccess) return TESS_ERR_HIP;
+    c.key = key;
+    c.valid = true;
+  }
+  TESS_HIP_CHECK(hipGraphLaunch(c.exec, st));
+  *done = true;
+  return TESS_OK;
+}
+}  // namespace
+
 extern "C" {
 
 int32_t tess_abi_version(void) { return 1; }
@@ -137,6 +216,13 @@ int32_t tess_timing_enable(int32_t on) {
   for (auto& kv : t.open) hipEventDestroy(kv.second);
   t.open.clear();
   t.on = on != 0;
+  return TESS_OK;
+}
+
+int32_t tess_timing_only(const char* kernel) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  t.only = kernel ? kernel : "";
   return TESS_OK;
 }
 
@@ -242,45 +328,65 @@ int32_t tess_md_steps(const tess_model_desc* d, const float* weights, int32_t n,
   if (n < 1 || n >= (1 << 27) || n_steps < 0 || rebuild_every < 1 || edge_cap < 0 || !box ||
       !n_edges || !weights || !pos || !vel || !species || !mass_by_species || !perm_accum ||
       !forces || !row_ptr || !col_shift || !rev || !(dt_fs > 0.0f) || !(r_cut > 0.0f) ||
-      !(skin >= 0.0f) || d->r_cut != r_cut)
+      !(skin >= 0.0f) || d->r_cut != r_cut || (flags & ~(TESS_MD_FORCES_VALID | TESS_MD_GRAPH)))
     return TESS_ERR_ARG;
   if (!box_ok(box, r_cut, skin)) return TESS_ERR_BOX;
   Layout L = layout(reinterpret_cast<char*>(workspace), d, n, edge_cap);
   if (!workspace || ws_bytes < L.total) return TESS_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
   const float half_skin2 = 0.25f * skin * skin;
-  bool forces_valid = (flags & TESS_MD_FORCES_VALID) != 0;
+  const bool forces_valid = (flags & TESS_MD_FORCES_VALID) != 0;
+  // graph replay needs a capturable stream and no per-launch timing events
+  const bool use_graph = (flags & TESS_MD_GRAPH) != 0 && st != nullptr && !timing_on();
   int64_t ne = *n_edges;
   TESS_HIP_CHECK(hipMemsetAsync(L.flag, 0, sizeof(int32_t), st));
-  for (int32_t s = 0; s < n_steps; s++) {
-    if (s % rebuild_every == 0) {
-      if (s > 0) {
-        int32_t f = 0;
-        TESS_HIP_CHECK(hipMemcpyAsync(&f, L.flag, sizeof(int32_t), hipMemcpyDeviceToHost, st));
-        TESS_HIP_CHECK(hipStreamSynchronize(st));
-        if (f) return TESS_ERR_SKIN;
-      }
-      int32_t rc = build_neighbors_impl(n, box, r_cut, skin, pos, species, vel, L.ref_pos,
-                                        (forces_valid || s > 0) ? forces : nullptr, perm_accum,
-                                        L.perm, nullptr, row_ptr, col_shift, rev, edge_cap, &ne,
-                                        L.nbr, st);
-      *n_edges = ne;
-      if (rc != TESS_OK) return rc;
-      if (s == 0 && !forces_valid) {
-        rc = ef_dispatch(*d, weights, n, box, pos, species, row_ptr, col_shift, rev, ne, edge_cap,
-                         L.epot, nullptr, forces, L.ef, L.ef_bytes, st);
-        if (rc != TESS_OK) return rc;
-      }
-    }
-    k_vv_kick_drift<<<gridn(n, 256), 256, 0, st>>>(n, dt_fs, forces, species, mass_by_species, pos,
-                                                   vel, L.ref_pos, half_skin2, L.flag);
+  // one velocity-Verlet step; `grid_edges` sizes the edge-kernel grids (the kernels stop at
+  // the device-side active-edge count, so any value >= the pair count gives the same result)
+  auto step = [&](int32_t s, int64_t grid_edges) -> int32_t {
+    k_vv_kick_drift<<<gridn(n, 256), 256, 0, st>>>(n, dt_fs, forces, species, mass_by_species,
+                                                   pos, vel, L.ref_pos, half_skin2, L.flag);
     TESS_HIP_CHECK(hipGetLastError());
-    int32_t rc = ef_dispatch(*d, weights, n, box, pos, species, row_ptr, col_shift, rev, ne,
-                             edge_cap, epot_trace ? epot_trace + s : L.epot, nullptr, forces, L.ef,
-                             L.ef_bytes, st);
+    int32_t rc = ef_dispatch(*d, weights, n, box, pos, species, row_ptr, col_shift, rev,
+                             grid_edges, edge_cap, epot_trace ? epot_trace + s : L.epot, nullptr,
+                             forces, L.ef, L.ef_bytes, st);
     if (rc != TESS_OK) return rc;
     k_vv_kick<<<gridn(n, 256), 256, 0, st>>>(n, dt_fs, forces, species, mass_by_species, vel);
     TESS_HIP_CHECK(hipGetLastError());
+    return TESS_OK;
+  };
+  for (int32_t s = 0; s < n_steps;) {
+    if (s > 0) {
+      int32_t f = 0;
+      TESS_HIP_CHECK(hipMemcpyAsync(&f, L.flag, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+      TESS_HIP_CHECK(hipStreamSynchronize(st));
+      if (f) return TESS_ERR_SKIN;
+    }
+    int32_t rc = build_neighbors_impl(n, box, r_cut, skin, pos, species, vel, L.ref_pos,
+                                      (forces_valid || s > 0) ? forces : nullptr, perm_accum,
+                                      L.perm, nullptr, row_ptr, col_shift, rev, edge_cap, &ne,
+                                      L.nbr, st);
+    *n_edges = ne;
+    if (rc != TESS_OK) return rc;
+    if (s == 0 && !forces_valid) {
+      rc = ef_dispatch(*d, weights, n, box, pos, species, row_ptr, col_shift, rev, ne, edge_cap,
+                       L.epot, nullptr, forces, L.ef, L.ef_bytes, st);
+      if (rc != TESS_OK) return rc;
+    }
+    const int32_t k = n_steps - s < rebuild_every ? n_steps - s : rebuild_every;
+    bool done = false;
+    if (use_graph) {
+      rc = md_interval_graph(d, weights, n, box, pos, vel, species, mass_by_species, dt_fs,
+                             forces, epot_trace ? epot_trace + s : L.epot, row_ptr, col_shift,
+                             rev, edge_cap, workspace, k, st,
+                             [&](int32_t j) { return step(s + j, edge_cap); }, &done);
+      if (rc != TESS_OK) return rc;
+    }
+    if (!done)
+      for (int32_t j = 0; j < k; j++) {
+        rc = step(s + j, ne);
+        if (rc != TESS_OK) return rc;
+      }
+    s += k;
   }
   int32_t f = 0;
   TESS_HIP_CHECK(hipMemcpyAsync(&f, L.flag, sizeof(int32_t), hipMemcpyDeviceToHost, st));

@@ -200,6 +200,16 @@ hipError_t gemm(hipStream_t st, int64_t M, int K, int O, const float* X, RowMap 
 // (blockIdx.y = layer). Per layer of the blob (row-major [out][in]): W_q, W_k, W1, W2, W_lin0,
 // W_lin^l; written as [W_q^T | W_k^T] ([C][2C]), W_lin0^T ([C][G]) and W_lin^l^T ([C][C]).
 // ---------------------------------------------------------------------------------------
+// Small fills (used instead of memset nodes so the pass can be captured in a HIP graph).
+__global__ void k_fill_i32(int32_t* __restrict__ p, int64_t n, int32_t v) {
+  int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k < n) p[k] = v;
+}
+__global__ void k_fill_f32(float* __restrict__ p, int64_t n, float v) {
+  int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k < n) p[k] = v;
+}
+
 template <int LMAX, int C, int R>
 __global__ void k_prep_weights(const float* __restrict__ weights, int S, int K,
                                float* __restrict__ WqkT, float* __restrict__ W0T,
@@ -1160,7 +1170,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     }
     k_active_count<<<gridn(n, 4), 256, 0, st>>>(n, pos, row_ptr, col_shift, box[0], box[1], box[2],
                                                 rc * rc, w.arow);
-    TESS_HIP_CHECK(hipMemsetAsync(w.arow + n, 0, sizeof(int32_t), st));
+    k_fill_i32<<<1, 64, 0, st>>>(w.arow + n, 1, 0);
     TESS_HIP_CHECK(scan_exclusive_i32(w.arow, (int64_t)n + 1, w.scan_tmp, st));
     k_active_fill<<<gridn(n, 4), 256, 0, st>>>(n, pos, row_ptr, col_shift, box[0], box[1], box[2],
                                                rc * rc, w.arow, w.adst, w.asrc, w.aslot,
@@ -1168,7 +1178,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     k_active_rev<<<gridn(cap, 256), 256, 0, st>>>(w.arow + n, w.aslot, rev, w.slot2act, w.arev, cap);
     TESS_HIP_CHECK(hipGetLastError());
   } else {
-    TESS_HIP_CHECK(hipMemsetAsync(w.arow, 0, sizeof(int32_t) * ((size_t)n + 1), st));
+    k_fill_i32<<<gridn((int64_t)n + 1, 256), 256, 0, st>>>(w.arow, (int64_t)n + 1, 0);
   }
   const RowMap feat0{(int64_t)D * C, C, 0, 1};
   // ---------------- forward ----------------
@@ -1293,7 +1303,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
   if (cap > 0) {
     k_forces<<<gridn(n, 4), 256, 0, st>>>(n, w.arow, w.arev, w.gacc, forces);
   } else if (n > 0) {
-    TESS_HIP_CHECK(hipMemsetAsync(forces, 0, sizeof(float) * 3 * (size_t)n, st));
+    k_fill_f32<<<gridn(3 * (int64_t)n, 256), 256, 0, st>>>(forces, 3 * (int64_t)n, 0.0f);
   }
   TESS_HIP_CHECK(hipGetLastError());
   return TESS_OK;

@@ -307,11 +307,12 @@ int32_t ef_dispatch(const tess_model_desc& md, const float* weights, int32_t n, 
 // the launching stream around each instrumented launch.
 namespace tess {
 bool timing_on();
+bool timing_wants(const char* name);
 void timing_mark(const char* name, hipStream_t st, bool begin);
 }  // namespace tess
 #define TESS_TIMED(name, st, ...)            \
   do {                                       \
-    if (tess::timing_on()) {                 \
+    if (tess::timing_wants(name)) {          \
       tess::timing_mark(name, st, true);     \
       __VA_ARGS__;                           \
       tess::timing_mark(name, st, false);    \

@@ -20,6 +20,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "tess.h")
 OK, ERR_ARG, ERR_BOX, ERR_CAPACITY, ERR_WORKSPACE, ERR_HIP, ERR_SKIN, ERR_SPECIES, ERR_ROW = (
     0, -1, -2, -3, -4, -5, -6, -7, -8)
 MD_FORCES_VALID = 1
+MD_GRAPH = 2
 
 
 class TessError(RuntimeError):
@@ -64,12 +65,19 @@ def lib() -> C.CDLL:
         L.tess_timing_enable.argtypes = [i32]
         L.tess_timing_read.restype = i32
         L.tess_timing_read.argtypes = [C.c_char_p, p, p]
+        L.tess_timing_only.restype = i32
+        L.tess_timing_only.argtypes = [C.c_char_p]
         _lib = L
     return _lib
 
 
 def timing_enable(on: bool) -> None:
     lib().tess_timing_enable(1 if on else 0)
+
+
+def timing_only(kernel=None) -> None:
+    """Time only `kernel` (None: every instrumented kernel)."""
+    lib().tess_timing_only(kernel.encode() if kernel else None)
 
 
 def timing_read(kernel: str):
@@ -159,13 +167,14 @@ def energy_forces(spec, weights, box, pos, species, row_ptr, col_shift, rev, n_e
 
 def md_steps(spec, weights, box, r_cut, skin, pos, vel, species, mass_by_species, dt_fs, n_steps,
              rebuild_every, perm_accum, forces, row_ptr, col_shift, rev, ws, epot_trace=None,
-             forces_valid=False, check=True):
+             forces_valid=False, graph=False, check=True):
     n = int(pos.shape[0])
     ne = C.c_int64(0)
     st = lib().tess_md_steps(C.byref(desc(spec)), _p(weights), n, _box(box), float(r_cut),
                              float(skin), _p(pos), _p(vel), _p(species), _p(mass_by_species),
                              float(dt_fs), int(n_steps), int(rebuild_every),
-                             MD_FORCES_VALID if forces_valid else 0, _p(perm_accum), _p(forces),
+                             (MD_FORCES_VALID if forces_valid else 0) | (MD_GRAPH if graph else 0),
+                             _p(perm_accum), _p(forces),
                              _p(epot_trace), _p(row_ptr), _p(col_shift), _p(rev),
                              int(col_shift.numel()), C.byref(ne), _p(ws), int(ws.numel()),
                              _stream())

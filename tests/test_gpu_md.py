@@ -90,3 +90,51 @@ def test_md_skin_error(T, oracle_mod):
     dx = xg - xo
     dx -= float(wl.box[0]) * np.round(dx / float(wl.box[0]))
     assert np.abs(dx).max() <= 1e-4
+
+
+def test_md_graph_replay_matches_eager(T):
+    """TESS_MD_GRAPH: the steps of a rebuild interval are captured into a HIP graph once and
+    replayed. Two identical systems, one eager and one replayed, run three calls of two
+    20-step intervals each (the first interval captures, every later one replays), with
+    unrelated eager GPU work and synchronisations between the calls; after every call
+    positions, velocities, forces, the permutation and the energy trace are bit-identical."""
+    import torch
+    wl = W.load("salt4k")
+    w = W.make_weights(wl.model, 2002)
+    vel = W.maxwell_velocities(wl.species, wl.masses(), 50.0, 3002).astype(np.float32)
+    dev = "cuda"
+    masses = torch.from_numpy(wl.masses().astype(np.float32)).to(dev)
+    runs = []
+    for graph in (False, True):
+        s = T.System(wl, w)
+        runs.append(dict(s=s, graph=graph, vel=torch.from_numpy(vel.copy()).to(dev),
+                         pa=torch.arange(wl.n, dtype=torch.int32, device=dev),
+                         ep=torch.zeros(40, dtype=torch.float64, device=dev)))
+    other = T.System(W.load("water648"), W.make_weights(W.load("water648").model, 2001))
+    other.rebuild()
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()  # graphs are not captured on the NULL stream
+    with torch.cuda.stream(stream):
+        assert torch.cuda.current_stream().cuda_stream != 0
+        _graph_calls(T, torch, wl, masses, runs, other)
+
+
+def _graph_calls(T, torch, wl, masses, runs, other):
+    for call in range(3):
+        for r in runs:
+            s = r["s"]
+            st, _ = T.md_steps(s.spec, s.weights, s.box, s.r_cut, s.skin, s.pos, r["vel"],
+                               s.species, masses, wl.dt_fs, 40, 20, r["pa"], s.forces, s.row_ptr,
+                               s.col_shift, s.rev, s.ws, epot_trace=r["ep"],
+                               forces_valid=call > 0, graph=r["graph"], check=False)
+            assert st == T.OK
+            torch.cuda.synchronize()
+            other.energy_forces()  # eager work between replays
+            torch.cuda.synchronize()
+        a, b = runs[0], runs[1]
+        assert torch.equal(a["s"].pos, b["s"].pos)
+        assert torch.equal(a["vel"], b["vel"])
+        assert torch.equal(a["s"].forces, b["s"].forces)
+        assert torch.equal(a["pa"], b["pa"])
+        assert torch.equal(a["ep"], b["ep"])
+        print("call %d: identical, E=%.6f" % (call, float(b["ep"][-1])), flush=True)
