@@ -85,6 +85,8 @@ def main():
                     help="replay each rebuild interval from a captured HIP graph "
                          "(TESS_MD_GRAPH); per-kernel timing then comes from a second, eager "
                          "pass of the same length")
+    ap.add_argument("--curve", choices=("hilbert", "morton"), default="hilbert",
+                    help="atom order of the rebuilds (morton: locality comparison)")
     ap.add_argument("--no-hooks", action="store_true",
                     help="time the MD steps without the per-kernel HIP events (A/B of their "
                          "cost); per-kernel timing then comes from a second pass")
@@ -112,6 +114,7 @@ def run(args):
     from molecular_dynamics_hilbert_amd import workloads as W
 
     dev = "cuda"
+    T.set_curve(args.curve)
     wl = W.load(args.workload)
     seed = {"salt60k": 2003, "capsid39k": 2004, "salt500k": 2005}.get(args.workload, 2003)
     w = W.make_weights(wl.model, seed)
@@ -227,7 +230,7 @@ def run(args):
                    "l_max": wl.model.l_max, "heads": wl.model.n_heads,
                    "rebuild_every": every, "dt_fs": wl.dt_fs, "pairs_r_c_plus_skin": n_cand,
                    "pairs_r_c": n_active, "skin_flagged_intervals": skin_timed,
-                   "launch": "hip_graph" if args.graph else "eager",
+                   "launch": "hip_graph" if args.graph else "eager", "curve": args.curve,
                    "kernel_events_in_timed_region": dom if hooks_in_region else None},
         "rebuild_ms": round(statistics.median(rb), 4),
         "ef_ms": round(statistics.median(ef), 4),

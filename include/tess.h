@@ -134,6 +134,12 @@ int32_t tess_md_steps(const tess_model_desc* desc, const float* weights, int32_t
                       int32_t* row_ptr, uint32_t* col_shift, int32_t* rev, int64_t edge_cap,
                       int64_t* n_edges, void* workspace, int64_t ws_bytes, void* hip_stream);
 
+/* Space-filling curve used by later rebuilds in this process: 0 = Hilbert (default, the
+ * method's), 1 = Morton (Z-order of the same 10-bit cells; for locality comparisons only, the
+ * pair set is the same, the atom order and hence perm/hkey differ). Returns TESS_ERR_ARG for
+ * other values. Not thread-safe with concurrent rebuilds. */
+int32_t tess_set_curve(int32_t curve);
+
 /* Optional kernel timing for benchmarks (not part of the method). tess_timing_enable(1)
  * clears the counters and, until tess_timing_enable(0), records a pair of HIP events on the
  * launching stream around each launch of the instrumented kernels ("edge_prep",

@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstring>
 
+#include <atomic>
 #include <map>
 #include <mutex>
 #include <string>
@@ -28,6 +29,11 @@ TimingState& timing() {
 }  // namespace
 
 bool timing_on() { return timing().on; }
+
+namespace {
+std::atomic<int> g_curve{0};
+}
+int sort_curve() { return g_curve.load(); }
 
 bool timing_wants(const char* name) {
   TimingState& t = timing();
@@ -216,6 +222,12 @@ int32_t tess_timing_enable(int32_t on) {
   for (auto& kv : t.open) hipEventDestroy(kv.second);
   t.open.clear();
   t.on = on != 0;
+  return TESS_OK;
+}
+
+int32_t tess_set_curve(int32_t curve) {
+  if (curve != 0 && curve != 1) return TESS_ERR_ARG;
+  g_curve.store(curve);
   return TESS_OK;
 }
 

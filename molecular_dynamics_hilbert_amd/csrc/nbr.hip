@@ -69,7 +69,18 @@ __device__ __forceinline__ uint32_t hilbert30(uint32_t x0, uint32_t x1, uint32_t
   return key;
 }
 
-__global__ void k_wrap_key(int32_t n, double Lx, double Ly, double Lz, const float* __restrict__ pos,
+// Morton (Z-order) key of the same quantised cell: bits interleaved level by level, axis 0
+// most significant within a level. Used only when a comparison run selects it.
+__device__ __forceinline__ uint32_t morton30(uint32_t x0, uint32_t x1, uint32_t x2) {
+  uint32_t key = 0;
+#pragma unroll
+  for (int lev = 9; lev >= 0; lev--)
+    key = (key << 3) | (((x0 >> lev) & 1u) << 2) | (((x1 >> lev) & 1u) << 1) | ((x2 >> lev) & 1u);
+  return key;
+}
+
+__global__ void k_wrap_key(int32_t n, int curve, double Lx, double Ly, double Lz,
+                           const float* __restrict__ pos,
                            const int32_t* __restrict__ species, const float* __restrict__ vel,
                            const float* __restrict__ forces, const int32_t* __restrict__ pa,
                            float* __restrict__ pos_w, uint32_t* __restrict__ key,
@@ -84,7 +95,8 @@ __global__ void k_wrap_key(int32_t n, double Lx, double Ly, double Lz, const flo
   pos_w[3 * i + 0] = x;
   pos_w[3 * i + 1] = y;
   pos_w[3 * i + 2] = z;
-  key[i] = hilbert30(quant10(x, Lx), quant10(y, Ly), quant10(z, Lz));
+  const uint32_t q0 = quant10(x, Lx), q1 = quant10(y, Ly), q2 = quant10(z, Lz);
+  key[i] = curve == 1 ? morton30(q0, q1, q2) : hilbert30(q0, q1, q2);
   idx[i] = i;
   sp_tmp[i] = species[i];
   if (vel)
@@ -540,7 +552,8 @@ int32_t build_neighbors_impl(int32_t n, const float box[3], float r_cut, float s
   const double rcs = (double)r_cut + (double)skin;
   const double rcs2 = rcs * rcs;
   // 1. wrap + keys
-  k_wrap_key<<<grid(n, 256), 256, 0, st>>>(n, L[0], L[1], L[2], pos, species, vel, forces,
+  k_wrap_key<<<grid(n, 256), 256, 0, st>>>(n, sort_curve(), L[0], L[1], L[2], pos, species,
+                                           vel, forces,
                                            perm_accum, ws.pos_w, ws.key[0], ws.idx[0], ws.sp_tmp,
                                            ws.v_tmp, ws.f_tmp, ws.pa_tmp);
   TESS_HIP_CHECK(hipGetLastError());

@@ -306,6 +306,8 @@ int32_t ef_dispatch(const tess_model_desc& md, const float* weights, int32_t n, 
 // Optional per-kernel timing (tess_timing_enable / tess_timing_read): HIP events recorded on
 // the launching stream around each instrumented launch.
 namespace tess {
+// Space-filling curve of the atom order: 0 Hilbert (the method's), 1 Morton (comparisons).
+int sort_curve();
 bool timing_on();
 bool timing_wants(const char* name);
 void timing_mark(const char* name, hipStream_t st, bool begin);

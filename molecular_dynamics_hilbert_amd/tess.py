@@ -67,12 +67,21 @@ def lib() -> C.CDLL:
         L.tess_timing_read.argtypes = [C.c_char_p, p, p]
         L.tess_timing_only.restype = i32
         L.tess_timing_only.argtypes = [C.c_char_p]
+        L.tess_set_curve.restype = i32
+        L.tess_set_curve.argtypes = [i32]
         _lib = L
     return _lib
 
 
 def timing_enable(on: bool) -> None:
     lib().tess_timing_enable(1 if on else 0)
+
+
+def set_curve(curve: str) -> None:
+    """Atom order of later rebuilds: "hilbert" (default) or "morton" (comparison runs)."""
+    st = lib().tess_set_curve({"hilbert": 0, "morton": 1}[curve])
+    if st != OK:
+        raise TessError(st, "tess_set_curve")
 
 
 def timing_only(kernel=None) -> None:

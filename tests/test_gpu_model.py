@@ -168,3 +168,37 @@ def test_no_pairs_within_cutoff(T, oracle_mod):
                                    nb["species"], nb["row_ptr"], nb["col_shift"])
     assert abs(g["energy"] - ref["energy"]) <= 1e-5 * abs(ref["energy"])
     assert np.all(g["forces"] == 0.0)
+
+
+def test_morton_order_same_physics(T, oracle_mod):
+    """With the Morton curve selected (a locality comparison mode) the atoms come out in
+    another order, but the pair set, the energy and every atom's force (by original id) match
+    the oracle's Hilbert-ordered result to the same bar."""
+    wl = W.load("salt4k")
+    w = W.make_weights(wl.model, WEIGHT_SEED["salt4k"])
+    nb = oracle_mod.build_neighbors(wl.box, wl.pos, wl.species, wl.model.r_cut, wl.skin)
+    ref = oracle_mod.energy_forces(wl.model, w, wl.box, nb["pos"].astype(np.float64),
+                                   nb["species"], nb["row_ptr"], nb["col_shift"])
+    T.set_curve("morton")
+    try:
+        g = _run(T, wl, w)
+        s = g["sys"]
+        rp = s.row_ptr.cpu().numpy()
+        col = s.col_shift[:int(rp[-1])].cpu().numpy().view(np.uint32)
+    finally:
+        T.set_curve("hilbert")
+    perm_h = np.asarray(nb["perm"])
+    assert not np.array_equal(g["perm"], perm_h)
+
+    def pairs(perm, rowp, c):
+        i = np.repeat(np.arange(len(rowp) - 1), np.diff(rowp))
+        j = (c & 0x7FFFFFF).astype(np.int64)
+        code = (c >> 27).astype(np.int64)
+        return set(zip(perm[i].tolist(), perm[j].tolist(), code.tolist()))
+
+    pm = pairs(g["perm"], rp, col)
+    ph = pairs(perm_h, np.asarray(nb["row_ptr"]), np.asarray(nb["col_shift"]).astype(np.uint32))
+    assert pm == ph
+    Fm = np.empty_like(g["forces"]); Fm[g["perm"]] = g["forces"]
+    Fh = np.empty_like(ref["forces"]); Fh[perm_h] = ref["forces"]
+    _assert_ef(g["energy"], Fm, ref["energy"], Fh, "salt4k morton")
