@@ -448,7 +448,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
     int32_t n, const int32_t* __restrict__ arow, const float4* __restrict__ ageo,
     const int32_t* __restrict__ asrc, const int32_t* __restrict__ arev,
     const float* __restrict__ ew, const float4* __restrict__ es, const float* __restrict__ X,
-    float rc, float* __restrict__ out, const float* __restrict__ base, float* __restrict__ MZ,
+    float rc, float* __restrict__ out, const float* __restrict__ base, float4* __restrict__ P,
     const float4* __restrict__ sbar, const float* __restrict__ qk, float* __restrict__ qkbar) {
   constexpr int D = Dims<LMAX>::D;
   constexpr int DI = L0ONLY ? 1 : D;          // input components that can be non-zero
@@ -494,10 +494,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
     }
 #pragma unroll
     for (int hh = 0; hh < H; hh++) Zh[hh] = wave_sum(Zh[hh]);
-    if (lane < H) {
-      MZ[(int64_t)x * 2 * H + lane] = a1 > a0 ? Mh[lane] : 0.0f;
-      MZ[(int64_t)x * 2 * H + H + lane] = Zh[lane];
-    }
   }
   floatx4 acc[4][NDG];
 #pragma unroll
@@ -534,25 +530,30 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
       float u = 0.5f * (__cosf(kPi * geo.w / rc) + 1.0f);
       float sv[4];
       if (!TRANS) {
+        // softmax probability p_h = exp(s_h - M_h)/Z_h (kept for the backward), weight u p_h
         float4 s4 = pf_s4;
         sv[0] = s4.x; sv[1] = s4.y; sv[2] = s4.z; sv[3] = s4.w;
+        float ph[4];
 #pragma unroll
-        for (int hh = 0; hh < 4; hh++)
-          sAl[wv][lane][hh] = (hh < H && Zh[hh] > 0.0f) ? u * __expf(sv[hh] - Mh[hh]) / Zh[hh] : 0.0f;
+        for (int hh = 0; hh < 4; hh++) {
+          ph[hh] = (hh < H && Zh[hh] > 0.0f) ? __expf(sv[hh] - Mh[hh]) / Zh[hh] : 0.0f;
+          sAl[wv][lane][hh] = u * ph[hh];
+        }
+        P[a] = make_float4(ph[0], ph[1], ph[2], ph[3]);
       } else {
+        // the forward edge e' = rev(a) = (y <- x): its softmax probability from the forward
         const int32_t ep = arev[a];
-        float4 s4 = es[ep];
-        sv[0] = s4.x; sv[1] = s4.y; sv[2] = s4.z; sv[3] = s4.w;
+        const float4 p4 = P[ep];
+        const float ph[4] = {p4.x, p4.y, p4.z, p4.w};
         float4 sbs = sbar[ep], sbd = sbar[a];
         const float sbsv[4] = {sbs.x, sbs.y, sbs.z, sbs.w}, sbdv[4] = {sbd.x, sbd.y, sbd.z, sbd.w};
 #pragma unroll
         for (int hh = 0; hh < 4; hh++) {
-          float Zy = hh < H ? MZ[(int64_t)y * 2 * H + H + hh] : 0.0f;
-          float My = hh < H ? MZ[(int64_t)y * 2 * H + hh] : 0.0f;
-          sAl[wv][lane][hh] = (hh < H && Zy > 0.0f) ? u * __expf(sv[hh] - My) / Zy : 0.0f;
+          sAl[wv][lane][hh] = u * ph[hh];
           sSs[wv][TRANS ? lane : 0][hh] = sbsv[hh];
           sSd[wv][TRANS ? lane : 0][hh] = sbdv[hh];
         }
+        (void)sv;
       }
       const float ir = 1.0f / geo.w;
       const float sg = TRANS ? -1.0f : 1.0f;
@@ -808,7 +809,8 @@ __global__ void k_gbar_init(int32_t n, int C, int D, const float* __restrict__ w
 // Edge gradient for active edge e = (i <- j), destination-major. One lane per (edge, head):
 //   Abar^h = sum_{c in h} mbar_i[:,c] (x) h_j[:,c];  (wbar^h, Ybar^h) = coupling adjoint;
 //   abar_h = <A_e, Abar^h> = w . wbar^h;  sbar_h = alpha_h (abar_h - D_ih);
-//   ubar = sum_h p_h (abar_h - D_ih), p_h = exp(s_h - M_ih)/Z_ih, alpha_h = u p_h;
+//   ubar = sum_h p_h (abar_h - D_ih), p_h = exp(s_h - M_ih)/Z_ih (stored by the forward
+//   contraction), alpha_h = u p_h;
 //   wbar = sum_h alpha_h wbar^h, Ybar = sum_h alpha_h Ybar^h  (sums over the edge's lanes);
 //   dE/dr = wbar . dw/dr + ubar u'(r);  g = dE/dr n + (I - n n^T) J_Y^T Ybar / r.
 // g (dE/dr_vec) accumulates over layers per edge; sbar is kept for the q/k adjoints.
@@ -929,8 +931,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
                                                    const int32_t* __restrict__ asrc,
                                                    const float* __restrict__ ew,
                                                    const float* __restrict__ edw,
-                                                   const float4* __restrict__ es,
-                                                   const float* __restrict__ MZ,
+                                                   const float4* __restrict__ prob,
                                                    const float* __restrict__ Dst,
                                                    const float* __restrict__ mbar,
                                                    const float* __restrict__ h, float rc,
@@ -976,7 +977,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
     float w[P];
 #pragma unroll
     for (int p = 0; p < P; p++) w[p] = ew[a * 12 + p];
-    const float sv = reinterpret_cast<const float*>(es)[a * 4 + hh];
     float wb[P], Yb[9];
 #pragma unroll
     for (int p = 0; p < P; p++) wb[p] = 0.0f;
@@ -985,8 +985,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
     const float* h_j = h + (int64_t)j * D * C;
     const int lbase = (ri - b0) * (D * C / 4);
     auto mrow = [&](int off) { return smb[lbase + (off >> 2)]; };
-    const float Zi = MZ[(int64_t)i * 2 * H + H + hh];
-    const float p_h = Zi > 0.0f ? __expf(sv - MZ[(int64_t)i * 2 * H + hh]) / Zi : 0.0f;
+    const float p_h = reinterpret_cast<const float*>(prob)[a * 4 + hh];
     const float al = u * p_h;
     float abar = 0.0f;
     const int c0 = hh * dh;
@@ -1061,11 +1060,12 @@ __global__ void __launch_bounds__(256) k_forces(int32_t n, const int32_t* __rest
 // ---------------------------------------------------------------------------------------
 struct EFWS {
   float *WqkT, *W0T, *WlT;  // per layer transposed weights
-  float *h, *qk, *MZ, *m, *yg, *yl;
+  float *h, *qk, *m, *yg, *yl;
   int32_t *arow, *adst, *asrc, *aslot, *slot2act, *arev, *rev_own;
   float4* ageo;
   float *ew, *edw;
   float4* es;
+  float4* P;  // per layer and active edge: softmax probability of each head
   float *gbar, *hbar, *mbar, *xcat, *ybl, *qkbar, *Dst, *gacc;
   float4* sbar;
   double* epart;
@@ -1082,7 +1082,6 @@ static EFWS carve_ef(Carver& cv, const tess_model_desc& md, int32_t n, int64_t c
   w.WlT = cv.take<float>(T * Lm * C * C + 1);
   w.h = cv.take<float>((T + 1) * nn * D * C);
   w.qk = cv.take<float>(T * nn * 2 * C);
-  w.MZ = cv.take<float>(T * nn * 2 * H);
   w.m = cv.take<float>(T * nn * D * C);
   w.yg = cv.take<float>(T * nn * C * (1 + Lm));
   w.yl = cv.take<float>(T * nn * D * C);
@@ -1097,6 +1096,7 @@ static EFWS carve_ef(Carver& cv, const tess_model_desc& md, int32_t n, int64_t c
   w.ew = cv.take<float>(T * ec * 12);
   w.edw = cv.take<float>(T * ec * 12);
   w.es = cv.take<float4>(T * ec);
+  w.P = cv.take<float4>(T * ec);
   w.gbar = cv.take<float>(nn * D * C);
   w.hbar = cv.take<float>(nn * D * C);
   w.mbar = cv.take<float>(nn * D * C);
@@ -1186,7 +1186,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     float* ht = w.h + (int64_t)t * NDC;
     float* hn = w.h + (int64_t)(t + 1) * NDC;
     float* qk = w.qk + (int64_t)t * n * 2 * C;
-    float* MZ = w.MZ + (int64_t)t * n * 2 * H;
+    float4* Pt = w.P + (int64_t)t * ecap;
     float* mt = w.m + (int64_t)t * NDC;
     float* yg = w.yg + (int64_t)t * n * G;
     float* yl = w.yl + (int64_t)t * NDC;
@@ -1205,12 +1205,12 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     if (t == 0)
       TESS_TIMED("edge_apply", st,
                  k_edge_contract<LMAX, C, H, true, false><<<gridn(n, 4), 256, 0, st>>>(
-                     n, w.arow, w.ageo, w.asrc, w.arev, ew, es, ht, rc, mt, nullptr, MZ, nullptr,
+                     n, w.arow, w.ageo, w.asrc, w.arev, ew, es, ht, rc, mt, nullptr, Pt, nullptr,
                      nullptr, nullptr));
     else
       TESS_TIMED("edge_apply", st,
                  k_edge_contract<LMAX, C, H, false, false><<<gridn(n, 4), 256, 0, st>>>(
-                     n, w.arow, w.ageo, w.asrc, w.arev, ew, es, ht, rc, mt, nullptr, MZ, nullptr,
+                     n, w.arow, w.ageo, w.asrc, w.arev, ew, es, ht, rc, mt, nullptr, Pt, nullptr,
                      nullptr, nullptr));
     TESS_HIP_CHECK(hipGetLastError());
     Epi eu{};
@@ -1251,7 +1251,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
   for (int t = T - 1; t >= 0; t--) {
     const float* ht = w.h + (int64_t)t * NDC;
     const float* qk = w.qk + (int64_t)t * n * 2 * C;
-    const float* MZ = w.MZ + (int64_t)t * n * 2 * H;
+    float4* Pt = w.P + (int64_t)t * ecap;
     const float* mt = w.m + (int64_t)t * NDC;
     const float* yg = w.yg + (int64_t)t * n * G;
     const float* yl = w.yl + (int64_t)t * NDC;
@@ -1277,12 +1277,12 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
       if (t == 0)
         TESS_TIMED("edge_grad", st,
                    k_edge_grad<LMAX, C, H, true><<<gb, 256, 0, st>>>(
-                       w.arow + n, w.ageo, w.adst, w.asrc, ew, edw, es, MZ, w.Dst, w.mbar, ht, rc,
+                       w.arow + n, w.ageo, w.adst, w.asrc, ew, edw, Pt, w.Dst, w.mbar, ht, rc,
                        w.sbar, w.gacc, t != T - 1, cap));
       else
         TESS_TIMED("edge_grad", st,
                    k_edge_grad<LMAX, C, H, false><<<gb, 256, 0, st>>>(
-                       w.arow + n, w.ageo, w.adst, w.asrc, ew, edw, es, MZ, w.Dst, w.mbar, ht, rc,
+                       w.arow + n, w.ageo, w.adst, w.asrc, ew, edw, Pt, w.Dst, w.mbar, ht, rc,
                        w.sbar, w.gacc, t != T - 1, cap));
     }
     TESS_HIP_CHECK(hipGetLastError());
@@ -1290,7 +1290,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
       TESS_TIMED("edge_tapply", st,
                  k_edge_contract<LMAX, C, H, false, true><<<gridn(n, 4), 256, 0, st>>>(
                      n, w.arow, w.ageo, w.asrc, w.arev, ew, es, w.mbar, rc, hbar, gbar,
-                     const_cast<float*>(MZ), w.sbar, qk, w.qkbar));
+                     Pt, w.sbar, qk, w.qkbar));
       Epi ea{};
       ea.y = hbar;
       ea.ym = feat0;
