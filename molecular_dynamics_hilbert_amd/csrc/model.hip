@@ -818,7 +818,8 @@ __global__ void k_gbar_init(int32_t n, int C, int D, const float* __restrict__ w
 // 16-byte loads, so the H lanes of an edge together read whole rows; m_bar rows of the
 // block's destinations are staged in LDS.
 // ---------------------------------------------------------------------------------------
-constexpr int kGradRows = 8;  // destination rows of m_bar staged in LDS at a time
+constexpr int kGradRows = 8;    // destination rows of m_bar staged in LDS at a time
+constexpr int kGradPasses = 2;  // edges per thread for one staging of m_bar rows
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
@@ -942,20 +943,19 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
   constexpr int D = Dims<LMAX>::D;
   constexpr int P = Dims<LMAX>::P;
   constexpr int dh = C / H;
-  constexpr int EPB = 256 / H;  // edges per block
+  constexpr int EPW = 256 / H;               // edges per pass of the block's threads
+  constexpr int EPB = kGradPasses * EPW;     // edges per block
   __shared__ float4 smb[kGradRows * D * C / 4];
   const int64_t n_act = *arow_n;
   const uint32_t nb_act = (uint32_t)((n_act + EPB - 1) / EPB);
   if (blockIdx.x >= nb_act) return;  // whole block idle
   const int64_t a_base = (int64_t)xcd_block(blockIdx.x, nb_act) * EPB;
   const int hh = (int)threadIdx.x % H;
-  const int64_t a = a_base + threadIdx.x / H;
-  const bool active = a < n_act && a < cap;
   // The block's destinations (edges are destination-major) are staged in LDS kGradRows
-  // m_bar rows at a time; each edge is processed in the batch that holds its row.
+  // m_bar rows at a time; each edge is processed in the batch that holds its row, and the
+  // block's threads take kGradPasses edges each per staged batch.
   const int32_t i_first = adst[a_base];
   const int32_t nrows = adst[min(a_base + (int64_t)EPB, n_act) - 1] - i_first + 1;
-  const int ri = active ? adst[a] - i_first : -1;
   for (int b0 = 0; b0 < nrows; b0 += kGradRows) {
     const int nst = min(nrows - b0, kGradRows);
     if (b0 > 0) __syncthreads();
@@ -964,6 +964,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
       for (int k = threadIdx.x; k < nst * D * C / 4; k += blockDim.x) smb[k] = src[k];
     }
     __syncthreads();
+#pragma unroll 1
+  for (int ps = 0; ps < kGradPasses; ps++) {
+    const int64_t a = a_base + ps * EPW + threadIdx.x / H;
+    const bool active = a < n_act && a < cap;
+    const int ri = active ? adst[a] - i_first : -1;
     if (ri < b0 || ri >= b0 + nst) continue;
     const int32_t i = i_first + ri, j = asrc[a];
     float4 g = ageo[a];
@@ -1024,6 +1029,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
       gacc[a * 3 + 1] = gyv;
       gacc[a * 3 + 2] = gz;
     }
+  }
   }
 }
 
@@ -1273,7 +1279,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     }
     k_dst<LMAX, C, H><<<gridn(n, 4), 256, 0, st>>>(n, w.mbar, mt, w.Dst);
     if (cap > 0) {
-      const int32_t gb = gridn(cap, 256 / H);
+      const int32_t gb = gridn(cap, kGradPasses * 256 / H);
       if (t == 0)
         TESS_TIMED("edge_grad", st,
                    k_edge_grad<LMAX, C, H, true><<<gb, 256, 0, st>>>(
