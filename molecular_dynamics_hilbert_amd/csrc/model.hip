@@ -472,28 +472,31 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
   const int32_t a0 = arow[x], a1 = arow[x + 1];
   float Mh[4] = {0.0f, 0.0f, 0.0f, 0.0f}, Zh[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   if (!TRANS) {
-    // softmax statistics over the row (lane = edge)
+    // softmax statistics over the row in one pass (lane = edge): each lane keeps its running
+    // maximum and its sum of u exp(s - max), rescaled when the maximum grows; lanes are then
+    // combined with the wave maximum
+    float ml[4], zl[4];
 #pragma unroll
-    for (int hh = 0; hh < 4; hh++) Mh[hh] = -INFINITY;
+    for (int hh = 0; hh < 4; hh++) { ml[hh] = -INFINITY; zl[hh] = 0.0f; }
     for (int32_t a = a0 + lane; a < a1; a += 64) {
-      float4 sv = es[a];
-      Mh[0] = fmaxf(Mh[0], sv.x);
-      if (H > 1) { Mh[1] = fmaxf(Mh[1], sv.y); Mh[2] = fmaxf(Mh[2], sv.z); Mh[3] = fmaxf(Mh[3], sv.w); }
-    }
+      const float4 s4 = es[a];
+      const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+      const float u = 0.5f * (__cosf(kPi * ageo[a].w / rc) + 1.0f);
 #pragma unroll
-    for (int hh = 0; hh < H; hh++) Mh[hh] = wave_max(Mh[hh]);
-    for (int32_t a = a0 + lane; a < a1; a += 64) {
-      float4 sv = es[a];
-      float u = 0.5f * (__cosf(kPi * ageo[a].w / rc) + 1.0f);
-      Zh[0] += u * __expf(sv.x - Mh[0]);
-      if (H > 1) {
-        Zh[1] += u * __expf(sv.y - Mh[1]);
-        Zh[2] += u * __expf(sv.z - Mh[2]);
-        Zh[3] += u * __expf(sv.w - Mh[3]);
+      for (int hh = 0; hh < H; hh++) {
+        if (sv[hh] > ml[hh]) {
+          zl[hh] = zl[hh] * __expf(ml[hh] - sv[hh]) + u;
+          ml[hh] = sv[hh];
+        } else {
+          zl[hh] += u * __expf(sv[hh] - ml[hh]);
+        }
       }
     }
 #pragma unroll
-    for (int hh = 0; hh < H; hh++) Zh[hh] = wave_sum(Zh[hh]);
+    for (int hh = 0; hh < H; hh++) {
+      Mh[hh] = wave_max(ml[hh]);
+      Zh[hh] = wave_sum(ml[hh] == -INFINITY ? 0.0f : zl[hh] * __expf(ml[hh] - Mh[hh]));
+    }
   }
   floatx4 acc[4][NDG];
 #pragma unroll
