@@ -72,7 +72,8 @@ def lib():
         L.tor_energy_forces.argtypes = [p, p, C.c_int32, p, p, p, p, p, p, p, p, p]
         L.tor_md_steps.restype = C.c_int32
         L.tor_md_steps.argtypes = [p, p, C.c_int32, p, C.c_float, C.c_float, p, p, p, p,
-                                   C.c_double, C.c_int32, C.c_int32, p, p, C.c_int32, p, C.c_int64]
+                                   C.c_double, C.c_int32, C.c_int32, p, p, C.c_int32, p, C.c_int64,
+                                   C.c_int32, C.c_double, C.c_double, p, p]
     return _lib
 
 
@@ -255,7 +256,8 @@ def energy_forces_status(spec, weights, box, pos, species, row_ptr, col_shift):
 
 
 def md_steps(spec, weights, box, r_cut, skin, pos, vel, species, masses, dt_fs, n_steps,
-             rebuild_every, perm_accum=None, forces=None, cap=None):
+             rebuild_every, perm_accum=None, forces=None, cap=None, thermostat=0,
+             t_target_K=0.0, tau_fs=0.0):
     m = model_struct(spec)
     pos = np.ascontiguousarray(pos, dtype=np.float64).reshape(-1, 3).copy()
     vel = np.ascontiguousarray(vel, dtype=np.float64).reshape(-1, 3).copy()
@@ -267,11 +269,15 @@ def md_steps(spec, weights, box, r_cut, skin, pos, vel, species, masses, dt_fs, 
     F = np.zeros((n, 3), np.float64) if forces is None else np.ascontiguousarray(
         forces, dtype=np.float64).reshape(-1, 3).copy()
     ep = np.zeros(max(n_steps, 1), np.float64)
+    ke = np.zeros(max(n_steps, 1), np.float64)
+    rmin = np.zeros(max(n_steps, 1), np.float64)
     if cap is None:
         cap = 400 * n
     ms = np.ascontiguousarray(masses, dtype=np.float64)
     rc = lib().tor_md_steps(C.byref(m), _ptr(_f32(weights)), n, _ptr(_box(box)), r_cut, skin,
                             _ptr(pos), _ptr(vel), _ptr(sp), _ptr(ms), dt_fs, n_steps,
-                            rebuild_every, _ptr(pa), _ptr(F), int(valid), _ptr(ep), int(cap))
+                            rebuild_every, _ptr(pa), _ptr(F), int(valid), _ptr(ep), int(cap),
+                            int(thermostat), float(t_target_K), float(tau_fs), _ptr(ke),
+                            _ptr(rmin))
     return dict(status=int(rc), pos=pos, vel=vel, species=sp, perm_accum=pa, forces=F,
-                epot=ep[:n_steps])
+                epot=ep[:n_steps], ke=ke[:n_steps], rmin=rmin[:n_steps])

@@ -1031,15 +1031,56 @@ int32_t tor_energy_forces(const tor_model* mdesc, const float* weights, int32_t 
  *     reference positions for the skin check reset); if s == 0 and forces are not valid,
  *     compute them;
  *   v += dt/2 a; x += dt v (not re-wrapped); flag if any |x - x_ref| > skin/2;
- *   F = -dE/dx (epot_trace[s] = E); v += dt/2 a.
+ *   F = -dE/dx (epot_trace[s] = E); v += dt/2 a;
+ *   with thermostat 1, v *= lambda (Berendsen coupling, below);
+ *   ke_trace[s] = kinetic energy; rmin_trace[s] = shortest pair distance below r_cut.
  * After an interval whose flag is set the call stops and returns TOR_ERR_SKIN.
+ *
+ * NVT and monitors (Tessera abstract: NVT runs of the capsid with no anomalously close
+ * pairs; the pages name no thermostat). Reading: the weak-coupling thermostat of
+ * Berendsen et al. (J. Chem. Phys. 81, 3684, 1984) on the instantaneous kinetic temperature
+ * T = 2 KE / (3 N k_B), 3N degrees of freedom, KE = sum m v^2 / 2 (amu A^2/fs^2 converted to
+ * eV by 1/9.648533e-3): after the second half-kick each velocity is multiplied by
+ * lambda = sqrt(1 + (dt/tau)(t_target/T - 1)) (lambda = 1 when T = 0; tau >= dt keeps the
+ * radicand >= 0). The shortest pair distance is taken over the pairs of the current list
+ * with r < r_cut at the positions where the forces were evaluated (+inf when none).
  * ---------------------------------------------------------------------------------- */
+#define KB_EV_PER_K 8.617333262e-5
+
+static double kinetic_energy(int32_t n, const double* vel, const int32_t* species,
+                             const double* mass_by_species, double conv) {
+  double s = 0.0;
+  for (int32_t k = 0; k < n; k++) {
+    double v2 = 0.0;
+    for (int a = 0; a < 3; a++) v2 += vel[3 * k + a] * vel[3 * k + a];
+    s += mass_by_species[species[k]] * v2;
+  }
+  return 0.5 * s / conv;
+}
+
+static double min_pair_distance(int32_t n, const double* pos, const double L[3],
+                                const int32_t* row_ptr, const uint32_t* col, double rc) {
+  double best = INFINITY;
+  for (int32_t i = 0; i < n; i++)
+    for (int32_t e = row_ptr[i]; e < row_ptr[i + 1]; e++) {
+      double rv[3];
+      edge_vec(pos, L, i, (int32_t)(col[e] & 0x7FFFFFFu), (int)(col[e] >> 27), rv);
+      double r = sqrt((rv[0] * rv[0] + rv[1] * rv[1]) + rv[2] * rv[2]);
+      if (r < rc && r < best) best = r;
+    }
+  return best;
+}
+
 int32_t tor_md_steps(const tor_model* m, const float* weights, int32_t n, const float box[3],
                      float r_cut, float skin, double* pos, double* vel, int32_t* species,
                      const double* mass_by_species, double dt_fs, int32_t n_steps,
                      int32_t rebuild_every, int32_t* perm_accum, double* forces,
-                     int32_t forces_valid, double* epot_trace, int64_t cap) {
+                     int32_t forces_valid, double* epot_trace, int64_t cap, int32_t thermostat,
+                     double t_target_K, double tau_fs, double* ke_trace, double* rmin_trace) {
   const double conv = 9.648533e-3;
+  const double L[3] = {(double)box[0], (double)box[1], (double)box[2]};
+  if (thermostat != 0 && (thermostat != 1 || !(tau_fs >= dt_fs) || !(t_target_K >= 0.0)))
+    return TOR_ERR_ARG;
   int32_t* row_ptr = (int32_t*)malloc(sizeof(int32_t) * ((size_t)n + 1));
   uint32_t* col = (uint32_t*)malloc(sizeof(uint32_t) * (size_t)(cap > 0 ? cap : 1));
   int32_t* perm = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
@@ -1093,6 +1134,14 @@ int32_t tor_md_steps(const tor_model* m, const float* weights, int32_t n, const 
       double im = conv / mass_by_species[species[k]];
       for (int a = 0; a < 3; a++) vel[3 * k + a] += 0.5 * dt_fs * forces[3 * k + a] * im;
     }
+    if (thermostat == 1) {
+      double T = 2.0 * kinetic_energy(n, vel, species, mass_by_species, conv) /
+                 (3.0 * (double)n * KB_EV_PER_K);
+      double lam = T > 0.0 ? sqrt(1.0 + (dt_fs / tau_fs) * (t_target_K / T - 1.0)) : 1.0;
+      for (int32_t k = 0; k < 3 * n; k++) vel[k] *= lam;
+    }
+    if (ke_trace) ke_trace[s] = kinetic_energy(n, vel, species, mass_by_species, conv);
+    if (rmin_trace) rmin_trace[s] = min_pair_distance(n, pos, L, row_ptr, col, (double)r_cut);
   }
   if (status == TOR_OK && flag) status = TOR_ERR_SKIN;
   free(row_ptr); free(col); free(perm); free(pf); free(ref); free(tmp); free(itmp);

@@ -75,12 +75,16 @@ int32_t tor_energy_forces(const tor_model* m, const float* weights, int32_t n,
                           const int32_t* row_ptr, const uint32_t* col_shift,
                           double* energy, double* e_atom, double* forces, double* feats);
 
-/* Velocity-Verlet between rebuilds (see tor_md_steps in the source for the exact loop). */
+/* Velocity-Verlet between rebuilds (see tor_md_steps in the source for the exact loop);
+ * thermostat 0 = NVE, 1 = Berendsen coupling to t_target_K with time constant tau_fs;
+ * ke_trace / rmin_trace (nullable) receive the kinetic energy (eV) and the shortest pair
+ * distance below r_cut (A) of every step. */
 int32_t tor_md_steps(const tor_model* m, const float* weights, int32_t n, const float box[3],
                      float r_cut, float skin, double* pos, double* vel, int32_t* species,
                      const double* mass_by_species, double dt_fs, int32_t n_steps,
                      int32_t rebuild_every, int32_t* perm_accum, double* forces,
-                     int32_t forces_valid, double* epot_trace, int64_t cap);
+                     int32_t forces_valid, double* epot_trace, int64_t cap, int32_t thermostat,
+                     double t_target_K, double tau_fs, double* ke_trace, double* rmin_trace);
 
 #ifdef __cplusplus
 }

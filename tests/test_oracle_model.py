@@ -361,3 +361,82 @@ def test_md_skin_flag(oracle_mod):
     r = oracle_mod.md_steps(wl.model, w, wl.box, RC, 0.01, wl.pos, v * 20, wl.species,
                             wl.masses(), 0.5, 20, 20)
     assert r["status"] == oracle_mod.ERR_SKIN
+
+
+# ---- NVT (Berendsen weak coupling) and monitors -------------------------------------------
+# Constants from their SI definitions (CODATA 2018), independent of the oracle's values.
+KB_EV = 1.380649e-23 / 1.602176634e-19               # eV/K
+AMU_A2FS2_EV = 1.66053906660e-27 * 1e10 / 1.602176634e-19  # 1 amu A^2/fs^2 in eV
+
+
+def _ke_ev(vel, species, masses):
+    m = masses[species]
+    return 0.5 * float((m[:, None] * np.asarray(vel, np.float64) ** 2).sum()) * AMU_A2FS2_EV
+
+
+def test_ke_trace_is_kinetic_energy(oracle_mod):
+    wl, w, v = _md_setup(oracle_mod)
+    a = oracle_mod.md_steps(wl.model, w, wl.box, RC, SKIN, wl.pos, v, wl.species, wl.masses(),
+                            0.5, 6, 20)
+    assert a["status"] == 0
+    ke = _ke_ev(a["vel"], a["species"], wl.masses())
+    assert abs(a["ke"][-1] - ke) <= 1e-7 * ke  # the oracle's 9.648533e-3 is rounded to 7 digits
+    # NVE: kinetic + potential energy is conserved to the integrator's error
+    etot = a["ke"] + a["epot"]
+    assert np.abs(etot - etot[0]).max() < 1e-3 * np.abs(a["ke"]).max()
+
+
+def test_berendsen_tau_equal_dt_reaches_target(oracle_mod):
+    """With tau = dt the scale factor is sqrt(T0/T): right after the thermostat the kinetic
+    energy is exactly (3N/2) k_B T0 at every step, whatever the forces did."""
+    wl, w, v = _md_setup(oracle_mod)
+    for T0 in (150.0, 450.0):
+        a = oracle_mod.md_steps(wl.model, w, wl.box, RC, SKIN, wl.pos, v, wl.species,
+                                wl.masses(), 0.5, 5, 20, thermostat=1, t_target_K=T0, tau_fs=0.5)
+        assert a["status"] == 0
+        target = 1.5 * wl.n * KB_EV * T0
+        assert np.abs(a["ke"] / target - 1.0).max() < 1e-7
+        assert abs(_ke_ev(a["vel"], a["species"], wl.masses()) / target - 1.0) < 1e-7
+
+
+def test_berendsen_ideal_gas_relaxes_geometrically(oracle_mod):
+    """Zero weights give zero forces (an ideal gas). Each step then sets
+    T <- T + (dt/tau)(T0 - T), so T_s - T0 = (1 - dt/tau)^(s+1) (T_init - T0)."""
+    wl = W.load("water648")
+    w = np.zeros(W.weight_count(wl.model), np.float32)
+    v = W.maxwell_velocities(wl.species, wl.masses(), 40.0, 3002).astype(np.float64)
+    T_init = 2.0 * _ke_ev(v, wl.species, wl.masses()) / (3 * wl.n * KB_EV)
+    T0, dt, tau, n = 25.0, 0.5, 4.0, 12
+    a = oracle_mod.md_steps(wl.model, w, wl.box, RC, SKIN, wl.pos, v, wl.species, wl.masses(),
+                            dt, n, 20, thermostat=1, t_target_K=T0, tau_fs=tau)
+    assert a["status"] == 0
+    assert np.all(a["epot"] == 0.0)
+    T = 2.0 * a["ke"] / (3 * wl.n * KB_EV)
+    expect = T0 + (1.0 - dt / tau) ** np.arange(1, n + 1) * (T_init - T0)
+    assert np.abs(T / expect - 1.0).max() < 1e-7
+
+
+def test_berendsen_arguments(oracle_mod):
+    wl, w, v = _md_setup(oracle_mod)
+    for kw in (dict(thermostat=1, t_target_K=300.0, tau_fs=0.25),  # tau < dt
+               dict(thermostat=1, t_target_K=-1.0, tau_fs=10.0),
+               dict(thermostat=2, t_target_K=300.0, tau_fs=10.0)):
+        a = oracle_mod.md_steps(wl.model, w, wl.box, RC, SKIN, wl.pos, v, wl.species,
+                                wl.masses(), 0.5, 2, 20, **kw)
+        assert a["status"] == oracle_mod.ERR_ARG
+
+
+def test_rmin_trace_brute_force(oracle_mod):
+    """Shortest pair distance: every pair of the returned positions, minimum image."""
+    wl, w, v = _md_setup(oracle_mod)
+    a = oracle_mod.md_steps(wl.model, w, wl.box, RC, SKIN, wl.pos, v, wl.species, wl.masses(),
+                            0.5, 4, 20)
+    assert a["status"] == 0
+    x = a["pos"]
+    L = wl.box.astype(np.float64)
+    d = x[:, None, :] - x[None, :, :]
+    d -= L * np.round(d / L)
+    r = np.sqrt((d ** 2).sum(-1))
+    r[np.arange(wl.n), np.arange(wl.n)] = np.inf
+    assert r.min() < RC
+    assert abs(a["rmin"][-1] - r.min()) < 1e-12
