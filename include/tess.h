@@ -134,6 +134,45 @@ int32_t tess_md_steps(const tess_model_desc* desc, const float* weights, int32_t
                       int32_t* row_ptr, uint32_t* col_shift, int32_t* rev, int64_t edge_cap,
                       int64_t* n_edges, void* workspace, int64_t ws_bytes, void* hip_stream);
 
+/* Thermostat and per-step monitors for tess_md_steps_ex (Tessera abstract: the capsid runs
+ * under NVT and shows no anomalously close pairs; the pages do not name the thermostat).
+ *  thermostat  TESS_THERMOSTAT_NONE: NVE, as tess_md_steps.
+ *              TESS_THERMOSTAT_BERENDSEN: weak coupling (Berendsen et al., J. Chem. Phys. 81,
+ *              3684, 1984) of the kinetic temperature T = 2 KE / (3 N k_B) (3N degrees of
+ *              freedom, k_B = 8.617333262e-5 eV/K, KE = sum m v^2 / 2 converted to eV by
+ *              1/9.648533e-3) to t_target_K: after the second half-kick of every step all
+ *              velocities are multiplied by lambda = sqrt(1 + (dt/tau_fs)(t_target_K/T - 1))
+ *              (lambda = 1 when T = 0). Requires tau_fs >= dt_fs and t_target_K >= 0.
+ *  ke_trace    device double[n_steps] (nullable): kinetic energy in eV at the end of step s
+ *              (after the thermostat), so ke_trace[s] + epot_trace[s] is the total energy.
+ *  rmin_trace  device float[n_steps] (nullable): shortest distance (A) over the listed pairs
+ *              with r < r_cut at the positions where step s evaluated the forces; +inf when
+ *              no pair is that close.
+ * KE is summed in fp64 per block of atoms and the blocks in a fixed order, so traces and
+ * velocities are deterministic. */
+#define TESS_THERMOSTAT_NONE 0
+#define TESS_THERMOSTAT_BERENDSEN 1
+typedef struct {
+  int32_t thermostat;
+  float t_target_K;
+  float tau_fs;
+  double* ke_trace;
+  float* rmin_trace;
+} tess_md_options;
+
+/* tess_md_steps_ex -- tess_md_steps with a thermostat and monitors. `opt` is a HOST pointer
+ * (nullable: identical to tess_md_steps); every other argument, the loop, the flags, the
+ * synchronisation and the errors are those of tess_md_steps. Invalid options: TESS_ERR_ARG
+ * before anything is enqueued. With TESS_MD_GRAPH the options are part of the graph's key. */
+int32_t tess_md_steps_ex(const tess_model_desc* desc, const float* weights, int32_t n,
+                         const float box[3], float r_cut, float skin, float* pos, float* vel,
+                         int32_t* species, const float* mass_by_species, float dt_fs,
+                         int32_t n_steps, int32_t rebuild_every, int32_t flags,
+                         int32_t* perm_accum, float* forces, double* epot_trace,
+                         int32_t* row_ptr, uint32_t* col_shift, int32_t* rev, int64_t edge_cap,
+                         int64_t* n_edges, void* workspace, int64_t ws_bytes,
+                         const tess_md_options* opt, void* hip_stream);
+
 /* Space-filling curve used by later rebuilds in this process: 0 = Hilbert (default, the
  * method's), 1 = Morton (Z-order of the same 10-bit cells; for locality comparisons only, the
  * pair set is the same, the atom order and hence perm/hkey differ). Returns TESS_ERR_ARG for

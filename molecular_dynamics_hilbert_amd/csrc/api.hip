@@ -95,6 +95,83 @@ __global__ void k_vv_kick(int32_t n, float dt, const float* __restrict__ F,
   for (int a = 0; a < 3; a++) vel[3 * i + a] += 0.5f * dt * F[3 * i + a] * im;
 }
 
+// Sum over the 256 threads of a block in a fixed order (every thread gets the same value).
+__device__ __forceinline__ double block_sum_256(double v) {
+  __shared__ double red[4];
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// Second half with the block's kinetic-energy sum: v += dt/2 F/m (as k_vv_kick), then
+// part[block] = sum of m |v|^2 over the block's atoms in fp64 (amu A^2/fs^2).
+__global__ void __launch_bounds__(256) k_vv_kick_ke(int32_t n, float dt,
+                                                    const float* __restrict__ F,
+                                                    const int32_t* __restrict__ species,
+                                                    const float* __restrict__ mass,
+                                                    float* __restrict__ vel,
+                                                    double* __restrict__ part) {
+  int32_t i = blockIdx.x * 256 + threadIdx.x;
+  double mv2 = 0.0;
+  if (i < n) {
+    const float m = mass[species[i]];
+    const float im = kAccelConv / m;
+    double v2 = 0.0;
+#pragma unroll
+    for (int a = 0; a < 3; a++) {
+      const float v = vel[3 * i + a] + 0.5f * dt * F[3 * i + a] * im;
+      vel[3 * i + a] = v;
+      v2 += (double)v * (double)v;
+    }
+    mv2 = (double)m * v2;
+  }
+  mv2 = block_sum_256(mv2);
+  if (threadIdx.x == 0) part[blockIdx.x] = mv2;
+}
+
+constexpr double kAccelConvD = 9.648533e-3;  // eV/A/amu -> A/fs^2, so amu A^2/fs^2 -> eV is 1/it
+constexpr double kBoltzmannEv = 8.617333262e-5;  // eV/K
+
+// End of a step with a thermostat or monitors. Every block sums the kinetic-energy block
+// sums in the same order, so all blocks obtain the same KE and lambda. Berendsen weak
+// coupling: lambda^2 = 1 + (dt/tau)(T0/T - 1) with T = 2 KE / (3 N k_B) (lambda = 1 when
+// T = 0); velocities are scaled by lambda. Block 0 writes the traces: KE after scaling
+// (lambda^2 KE) and the shortest pair distance, whose squared value it then resets to +inf
+// for the next step.
+__global__ void __launch_bounds__(256) k_md_thermo(int32_t n, int32_t nparts,
+                                                   const double* __restrict__ part,
+                                                   int32_t berendsen, double dt_over_tau,
+                                                   double t_target, float* __restrict__ vel,
+                                                   double* __restrict__ ke_out,
+                                                   uint32_t* __restrict__ rmin2_bits,
+                                                   float* __restrict__ rmin_out) {
+  double s = 0.0;
+  for (int32_t k = threadIdx.x; k < nparts; k += 256) s += part[k];
+  s = block_sum_256(s);
+  const double ke = 0.5 * s / kAccelConvD;
+  double lam2 = 1.0;
+  if (berendsen) {
+    const double T = 2.0 * ke / (3.0 * (double)n * kBoltzmannEv);
+    if (T > 0.0) lam2 = 1.0 + dt_over_tau * (t_target / T - 1.0);
+    const float lam = (float)sqrt(lam2);
+    const int32_t i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) {
+#pragma unroll
+      for (int a = 0; a < 3; a++) vel[3 * i + a] *= lam;
+    }
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (ke_out) *ke_out = lam2 * ke;
+    if (rmin_out) {
+      *rmin_out = sqrtf(__uint_as_float(*rmin2_bits));
+      *rmin2_bits = 0x7f800000u;
+    }
+  }
+}
+
+__global__ void k_set_u32(uint32_t* __restrict__ p, uint32_t v) { *p = v; }
+
 inline int32_t gridn(int64_t n, int b) { return (int32_t)((n + b - 1) / b); }
 
 struct Layout {
@@ -106,6 +183,8 @@ struct Layout {
   int32_t* perm;
   int32_t* flag;
   double* epot;
+  double* ke_part;      // kinetic-energy sums, one per block of 256 atoms
+  uint32_t* rmin2_bits;  // shortest squared pair distance of the step (float bits)
   int64_t total;
 };
 
@@ -118,6 +197,8 @@ Layout layout(char* base, const tess_model_desc* md, int32_t n, int64_t cap) {
   L.perm = cv.take<int32_t>(nn);
   L.flag = cv.take<int32_t>(64);
   L.epot = cv.take<double>(4);
+  L.ke_part = cv.take<double>(gridn(nn, 256));
+  L.rmin2_bits = cv.take<uint32_t>(64);
   if (md) {
     L.ef_bytes = ef_workspace_bytes(*md, n, cap);
     L.ef = cv.take<char>(L.ef_bytes);
@@ -145,8 +226,8 @@ using namespace tess;
 namespace {
 struct GraphKey {
   const void* p[14];
-  int64_t i[6];
-  float f[5];
+  int64_t i[7];
+  float f[7];
   bool operator==(const GraphKey& o) const { return std::memcmp(this, &o, sizeof(*this)) == 0; }
 };
 struct GraphCache {
@@ -165,18 +246,21 @@ int32_t md_interval_graph(const tess_model_desc* d, const float* weights, int32_
                           const float box[3], float* pos, float* vel, int32_t* species,
                           const float* mass, float dt, float* forces, double* epot0,
                           int32_t* row_ptr, uint32_t* col_shift, int32_t* rev, int64_t edge_cap,
-                          void* ws, int32_t k, hipStream_t st, StepFn step, bool* done) {
+                          void* ws, const tess_md_options& opt, double* ke0, float* rmin0,
+                          int32_t k, hipStream_t st, StepFn step, bool* done) {
   GraphKey key;
   std::memset(&key, 0, sizeof(key));
   // the model description and the box are host arrays: their values are part of the key
   const void* ps[14] = {weights, pos, vel, species, mass, forces, epot0, row_ptr, col_shift,
-                        rev, ws, nullptr, nullptr, nullptr};
+                        rev, ws, ke0, rmin0, nullptr};
   for (int a = 0; a < 14; a++) key.p[a] = ps[a];
   key.i[0] = n; key.i[1] = edge_cap; key.i[2] = k;
   key.i[3] = d->n_species; key.i[4] = d->n_layers;
   key.i[5] = ((int64_t)d->channels << 40) | ((int64_t)d->radial_hidden << 24) |
              ((int64_t)d->n_rbf << 16) | ((int64_t)d->l_max << 8) | d->n_heads;
+  key.i[6] = opt.thermostat;
   key.f[0] = dt; key.f[1] = box[0]; key.f[2] = box[1]; key.f[3] = box[2]; key.f[4] = d->r_cut;
+  key.f[5] = opt.t_target_K; key.f[6] = opt.tau_fs;
   GraphCache& c = graph_cache();
   std::lock_guard<std::mutex> g(c.mu);
   if (!(c.valid && c.key == key)) {
@@ -329,18 +413,26 @@ int32_t tess_energy_forces(const tess_model_desc* d, const float* weights, int32
                      energy, e_atom, forces, L.ef, L.ef_bytes, st);
 }
 
-int32_t tess_md_steps(const tess_model_desc* d, const float* weights, int32_t n, const float box[3],
-                      float r_cut, float skin, float* pos, float* vel, int32_t* species,
-                      const float* mass_by_species, float dt_fs, int32_t n_steps,
-                      int32_t rebuild_every, int32_t flags, int32_t* perm_accum, float* forces,
-                      double* epot_trace, int32_t* row_ptr, uint32_t* col_shift, int32_t* rev,
-                      int64_t edge_cap, int64_t* n_edges, void* workspace, int64_t ws_bytes,
-                      void* hip_stream) {
+int32_t tess_md_steps_ex(const tess_model_desc* d, const float* weights, int32_t n,
+                         const float box[3], float r_cut, float skin, float* pos, float* vel,
+                         int32_t* species, const float* mass_by_species, float dt_fs,
+                         int32_t n_steps, int32_t rebuild_every, int32_t flags,
+                         int32_t* perm_accum, float* forces, double* epot_trace,
+                         int32_t* row_ptr, uint32_t* col_shift, int32_t* rev, int64_t edge_cap,
+                         int64_t* n_edges, void* workspace, int64_t ws_bytes,
+                         const tess_md_options* opt_in, void* hip_stream) {
   if (!d || !ef_shape_supported(*d)) return TESS_ERR_ARG;
   if (n < 1 || n >= (1 << 27) || n_steps < 0 || rebuild_every < 1 || edge_cap < 0 || !box ||
       !n_edges || !weights || !pos || !vel || !species || !mass_by_species || !perm_accum ||
       !forces || !row_ptr || !col_shift || !rev || !(dt_fs > 0.0f) || !(r_cut > 0.0f) ||
       !(skin >= 0.0f) || d->r_cut != r_cut || (flags & ~(TESS_MD_FORCES_VALID | TESS_MD_GRAPH)))
+    return TESS_ERR_ARG;
+  tess_md_options opt{TESS_THERMOSTAT_NONE, 0.0f, 0.0f, nullptr, nullptr};
+  if (opt_in) opt = *opt_in;
+  if (opt.thermostat != TESS_THERMOSTAT_NONE &&
+      (opt.thermostat != TESS_THERMOSTAT_BERENDSEN || !(opt.tau_fs >= dt_fs) ||
+       !(opt.t_target_K >= 0.0f) || !std::isfinite(opt.t_target_K) ||
+       !std::isfinite(opt.tau_fs)))
     return TESS_ERR_ARG;
   if (!box_ok(box, r_cut, skin)) return TESS_ERR_BOX;
   Layout L = layout(reinterpret_cast<char*>(workspace), d, n, edge_cap);
@@ -350,20 +442,41 @@ int32_t tess_md_steps(const tess_model_desc* d, const float* weights, int32_t n,
   const bool forces_valid = (flags & TESS_MD_FORCES_VALID) != 0;
   // graph replay needs a capturable stream and no per-launch timing events
   const bool use_graph = (flags & TESS_MD_GRAPH) != 0 && st != nullptr && !timing_on();
+  const bool berendsen = opt.thermostat == TESS_THERMOSTAT_BERENDSEN;
+  const bool need_ke = berendsen || opt.ke_trace;
+  const bool end_kernel = need_ke || opt.rmin_trace;
+  const int32_t nb = gridn(n, 256);
   int64_t ne = *n_edges;
   TESS_HIP_CHECK(hipMemsetAsync(L.flag, 0, sizeof(int32_t), st));
+  if (opt.rmin_trace) {
+    k_set_u32<<<1, 1, 0, st>>>(L.rmin2_bits, 0x7f800000u);
+    TESS_HIP_CHECK(hipGetLastError());
+  }
   // one velocity-Verlet step; `grid_edges` sizes the edge-kernel grids (the kernels stop at
   // the device-side active-edge count, so any value >= the pair count gives the same result)
   auto step = [&](int32_t s, int64_t grid_edges) -> int32_t {
-    k_vv_kick_drift<<<gridn(n, 256), 256, 0, st>>>(n, dt_fs, forces, species, mass_by_species,
-                                                   pos, vel, L.ref_pos, half_skin2, L.flag);
+    k_vv_kick_drift<<<nb, 256, 0, st>>>(n, dt_fs, forces, species, mass_by_species, pos, vel,
+                                        L.ref_pos, half_skin2, L.flag);
     TESS_HIP_CHECK(hipGetLastError());
     int32_t rc = ef_dispatch(*d, weights, n, box, pos, species, row_ptr, col_shift, rev,
                              grid_edges, edge_cap, epot_trace ? epot_trace + s : L.epot, nullptr,
-                             forces, L.ef, L.ef_bytes, st);
+                             forces, L.ef, L.ef_bytes, st,
+                             opt.rmin_trace ? L.rmin2_bits : nullptr);
     if (rc != TESS_OK) return rc;
-    k_vv_kick<<<gridn(n, 256), 256, 0, st>>>(n, dt_fs, forces, species, mass_by_species, vel);
+    if (need_ke)
+      k_vv_kick_ke<<<nb, 256, 0, st>>>(n, dt_fs, forces, species, mass_by_species, vel,
+                                       L.ke_part);
+    else
+      k_vv_kick<<<nb, 256, 0, st>>>(n, dt_fs, forces, species, mass_by_species, vel);
     TESS_HIP_CHECK(hipGetLastError());
+    if (end_kernel) {
+      k_md_thermo<<<berendsen ? nb : 1, 256, 0, st>>>(
+          n, need_ke ? nb : 0, L.ke_part, berendsen ? 1 : 0,
+          berendsen ? (double)dt_fs / (double)opt.tau_fs : 0.0, (double)opt.t_target_K, vel,
+          opt.ke_trace ? opt.ke_trace + s : nullptr, L.rmin2_bits,
+          opt.rmin_trace ? opt.rmin_trace + s : nullptr);
+      TESS_HIP_CHECK(hipGetLastError());
+    }
     return TESS_OK;
   };
   for (int32_t s = 0; s < n_steps;) {
@@ -389,7 +502,9 @@ int32_t tess_md_steps(const tess_model_desc* d, const float* weights, int32_t n,
     if (use_graph) {
       rc = md_interval_graph(d, weights, n, box, pos, vel, species, mass_by_species, dt_fs,
                              forces, epot_trace ? epot_trace + s : L.epot, row_ptr, col_shift,
-                             rev, edge_cap, workspace, k, st,
+                             rev, edge_cap, workspace, opt,
+                             opt.ke_trace ? opt.ke_trace + s : nullptr,
+                             opt.rmin_trace ? opt.rmin_trace + s : nullptr, k, st,
                              [&](int32_t j) { return step(s + j, edge_cap); }, &done);
       if (rc != TESS_OK) return rc;
     }
@@ -404,6 +519,19 @@ int32_t tess_md_steps(const tess_model_desc* d, const float* weights, int32_t n,
   TESS_HIP_CHECK(hipMemcpyAsync(&f, L.flag, sizeof(int32_t), hipMemcpyDeviceToHost, st));
   TESS_HIP_CHECK(hipStreamSynchronize(st));
   return f ? TESS_ERR_SKIN : TESS_OK;
+}
+
+int32_t tess_md_steps(const tess_model_desc* d, const float* weights, int32_t n, const float box[3],
+                      float r_cut, float skin, float* pos, float* vel, int32_t* species,
+                      const float* mass_by_species, float dt_fs, int32_t n_steps,
+                      int32_t rebuild_every, int32_t flags, int32_t* perm_accum, float* forces,
+                      double* epot_trace, int32_t* row_ptr, uint32_t* col_shift, int32_t* rev,
+                      int64_t edge_cap, int64_t* n_edges, void* workspace, int64_t ws_bytes,
+                      void* hip_stream) {
+  return tess_md_steps_ex(d, weights, n, box, r_cut, skin, pos, vel, species, mass_by_species,
+                          dt_fs, n_steps, rebuild_every, flags, perm_accum, forces, epot_trace,
+                          row_ptr, col_shift, rev, edge_cap, n_edges, workspace, ws_bytes,
+                          nullptr, hip_stream);
 }
 
 }  // extern "C"

@@ -267,18 +267,27 @@ __global__ void __launch_bounds__(256) k_active_count(int32_t n, const float* __
                                                       const int32_t* __restrict__ row_ptr,
                                                       const uint32_t* __restrict__ col, float Lx,
                                                       float Ly, float Lz, float rc2,
-                                                      int32_t* __restrict__ acnt) {
+                                                      int32_t* __restrict__ acnt,
+                                                      uint32_t* __restrict__ rmin2_bits) {
   int32_t i = blockIdx.x * 4 + (threadIdx.x >> 6);
   int lane = threadIdx.x & 63;
   if (i >= n) return;
   int cnt = 0;
+  float mn = INFINITY;
   for (int32_t e = row_ptr[i] + lane; e < row_ptr[i + 1]; e += 64) {
     int32_t j;
     float4 r = edge_vec(pos, i, col[e], Lx, Ly, Lz, &j);
-    cnt += r.w < rc2;
+    const bool act = r.w < rc2;
+    cnt += act;
+    if (act) mn = fminf(mn, r.w);
   }
   for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
   if (lane == 0) acnt[i] = cnt;
+  if (rmin2_bits) {
+    // shortest squared pair distance: non-negative floats order like their bit patterns
+    for (int o = 32; o >= 1; o >>= 1) mn = fminf(mn, __shfl_xor(mn, o, 64));
+    if (lane == 0 && mn < INFINITY) atomicMin(rmin2_bits, __float_as_uint(mn));
+  }
 }
 
 __global__ void __launch_bounds__(256) k_active_fill(int32_t n, const float* __restrict__ pos,
@@ -1136,7 +1145,8 @@ template <int LMAX, int C, int H, int R>
 int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const float box[3],
                const float* pos, const int32_t* species, const int32_t* row_ptr,
                const uint32_t* col_shift, const int32_t* rev_in, int64_t n_edges, int64_t ecap,
-               double* energy, float* e_atom, float* forces, const EFWS& w, hipStream_t st) {
+               double* energy, float* e_atom, float* forces, const EFWS& w, hipStream_t st,
+               uint32_t* rmin2_bits) {
   constexpr int D = Dims<LMAX>::D;
   constexpr int P = Dims<LMAX>::P;
   constexpr int G = C * (1 + LMAX);
@@ -1178,7 +1188,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
       rev = w.rev_own;
     }
     k_active_count<<<gridn(n, 4), 256, 0, st>>>(n, pos, row_ptr, col_shift, box[0], box[1], box[2],
-                                                rc * rc, w.arow);
+                                                rc * rc, w.arow, rmin2_bits);
     k_fill_i32<<<1, 64, 0, st>>>(w.arow + n, 1, 0);
     TESS_HIP_CHECK(scan_exclusive_i32(w.arow, (int64_t)n + 1, w.scan_tmp, st));
     k_active_fill<<<gridn(n, 4), 256, 0, st>>>(n, pos, row_ptr, col_shift, box[0], box[1], box[2],
@@ -1334,7 +1344,7 @@ int32_t ef_dispatch(const tess_model_desc& md, const float* weights, int32_t n, 
                     const float* pos, const int32_t* species, const int32_t* row_ptr,
                     const uint32_t* col_shift, const int32_t* rev, int64_t n_edges,
                     int64_t ecap, double* energy, float* e_atom, float* forces, char* ws,
-                    int64_t ws_bytes, hipStream_t st) {
+                    int64_t ws_bytes, hipStream_t st, uint32_t* rmin2_bits) {
   Carver cv{ws, 0};
   EFWS w = carve_ef(cv, md, n, ecap);
   if (cv.off > ws_bytes) return TESS_ERR_WORKSPACE;
@@ -1342,7 +1352,7 @@ int32_t ef_dispatch(const tess_model_desc& md, const float* weights, int32_t n, 
 #define TESS_EF_CASE(L_, C_, H_, R_)                                                          \
   if (l == L_ && c == C_ && h == H_ && r == R_)                                               \
     return ef_run<L_, C_, H_, R_>(md, weights, n, box, pos, species, row_ptr, col_shift, rev, \
-                                  n_edges, ecap, energy, e_atom, forces, w, st);
+                                  n_edges, ecap, energy, e_atom, forces, w, st, rmin2_bits);
   TESS_EF_CASE(1, 16, 1, 32)
   TESS_EF_CASE(2, 32, 4, 32)
   TESS_EF_CASE(2, 64, 4, 64)

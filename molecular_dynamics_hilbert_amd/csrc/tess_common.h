@@ -294,7 +294,7 @@ int32_t ef_dispatch(const tess_model_desc& md, const float* weights, int32_t n, 
                     const float* pos, const int32_t* species, const int32_t* row_ptr,
                     const uint32_t* col_shift, const int32_t* rev, int64_t n_edges,
                     int64_t ecap, double* energy, float* e_atom, float* forces, char* ws,
-                    int64_t ws_bytes, hipStream_t st);
+                    int64_t ws_bytes, hipStream_t st, uint32_t* rmin2_bits = nullptr);
 }  // namespace tess
 
 #define TESS_HIP_CHECK(expr)                       \

@@ -35,6 +35,14 @@ class ModelDesc(C.Structure):
                 ("radial_hidden", C.c_int32), ("r_cut", C.c_float)]
 
 
+THERMOSTAT_NONE, THERMOSTAT_BERENDSEN = 0, 1
+
+
+class MdOptions(C.Structure):
+    _fields_ = [("thermostat", C.c_int32), ("t_target_K", C.c_float), ("tau_fs", C.c_float),
+                ("ke_trace", C.c_void_p), ("rmin_trace", C.c_void_p)]
+
+
 _lib = None
 
 
@@ -61,6 +69,9 @@ def lib() -> C.CDLL:
         L.tess_md_steps.restype = i32
         L.tess_md_steps.argtypes = [p, p, i32, p, f32, f32, p, p, p, p, f32, i32, i32, i32, p, p,
                                     p, p, p, p, i64, p, p, i64, p]
+        L.tess_md_steps_ex.restype = i32
+        L.tess_md_steps_ex.argtypes = [p, p, i32, p, f32, f32, p, p, p, p, f32, i32, i32, i32, p,
+                                       p, p, p, p, p, i64, p, p, i64, p, p]
         L.tess_timing_enable.restype = i32
         L.tess_timing_enable.argtypes = [i32]
         L.tess_timing_read.restype = i32
@@ -176,19 +187,30 @@ def energy_forces(spec, weights, box, pos, species, row_ptr, col_shift, rev, n_e
 
 def md_steps(spec, weights, box, r_cut, skin, pos, vel, species, mass_by_species, dt_fs, n_steps,
              rebuild_every, perm_accum, forces, row_ptr, col_shift, rev, ws, epot_trace=None,
-             forces_valid=False, graph=False, check=True):
+             forces_valid=False, graph=False, check=True, thermostat=None, t_target_K=0.0,
+             tau_fs=0.0, ke_trace=None, rmin_trace=None):
+    """tess_md_steps, or tess_md_steps_ex when a thermostat ("berendsen") or a trace
+    (ke_trace float64[n_steps], rmin_trace float32[n_steps]) is given."""
     n = int(pos.shape[0])
     ne = C.c_int64(0)
-    st = lib().tess_md_steps(C.byref(desc(spec)), _p(weights), n, _box(box), float(r_cut),
-                             float(skin), _p(pos), _p(vel), _p(species), _p(mass_by_species),
-                             float(dt_fs), int(n_steps), int(rebuild_every),
-                             (MD_FORCES_VALID if forces_valid else 0) | (MD_GRAPH if graph else 0),
-                             _p(perm_accum), _p(forces),
-                             _p(epot_trace), _p(row_ptr), _p(col_shift), _p(rev),
-                             int(col_shift.numel()), C.byref(ne), _p(ws), int(ws.numel()),
-                             _stream())
+    args = [C.byref(desc(spec)), _p(weights), n, _box(box), float(r_cut), float(skin), _p(pos),
+            _p(vel), _p(species), _p(mass_by_species), float(dt_fs), int(n_steps),
+            int(rebuild_every),
+            (MD_FORCES_VALID if forces_valid else 0) | (MD_GRAPH if graph else 0),
+            _p(perm_accum), _p(forces), _p(epot_trace), _p(row_ptr), _p(col_shift), _p(rev),
+            int(col_shift.numel()), C.byref(ne), _p(ws), int(ws.numel())]
+    if thermostat is None and ke_trace is None and rmin_trace is None:
+        st = lib().tess_md_steps(*args, _stream())
+        name = "tess_md_steps"
+    else:
+        kinds = {None: THERMOSTAT_NONE, "none": THERMOSTAT_NONE,
+                 "berendsen": THERMOSTAT_BERENDSEN}
+        opt = MdOptions(kinds[thermostat] if thermostat in kinds else int(thermostat),
+                        float(t_target_K), float(tau_fs), _p(ke_trace), _p(rmin_trace))
+        st = lib().tess_md_steps_ex(*args, C.byref(opt), _stream())
+        name = "tess_md_steps_ex"
     if check and st != OK:
-        raise TessError(st, "tess_md_steps")
+        raise TessError(st, name)
     return st, int(ne.value)
 
 

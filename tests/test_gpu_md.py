@@ -19,7 +19,7 @@ def T():
     return tess
 
 
-def _gpu_md(T, wl, w, vel, steps, every, skin=None, scale_v=1.0):
+def _gpu_md(T, wl, w, vel, steps, every, skin=None, scale_v=1.0, traces=False, **thermo):
     import torch
     s = T.System(wl, w, skin=skin)
     dev = "cuda"
@@ -27,26 +27,41 @@ def _gpu_md(T, wl, w, vel, steps, every, skin=None, scale_v=1.0):
     masses = torch.from_numpy(wl.masses().astype(np.float32)).to(dev)
     pa = torch.arange(wl.n, dtype=torch.int32, device=dev)
     ep = torch.zeros(steps, dtype=torch.float64, device=dev)
+    ke = torch.zeros(steps, dtype=torch.float64, device=dev) if traces else None
+    rmin = torch.zeros(steps, dtype=torch.float32, device=dev) if traces else None
     st, ne = T.md_steps(s.spec, s.weights, s.box, s.r_cut, s.skin, s.pos, vel_t, s.species, masses,
                         wl.dt_fs, steps, every, pa, s.forces, s.row_ptr, s.col_shift, s.rev, s.ws,
-                        epot_trace=ep, check=False)
+                        epot_trace=ep, check=False, ke_trace=ke, rmin_trace=rmin, **thermo)
     torch.cuda.synchronize()
     return dict(status=st, pos=s.pos.cpu().numpy().astype(np.float64),
                 vel=vel_t.cpu().numpy().astype(np.float64), pa=pa.cpu().numpy(),
-                forces=s.forces.cpu().numpy().astype(np.float64), epot=ep.cpu().numpy())
+                forces=s.forces.cpu().numpy().astype(np.float64), epot=ep.cpu().numpy(),
+                ke=None if ke is None else ke.cpu().numpy(),
+                rmin=None if rmin is None else rmin.cpu().numpy().astype(np.float64))
 
 
-def _compare(T, oracle_mod, wname, steps, every, wseed, scale=1.0, temp=50.0):
+def _compare(T, oracle_mod, wname, steps, every, wseed, scale=1.0, temp=50.0, traces=False,
+             **thermo):
     """Random weights bind nothing, so at 300 K the fastest H atoms pass skin/2 within one
     20-step interval; the parity runs start at 50 K so that no interval is flagged."""
     wl = W.load(wname)
     w = W.make_weights(wl.model, wseed)
     w[-wl.model.channels:] *= scale
     vel = W.maxwell_velocities(wl.species, wl.masses(), temp, 3000 + wseed % 1000)
-    g = _gpu_md(T, wl, w, vel, steps, every)
+    g = _gpu_md(T, wl, w, vel, steps, every, traces=traces, **thermo)
+    othermo = {}
+    if thermo.get("thermostat") == "berendsen":
+        othermo = dict(thermostat=1, t_target_K=thermo["t_target_K"], tau_fs=thermo["tau_fs"])
     o = oracle_mod.md_steps(wl.model, w, wl.box, wl.model.r_cut, wl.skin, wl.pos, vel, wl.species,
-                            wl.masses(), wl.dt_fs, steps, every)
+                            wl.masses(), wl.dt_fs, steps, every, **othermo)
     assert g["status"] == o["status"] == 0
+    if traces:
+        dke = np.abs(g["ke"] / o["ke"] - 1.0).max()
+        drm = np.abs(g["rmin"] - o["rmin"]).max()
+        print("%s traces: max rel dKE=%.2e max |d rmin|=%.2e A (rmin %.4f..%.4f)" % (
+            wname, dke, drm, o["rmin"].min(), o["rmin"].max()), flush=True)
+        assert dke <= 1e-5
+        assert drm <= 1e-4
     assert np.array_equal(np.sort(g["pa"]), np.arange(wl.n))
     xg = np.empty((wl.n, 3)); xg[g["pa"]] = g["pos"]
     xo = np.empty((wl.n, 3)); xo[o["perm_accum"]] = o["pos"]
@@ -75,6 +90,91 @@ def test_md_salt4k_short(T, oracle_mod):
     _compare(T, oracle_mod, "salt4k", 6, 3, 2002)
 
 
+def test_md_traces_nve_water(T, oracle_mod):
+    """Kinetic-energy and shortest-pair-distance traces (tess_md_steps_ex, no thermostat)
+    against the oracle's; two intervals with a rebuild between them."""
+    _compare(T, oracle_mod, "water648", 20, 10, 2001, scale=10.0, traces=True)
+
+
+def test_md_traces_leave_nve_unchanged(T):
+    """Asking for traces does not change the trajectory: bit-identical to tess_md_steps."""
+    wl = W.load("salt4k")
+    w = W.make_weights(wl.model, 2002)
+    vel = W.maxwell_velocities(wl.species, wl.masses(), 50.0, 3002)
+    a = _gpu_md(T, wl, w, vel, 6, 3)
+    b = _gpu_md(T, wl, w, vel, 6, 3, traces=True)
+    assert a["status"] == b["status"] == 0
+    for k in ("pos", "vel", "forces", "epot", "pa"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_md_nvt_berendsen_water(T, oracle_mod):
+    """Berendsen coupling (50 K start, T0 = 100 K, tau = 10 fs) over two intervals."""
+    _compare(T, oracle_mod, "water648", 20, 10, 2001, scale=10.0, traces=True,
+             thermostat="berendsen", t_target_K=100.0, tau_fs=10.0)
+
+
+def test_md_nvt_berendsen_salt4k(T, oracle_mod):
+    _compare(T, oracle_mod, "salt4k", 6, 3, 2002, traces=True, thermostat="berendsen",
+             t_target_K=20.0, tau_fs=2.0)
+
+
+def test_nvt_ideal_gas_closed_form(T):
+    """Zero weights give zero forces. Each Berendsen step then sets T <- T + (dt/tau)(T0 - T),
+    so T_s - T0 = (1 - dt/tau)^(s+1) (T_init - T0) exactly (salt60k, 12 steps)."""
+    wl = W.load("salt60k")
+    w = np.zeros(W.weight_count(wl.model), np.float32)
+    vel = W.maxwell_velocities(wl.species, wl.masses(), 40.0, 3005)
+    kb = 1.380649e-23 / 1.602176634e-19
+    amu = 1.66053906660e-27 * 1e10 / 1.602176634e-19
+    m = wl.masses()[wl.species]
+    v64 = vel.astype(np.float64)
+    T_init = (m[:, None] * v64 ** 2).sum() * amu / (3 * wl.n * kb)
+    T0, tau, n = 25.0, 4.0, 12
+    g = _gpu_md(T, wl, w, vel, n, 20, traces=True, thermostat="berendsen", t_target_K=T0,
+                tau_fs=tau)
+    assert g["status"] == 0
+    assert np.all(g["epot"] == 0.0)
+    Tg = 2.0 * g["ke"] / (3 * wl.n * kb)
+    expect = T0 + (1.0 - wl.dt_fs / tau) ** np.arange(1, n + 1) * (T_init - T0)
+    print("ideal gas: T %.3f -> %.3f, max rel err %.2e" % (T_init, Tg[-1],
+                                                           np.abs(Tg / expect - 1).max()), flush=True)
+    assert np.abs(Tg / expect - 1.0).max() < 1e-5
+
+
+def test_nvt_relaxation_and_close_pairs(T):
+    """NVT harness: salt4k from 50 K coupled to 30 K (tau = 10 fs), 400 steps of 0.5 fs with a
+    rebuild every 20. The kinetic temperature settles near the target (mean over the last
+    100 steps within 10%; the random-weight potential keeps releasing energy, which holds T
+    slightly above T0 at a rate the coupling balances). The shortest-pair-distance monitor at
+    the last step equals a brute-force minimum over all pairs of the final positions. Random
+    weights have no short-range repulsion, so pairs do drift together: the monitor is what
+    reports such anomalously close pairs."""
+    wl = W.load("salt4k")
+    w = W.make_weights(wl.model, 2002)
+    vel = W.maxwell_velocities(wl.species, wl.masses(), 50.0, 3002)
+    g = _gpu_md(T, wl, w, vel, 400, 20, traces=True, thermostat="berendsen", t_target_K=30.0,
+                tau_fs=10.0)
+    assert g["status"] == 0
+    kb = 1.380649e-23 / 1.602176634e-19
+    Tk = 2.0 * g["ke"] / (3 * wl.n * kb)
+    x = g["pos"]
+    L = wl.box.astype(np.float64)
+    best = np.inf
+    for a in range(0, wl.n, 500):
+        d = x[a:a + 500, None, :] - x[None, :, :]
+        d -= L * np.round(d / L)
+        r = np.sqrt((d ** 2).sum(-1))
+        r[np.arange(r.shape[0]), np.arange(a, a + r.shape[0])] = np.inf
+        best = min(best, float(r.min()))
+    print("NVT salt4k: T %.2f -> mean(last 100) %.2f K; rmin %.4f (start) -> %.4f (end), "
+          "brute force %.4f A" % (Tk[0], Tk[-100:].mean(), g["rmin"][0], g["rmin"][-1], best),
+          flush=True)
+    assert abs(Tk[-100:].mean() / 30.0 - 1.0) < 0.10
+    assert np.all(np.isfinite(g["rmin"]))
+    assert abs(g["rmin"][-1] - best) < 1e-4
+
+
 def test_md_skin_error(T, oracle_mod):
     """At 300 K some H atom passes skin/2 within the first interval: both the library and the
     oracle finish that interval and report it."""
@@ -92,7 +192,8 @@ def test_md_skin_error(T, oracle_mod):
     assert np.abs(dx).max() <= 1e-4
 
 
-def test_md_graph_replay_matches_eager(T):
+@pytest.mark.parametrize("nvt", [False, True])
+def test_md_graph_replay_matches_eager(T, nvt):
     """TESS_MD_GRAPH: the steps of a rebuild interval are captured into a HIP graph once and
     replayed. Two identical systems, one eager and one replayed, run three calls of two
     20-step intervals each (the first interval captures, every later one replays), with
@@ -110,6 +211,11 @@ def test_md_graph_replay_matches_eager(T):
         runs.append(dict(s=s, graph=graph, vel=torch.from_numpy(vel.copy()).to(dev),
                          pa=torch.arange(wl.n, dtype=torch.int32, device=dev),
                          ep=torch.zeros(40, dtype=torch.float64, device=dev)))
+        if nvt:  # Berendsen thermostat and both traces inside the captured steps
+            runs[-1].update(thermo=dict(thermostat="berendsen", t_target_K=40.0, tau_fs=10.0,
+                                        ke_trace=torch.zeros(40, dtype=torch.float64, device=dev),
+                                        rmin_trace=torch.zeros(40, dtype=torch.float32,
+                                                               device=dev)))
     other = T.System(W.load("water648"), W.make_weights(W.load("water648").model, 2001))
     other.rebuild()
     torch.cuda.synchronize()
@@ -126,7 +232,8 @@ def _graph_calls(T, torch, wl, masses, runs, other):
             st, _ = T.md_steps(s.spec, s.weights, s.box, s.r_cut, s.skin, s.pos, r["vel"],
                                s.species, masses, wl.dt_fs, 40, 20, r["pa"], s.forces, s.row_ptr,
                                s.col_shift, s.rev, s.ws, epot_trace=r["ep"],
-                               forces_valid=call > 0, graph=r["graph"], check=False)
+                               forces_valid=call > 0, graph=r["graph"], check=False,
+                               **r.get("thermo", {}))
             assert st == T.OK
             torch.cuda.synchronize()
             other.energy_forces()  # eager work between replays
@@ -137,6 +244,9 @@ def _graph_calls(T, torch, wl, masses, runs, other):
         assert torch.equal(a["s"].forces, b["s"].forces)
         assert torch.equal(a["pa"], b["pa"])
         assert torch.equal(a["ep"], b["ep"])
+        if "thermo" in a:
+            for k in ("ke_trace", "rmin_trace"):
+                assert torch.equal(a["thermo"][k], b["thermo"][k]), k
         print("call %d: identical, E=%.6f" % (call, float(b["ep"][-1])), flush=True)
 
 

@@ -61,3 +61,28 @@ def test_host_side_rejections(T):
     e = L.tess_energy_forces(C.byref(good), fake, 10, ok_box, fake, fake, fake, fake, None, 10,
                              fake, None, None, fake, 8, None)
     assert e == T.ERR_WORKSPACE
+
+
+def test_md_options_rejected_host_side(T):
+    """tess_md_steps_ex checks its thermostat options before enqueueing anything."""
+    L = T.lib()
+    fake = C.c_void_p(0x1000)
+    ne = C.c_int64(0)
+    box = (C.c_float * 3)(30.0, 30.0, 30.0)
+    good = T.desc(W.water648().model)
+    rc = float(W.water648().model.r_cut)
+
+    def call(opt, ws_bytes=1 << 40):
+        return L.tess_md_steps_ex(C.byref(good), fake, 10, box, rc, 1.0, fake, fake, fake, fake,
+                                  0.5, 4, 20, 0, fake, fake, None, fake, fake, fake, 100,
+                                  C.byref(ne), fake, ws_bytes, opt, None)
+
+    for o in (T.MdOptions(T.THERMOSTAT_BERENDSEN, 300.0, 0.25, None, None),  # tau < dt
+              T.MdOptions(T.THERMOSTAT_BERENDSEN, -5.0, 10.0, None, None),
+              T.MdOptions(T.THERMOSTAT_BERENDSEN, float("nan"), 10.0, None, None),
+              T.MdOptions(7, 300.0, 10.0, None, None)):
+        assert call(C.byref(o)) == T.ERR_ARG
+    # valid options reach the workspace check
+    o = T.MdOptions(T.THERMOSTAT_BERENDSEN, 300.0, 10.0, None, None)
+    assert call(C.byref(o), ws_bytes=8) == T.ERR_WORKSPACE
+    assert call(None, ws_bytes=8) == T.ERR_WORKSPACE
