@@ -436,8 +436,7 @@ __global__ void __launch_bounds__(256) k_edge_prep(const int32_t* __restrict__ a
 //     M_h = max_a s_ah, Z_h = sum_a u_a exp(s_ah - M_h), alpha_ah = u_a exp(s_ah - M_h)/Z_h,
 //     m_i[d3][c] = sum_a alpha_a,h(c) sum_d1 A_a[d3][d1] h_j[d1][c];
 //   adjoint (TRANS = true), row = x, edges a = (x <- y) with forward edge e' = rev(a) = (y <- x):
-//     hbar_x[d1][c] += alpha_e',h(c) sum_d3 A_e'[d3][d1] mbar_y[d3][c]   (A_e' uses Y(-n_a)),
-//     kbar_x[c] += sbar_e',h(c) q_y[c] / sqrt(d),  qbar_x[c] += sbar_a,h(c) k_y[c] / sqrt(d).
+//     hbar_x[d1][c] += alpha_e',h(c) sum_d3 A_e'[d3][d1] mbar_y[d3][c]   (A_e' uses Y(-n_a)).
 //
 // Chunks of 32 (adjoint: 24) edges: lanes first build alpha and A_e (lane = edge) into
 // LDS. The channel sums then run on 4x4x1 MFMA blocks (v_mfma_f32_4x4x1f32: 16 independent
@@ -457,8 +456,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
     int32_t n, const int32_t* __restrict__ arow, const float4* __restrict__ ageo,
     const int32_t* __restrict__ asrc, const int32_t* __restrict__ arev,
     const float* __restrict__ ew, const float4* __restrict__ es, const float* __restrict__ X,
-    float rc, float* __restrict__ out, const float* __restrict__ base, float4* __restrict__ P,
-    const float4* __restrict__ sbar, const float* __restrict__ qk, float* __restrict__ qkbar) {
+    float rc, float* __restrict__ out, const float* __restrict__ base, float4* __restrict__ P) {
   constexpr int D = Dims<LMAX>::D;
   constexpr int DI = L0ONLY ? 1 : D;          // input components that can be non-zero
   constexpr int CQ = C / 4;                   // channel quads
@@ -471,8 +469,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
   constexpr int kChunk = TRANS ? 24 : 32;
   __shared__ float sA[4][kChunk][D * DI];
   __shared__ float sAl[4][kChunk][4];
-  __shared__ float sSs[4][TRANS ? kChunk : 1][4];
-  __shared__ float sSd[4][TRANS ? kChunk : 1][4];
   __shared__ int32_t sJ[4][kChunk];
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int q = lane / CQ, m = lane % CQ, jj = lane & 3;
@@ -514,8 +510,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
     for (int d = 0; d < NDG; d++) acc[t][d] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   float4 acc8 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   const int hl = (4 * m) / dh;  // head of this lane's channels
-  float qacc = 0.0f, kacc = 0.0f;
-  const int hc = (lane < C ? lane : 0) / dh;  // head of channel `lane` (q/k adjoints)
   // Per-edge inputs of a chunk's prologue (lane = edge). The forward requests those of the
   // next chunk before the current chunk's MFMA groups, so their latency is hidden.
   constexpr int PP = Dims<LMAX>::P;
@@ -557,14 +551,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
         const int32_t ep = arev[a];
         const float4 p4 = P[ep];
         const float ph[4] = {p4.x, p4.y, p4.z, p4.w};
-        float4 sbs = sbar[ep], sbd = sbar[a];
-        const float sbsv[4] = {sbs.x, sbs.y, sbs.z, sbs.w}, sbdv[4] = {sbd.x, sbd.y, sbd.z, sbd.w};
 #pragma unroll
-        for (int hh = 0; hh < 4; hh++) {
-          sAl[wv][lane][hh] = u * ph[hh];
-          sSs[wv][TRANS ? lane : 0][hh] = sbsv[hh];
-          sSd[wv][TRANS ? lane : 0][hh] = sbdv[hh];
-        }
+        for (int hh = 0; hh < 4; hh++) sAl[wv][lane][hh] = u * ph[hh];
         (void)sv;
       }
       const float ir = 1.0f / geo.w;
@@ -651,13 +639,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
       fetch(E + 2, xa, ala, ea);
       mma(xb, alb, eb);
     }
-    if (TRANS && lane < C) {
-      for (int e = 0; e < cnt; e++) {
-        const int32_t y = sJ[wv][e];
-        kacc += sSs[wv][TRANS ? e : 0][hc] * qk[(int64_t)y * 2 * C + lane];
-        qacc += sSd[wv][TRANS ? e : 0][hc] * qk[(int64_t)y * 2 * C + C + lane];
-      }
-    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
@@ -707,10 +688,95 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
       *reinterpret_cast<float4*>(out + off) = v;
     }
   }
-  if (TRANS && lane < C) {
+}
+
+// ---------------------------------------------------------------------------------------
+// Adjoints of the attention projections, one wave per row x:
+//   qbar_x[c] = sum_a sbar_a,h(c) k_y[c] / sqrt(d)        (x as destination of a = (x <- y)),
+//   kbar_x[c] = sum_a sbar_rev(a),h(c) q_y[c] / sqrt(d)   (x as source of rev(a) = (y <- x)).
+// The row's per-edge data (neighbour, both logit adjoints) is staged in LDS 128 edges at a
+// time (two loads per lane; one stage covers most rows). Lane = (edge slot q of 64/(C/4),
+// channel quad m): each 16-byte load covers 4 channels, so one wave request brings whole q|k
+// rows of several neighbours. Eight groups of edges are requested before any is used; past
+// the row's end a slot repeats the last edge with weight 0. The slots' partial sums are added
+// at the end.
+// ---------------------------------------------------------------------------------------
+template <int C, int H>
+__global__ void __launch_bounds__(256) k_qk_bar(int32_t n, const int32_t* __restrict__ arow,
+                                                const int32_t* __restrict__ asrc,
+                                                const int32_t* __restrict__ arev,
+                                                const float4* __restrict__ sbar,
+                                                const float* __restrict__ qk,
+                                                float* __restrict__ qkbar) {
+  constexpr int dh = C / H;
+  constexpr int CQ = C / 4;     // channel quads
+  constexpr int EPG = 64 / CQ;  // edges per group (one per slot)
+  constexpr int kG = 8;         // groups requested together
+  static_assert(dh % 4 == 0, "a channel quad must lie in one head");
+  __shared__ int32_t sY[4][128];
+  __shared__ float4 sS[4][128];
+  __shared__ float4 sD[4][128];
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int q = lane / CQ, m = lane % CQ;
+  const int32_t x = xcd_block(blockIdx.x, gridDim.x) * 4 + wv;
+  if (x >= n) return;
+  const int hl = (4 * m) / dh;
+  float4 qacc = make_float4(0.0f, 0.0f, 0.0f, 0.0f), kacc = qacc;
+  const int32_t a0 = arow[x], a1 = arow[x + 1];
+  for (int32_t b = a0; b < a1; b += 128) {
+    const int cnt = min(128, a1 - b);
+#pragma unroll
+    for (int h2 = 0; h2 < 2; h2++) {
+      const int l2 = lane + 64 * h2;
+      if (l2 < cnt) {
+        const int32_t e = b + l2;
+        sY[wv][l2] = asrc[e];
+        sS[wv][l2] = sbar[arev[e]];
+        sD[wv][l2] = sbar[e];
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    for (int u = 0; u < cnt; u += kG * EPG) {
+      float4 qv[kG], kv[kG];
+#pragma unroll
+      for (int g = 0; g < kG; g++) {
+        const int e = min(u + g * EPG + q, cnt - 1);
+        const float* row = qk + (int64_t)sY[wv][e] * 2 * C + 4 * m;
+        qv[g] = *reinterpret_cast<const float4*>(row);
+        kv[g] = *reinterpret_cast<const float4*>(row + C);
+      }
+#pragma unroll
+      for (int g = 0; g < kG; g++) {
+        const bool ok = u + g * EPG + q < cnt;
+        const int e = min(u + g * EPG + q, cnt - 1);
+        const float ss = ok ? reinterpret_cast<const float*>(&sS[wv][e])[hl] : 0.0f;
+        const float sd = ok ? reinterpret_cast<const float*>(&sD[wv][e])[hl] : 0.0f;
+        kacc.x += ss * qv[g].x; kacc.y += ss * qv[g].y;
+        kacc.z += ss * qv[g].z; kacc.w += ss * qv[g].w;
+        qacc.x += sd * kv[g].x; qacc.y += sd * kv[g].y;
+        qacc.z += sd * kv[g].z; qacc.w += sd * kv[g].w;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  }
+#pragma unroll
+  for (int o = CQ; o < 64; o <<= 1) {
+    qacc.x += __shfl_xor(qacc.x, o, 64); qacc.y += __shfl_xor(qacc.y, o, 64);
+    qacc.z += __shfl_xor(qacc.z, o, 64); qacc.w += __shfl_xor(qacc.w, o, 64);
+    kacc.x += __shfl_xor(kacc.x, o, 64); kacc.y += __shfl_xor(kacc.y, o, 64);
+    kacc.z += __shfl_xor(kacc.z, o, 64); kacc.w += __shfl_xor(kacc.w, o, 64);
+  }
+  if (lane < CQ) {
     const float isd = rsqrtf((float)dh);
-    qkbar[(int64_t)x * 2 * C + lane] = qacc * isd;
-    qkbar[(int64_t)x * 2 * C + C + lane] = kacc * isd;
+    float* out = qkbar + (int64_t)x * 2 * C + 4 * m;
+    *reinterpret_cast<float4*>(out) =
+        make_float4(qacc.x * isd, qacc.y * isd, qacc.z * isd, qacc.w * isd);
+    *reinterpret_cast<float4*>(out + C) =
+        make_float4(kacc.x * isd, kacc.y * isd, kacc.z * isd, kacc.w * isd);
   }
 }
 
@@ -1224,13 +1290,11 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     if (t == 0)
       TESS_TIMED("edge_apply", st,
                  k_edge_contract<LMAX, C, H, true, false><<<gridn(n, 4), 256, 0, st>>>(
-                     n, w.arow, w.ageo, w.asrc, w.arev, ew, es, ht, rc, mt, nullptr, Pt, nullptr,
-                     nullptr, nullptr));
+                     n, w.arow, w.ageo, w.asrc, w.arev, ew, es, ht, rc, mt, nullptr, Pt));
     else
       TESS_TIMED("edge_apply", st,
                  k_edge_contract<LMAX, C, H, false, false><<<gridn(n, 4), 256, 0, st>>>(
-                     n, w.arow, w.ageo, w.asrc, w.arev, ew, es, ht, rc, mt, nullptr, Pt, nullptr,
-                     nullptr, nullptr));
+                     n, w.arow, w.ageo, w.asrc, w.arev, ew, es, ht, rc, mt, nullptr, Pt));
     TESS_HIP_CHECK(hipGetLastError());
     Epi eu{};
     eu.y = yg;
@@ -1308,8 +1372,9 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     if (t > 0) {
       TESS_TIMED("edge_tapply", st,
                  k_edge_contract<LMAX, C, H, false, true><<<gridn(n, 4), 256, 0, st>>>(
-                     n, w.arow, w.ageo, w.asrc, w.arev, ew, es, w.mbar, rc, hbar, gbar,
-                     Pt, w.sbar, qk, w.qkbar));
+                     n, w.arow, w.ageo, w.asrc, w.arev, ew, es, w.mbar, rc, hbar, gbar, Pt));
+      k_qk_bar<C, H><<<gridn(n, 4), 256, 0, st>>>(n, w.arow, w.asrc, w.arev, w.sbar, qk,
+                                                 w.qkbar);
       Epi ea{};
       ea.y = hbar;
       ea.ym = feat0;
