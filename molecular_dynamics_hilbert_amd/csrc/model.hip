@@ -347,17 +347,19 @@ struct RadialOut {
   float b[8], db[8];
 };
 __device__ __forceinline__ void radial8(float r, float rc, RadialOut& o) {
-  float th = kPi * r / rc;
+  // 1/rc and sqrt(2/rc) are the same for every lane; 1/r uses the hardware reciprocal
+  const float wk = kPi / rc;
+  const float th = wk * r;
   float s1, c1;
   __sincosf(th, &s1, &c1);
   o.u = 0.5f * (c1 + 1.0f);
-  o.du = -0.5f * (kPi / rc) * s1;
+  o.du = -0.5f * wk * s1;
   const float pref = sqrtf(2.0f / rc);
-  const float ir = 1.0f / r;
+  const float ir = __builtin_amdgcn_rcpf(r);
   float sk = s1, ck = c1;
 #pragma unroll
   for (int k = 0; k < 8; k++) {
-    float a = (k + 1) * kPi / rc;
+    const float a = (float)(k + 1) * wk;
     float B = pref * sk * ir;
     float dB = pref * (a * ck * ir - sk * ir * ir);
     o.b[k] = o.u * B;
@@ -370,7 +372,16 @@ __device__ __forceinline__ void radial8(float r, float rc, RadialOut& o) {
 }
 
 // Per active edge and layer: radial weights w_p = W2 SiLU(W1 b), their r-derivative, and the
-// per-head logits s_h = <q_i^h, k_j^h>/sqrt(d).
+// per-head logits s_h = <q_i^h, k_j^h>/sqrt(d). Lane = edge (64 consecutive active edges per
+// wave). Both layers of the radial MLP run on 4x4x1 MFMA blocks (block b = lanes 4b..4b+3,
+// D_b[r][j] += A[r] B[j] with A from lane 4b+r and B from lane 4b+j): A is a weight picked by
+// lane & 3 (4 hidden units, resp. 4 paths, per block) and B is the lane's own edge value, so
+// lane 4b+j ends with its own edge's 4 hidden pre-activations (resp. 4 path weights) in its
+// 4 accumulator registers. The activation, the Bessel basis and the logits stay on the VALU,
+// one edge per lane. Scheduling barriers keep each group's MFMAs together: on this chip
+// MFMAs interleaved one by one with independent VALU work of the same wave issue slower than
+// the two run back to back. Weights are staged in LDS in their row-major order (W2 padded with zero
+// rows to a multiple of 4 paths, so the 12th slot of each edge's weight row is written as 0).
 template <int LMAX, int C, int H, int R>
 __global__ void __launch_bounds__(256) k_edge_prep(const int32_t* __restrict__ arow_n,
                                                    const float4* __restrict__ ageo,
@@ -382,40 +393,77 @@ __global__ void __launch_bounds__(256) k_edge_prep(const int32_t* __restrict__ a
                                                    float* __restrict__ ew, float* __restrict__ edw,
                                                    float4* __restrict__ es, int64_t cap) {
   constexpr int P = Dims<LMAX>::P;
+  constexpr int PG = (P + 3) / 4;  // groups of 4 paths
+  constexpr int RG = R / 4;        // groups of 4 hidden units
   constexpr int dh = C / H;
+  static_assert(R % 4 == 0 && 4 * PG <= 12, "radial MLP shape");
+  __shared__ float4 sW1[RG][4][2];   // W1[4 rg + i][0..7]
+  __shared__ float4 sW2[PG][4][RG];  // W2[4 pg + i][4 rg .. 4 rg + 3]
   // only the first ceil(n_active/256) blocks work; spread them evenly over the XCDs
   const uint32_t nb_act = (uint32_t)((*arow_n + blockDim.x - 1) / blockDim.x);
   if (blockIdx.x >= nb_act) return;
-  int64_t a = (int64_t)xcd_block(blockIdx.x, nb_act) * blockDim.x + threadIdx.x;
-  if (a >= cap || a >= *arow_n) return;
-  float4 g = ageo[a];
+  for (int t = threadIdx.x; t < R * 8; t += 256) reinterpret_cast<float*>(sW1)[t] = W1[t];
+  for (int t = threadIdx.x; t < 4 * PG * R; t += 256)
+    reinterpret_cast<float*>(sW2)[t] = t < P * R ? W2[t] : 0.0f;
+  __syncthreads();
+  const int64_t a = (int64_t)xcd_block(blockIdx.x, nb_act) * blockDim.x + threadIdx.x;
+  // every lane takes part in the MFMAs; lanes past the last edge work on edge 0, store nothing
+  const bool valid = a < cap && a < *arow_n;
+  const int64_t ac = valid ? a : 0;
+  const int ii = threadIdx.x & 3;
+  const float4 g = ageo[ac];
   RadialOut ro;
   radial8(g.w, rc, ro);
-  float w[P], dw[P];
+  floatx4 wacc[PG], dwacc[PG];
 #pragma unroll
-  for (int p = 0; p < P; p++) { w[p] = 0.0f; dw[p] = 0.0f; }
-  for (int r = 0; r < R; r++) {
-    float z = 0.0f, zp = 0.0f;
+  for (int pg = 0; pg < PG; pg++) {
+    wacc[pg] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    dwacc[pg] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+#pragma unroll 2
+  for (int rg = 0; rg < RG; rg++) {
+    const float4 wa = sW1[rg][ii][0], wb = sW1[rg][ii][1];
+    const float w1[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+    floatx4 z = floatx4{0.0f, 0.0f, 0.0f, 0.0f}, zp = z;
+    float4 w2q[PG];
+#pragma unroll
+    for (int pg = 0; pg < PG; pg++) w2q[pg] = sW2[pg][ii][rg];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < 8; k++) {
-      float wk = W1[r * 8 + k];
-      z += wk * ro.b[k];
-      zp += wk * ro.db[k];
+      z = __builtin_amdgcn_mfma_f32_4x4x1f32(w1[k], ro.b[k], z, 0, 0, 0);
+      zp = __builtin_amdgcn_mfma_f32_4x4x1f32(w1[k], ro.db[k], zp, 0, 0, 0);
     }
-    float sg = sigmoidf_(z);
-    float act = z * sg;
-    float dact = sg * (1.0f + z * (1.0f - sg)) * zp;
+    __builtin_amdgcn_sched_barrier(0);
+    // z[r] = pre-activation of hidden unit 4 rg + r for this lane's edge
+    float act[4], dact[4];
 #pragma unroll
-    for (int p = 0; p < P; p++) {
-      float w2 = W2[p * R + r];
-      w[p] += w2 * act;
-      dw[p] += w2 * dact;
+    for (int r = 0; r < 4; r++) {
+      const float sg = sigmoidf_(z[r]);
+      act[r] = z[r] * sg;
+      dact[r] = sg * (1.0f + z[r] * (1.0f - sg)) * zp[r];
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int pg = 0; pg < PG; pg++) {
+      const float4 w2 = w2q[pg];
+      const float w2v[4] = {w2.x, w2.y, w2.z, w2.w};
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        wacc[pg] = __builtin_amdgcn_mfma_f32_4x4x1f32(w2v[r], act[r], wacc[pg], 0, 0, 0);
+        dwacc[pg] = __builtin_amdgcn_mfma_f32_4x4x1f32(w2v[r], dact[r], dwacc[pg], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
+  if (!valid) return;
+  // wacc[pg][r] = w_(4 pg + r) of this lane's edge
 #pragma unroll
-  for (int p = 0; p < P; p++) {
-    ew[a * 12 + p] = w[p];
-    edw[a * 12 + p] = dw[p];
+  for (int pg = 0; pg < PG; pg++) {
+    *reinterpret_cast<float4*>(ew + a * 12 + 4 * pg) =
+        make_float4(wacc[pg][0], wacc[pg][1], wacc[pg][2], wacc[pg][3]);
+    *reinterpret_cast<float4*>(edw + a * 12 + 4 * pg) =
+        make_float4(dwacc[pg][0], dwacc[pg][1], dwacc[pg][2], dwacc[pg][3]);
   }
   const float4* qi = reinterpret_cast<const float4*>(qk + (int64_t)adst[a] * 2 * C);
   const float4* kj = reinterpret_cast<const float4*>(qk + (int64_t)asrc[a] * 2 * C + C);
