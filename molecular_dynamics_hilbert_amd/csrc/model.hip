@@ -486,7 +486,7 @@ __global__ void __launch_bounds__(256) k_edge_prep(const int32_t* __restrict__ a
 //   adjoint (TRANS = true), row = x, edges a = (x <- y) with forward edge e' = rev(a) = (y <- x):
 //     hbar_x[d1][c] += alpha_e',h(c) sum_d3 A_e'[d3][d1] mbar_y[d3][c]   (A_e' uses Y(-n_a)).
 //
-// Chunks of 32 (adjoint: 24) edges: lanes first build alpha and A_e (lane = edge) into
+// Chunks of 32 (adjoint: 28) edges: lanes first build alpha and A_e (lane = edge) into
 // LDS. The channel sums then run on 4x4x1 MFMA blocks (v_mfma_f32_4x4x1f32: 16 independent
 // 4x4 outer products per instruction; block b takes its A column from lanes 4b..4b+3 and
 // its B row from the same lanes, and lane 4b+j ends with D_b[r][j] in register r). Lane =
@@ -514,7 +514,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
   constexpr int dh = C / H;
   static_assert(C % 16 == 0 && C <= 64 && dh % 4 == 0, "unsupported channel/head split");
   // edges per chunk (the adjoint keeps less in registers and runs 4 waves per SIMD)
-  constexpr int kChunk = TRANS ? 24 : 32;
+  constexpr int kChunk = TRANS ? 28 : 32;
   __shared__ float sA[4][kChunk][D * DI];
   __shared__ float sAl[4][kChunk][4];
   __shared__ int32_t sJ[4][kChunk];
