@@ -238,13 +238,17 @@ __global__ void k_prep_weights(const float* __restrict__ weights, int S, int K,
 
 // h^0: the species embedding in the l = 0 component. The l >= 1 components of h^0 are zero
 // and never read (layer 0 contracts only l = 0 inputs and its gated update starts from zero).
-__global__ void k_embed(int32_t n, int C, int D, const int32_t* __restrict__ species,
+// Species index clamped to [0, S): an index out of range gives wrong values, never an access
+// outside the weights.
+__device__ __forceinline__ int sp_index(int32_t s, int S) { return min(max(s, 0), S - 1); }
+
+__global__ void k_embed(int32_t n, int C, int D, int S, const int32_t* __restrict__ species,
                         const float* __restrict__ emb, float* __restrict__ h) {
   int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (k >= (int64_t)n * C) return;
   int64_t i = k / C;
   int c = (int)(k - i * C);
-  h[i * D * C + c] = emb[species[i] * C + c];
+  h[i * D * C + c] = emb[sp_index(species[i], S) * C + c];
 }
 
 // ---------------------------------------------------------------------------------------
@@ -371,6 +375,37 @@ __device__ __forceinline__ void radial8(float r, float rc, RadialOut& o) {
   }
 }
 
+// First layer: the input features are the species embedding, so q = W_q e_s and k = W_k e_s
+// take one value per species and the logits one value per (destination species, source
+// species) pair: tab[s_i S + s_j].h = <q_(s_i)^h, k_(s_j)^h>/sqrt(d) (heads past H are 0).
+// One block.
+template <int C, int H>
+__global__ void __launch_bounds__(256) k_l0_logits(int S, const float* __restrict__ emb,
+                                                   const float* __restrict__ Wq,
+                                                   const float* __restrict__ Wk,
+                                                   float4* __restrict__ tab) {
+  constexpr int dh = C / H;
+  __shared__ float sq[16][C], sk[16][C];
+  for (int t = threadIdx.x; t < S * C; t += blockDim.x) {
+    const int sp = t / C, c = t % C;
+    float q = 0.0f, k = 0.0f;
+    for (int c2 = 0; c2 < C; c2++) {
+      q += Wq[c * C + c2] * emb[sp * C + c2];
+      k += Wk[c * C + c2] * emb[sp * C + c2];
+    }
+    sq[sp][c] = q;
+    sk[sp][c] = k;
+  }
+  __syncthreads();
+  const float isd = rsqrtf((float)dh);
+  for (int t = threadIdx.x; t < S * S; t += blockDim.x) {
+    const int si = t / S, sj = t % S;
+    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int c = 0; c < C; c++) v[c / dh] += sq[si][c] * sk[sj][c];
+    tab[t] = make_float4(v[0] * isd, v[1] * isd, v[2] * isd, v[3] * isd);
+  }
+}
+
 // Per active edge and layer: radial weights w_p = W2 SiLU(W1 b), their r-derivative, and the
 // per-head logits s_h = <q_i^h, k_j^h>/sqrt(d). Lane = edge (64 consecutive active edges per
 // wave). Both layers of the radial MLP run on 4x4x1 MFMA blocks (block b = lanes 4b..4b+3,
@@ -380,9 +415,9 @@ __device__ __forceinline__ void radial8(float r, float rc, RadialOut& o) {
 // 4 accumulator registers. The activation, the Bessel basis and the logits stay on the VALU,
 // one edge per lane. Scheduling barriers keep each group's MFMAs together: on this chip
 // MFMAs interleaved one by one with independent VALU work of the same wave issue slower than
-// the two run back to back. Weights are staged in LDS in their row-major order (W2 padded with zero
-// rows to a multiple of 4 paths, so the 12th slot of each edge's weight row is written as 0).
-template <int LMAX, int C, int H, int R>
+// the two run back to back. Weights are staged in LDS (W2 padded with zero rows to a multiple
+// of 4 paths, so the 12th slot of each edge's weight row is written as 0).
+template <int LMAX, int C, int H, int R, bool L0>
 __global__ void __launch_bounds__(256) k_edge_prep(const int32_t* __restrict__ arow_n,
                                                    const float4* __restrict__ ageo,
                                                    const int32_t* __restrict__ adst,
@@ -391,20 +426,26 @@ __global__ void __launch_bounds__(256) k_edge_prep(const int32_t* __restrict__ a
                                                    const float* __restrict__ W2,
                                                    const float* __restrict__ qk, float rc,
                                                    float* __restrict__ ew, float* __restrict__ edw,
-                                                   float4* __restrict__ es, int64_t cap) {
+                                                   float4* __restrict__ es, int64_t cap,
+                                                   const int32_t* __restrict__ species,
+                                                   const float4* __restrict__ l0tab, int S) {
   constexpr int P = Dims<LMAX>::P;
   constexpr int PG = (P + 3) / 4;  // groups of 4 paths
   constexpr int RG = R / 4;        // groups of 4 hidden units
   constexpr int dh = C / H;
   static_assert(R % 4 == 0 && 4 * PG <= 12, "radial MLP shape");
   __shared__ float4 sW1[RG][4][2];   // W1[4 rg + i][0..7]
-  __shared__ float4 sW2[PG][4][RG];  // W2[4 pg + i][4 rg .. 4 rg + 3]
+  __shared__ float4 sW2[PG][RG][4];  // W2[4 pg + i][4 rg .. 4 rg + 3] at [pg][rg][i]
   // only the first ceil(n_active/256) blocks work; spread them evenly over the XCDs
   const uint32_t nb_act = (uint32_t)((*arow_n + blockDim.x - 1) / blockDim.x);
   if (blockIdx.x >= nb_act) return;
   for (int t = threadIdx.x; t < R * 8; t += 256) reinterpret_cast<float*>(sW1)[t] = W1[t];
-  for (int t = threadIdx.x; t < 4 * PG * R; t += 256)
-    reinterpret_cast<float*>(sW2)[t] = t < P * R ? W2[t] : 0.0f;
+  // the four paths a block's lanes read together are 16 bytes apart (distinct LDS banks)
+  for (int t = threadIdx.x; t < 4 * PG * R; t += 256) {
+    const int p = t / R, h = t % R;
+    reinterpret_cast<float*>(sW2)[(((p >> 2) * RG + (h >> 2)) * 4 + (p & 3)) * 4 + (h & 3)] =
+        t < P * R ? W2[t] : 0.0f;
+  }
   __syncthreads();
   const int64_t a = (int64_t)xcd_block(blockIdx.x, nb_act) * blockDim.x + threadIdx.x;
   // every lane takes part in the MFMAs; lanes past the last edge work on edge 0, store nothing
@@ -427,7 +468,7 @@ __global__ void __launch_bounds__(256) k_edge_prep(const int32_t* __restrict__ a
     floatx4 z = floatx4{0.0f, 0.0f, 0.0f, 0.0f}, zp = z;
     float4 w2q[PG];
 #pragma unroll
-    for (int pg = 0; pg < PG; pg++) w2q[pg] = sW2[pg][ii][rg];
+    for (int pg = 0; pg < PG; pg++) w2q[pg] = sW2[pg][rg][ii];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < 8; k++) {
@@ -464,6 +505,11 @@ __global__ void __launch_bounds__(256) k_edge_prep(const int32_t* __restrict__ a
         make_float4(wacc[pg][0], wacc[pg][1], wacc[pg][2], wacc[pg][3]);
     *reinterpret_cast<float4*>(edw + a * 12 + 4 * pg) =
         make_float4(dwacc[pg][0], dwacc[pg][1], dwacc[pg][2], dwacc[pg][3]);
+  }
+  if constexpr (L0) {
+    // first layer: q and k depend on the species only, the logits come from their table
+    es[a] = l0tab[sp_index(species[adst[a]], S) * S + sp_index(species[asrc[a]], S)];
+    return;
   }
   const float4* qi = reinterpret_cast<const float4*>(qk + (int64_t)adst[a] * 2 * C);
   const float4* kj = reinterpret_cast<const float4*>(qk + (int64_t)asrc[a] * 2 * C + C);
@@ -959,18 +1005,59 @@ __device__ __forceinline__ float quad_sum(float v) {
   return v;
 }
 
+// Coupling adjoint of the rows d1 = L1^2 + S0 .. + NR - 1 of one head's Abar (Ab[d3 NR + m]):
+//   t^p[m2] = sum_{m1 in rows, m3} C^p[m1][m2][m3] Abar[(l3,m3)][m1],  wbar^p = t^p . Y_l2;
+//   abar += w_p wbar^p;  wb[p] += alpha wbar^p;  Yb[l2^2+m2] += alpha w_p t^p[m2].
+// Used by the first layer's edge gradient. grad_rows below carries the same loop inline:
+// calling this function from it made the compiler spill the full-layer kernel's registers.
+template <int LMAX, int L1, int S0, int NR, int NA>
+__device__ __forceinline__ void grad_adjoint(const float (&Ab)[NA], const float* w,
+                                             const float* Y, float al, float& abar, float* wb,
+                                             float* Yb) {
+  constexpr const CGTable& T = cg_table<LMAX>();
+#pragma unroll
+  for (int p = 0; p < Dims<LMAX>::P; p++) {
+    if (T.l1[p] != L1) continue;
+    const float alw = al * w[p];
+    float wbh = 0.0f;
+    bool touched = false;
+#pragma unroll
+    for (int m2 = 0; m2 < 5; m2++) {
+      if (m2 >= 2 * T.l2[p] + 1) continue;
+      float tpm = 0.0f;
+      bool any = false;
+#pragma unroll
+      for (int m = 0; m < NR; m++)
+#pragma unroll
+        for (int m3 = 0; m3 < 5; m3++) {
+          if (m3 < 2 * T.l3[p] + 1 && T.v[p][S0 + m][m2][m3] != 0.0) {
+            tpm += (float)T.v[p][S0 + m][m2][m3] * Ab[(T.l3[p] * T.l3[p] + m3) * NR + m];
+            any = true;
+          }
+        }
+      if (any) {
+        wbh += tpm * Y[T.l2[p] * T.l2[p] + m2];
+        Yb[T.l2[p] * T.l2[p] + m2] += alw * tpm;
+        touched = true;
+      }
+    }
+    if (touched) {
+      abar += w[p] * wbh;
+      wb[p] += al * wbh;
+    }
+  }
+}
+
 // Rows d1 = L1^2 + S0 .. L1^2 + S0 + NR - 1 (sender degree L1) of one head's gradient:
 // Abar[d3][m1] = sum_{c in head} mbar_i[d3][c] h_j[d1][c] for every output component d3 (all of
 // a row's head channels loaded at once), then the part of the coupling adjoint that these
-// columns feed (the adjoint is a sum over (d3, d1) entries, so it splits by column):
-//   t^p[m2] = sum_{m1 in rows, m3} C^p[m1][m2][m3] Abar[(l3,m3)][m1],  wbar^p = t^p . Y_l2;
-//   abar += w_p wbar^p;  wb[p] += alpha wbar^p;  Yb[l2^2+m2] += alpha w_p t^p[m2].
+// columns feed (the adjoint is a sum over (d3, d1) entries, so it splits by column; the same
+// sums as grad_adjoint).
 template <int LMAX, int C, int DH, int L1, int S0, int NR, class MRow>
 __device__ __forceinline__ void grad_rows(MRow mrow, const float* __restrict__ h_j, int c0,
                                           const float* w, const float* Y, float al,
                                           float& abar, float* wb, float* Yb) {
   constexpr int D = Dims<LMAX>::D, B0 = L1 * L1 + S0, NC = DH / 4;
-  constexpr const CGTable& T = cg_table<LMAX>();
   float4 hv[NR][NC];
 #pragma unroll
   for (int m = 0; m < NR; m++)
@@ -1003,6 +1090,7 @@ __device__ __forceinline__ void grad_rows(MRow mrow, const float* __restrict__ h
 #pragma unroll
     for (int t = 0; t < NC; t++) mv[t] = mn[t];
   }
+  constexpr const CGTable& T = cg_table<LMAX>();
 #pragma unroll
   for (int p = 0; p < Dims<LMAX>::P; p++) {
     if (T.l1[p] != L1) continue;
@@ -1064,7 +1152,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
                                                    const float* __restrict__ h, float rc,
                                                    float4* __restrict__ sbar,
                                                    float* __restrict__ gacc, bool accumulate,
-                                                   int64_t cap) {
+                                                   int64_t cap, const int32_t* __restrict__ species,
+                                                   const float* __restrict__ emb, int S) {
   static_assert(H == 1 || H == 4, "one lane or a quad of lanes per edge");
   constexpr int D = Dims<LMAX>::D;
   constexpr int P = Dims<LMAX>::P;
@@ -1072,6 +1161,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
   constexpr int EPW = 256 / H;               // edges per pass of the block's threads
   constexpr int EPB = kGradPasses * EPW;     // edges per block
   __shared__ float4 smb[kGradRows * D * C / 4];
+  // first layer: h_j = (e_(s_j), 0, ..., 0) depends on the species only, so
+  // Abar^h[d3][0] = sum_{c in h} mbar_i[d3][c] e_s[c] is tabulated per staged row and species
+  __shared__ float sU[L0ONLY ? kGradRows * 16 * H * D : 1];
   const int64_t n_act = *arow_n;
   const uint32_t nb_act = (uint32_t)((n_act + EPB - 1) / EPB);
   if (blockIdx.x >= nb_act) return;  // whole block idle
@@ -1090,6 +1182,21 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
       for (int k = threadIdx.x; k < nst * D * C / 4; k += blockDim.x) smb[k] = src[k];
     }
     __syncthreads();
+    if constexpr (L0ONLY) {
+      // same channel order as the per-edge sum of the other layers
+      const float* mf = reinterpret_cast<const float*>(smb);
+      for (int k = threadIdx.x; k < nst * S * H * D; k += blockDim.x) {
+        const int r = k / (S * H * D), rem = k % (S * H * D);
+        const int sp = rem / (H * D), hq = (rem / D) % H, d3 = rem % D;
+        const float* mr = mf + (r * D + d3) * C + hq * dh;
+        const float* er = emb + sp * C + hq * dh;
+        float acc = 0.0f;
+#pragma unroll
+        for (int c = 0; c < dh; c++) acc = __builtin_fmaf(mr[c], er[c], acc);
+        sU[k] = acc;
+      }
+      __syncthreads();
+    }
 #pragma unroll 1
   for (int ps = 0; ps < kGradPasses; ps++) {
     const int64_t a = a_base + ps * EPW + threadIdx.x / H;
@@ -1097,6 +1204,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
     const int ri = active ? adst[a] - i_first : -1;
     if (ri < b0 || ri >= b0 + nst) continue;
     const int32_t i = i_first + ri, j = asrc[a];
+    const int sj = L0ONLY ? sp_index(species[j], S) : 0;
     float4 g = ageo[a];
     const float r = g.w, ir = 1.0f / r;
     const float nx = g.x * ir, ny = g.y * ir, nz = g.z * ir;
@@ -1120,8 +1228,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
     const float al = u * p_h;
     float abar = 0.0f;
     const int c0 = hh * dh;
-    grad_block<LMAX, C, dh, 0>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
-    if constexpr (!L0ONLY) {
+    if constexpr (L0ONLY) {
+      const float* u0 = sU + (((ri - b0) * S + sj) * H + hh) * D;
+      float Ab[D];
+#pragma unroll
+      for (int d3 = 0; d3 < D; d3++) Ab[d3] = u0[d3];
+      grad_adjoint<LMAX, 0, 0, 1>(Ab, w, Y, al, abar, wb, Yb);
+      (void)h_j;
+      (void)mrow;
+    } else {
+      grad_block<LMAX, C, dh, 0>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
       grad_block<LMAX, C, dh, 1>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
       if constexpr (LMAX >= 2) grad_block<LMAX, C, dh, 2>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
     }
@@ -1200,6 +1316,7 @@ struct EFWS {
   float4* P;  // per layer and active edge: softmax probability of each head
   float *gbar, *hbar, *mbar, *xcat, *ybl, *qkbar, *Dst, *gacc;
   float4* sbar;
+  float4* l0tab;  // first layer: logits of every (destination species, source species) pair
   double* epart;
   int32_t* scan_tmp;
 };
@@ -1238,6 +1355,7 @@ static EFWS carve_ef(Carver& cv, const tess_model_desc& md, int32_t n, int64_t c
   w.Dst = cv.take<float>(nn * H);
   w.gacc = cv.take<float>(ec * 3);
   w.sbar = cv.take<float4>(ec);
+  w.l0tab = cv.take<float4>(16 * 16);
   w.epart = cv.take<double>(nn / 256 + 2);
   w.scan_tmp = cv.take<int32_t>(nn / 4096 + 4);
   return w;
@@ -1292,7 +1410,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
   TESS_HIP_CHECK(hipGetLastError());
   const int64_t NDC = (int64_t)n * D * C;
   // embedding
-  k_embed<<<gridn((int64_t)n * C, 256), 256, 0, st>>>(n, C, D, species, emb, w.h);
+  k_embed<<<gridn((int64_t)n * C, 256), 256, 0, st>>>(n, C, D, S, species, emb, w.h);
   // active edges
   const int32_t* rev = rev_in;
   if (cap > 0) {
@@ -1329,12 +1447,24 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     Epi e0{};
     e0.y = qk;
     e0.ym = RowMap{2 * C, 0, 0, 1};
-    TESS_HIP_CHECK(gemm<EPI_STORE>(st, n, C, 2 * C, ht, feat0, w.WqkT + (int64_t)t * C * 2 * C, e0));
-    if (cap > 0)
-      TESS_TIMED("edge_prep", st,
-                 k_edge_prep<LMAX, C, H, R><<<gridn(cap, 256), 256, 0, st>>>(
-                     w.arow + n, w.ageo, w.adst, w.asrc, lw[t].W1, lw[t].W2, qk, rc, ew, edw, es,
-                     cap));
+    if (t == 0) {
+      // first layer: logits from the per-species table (q and k of the first layer are not
+      // needed anywhere else: the backward stops before dE/dh^0)
+      k_l0_logits<C, H><<<1, 256, 0, st>>>(S, emb, lw[0].Wq, lw[0].Wk, w.l0tab);
+      if (cap > 0)
+        TESS_TIMED("edge_prep", st,
+                   k_edge_prep<LMAX, C, H, R, true><<<gridn(cap, 256), 256, 0, st>>>(
+                       w.arow + n, w.ageo, w.adst, w.asrc, lw[t].W1, lw[t].W2, qk, rc, ew, edw,
+                       es, cap, species, w.l0tab, S));
+    } else {
+      TESS_HIP_CHECK(
+          gemm<EPI_STORE>(st, n, C, 2 * C, ht, feat0, w.WqkT + (int64_t)t * C * 2 * C, e0));
+      if (cap > 0)
+        TESS_TIMED("edge_prep", st,
+                   k_edge_prep<LMAX, C, H, R, false><<<gridn(cap, 256), 256, 0, st>>>(
+                       w.arow + n, w.ageo, w.adst, w.asrc, lw[t].W1, lw[t].W2, qk, rc, ew, edw,
+                       es, cap, species, w.l0tab, S));
+    }
     if (t == 0)
       TESS_TIMED("edge_apply", st,
                  k_edge_contract<LMAX, C, H, true, false><<<gridn(n, 4), 256, 0, st>>>(
@@ -1409,12 +1539,12 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
         TESS_TIMED("edge_grad", st,
                    k_edge_grad<LMAX, C, H, true><<<gb, 256, 0, st>>>(
                        w.arow + n, w.ageo, w.adst, w.asrc, ew, edw, Pt, w.Dst, w.mbar, ht, rc,
-                       w.sbar, w.gacc, t != T - 1, cap));
+                       w.sbar, w.gacc, t != T - 1, cap, species, emb, S));
       else
         TESS_TIMED("edge_grad", st,
                    k_edge_grad<LMAX, C, H, false><<<gb, 256, 0, st>>>(
                        w.arow + n, w.ageo, w.adst, w.asrc, ew, edw, Pt, w.Dst, w.mbar, ht, rc,
-                       w.sbar, w.gacc, t != T - 1, cap));
+                       w.sbar, w.gacc, t != T - 1, cap, species, emb, S));
     }
     TESS_HIP_CHECK(hipGetLastError());
     if (t > 0) {
