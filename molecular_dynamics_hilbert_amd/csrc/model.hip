@@ -550,7 +550,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
     int32_t n, const int32_t* __restrict__ arow, const float4* __restrict__ ageo,
     const int32_t* __restrict__ asrc, const int32_t* __restrict__ arev,
     const float* __restrict__ ew, const float4* __restrict__ es, const float* __restrict__ X,
-    float rc, float* __restrict__ out, const float* __restrict__ base, float4* __restrict__ P) {
+    float rc, float* __restrict__ out, const float* __restrict__ base, float4* __restrict__ P,
+    const int32_t* __restrict__ species, const float* __restrict__ emb, int S) {
   constexpr int D = Dims<LMAX>::D;
   constexpr int DI = L0ONLY ? 1 : D;          // input components that can be non-zero
   constexpr int CQ = C / 4;                   // channel quads
@@ -564,8 +565,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
   __shared__ float sA[4][kChunk][D * DI];
   __shared__ float sAl[4][kChunk][4];
   __shared__ int32_t sJ[4][kChunk];
+  // first layer: the input features are the species embedding (comp 0 only), read from an
+  // LDS copy of the table by the source's species instead of gathering the source's row
+  __shared__ float4 sEmb[L0ONLY ? 16 * C / 4 : 1];
+  __shared__ int32_t sSp[4][L0ONLY ? kChunk : 1];
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int q = lane / CQ, m = lane % CQ, jj = lane & 3;
+  if constexpr (L0ONLY) {
+    for (int t = threadIdx.x; t < S * C / 4; t += blockDim.x)
+      sEmb[t] = reinterpret_cast<const float4*>(emb)[t];
+    __syncthreads();
+  }
   const int32_t x = xcd_block(blockIdx.x, gridDim.x) * 4 + wv;
   if (x >= n) return;
   const int32_t a0 = arow[x], a1 = arow[x + 1];
@@ -666,6 +676,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
 #pragma unroll
         for (int k = 0; k < DI; k++) sA[wv][lane][o * DI + k] = TRANS ? A[k * D + o] : A[o * D + k];
       sJ[wv][lane] = y;
+      if constexpr (L0ONLY) sSp[wv][TRANS ? 0 : lane] = sp_index(species[y], S);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
@@ -680,9 +691,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
       const int e = e0 < cnt ? e0 : cnt - 1;
       ao = e0 < cnt ? sAl[wv][e][hl] : 0.0f;
       eo = e;
-      const float* Xy = X + (int64_t)sJ[wv][e] * D * C + 4 * m;
+      if constexpr (L0ONLY) {
+        xo[0] = sEmb[sSp[wv][TRANS ? 0 : e] * (C / 4) + m];
+      } else {
+        const float* Xy = X + (int64_t)sJ[wv][e] * D * C + 4 * m;
 #pragma unroll
-      for (int k = 0; k < DI; k++) xo[k] = *reinterpret_cast<const float4*>(Xy + k * C);
+        for (int k = 0; k < DI; k++) xo[k] = *reinterpret_cast<const float4*>(Xy + k * C);
+      }
     };
     // alpha depends on (edge, head of the channel). When a head spans 16 channels, the four
     // rows of an MFMA block (channels 16(b%4)+4i+s) share one head, which is also the head of
@@ -1468,11 +1483,13 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     if (t == 0)
       TESS_TIMED("edge_apply", st,
                  k_edge_contract<LMAX, C, H, true, false><<<gridn(n, 4), 256, 0, st>>>(
-                     n, w.arow, w.ageo, w.asrc, w.arev, ew, es, ht, rc, mt, nullptr, Pt));
+                     n, w.arow, w.ageo, w.asrc, w.arev, ew, es, ht, rc, mt, nullptr, Pt, species,
+                     emb, S));
     else
       TESS_TIMED("edge_apply", st,
                  k_edge_contract<LMAX, C, H, false, false><<<gridn(n, 4), 256, 0, st>>>(
-                     n, w.arow, w.ageo, w.asrc, w.arev, ew, es, ht, rc, mt, nullptr, Pt));
+                     n, w.arow, w.ageo, w.asrc, w.arev, ew, es, ht, rc, mt, nullptr, Pt, species,
+                     emb, S));
     TESS_HIP_CHECK(hipGetLastError());
     Epi eu{};
     eu.y = yg;
@@ -1550,7 +1567,8 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     if (t > 0) {
       TESS_TIMED("edge_tapply", st,
                  k_edge_contract<LMAX, C, H, false, true><<<gridn(n, 4), 256, 0, st>>>(
-                     n, w.arow, w.ageo, w.asrc, w.arev, ew, es, w.mbar, rc, hbar, gbar, Pt));
+                     n, w.arow, w.ageo, w.asrc, w.arev, ew, es, w.mbar, rc, hbar, gbar, Pt, species,
+                     emb, S));
       k_qk_bar<C, H><<<gridn(n, 4), 256, 0, st>>>(n, w.arow, w.asrc, w.arev, w.sbar, qk,
                                                  w.qkbar);
       Epi ea{};
