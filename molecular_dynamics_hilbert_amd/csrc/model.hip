@@ -542,7 +542,8 @@ __global__ void __launch_bounds__(256) k_edge_prep(const int32_t* __restrict__ a
 // 4g+(lane&3) of the same edge. Blocks of different edges add into separate accumulators
 // that are summed over the group's edges once per row. Output components 0..7 use the
 // matrix cores (two groups of four), component 8 (l = 2, m = 2) is a vector FMA.
-// L0ONLY: only the l = 0 input component is non-zero (first layer).
+// L0ONLY: only the l = 0 input component is non-zero: the features of the first layer
+// (forward; they are the species embedding) or m_bar of the last layer (adjoint).
 // ---------------------------------------------------------------------------------------
 
 template <int LMAX, int C, int H, bool L0ONLY, bool TRANS>
@@ -565,13 +566,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
   __shared__ float sA[4][kChunk][D * DI];
   __shared__ float sAl[4][kChunk][4];
   __shared__ int32_t sJ[4][kChunk];
-  // first layer: the input features are the species embedding (comp 0 only), read from an
-  // LDS copy of the table by the source's species instead of gathering the source's row
-  __shared__ float4 sEmb[L0ONLY ? 16 * C / 4 : 1];
-  __shared__ int32_t sSp[4][L0ONLY ? kChunk : 1];
+  // first layer (forward): the input features are the species embedding (comp 0 only), read
+  // from an LDS copy of the table by the source's species instead of gathering the source's row
+  constexpr bool EMB = L0ONLY && !TRANS;
+  __shared__ float4 sEmb[EMB ? 16 * C / 4 : 1];
+  __shared__ int32_t sSp[4][EMB ? kChunk : 1];
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int q = lane / CQ, m = lane % CQ, jj = lane & 3;
-  if constexpr (L0ONLY) {
+  if constexpr (EMB) {
     for (int t = threadIdx.x; t < S * C / 4; t += blockDim.x)
       sEmb[t] = reinterpret_cast<const float4*>(emb)[t];
     __syncthreads();
@@ -676,7 +678,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
 #pragma unroll
         for (int k = 0; k < DI; k++) sA[wv][lane][o * DI + k] = TRANS ? A[k * D + o] : A[o * D + k];
       sJ[wv][lane] = y;
-      if constexpr (L0ONLY) sSp[wv][TRANS ? 0 : lane] = sp_index(species[y], S);
+      if constexpr (EMB) sSp[wv][lane] = sp_index(species[y], S);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
@@ -691,8 +693,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
       const int e = e0 < cnt ? e0 : cnt - 1;
       ao = e0 < cnt ? sAl[wv][e][hl] : 0.0f;
       eo = e;
-      if constexpr (L0ONLY) {
-        xo[0] = sEmb[sSp[wv][TRANS ? 0 : e] * (C / 4) + m];
+      if constexpr (EMB) {
+        xo[0] = sEmb[sSp[wv][e] * (C / 4) + m];
       } else {
         const float* Xy = X + (int64_t)sJ[wv][e] * D * C + 4 * m;
 #pragma unroll
@@ -964,11 +966,13 @@ __global__ void k_bwd_update(int32_t n, int C, const float* __restrict__ gbar,
   }
 }
 
-// D_i^h = <mbar_i^h, m_i^h> over the head's channels and all components. Wave per node.
-template <int LMAX, int C, int H>
+// D_i^h = <mbar_i^h, m_i^h> over the head's channels and all components (MB0: mbar has only
+// its l = 0 component). Wave per node.
+template <int LMAX, int C, int H, bool MB0>
 __global__ void __launch_bounds__(256) k_dst(int32_t n, const float* __restrict__ mbar,
                                              const float* __restrict__ m, float* __restrict__ Dst) {
-  constexpr int D = Dims<LMAX>::D;
+  constexpr int D = MB0 ? 1 : Dims<LMAX>::D;
+  constexpr int DS = Dims<LMAX>::D;  // row stride in components
   constexpr int dh = C / H;
   int32_t i = blockIdx.x * 4 + (threadIdx.x >> 6);
   int lane = threadIdx.x & 63;
@@ -977,7 +981,7 @@ __global__ void __launch_bounds__(256) k_dst(int32_t n, const float* __restrict_
   if (lane < C) {
 #pragma unroll
     for (int d = 0; d < D; d++)
-      v += mbar[(int64_t)i * D * C + d * C + lane] * m[(int64_t)i * D * C + d * C + lane];
+      v += mbar[(int64_t)i * DS * C + d * C + lane] * m[(int64_t)i * DS * C + d * C + lane];
   }
 #pragma unroll
   for (int o = 1; o < dh; o <<= 1) v += __shfl_xor(v, o, 64);
@@ -1068,7 +1072,7 @@ __device__ __forceinline__ void grad_adjoint(const float (&Ab)[NA], const float*
 // a row's head channels loaded at once), then the part of the coupling adjoint that these
 // columns feed (the adjoint is a sum over (d3, d1) entries, so it splits by column; the same
 // sums as grad_adjoint).
-template <int LMAX, int C, int DH, int L1, int S0, int NR, class MRow>
+template <int LMAX, int C, int DH, int L1, int S0, int NR, int D3N, class MRow>
 __device__ __forceinline__ void grad_rows(MRow mrow, const float* __restrict__ h_j, int c0,
                                           const float* w, const float* Y, float al,
                                           float& abar, float* wb, float* Yb) {
@@ -1084,8 +1088,8 @@ __device__ __forceinline__ void grad_rows(MRow mrow, const float* __restrict__ h
 #pragma unroll
   for (int t = 0; t < NC; t++) mv[t] = mrow(c0 + 4 * t);
 #pragma unroll
-  for (int d3 = 0; d3 < D; d3++) {
-    if (d3 + 1 < D) {
+  for (int d3 = 0; d3 < D3N; d3++) {
+    if (d3 + 1 < D3N) {
 #pragma unroll
       for (int t = 0; t < NC; t++) mn[t] = mrow((d3 + 1) * C + c0 + 4 * t);
     }
@@ -1121,7 +1125,8 @@ __device__ __forceinline__ void grad_rows(MRow mrow, const float* __restrict__ h
       for (int m = 0; m < NR; m++)
 #pragma unroll
         for (int m3 = 0; m3 < 5; m3++) {
-          if (m3 < 2 * T.l3[p] + 1 && T.v[p][S0 + m][m2][m3] != 0.0) {
+          if (m3 < 2 * T.l3[p] + 1 && T.l3[p] * T.l3[p] + m3 < D3N &&
+              T.v[p][S0 + m][m2][m3] != 0.0) {
             tpm += (float)T.v[p][S0 + m][m2][m3] * Ab[(T.l3[p] * T.l3[p] + m3) * NR + m];
             any = true;
           }
@@ -1139,22 +1144,23 @@ __device__ __forceinline__ void grad_rows(MRow mrow, const float* __restrict__ h
   }
 }
 
-// All rows of sender degree L1, at most 3 rows at a time.
-template <int LMAX, int C, int DH, int L1, class MRow>
+// All rows of sender degree L1, at most 3 rows at a time; output components d3 < D3N of m_bar
+// (the others are zero).
+template <int LMAX, int C, int DH, int L1, int D3N, class MRow>
 __device__ __forceinline__ void grad_block(MRow mrow, const float* __restrict__ h_j, int c0,
                                            const float* w, const float* Y, float al,
                                            float& abar, float* wb, float* Yb) {
   if constexpr (L1 == 0) {
-    grad_rows<LMAX, C, DH, 0, 0, 1>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
+    grad_rows<LMAX, C, DH, 0, 0, 1, D3N>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
   } else if constexpr (L1 == 1) {
-    grad_rows<LMAX, C, DH, 1, 0, 3>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
+    grad_rows<LMAX, C, DH, 1, 0, 3, D3N>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
   } else {
-    grad_rows<LMAX, C, DH, 2, 0, 3>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
-    grad_rows<LMAX, C, DH, 2, 3, 2>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
+    grad_rows<LMAX, C, DH, 2, 0, 3, D3N>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
+    grad_rows<LMAX, C, DH, 2, 3, 2, D3N>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
   }
 }
 
-template <int LMAX, int C, int H, bool L0ONLY>
+template <int LMAX, int C, int H, bool L0ONLY, bool MB0>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) k_edge_grad(const int32_t* __restrict__ arow_n,
                                                    const float4* __restrict__ ageo,
                                                    const int32_t* __restrict__ adst,
@@ -1252,9 +1258,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
       (void)h_j;
       (void)mrow;
     } else {
-      grad_block<LMAX, C, dh, 0>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
-      grad_block<LMAX, C, dh, 1>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
-      if constexpr (LMAX >= 2) grad_block<LMAX, C, dh, 2>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
+      // MB0 (last layer): m_bar has only its l = 0 component, so Abar has a single row
+      constexpr int D3N = MB0 ? 1 : D;
+      grad_block<LMAX, C, dh, 0, D3N>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
+      grad_block<LMAX, C, dh, 1, D3N>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
+      if constexpr (LMAX >= 2)
+        grad_block<LMAX, C, dh, 2, D3N>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
     }
     const float diff = abar - Dst[(int64_t)i * H + hh];
     const float sb = al * diff;
@@ -1538,37 +1547,57 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     const float4* es = w.es + (int64_t)t * ecap;
     k_bwd_update<LMAX><<<gridn((int64_t)n * C, 256), 256, 0, st>>>(n, C, gbar, yg, yl, w.xcat,
                                                                  w.ybl);
+    // The energy reads only the l = 0 channels of the last features, so at the last layer
+    // dE/dh^(l>=1) = 0: the gate adjoints and the l >= 1 components of m_bar vanish. That layer
+    // (when it is not also the first) forms only m_bar's l = 0 component and its edge kernels
+    // use only that component (the other components of the buffer are never read).
+    const bool mb0 = t == T - 1 && t > 0;
     Epi em{};
     em.y = w.mbar;
     em.ym = feat0;
-    TESS_HIP_CHECK(gemm<EPI_STORE>(st, n, G, C, w.xcat, RowMap{G, 0, 0, 1}, lw[t].W0, em));
-    for (int l = 1; l <= LMAX; l++) {
+    TESS_HIP_CHECK(gemm<EPI_STORE>(st, n, mb0 ? C : G, C, w.xcat, RowMap{G, 0, 0, 1}, lw[t].W0,
+                                   em));
+    for (int l = 1; l <= LMAX && !mb0; l++) {
       RowMap ml{(int64_t)D * C, C, l * l, 2 * l + 1};
       Epi el{};
       el.y = w.mbar;
       el.ym = ml;
       TESS_HIP_CHECK(gemm<EPI_STORE>(st, (int64_t)n * (2 * l + 1), C, C, w.ybl, ml, lw[t].Wl[l], el));
     }
-    k_dst<LMAX, C, H><<<gridn(n, 4), 256, 0, st>>>(n, w.mbar, mt, w.Dst);
+    if (mb0)
+      k_dst<LMAX, C, H, true><<<gridn(n, 4), 256, 0, st>>>(n, w.mbar, mt, w.Dst);
+    else
+      k_dst<LMAX, C, H, false><<<gridn(n, 4), 256, 0, st>>>(n, w.mbar, mt, w.Dst);
     if (cap > 0) {
       const int32_t gb = gridn(cap, kGradPasses * 256 / H);
       if (t == 0)
         TESS_TIMED("edge_grad", st,
-                   k_edge_grad<LMAX, C, H, true><<<gb, 256, 0, st>>>(
+                   k_edge_grad<LMAX, C, H, true, false><<<gb, 256, 0, st>>>(
+                       w.arow + n, w.ageo, w.adst, w.asrc, ew, edw, Pt, w.Dst, w.mbar, ht, rc,
+                       w.sbar, w.gacc, t != T - 1, cap, species, emb, S));
+      else if (mb0)
+        TESS_TIMED("edge_grad", st,
+                   k_edge_grad<LMAX, C, H, false, true><<<gb, 256, 0, st>>>(
                        w.arow + n, w.ageo, w.adst, w.asrc, ew, edw, Pt, w.Dst, w.mbar, ht, rc,
                        w.sbar, w.gacc, t != T - 1, cap, species, emb, S));
       else
         TESS_TIMED("edge_grad", st,
-                   k_edge_grad<LMAX, C, H, false><<<gb, 256, 0, st>>>(
+                   k_edge_grad<LMAX, C, H, false, false><<<gb, 256, 0, st>>>(
                        w.arow + n, w.ageo, w.adst, w.asrc, ew, edw, Pt, w.Dst, w.mbar, ht, rc,
                        w.sbar, w.gacc, t != T - 1, cap, species, emb, S));
     }
     TESS_HIP_CHECK(hipGetLastError());
     if (t > 0) {
-      TESS_TIMED("edge_tapply", st,
-                 k_edge_contract<LMAX, C, H, false, true><<<gridn(n, 4), 256, 0, st>>>(
-                     n, w.arow, w.ageo, w.asrc, w.arev, ew, es, w.mbar, rc, hbar, gbar, Pt, species,
-                     emb, S));
+      if (mb0)  // only m_bar's l = 0 component enters the adjoint contraction
+        TESS_TIMED("edge_tapply", st,
+                   k_edge_contract<LMAX, C, H, true, true><<<gridn(n, 4), 256, 0, st>>>(
+                       n, w.arow, w.ageo, w.asrc, w.arev, ew, es, w.mbar, rc, hbar, gbar, Pt,
+                       species, emb, S));
+      else
+        TESS_TIMED("edge_tapply", st,
+                   k_edge_contract<LMAX, C, H, false, true><<<gridn(n, 4), 256, 0, st>>>(
+                       n, w.arow, w.ageo, w.asrc, w.arev, ew, es, w.mbar, rc, hbar, gbar, Pt,
+                       species, emb, S));
       k_qk_bar<C, H><<<gridn(n, 4), 256, 0, st>>>(n, w.arow, w.asrc, w.arev, w.sbar, qk,
                                                  w.qkbar);
       Epi ea{};
