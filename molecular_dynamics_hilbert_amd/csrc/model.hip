@@ -177,11 +177,13 @@ __global__ void __launch_bounds__(256) k_gemm(int64_t M, int O, const float* __r
   }
 }
 
+// o_first: when > 0, only output columns [0, o_first) are computed (O stays the row length of
+// Wt and of the outputs).
 template <int EPI>
 hipError_t gemm(hipStream_t st, int64_t M, int K, int O, const float* X, RowMap xm,
-                const float* Wt, const Epi& ep) {
+                const float* Wt, const Epi& ep, int o_first = 0) {
   if (M <= 0) return hipSuccess;
-  dim3 g((unsigned)((M + 127) / 128), (unsigned)((O + 63) / 64));
+  dim3 g((unsigned)((M + 127) / 128), (unsigned)(((o_first > 0 ? o_first : O) + 63) / 64));
   switch (K) {
     case 16: TESS_TIMED("node_gemm", st, k_gemm<EPI, 16><<<g, 256, 0, st>>>(M, O, X, xm, Wt, ep)); break;
     case 32: TESS_TIMED("node_gemm", st, k_gemm<EPI, 32><<<g, 256, 0, st>>>(M, O, X, xm, Wt, ep)); break;
@@ -936,8 +938,10 @@ __global__ void __launch_bounds__(256) k_energy_final(int32_t nb, const double* 
 //   xcat[n][lC:(l+1)C] = sum_m gbar^(l,m) y^(l,m) * sigmoid'(g_l)
 //   ybl[n][l^2+m][c]  = gbar^(l,m) * sigmoid(g_l)
 // (the residual path hbar = gbar + ... is added by the transposed edge contraction)
+// MB0 (last layer): only gbar^0 is non-zero and only xcat[n][0:C] is formed (the gates and
+// y^(l>=1) of that layer are never computed, so they are not read).
 // ---------------------------------------------------------------------------------------
-template <int LMAX>
+template <int LMAX, bool MB0>
 __global__ void k_bwd_update(int32_t n, int C, const float* __restrict__ gbar,
                              const float* __restrict__ yg, const float* __restrict__ yl,
                              float* __restrict__ xcat, float* __restrict__ ybl) {
@@ -951,6 +955,7 @@ __global__ void k_bwd_update(int32_t n, int C, const float* __restrict__ gbar,
   float y0 = yg[i * G + c];
   float sg0 = sigmoidf_(y0);
   xcat[i * G + c] = gb[0] * sg0 * (1.0f + y0 * (1.0f - sg0));
+  if constexpr (MB0) return;
 #pragma unroll
   for (int l = 1; l <= LMAX; l++) {
     float g = yg[i * G + l * C + c];
@@ -1507,8 +1512,13 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     eu.hout = hn;
     eu.hm = feat0;
     eu.cdim = C;
-    TESS_HIP_CHECK(gemm<EPI_UPD0>(st, n, C, G, mt, feat0, w.W0T + (int64_t)t * C * G, eu));
-    for (int l = 1; l <= LMAX; l++) {
+    // last layer (when not also the first): the energy reads only h^T's l = 0 channels, so
+    // neither the gates nor the l >= 1 updates are formed (the backward of that layer reads
+    // only y^0)
+    const bool last = t == T - 1 && t > 0;
+    TESS_HIP_CHECK(gemm<EPI_UPD0>(st, n, C, G, mt, feat0, w.W0T + (int64_t)t * C * G, eu,
+                                  last ? C : 0));
+    for (int l = 1; l <= LMAX && !last; l++) {
       RowMap ml{(int64_t)D * C, C, l * l, 2 * l + 1};
       Epi el{};
       el.y = yl;
@@ -1545,13 +1555,17 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     const float* ew = w.ew + (int64_t)t * ecap * 12;
     const float* edw = w.edw + (int64_t)t * ecap * 12;
     const float4* es = w.es + (int64_t)t * ecap;
-    k_bwd_update<LMAX><<<gridn((int64_t)n * C, 256), 256, 0, st>>>(n, C, gbar, yg, yl, w.xcat,
-                                                                 w.ybl);
+    const bool mb0 = t == T - 1 && t > 0;
+    if (mb0)
+      k_bwd_update<LMAX, true><<<gridn((int64_t)n * C, 256), 256, 0, st>>>(n, C, gbar, yg, yl,
+                                                                         w.xcat, w.ybl);
+    else
+      k_bwd_update<LMAX, false><<<gridn((int64_t)n * C, 256), 256, 0, st>>>(n, C, gbar, yg, yl,
+                                                                          w.xcat, w.ybl);
     // The energy reads only the l = 0 channels of the last features, so at the last layer
     // dE/dh^(l>=1) = 0: the gate adjoints and the l >= 1 components of m_bar vanish. That layer
     // (when it is not also the first) forms only m_bar's l = 0 component and its edge kernels
     // use only that component (the other components of the buffer are never read).
-    const bool mb0 = t == T - 1 && t > 0;
     Epi em{};
     em.y = w.mbar;
     em.ym = feat0;
