@@ -548,8 +548,10 @@ __global__ void __launch_bounds__(256) k_edge_prep(const int32_t* __restrict__ a
 // (forward; they are the species embedding) or m_bar of the last layer (adjoint).
 // ---------------------------------------------------------------------------------------
 
-template <int LMAX, int C, int H, bool L0ONLY, bool TRANS>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS ? 4 : (L0ONLY ? 4 : 3), 8))) k_edge_contract(
+// OUT0 (forward of the last layer): only output component 0 is formed, on the VALU (each lane
+// adds sum_k alpha A_e[0][k] h_j[k][4m..4m+3] for its edge); the energy reads nothing else.
+template <int LMAX, int C, int H, bool L0ONLY, bool TRANS, bool OUT0 = false>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((TRANS || L0ONLY || OUT0) ? 4 : 3, 8))) k_edge_contract(
     int32_t n, const int32_t* __restrict__ arow, const float4* __restrict__ ageo,
     const int32_t* __restrict__ asrc, const int32_t* __restrict__ arev,
     const float* __restrict__ ew, const float4* __restrict__ es, const float* __restrict__ X,
@@ -565,7 +567,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
   static_assert(C % 16 == 0 && C <= 64 && dh % 4 == 0, "unsupported channel/head split");
   // edges per chunk (the adjoint keeps less in registers and runs 4 waves per SIMD)
   constexpr int kChunk = TRANS ? 28 : 32;
-  __shared__ float sA[4][kChunk][D * DI];
+  constexpr int DO = OUT0 ? 1 : D;  // output components formed
+  __shared__ float sA[4][kChunk][DO * DI];
   __shared__ float sAl[4][kChunk][4];
   __shared__ int32_t sJ[4][kChunk];
   // first layer (forward): the input features are the species embedding (comp 0 only), read
@@ -617,6 +620,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
 #pragma unroll
     for (int d = 0; d < NDG; d++) acc[t][d] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   float4 acc8 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  float4 acc0 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);  // OUT0
   const int hl = (4 * m) / dh;  // head of this lane's channels
   // Per-edge inputs of a chunk's prologue (lane = edge). The forward requests those of the
   // next chunk before the current chunk's MFMA groups, so their latency is hidden.
@@ -676,7 +680,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
       // component that can be non-zero: A itself (forward) or its transpose (adjoint); the
       // entries that are never stored are never computed
 #pragma unroll
-      for (int o = 0; o < D; o++)
+      for (int o = 0; o < DO; o++)
 #pragma unroll
         for (int k = 0; k < DI; k++) sA[wv][lane][o * DI + k] = TRANS ? A[k * D + o] : A[o * D + k];
       sJ[wv][lane] = y;
@@ -709,6 +713,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
     constexpr bool AL_ON_B = dh % 16 == 0;
     auto mma = [&](const float4* xi, float ai, int e) {
       const float* Ae = sA[wv][e];
+      if constexpr (OUT0) {
+#pragma unroll
+        for (int k = 0; k < DI; k++) {
+          const float b = ai * Ae[k];
+          acc0.x = __builtin_fmaf(b, xi[k].x, acc0.x);
+          acc0.y = __builtin_fmaf(b, xi[k].y, acc0.y);
+          acc0.z = __builtin_fmaf(b, xi[k].z, acc0.z);
+          acc0.w = __builtin_fmaf(b, xi[k].w, acc0.w);
+        }
+        return;
+      }
       float bv[DI][NDG], b8v[DI];
 #pragma unroll
       for (int k = 0; k < DI; k++) {
@@ -755,6 +770,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TRANS 
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  }
+  if constexpr (OUT0) {
+#pragma unroll
+    for (int o = CQ; o < 64; o <<= 1) {
+      acc0.x += __shfl_xor(acc0.x, o, 64);
+      acc0.y += __shfl_xor(acc0.y, o, 64);
+      acc0.z += __shfl_xor(acc0.z, o, 64);
+      acc0.w += __shfl_xor(acc0.w, o, 64);
+    }
+    if (lane < CQ) *reinterpret_cast<float4*>(out + (int64_t)x * D * C + 4 * m) = acc0;
+    return;
   }
   // sum over the edge slots q of a group (lanes CQ apart)
 #pragma unroll
@@ -1497,6 +1523,11 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     if (t == 0)
       TESS_TIMED("edge_apply", st,
                  k_edge_contract<LMAX, C, H, true, false><<<gridn(n, 4), 256, 0, st>>>(
+                     n, w.arow, w.ageo, w.asrc, w.arev, ew, es, ht, rc, mt, nullptr, Pt, species,
+                     emb, S));
+    else if (t == T - 1)  // last layer: only m^0 is read (by the y^0 update)
+      TESS_TIMED("edge_apply", st,
+                 k_edge_contract<LMAX, C, H, false, false, true><<<gridn(n, 4), 256, 0, st>>>(
                      n, w.arow, w.ageo, w.asrc, w.arev, ew, es, ht, rc, mt, nullptr, Pt, species,
                      emb, S));
     else
