@@ -1058,88 +1058,13 @@ __device__ __forceinline__ float quad_sum(float v) {
 // Coupling adjoint of the rows d1 = L1^2 + S0 .. + NR - 1 of one head's Abar (Ab[d3 NR + m]):
 //   t^p[m2] = sum_{m1 in rows, m3} C^p[m1][m2][m3] Abar[(l3,m3)][m1],  wbar^p = t^p . Y_l2;
 //   abar += w_p wbar^p;  wb[p] += alpha wbar^p;  Yb[l2^2+m2] += alpha w_p t^p[m2].
-// Used by the first layer's edge gradient. grad_rows below carries the same loop inline:
+// Only the output components d3 < D3N of Abar are read (the others are zero). Used by the
+// first and last layers' edge gradients. grad_rows below carries the same loop inline:
 // calling this function from it made the compiler spill the full-layer kernel's registers.
-template <int LMAX, int L1, int S0, int NR, int NA>
+template <int LMAX, int L1, int S0, int NR, int D3N, int NA>
 __device__ __forceinline__ void grad_adjoint(const float (&Ab)[NA], const float* w,
                                              const float* Y, float al, float& abar, float* wb,
                                              float* Yb) {
-  constexpr const CGTable& T = cg_table<LMAX>();
-#pragma unroll
-  for (int p = 0; p < Dims<LMAX>::P; p++) {
-    if (T.l1[p] != L1) continue;
-    const float alw = al * w[p];
-    float wbh = 0.0f;
-    bool touched = false;
-#pragma unroll
-    for (int m2 = 0; m2 < 5; m2++) {
-      if (m2 >= 2 * T.l2[p] + 1) continue;
-      float tpm = 0.0f;
-      bool any = false;
-#pragma unroll
-      for (int m = 0; m < NR; m++)
-#pragma unroll
-        for (int m3 = 0; m3 < 5; m3++) {
-          if (m3 < 2 * T.l3[p] + 1 && T.v[p][S0 + m][m2][m3] != 0.0) {
-            tpm += (float)T.v[p][S0 + m][m2][m3] * Ab[(T.l3[p] * T.l3[p] + m3) * NR + m];
-            any = true;
-          }
-        }
-      if (any) {
-        wbh += tpm * Y[T.l2[p] * T.l2[p] + m2];
-        Yb[T.l2[p] * T.l2[p] + m2] += alw * tpm;
-        touched = true;
-      }
-    }
-    if (touched) {
-      abar += w[p] * wbh;
-      wb[p] += al * wbh;
-    }
-  }
-}
-
-// Rows d1 = L1^2 + S0 .. L1^2 + S0 + NR - 1 (sender degree L1) of one head's gradient:
-// Abar[d3][m1] = sum_{c in head} mbar_i[d3][c] h_j[d1][c] for every output component d3 (all of
-// a row's head channels loaded at once), then the part of the coupling adjoint that these
-// columns feed (the adjoint is a sum over (d3, d1) entries, so it splits by column; the same
-// sums as grad_adjoint).
-template <int LMAX, int C, int DH, int L1, int S0, int NR, int D3N, class MRow>
-__device__ __forceinline__ void grad_rows(MRow mrow, const float* __restrict__ h_j, int c0,
-                                          const float* w, const float* Y, float al,
-                                          float& abar, float* wb, float* Yb) {
-  constexpr int D = Dims<LMAX>::D, B0 = L1 * L1 + S0, NC = DH / 4;
-  float4 hv[NR][NC];
-#pragma unroll
-  for (int m = 0; m < NR; m++)
-#pragma unroll
-    for (int t = 0; t < NC; t++)
-      hv[m][t] = *reinterpret_cast<const float4*>(h_j + (B0 + m) * C + c0 + 4 * t);
-  float Ab[D * NR];
-  float4 mv[NC], mn[NC];
-#pragma unroll
-  for (int t = 0; t < NC; t++) mv[t] = mrow(c0 + 4 * t);
-#pragma unroll
-  for (int d3 = 0; d3 < D3N; d3++) {
-    if (d3 + 1 < D3N) {
-#pragma unroll
-      for (int t = 0; t < NC; t++) mn[t] = mrow((d3 + 1) * C + c0 + 4 * t);
-    }
-#pragma unroll
-    for (int m = 0; m < NR; m++) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int t = 0; t < NC; t++) {
-        acc = __builtin_fmaf(mv[t].x, hv[m][t].x, acc);
-        acc = __builtin_fmaf(mv[t].y, hv[m][t].y, acc);
-        acc = __builtin_fmaf(mv[t].z, hv[m][t].z, acc);
-        acc = __builtin_fmaf(mv[t].w, hv[m][t].w, acc);
-      }
-      Ab[d3 * NR + m] = acc;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int t = 0; t < NC; t++) mv[t] = mn[t];
-  }
   constexpr const CGTable& T = cg_table<LMAX>();
 #pragma unroll
   for (int p = 0; p < Dims<LMAX>::P; p++) {
@@ -1175,23 +1100,98 @@ __device__ __forceinline__ void grad_rows(MRow mrow, const float* __restrict__ h
   }
 }
 
-// All rows of sender degree L1, at most 3 rows at a time; output components d3 < D3N of m_bar
-// (the others are zero).
-template <int LMAX, int C, int DH, int L1, int D3N, class MRow>
+// Rows d1 = L1^2 + S0 .. L1^2 + S0 + NR - 1 (sender degree L1) of one head's gradient:
+// Abar[d3][m1] = sum_{c in head} mbar_i[d3][c] h_j[d1][c] for every output component d3 (all of
+// a row's head channels loaded at once), then the part of the coupling adjoint that these
+// columns feed (the adjoint is a sum over (d3, d1) entries, so it splits by column; the same
+// sums as grad_adjoint).
+template <int LMAX, int C, int DH, int L1, int S0, int NR, class MRow>
+__device__ __forceinline__ void grad_rows(MRow mrow, const float* __restrict__ h_j, int c0,
+                                          const float* w, const float* Y, float al,
+                                          float& abar, float* wb, float* Yb) {
+  constexpr int D = Dims<LMAX>::D, B0 = L1 * L1 + S0, NC = DH / 4;
+  float4 hv[NR][NC];
+#pragma unroll
+  for (int m = 0; m < NR; m++)
+#pragma unroll
+    for (int t = 0; t < NC; t++)
+      hv[m][t] = *reinterpret_cast<const float4*>(h_j + (B0 + m) * C + c0 + 4 * t);
+  float Ab[D * NR];
+  float4 mv[NC], mn[NC];
+#pragma unroll
+  for (int t = 0; t < NC; t++) mv[t] = mrow(c0 + 4 * t);
+#pragma unroll
+  for (int d3 = 0; d3 < D; d3++) {
+    if (d3 + 1 < D) {
+#pragma unroll
+      for (int t = 0; t < NC; t++) mn[t] = mrow((d3 + 1) * C + c0 + 4 * t);
+    }
+#pragma unroll
+    for (int m = 0; m < NR; m++) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int t = 0; t < NC; t++) {
+        acc = __builtin_fmaf(mv[t].x, hv[m][t].x, acc);
+        acc = __builtin_fmaf(mv[t].y, hv[m][t].y, acc);
+        acc = __builtin_fmaf(mv[t].z, hv[m][t].z, acc);
+        acc = __builtin_fmaf(mv[t].w, hv[m][t].w, acc);
+      }
+      Ab[d3 * NR + m] = acc;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < NC; t++) mv[t] = mn[t];
+  }
+  constexpr const CGTable& T = cg_table<LMAX>();
+#pragma unroll
+  for (int p = 0; p < Dims<LMAX>::P; p++) {
+    if (T.l1[p] != L1) continue;
+    const float alw = al * w[p];
+    float wbh = 0.0f;
+    bool touched = false;
+#pragma unroll
+    for (int m2 = 0; m2 < 5; m2++) {
+      if (m2 >= 2 * T.l2[p] + 1) continue;
+      float tpm = 0.0f;
+      bool any = false;
+#pragma unroll
+      for (int m = 0; m < NR; m++)
+#pragma unroll
+        for (int m3 = 0; m3 < 5; m3++) {
+          if (m3 < 2 * T.l3[p] + 1 && T.v[p][S0 + m][m2][m3] != 0.0) {
+            tpm += (float)T.v[p][S0 + m][m2][m3] * Ab[(T.l3[p] * T.l3[p] + m3) * NR + m];
+            any = true;
+          }
+        }
+      if (any) {
+        wbh += tpm * Y[T.l2[p] * T.l2[p] + m2];
+        Yb[T.l2[p] * T.l2[p] + m2] += alw * tpm;
+        touched = true;
+      }
+    }
+    if (touched) {
+      abar += w[p] * wbh;
+      wb[p] += al * wbh;
+    }
+  }
+}
+
+// All rows of sender degree L1, at most 3 rows at a time.
+template <int LMAX, int C, int DH, int L1, class MRow>
 __device__ __forceinline__ void grad_block(MRow mrow, const float* __restrict__ h_j, int c0,
                                            const float* w, const float* Y, float al,
                                            float& abar, float* wb, float* Yb) {
   if constexpr (L1 == 0) {
-    grad_rows<LMAX, C, DH, 0, 0, 1, D3N>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
+    grad_rows<LMAX, C, DH, 0, 0, 1>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
   } else if constexpr (L1 == 1) {
-    grad_rows<LMAX, C, DH, 1, 0, 3, D3N>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
+    grad_rows<LMAX, C, DH, 1, 0, 3>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
   } else {
-    grad_rows<LMAX, C, DH, 2, 0, 3, D3N>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
-    grad_rows<LMAX, C, DH, 2, 3, 2, D3N>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
+    grad_rows<LMAX, C, DH, 2, 0, 3>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
+    grad_rows<LMAX, C, DH, 2, 3, 2>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
   }
 }
 
-template <int LMAX, int C, int H, bool L0ONLY, bool MB0>
+template <int LMAX, int C, int H, bool L0ONLY>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) k_edge_grad(const int32_t* __restrict__ arow_n,
                                                    const float4* __restrict__ ageo,
                                                    const int32_t* __restrict__ adst,
@@ -1285,16 +1285,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
       float Ab[D];
 #pragma unroll
       for (int d3 = 0; d3 < D; d3++) Ab[d3] = u0[d3];
-      grad_adjoint<LMAX, 0, 0, 1>(Ab, w, Y, al, abar, wb, Yb);
+      grad_adjoint<LMAX, 0, 0, 1, D>(Ab, w, Y, al, abar, wb, Yb);
       (void)h_j;
       (void)mrow;
     } else {
-      // MB0 (last layer): m_bar has only its l = 0 component, so Abar has a single row
-      constexpr int D3N = MB0 ? 1 : D;
-      grad_block<LMAX, C, dh, 0, D3N>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
-      grad_block<LMAX, C, dh, 1, D3N>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
-      if constexpr (LMAX >= 2)
-        grad_block<LMAX, C, dh, 2, D3N>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
+      grad_block<LMAX, C, dh, 0>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
+      grad_block<LMAX, C, dh, 1>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
+      if constexpr (LMAX >= 2) grad_block<LMAX, C, dh, 2>(mrow, h_j, c0, w, Y, al, abar, wb, Yb);
     }
     const float diff = abar - Dst[(int64_t)i * H + hh];
     const float sb = al * diff;
@@ -1327,6 +1324,142 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
       gacc[a * 3 + 2] = gz;
     }
   }
+  }
+}
+
+// Edge gradient of the last layer, source-major. There m_bar has only its l = 0 component, so
+// Abar^h[0][d1] = sum_{c in h} mbar_i[0][c] h_j[d1][c] needs a full feature row only of the
+// source j. The lanes walk the active list grouped by row j (entry a' = (j <- i)) and
+// compute the gradient of the forward edge e = rev(a') = (i <- j): h_j rows are staged in LDS
+// per block and only mbar_i's l = 0 head slice (64 B per lane) is gathered, instead of the
+// 2.3 KB of h_j per edge of the destination-major form. The geometry of e is -r_vec(a') and
+// its radial weights are those of a' (both bit-exact, |r| is the same); the softmax
+// probability, D_i and the outputs sbar, g are read or written at e. The sums run in the same
+// order as in k_edge_grad, so the results are identical to its single-row form.
+template <int LMAX, int C, int H>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) k_edge_grad_last(
+    const int32_t* __restrict__ arow_n, const float4* __restrict__ ageo,
+    const int32_t* __restrict__ adst, const int32_t* __restrict__ asrc,
+    const int32_t* __restrict__ arev, const float* __restrict__ ew, const float* __restrict__ edw,
+    const float4* __restrict__ prob, const float* __restrict__ Dst,
+    const float* __restrict__ mbar, const float* __restrict__ h, float rc,
+    float4* __restrict__ sbar, float* __restrict__ gacc, bool accumulate, int64_t cap) {
+  static_assert(H == 1 || H == 4, "one lane or a quad of lanes per edge");
+  constexpr int D = Dims<LMAX>::D;
+  constexpr int P = Dims<LMAX>::P;
+  constexpr int dh = C / H;
+  constexpr int NC = dh / 4;
+  constexpr int EPW = 256 / H;
+  constexpr int EPB = kGradPasses * EPW;
+  __shared__ float4 shj[kGradRows * D * C / 4];
+  const int64_t n_act = *arow_n;
+  const uint32_t nb_act = (uint32_t)((n_act + EPB - 1) / EPB);
+  if (blockIdx.x >= nb_act) return;
+  const int64_t a_base = (int64_t)xcd_block(blockIdx.x, nb_act) * EPB;
+  const int hh = (int)threadIdx.x % H;
+  const int32_t j_first = adst[a_base];
+  const int32_t nrows = adst[min(a_base + (int64_t)EPB, n_act) - 1] - j_first + 1;
+  for (int b0 = 0; b0 < nrows; b0 += kGradRows) {
+    const int nst = min(nrows - b0, kGradRows);
+    if (b0 > 0) __syncthreads();
+    {
+      const float4* src = reinterpret_cast<const float4*>(h + (int64_t)(j_first + b0) * D * C);
+      for (int k = threadIdx.x; k < nst * D * C / 4; k += blockDim.x) shj[k] = src[k];
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int ps = 0; ps < kGradPasses; ps++) {
+      const int64_t a = a_base + ps * EPW + threadIdx.x / H;  // a' = (j <- i)
+      const bool active = a < n_act && a < cap;
+      const int rj = active ? adst[a] - j_first : -1;
+      if (rj < b0 || rj >= b0 + nst) continue;
+      const int32_t i = asrc[a];
+      const int64_t e = arev[a];  // e = (i <- j)
+      const float4 g = ageo[a];
+      const float r = g.w, ir = 1.0f / r;
+      const float nx = -g.x * ir, ny = -g.y * ir, nz = -g.z * ir;
+      float th = kPi * r / rc, s1, c1;
+      __sincosf(th, &s1, &c1);
+      const float u = 0.5f * (c1 + 1.0f), du = -0.5f * (kPi / rc) * s1;
+      float Y[9];
+      sph<LMAX>(nx, ny, nz, Y);
+      float w[P];
+#pragma unroll
+      for (int p = 0; p < P; p++) w[p] = ew[a * 12 + p];
+      float wb[P], Yb[9];
+#pragma unroll
+      for (int p = 0; p < P; p++) wb[p] = 0.0f;
+#pragma unroll
+      for (int d = 0; d < 9; d++) Yb[d] = 0.0f;
+      const float p_h = reinterpret_cast<const float*>(prob)[e * 4 + hh];
+      const float al = u * p_h;
+      const int c0 = hh * dh;
+      // mbar_i[0][head channels]
+      float4 mv[NC];
+#pragma unroll
+      for (int t = 0; t < NC; t++)
+        mv[t] = *reinterpret_cast<const float4*>(mbar + (int64_t)i * D * C + c0 + 4 * t);
+      const float4* hrow = shj + (rj - b0) * (D * C / 4) + c0 / 4;
+      float Ab[D];
+#pragma unroll
+      for (int d1 = 0; d1 < D; d1++) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int t = 0; t < NC; t++) {
+          const float4 hv = hrow[d1 * (C / 4) + t];
+          acc = __builtin_fmaf(mv[t].x, hv.x, acc);
+          acc = __builtin_fmaf(mv[t].y, hv.y, acc);
+          acc = __builtin_fmaf(mv[t].z, hv.z, acc);
+          acc = __builtin_fmaf(mv[t].w, hv.w, acc);
+        }
+        Ab[d1] = acc;
+      }
+      float abar = 0.0f;
+      {  // the same row blocks, in the same order, as the destination-major kernel
+        const float a0[1] = {Ab[0]};
+        grad_adjoint<LMAX, 0, 0, 1, 1>(a0, w, Y, al, abar, wb, Yb);
+        if constexpr (LMAX >= 1) {
+          const float a1[3] = {Ab[1], Ab[2], Ab[3]};
+          grad_adjoint<LMAX, 1, 0, 3, 1>(a1, w, Y, al, abar, wb, Yb);
+        }
+        if constexpr (LMAX >= 2) {
+          const float a2[3] = {Ab[4], Ab[5], Ab[6]};
+          grad_adjoint<LMAX, 2, 0, 3, 1>(a2, w, Y, al, abar, wb, Yb);
+          const float a3[2] = {Ab[7], Ab[8]};
+          grad_adjoint<LMAX, 2, 3, 2, 1>(a3, w, Y, al, abar, wb, Yb);
+        }
+      }
+      const float diff = abar - Dst[(int64_t)i * H + hh];
+      const float sb = al * diff;
+      float ubar = p_h * diff;
+      if constexpr (H == 4) {
+#pragma unroll
+        for (int p = 0; p < P; p++) wb[p] = quad_sum(wb[p]);
+#pragma unroll
+        for (int d = 0; d < 9; d++) Yb[d] = quad_sum(Yb[d]);
+        ubar = quad_sum(ubar);
+        reinterpret_cast<float*>(sbar)[e * 4 + hh] = sb;
+      } else {
+        sbar[e] = make_float4(sb, 0.0f, 0.0f, 0.0f);
+      }
+      if (hh == 0) {
+        float dEdr = ubar * du;
+#pragma unroll
+        for (int p = 0; p < P; p++) dEdr += wb[p] * edw[a * 12 + p];
+        float gy[3];
+        sph_vjp<LMAX>(nx, ny, nz, Yb, gy);
+        const float ng = nx * gy[0] + ny * gy[1] + nz * gy[2];
+        float gx = dEdr * nx + (gy[0] - ng * nx) * ir;
+        float gyv = dEdr * ny + (gy[1] - ng * ny) * ir;
+        float gz = dEdr * nz + (gy[2] - ng * nz) * ir;
+        if (accumulate) {
+          gx += gacc[e * 3]; gyv += gacc[e * 3 + 1]; gz += gacc[e * 3 + 2];
+        }
+        gacc[e * 3] = gx;
+        gacc[e * 3 + 1] = gyv;
+        gacc[e * 3 + 2] = gz;
+      }
+    }
   }
 }
 
@@ -1617,17 +1750,17 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
       const int32_t gb = gridn(cap, kGradPasses * 256 / H);
       if (t == 0)
         TESS_TIMED("edge_grad", st,
-                   k_edge_grad<LMAX, C, H, true, false><<<gb, 256, 0, st>>>(
+                   k_edge_grad<LMAX, C, H, true><<<gb, 256, 0, st>>>(
                        w.arow + n, w.ageo, w.adst, w.asrc, ew, edw, Pt, w.Dst, w.mbar, ht, rc,
                        w.sbar, w.gacc, t != T - 1, cap, species, emb, S));
       else if (mb0)
         TESS_TIMED("edge_grad", st,
-                   k_edge_grad<LMAX, C, H, false, true><<<gb, 256, 0, st>>>(
-                       w.arow + n, w.ageo, w.adst, w.asrc, ew, edw, Pt, w.Dst, w.mbar, ht, rc,
-                       w.sbar, w.gacc, t != T - 1, cap, species, emb, S));
+                   k_edge_grad_last<LMAX, C, H><<<gb, 256, 0, st>>>(
+                       w.arow + n, w.ageo, w.adst, w.asrc, w.arev, ew, edw, Pt, w.Dst, w.mbar, ht,
+                       rc, w.sbar, w.gacc, t != T - 1, cap));
       else
         TESS_TIMED("edge_grad", st,
-                   k_edge_grad<LMAX, C, H, false, false><<<gb, 256, 0, st>>>(
+                   k_edge_grad<LMAX, C, H, false><<<gb, 256, 0, st>>>(
                        w.arow + n, w.ageo, w.adst, w.asrc, ew, edw, Pt, w.Dst, w.mbar, ht, rc,
                        w.sbar, w.gacc, t != T - 1, cap, species, emb, S));
     }
