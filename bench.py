@@ -32,21 +32,29 @@ PEAK_HBM_GBS = 8000.0
 
 def edge_kernel_flops(spec, n_active: int) -> dict:
     """Algorithmic fp32 flops (FMA = 2) of the edge kernels over one E+F pass, counting only
-    the defining contractions (lower-order per-edge terms are left out):
-      edge_apply : sum_e alpha A_e h_j  -> C*D*D MAC per edge (layer 0: C*D, only l=0 inputs)
-      edge_grad  : Abar^h = sum_c mbar (x) h_j -> C*D*D MAC per edge (layer 0: C*D)
-      edge_tapply: A_e^T mbar -> C*D*D MAC per edge (layers 1..T-1)
-      edge_prep  : radial MLP and its r-derivative 2*(K*R + P*R) MAC + logits C MAC per edge"""
+    the defining contractions (lower-order per-edge terms are left out) and only the parts
+    the energy depends on. The first layer's input features have only the l = 0 component,
+    and the energy reads only the l = 0 channels of the last layer, whose m and m_bar are
+    then needed only in component 0:
+      edge_apply : sum_e alpha A_e h_j  -> C*D*D MAC per edge (first and last layers: C*D)
+      edge_grad  : Abar^h = sum_c mbar (x) h_j -> C*D*D MAC per edge (first layer: C*D)
+      edge_grad_last: the same at the last layer, one row of Abar -> C*D MAC per edge
+      edge_tapply: A_e^T mbar -> C*D*D MAC per edge (layers 1..T-1; the last: C*D)
+      edge_prep  : radial MLP and its r-derivative 2*(K*R + P*R) MAC, plus the logits C MAC
+                   per edge (the first layer's logits come from a per-species table)"""
     C, T, K, R = spec.channels, spec.n_layers, spec.n_rbf, spec.radial_hidden
     D = (spec.l_max + 1) ** 2
     P = spec.n_paths
-    full, l0 = C * D * D, C * D
-    return {
-        "edge_apply": 2.0 * n_active * (l0 + (T - 1) * full),
-        "edge_grad": 2.0 * n_active * (l0 + (T - 1) * full),
-        "edge_tapply": 2.0 * n_active * (T - 1) * full,
-        "edge_prep": 2.0 * n_active * T * (2 * (K * R + P * R) + C),
-    }
+    full, one = C * D * D, C * D
+    mac = {"edge_apply": 0, "edge_grad": 0, "edge_grad_last": 0, "edge_tapply": 0, "edge_prep": 0}
+    for t in range(T):
+        first, last = t == 0, t == T - 1 and t > 0
+        mac["edge_apply"] += one if (first or last) else full
+        mac["edge_grad_last" if last else "edge_grad"] += one if (first or last) else full
+        if t > 0:
+            mac["edge_tapply"] += one if last else full
+        mac["edge_prep"] += 2 * (K * R + P * R) + (0 if first else C)
+    return {k: 2.0 * n_active * v for k, v in mac.items()}
 
 
 def cpu_baseline(n_sample: int = 8000) -> dict:
@@ -150,8 +158,8 @@ def run(args):
     md(max(args.warmup, 1), False, args.graph)
     torch.cuda.synchronize()
     skin_flags[0] = 0
-    names = ("edge_prep", "edge_apply", "edge_grad", "edge_tapply", "node_gemm", "radix_scatter",
-             "nbr_count", "nbr_fill")
+    names = ("edge_prep", "edge_apply", "edge_grad", "edge_grad_last", "edge_tapply", "node_gemm",
+             "radix_scatter", "nbr_count", "nbr_fill")
     # profile pass (same length): HIP events around every instrumented kernel, giving the
     # per-kernel times and the dominant edge kernel
     T.timing_enable(True)
@@ -159,7 +167,8 @@ def run(args):
     torch.cuda.synchronize()
     kern = {k: T.timing_read(k) for k in names}
     T.timing_enable(False)
-    dom = max(("edge_apply", "edge_grad", "edge_tapply", "edge_prep"), key=lambda k: kern[k][0])
+    dom = max(("edge_apply", "edge_grad", "edge_grad_last", "edge_tapply", "edge_prep"),
+              key=lambda k: kern[k][0])
     skin_flags[0] = 0
     # timed region: exactly `steps` MD steps, inputs resident in HBM. Only the dominant kernel
     # carries HIP events in it (its roofline numbers come from this region); --graph and

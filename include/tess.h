@@ -95,8 +95,9 @@ int32_t tess_build_neighbors(int32_t n, const float box[3], float r_cut, float s
  *      then rebuilt in the workspace), n_edges = row_ptr[n].
  *  out energy   device double[1]; e_atom device float[n] (nullable);
  *      forces   device float[n][3] (nullable: energy only, no backward pass).
- * Fully asynchronous (no host synchronisation). Species outside [0, n_species) give
- * undefined values; validate species on the host first if they are not trusted. */
+ * Fully asynchronous (no host synchronisation). Species outside [0, n_species) are clamped
+ * into that range where they index the weights (the results are then meaningless, but no
+ * access leaves the weights); validate species on the host first if they are not trusted. */
 int32_t tess_energy_forces(const tess_model_desc* desc, const float* weights, int32_t n,
                            const float box[3], const float* pos, const int32_t* species,
                            const int32_t* row_ptr, const uint32_t* col_shift,
@@ -182,10 +183,10 @@ int32_t tess_set_curve(int32_t curve);
 /* Optional kernel timing for benchmarks (not part of the method). tess_timing_enable(1)
  * clears the counters and, until tess_timing_enable(0), records a pair of HIP events on the
  * launching stream around each launch of the instrumented kernels ("edge_prep",
- * "edge_apply", "edge_grad", "edge_tapply", "node_gemm", "radix_scatter", "nbr_count",
- * "nbr_fill"). tess_timing_read waits for those events and returns the summed milliseconds
- * and the launch count of one kernel. Host memory only; not thread-safe across concurrent
- * calls on several streams. */
+ * "edge_apply", "edge_grad", "edge_grad_last", "edge_tapply", "node_gemm", "radix_scatter",
+ * "nbr_count", "nbr_fill"). tess_timing_read waits for those events and returns the summed
+ * milliseconds and the launch count of one kernel. Host memory only; not thread-safe across
+ * concurrent calls on several streams. */
 int32_t tess_timing_enable(int32_t on);
 int32_t tess_timing_read(const char* kernel, double* total_ms, int64_t* launches);
 /* Restrict the timing events to one instrumented kernel (NULL or "" = all of them); an event

@@ -1754,7 +1754,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
                        w.arow + n, w.ageo, w.adst, w.asrc, ew, edw, Pt, w.Dst, w.mbar, ht, rc,
                        w.sbar, w.gacc, t != T - 1, cap, species, emb, S));
       else if (mb0)
-        TESS_TIMED("edge_grad", st,
+        TESS_TIMED("edge_grad_last", st,
                    k_edge_grad_last<LMAX, C, H><<<gb, 256, 0, st>>>(
                        w.arow + n, w.ageo, w.adst, w.asrc, w.arev, ew, edw, Pt, w.Dst, w.mbar, ht,
                        rc, w.sbar, w.gacc, t != T - 1, cap));
