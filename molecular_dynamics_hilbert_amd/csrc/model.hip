@@ -274,21 +274,29 @@ __global__ void __launch_bounds__(256) k_active_count(int32_t n, const float* __
                                                       const uint32_t* __restrict__ col, float Lx,
                                                       float Ly, float Lz, float rc2,
                                                       int32_t* __restrict__ acnt,
+                                                      int32_t* __restrict__ ccnt,
                                                       uint32_t* __restrict__ rmin2_bits) {
   int32_t i = blockIdx.x * 4 + (threadIdx.x >> 6);
   int lane = threadIdx.x & 63;
   if (i >= n) return;
-  int cnt = 0;
+  int cnt = 0, ccn = 0;
   float mn = INFINITY;
   for (int32_t e = row_ptr[i] + lane; e < row_ptr[i + 1]; e += 64) {
     int32_t j;
     float4 r = edge_vec(pos, i, col[e], Lx, Ly, Lz, &j);
     const bool act = r.w < rc2;
     cnt += act;
+    ccn += act && j > i;
     if (act) mn = fminf(mn, r.w);
   }
-  for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
-  if (lane == 0) acnt[i] = cnt;
+  for (int o = 32; o >= 1; o >>= 1) {
+    cnt += __shfl_xor(cnt, o, 64);
+    ccn += __shfl_xor(ccn, o, 64);
+  }
+  if (lane == 0) {
+    acnt[i] = cnt;
+    ccnt[i] = ccn;
+  }
   if (rmin2_bits) {
     // shortest squared pair distance: non-negative floats order like their bit patterns
     for (int o = 32; o >= 1; o >>= 1) mn = fminf(mn, __shfl_xor(mn, o, 64));
@@ -305,12 +313,14 @@ __global__ void __launch_bounds__(256) k_active_fill(int32_t n, const float* __r
                                                      int32_t* __restrict__ asrc,
                                                      int32_t* __restrict__ aslot,
                                                      int32_t* __restrict__ slot2act,
-                                                     float4* __restrict__ ageo) {
+                                                     float4* __restrict__ ageo,
+                                                     const int32_t* __restrict__ crow,
+                                                     int32_t* __restrict__ canon) {
   int32_t i = blockIdx.x * 4 + (threadIdx.x >> 6);
   int lane = threadIdx.x & 63;
   if (i >= n) return;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int32_t a0 = arow[i];
+  int32_t a0 = arow[i], c0 = crow[i];
   for (int32_t e0 = row_ptr[i]; e0 < row_ptr[i + 1]; e0 += 64) {
     int32_t e = e0 + lane;
     bool ok = e < row_ptr[i + 1];
@@ -322,6 +332,10 @@ __global__ void __launch_bounds__(256) k_active_fill(int32_t n, const float* __r
       act = r.w < rc2;
     }
     uint64_t m = __ballot(act);
+    const bool can = act && j > i;  // canonical: the pair's entry in the lower-index row
+    const uint64_t mc = __ballot(can);
+    if (can) canon[c0 + __popcll(mc & lt)] = a0 + __popcll(m & lt);
+    c0 += __popcll(mc);
     if (act) {
       int32_t a = a0 + __popcll(m & lt);
       adst[a] = i;
@@ -420,7 +434,9 @@ __global__ void __launch_bounds__(256) k_l0_logits(int S, const float* __restric
 // the two run back to back. Weights are staged in LDS (W2 padded with zero rows to a multiple
 // of 4 paths, so the 12th slot of each edge's weight row is written as 0).
 template <int LMAX, int C, int H, int R, bool L0>
-__global__ void __launch_bounds__(256) k_edge_prep(const int32_t* __restrict__ arow_n,
+__global__ void __launch_bounds__(256) k_edge_prep(const int32_t* __restrict__ crow_n,
+                                                   const int32_t* __restrict__ canon,
+                                                   const int32_t* __restrict__ arev,
                                                    const float4* __restrict__ ageo,
                                                    const int32_t* __restrict__ adst,
                                                    const int32_t* __restrict__ asrc,
@@ -438,8 +454,11 @@ __global__ void __launch_bounds__(256) k_edge_prep(const int32_t* __restrict__ a
   static_assert(R % 4 == 0 && 4 * PG <= 12, "radial MLP shape");
   __shared__ float4 sW1[RG][4][2];   // W1[4 rg + i][0..7]
   __shared__ float4 sW2[PG][RG][4];  // W2[4 pg + i][4 rg .. 4 rg + 3] at [pg][rg][i]
-  // only the first ceil(n_active/256) blocks work; spread them evenly over the XCDs
-  const uint32_t nb_act = (uint32_t)((*arow_n + blockDim.x - 1) / blockDim.x);
+  // one lane per pair: the canonical entry a (source index > destination index) and its
+  // reverse rev(a) have the same |r|, hence bit-identical radial weights. Only the first
+  // ceil(n_pairs/256) blocks work; spread them evenly over the XCDs.
+  const int64_t n_pairs = *crow_n;
+  const uint32_t nb_act = (uint32_t)((n_pairs + blockDim.x - 1) / blockDim.x);
   if (blockIdx.x >= nb_act) return;
   for (int t = threadIdx.x; t < R * 8; t += 256) reinterpret_cast<float*>(sW1)[t] = W1[t];
   // the four paths a block's lanes read together are 16 bytes apart (distinct LDS banks)
@@ -449,12 +468,12 @@ __global__ void __launch_bounds__(256) k_edge_prep(const int32_t* __restrict__ a
         t < P * R ? W2[t] : 0.0f;
   }
   __syncthreads();
-  const int64_t a = (int64_t)xcd_block(blockIdx.x, nb_act) * blockDim.x + threadIdx.x;
-  // every lane takes part in the MFMAs; lanes past the last edge work on edge 0, store nothing
-  const bool valid = a < cap && a < *arow_n;
-  const int64_t ac = valid ? a : 0;
+  const int64_t kp = (int64_t)xcd_block(blockIdx.x, nb_act) * blockDim.x + threadIdx.x;
+  // every lane takes part in the MFMAs; lanes past the last pair work on pair 0, store nothing
+  const bool valid = kp < cap && kp < n_pairs;
+  const int64_t a = canon[valid ? kp : 0];
   const int ii = threadIdx.x & 3;
-  const float4 g = ageo[ac];
+  const float4 g = ageo[a];
   RadialOut ro;
   radial8(g.w, rc, ro);
   floatx4 wacc[PG], dwacc[PG];
@@ -500,29 +519,86 @@ __global__ void __launch_bounds__(256) k_edge_prep(const int32_t* __restrict__ a
     __builtin_amdgcn_sched_barrier(0);
   }
   if (!valid) return;
-  // wacc[pg][r] = w_(4 pg + r) of this lane's edge
+  const int64_t ar = arev[a];
+  // wacc[pg][r] = w_(4 pg + r) of the pair, written to both of its entries
 #pragma unroll
   for (int pg = 0; pg < PG; pg++) {
-    *reinterpret_cast<float4*>(ew + a * 12 + 4 * pg) =
-        make_float4(wacc[pg][0], wacc[pg][1], wacc[pg][2], wacc[pg][3]);
-    *reinterpret_cast<float4*>(edw + a * 12 + 4 * pg) =
-        make_float4(dwacc[pg][0], dwacc[pg][1], dwacc[pg][2], dwacc[pg][3]);
+    const float4 wv = make_float4(wacc[pg][0], wacc[pg][1], wacc[pg][2], wacc[pg][3]);
+    const float4 dv = make_float4(dwacc[pg][0], dwacc[pg][1], dwacc[pg][2], dwacc[pg][3]);
+    *reinterpret_cast<float4*>(ew + a * 12 + 4 * pg) = wv;
+    *reinterpret_cast<float4*>(edw + a * 12 + 4 * pg) = dv;
+    *reinterpret_cast<float4*>(ew + ar * 12 + 4 * pg) = wv;
+    *reinterpret_cast<float4*>(edw + ar * 12 + 4 * pg) = dv;
   }
+  // logits of both directions: a = (i <- j) and rev(a) = (j <- i)
+  const int32_t i = adst[a], j = asrc[a];
   if constexpr (L0) {
     // first layer: q and k depend on the species only, the logits come from their table
-    es[a] = l0tab[sp_index(species[adst[a]], S) * S + sp_index(species[asrc[a]], S)];
+    const int si = sp_index(species[i], S), sj = sp_index(species[j], S);
+    es[a] = l0tab[si * S + sj];
+    es[ar] = l0tab[sj * S + si];
     return;
   }
-  const float4* qi = reinterpret_cast<const float4*>(qk + (int64_t)adst[a] * 2 * C);
-  const float4* kj = reinterpret_cast<const float4*>(qk + (int64_t)asrc[a] * 2 * C + C);
-  float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int c4 = 0; c4 < C / 4; c4++) {
-    float4 q = qi[c4], k = kj[c4];
-    s[(c4 * 4) / dh] += q.x * k.x + q.y * k.y + q.z * k.z + q.w * k.w;
-  }
+  (void)qk;  // the other layers' logits: k_logits
+}
+
+// ---------------------------------------------------------------------------------------
+// Logits s_h(a) = <q_i^h, k_j^h>/sqrt(d) of the active edges a = (i <- j), one wave per row i.
+// q_i is loaded once per row; the row's sources are staged in LDS 128 at a time. Lane = (edge
+// slot q of 64/(C/4), channel quad m): each 16-byte load brings 4 channels of k_j, eight
+// groups of edges are requested before any is used, and the quads of a head are summed with
+// lane swaps. The first lane of each head writes that head's logit.
+// ---------------------------------------------------------------------------------------
+template <int C, int H>
+__global__ void __launch_bounds__(256) k_logits(int32_t n, const int32_t* __restrict__ arow,
+                                                const int32_t* __restrict__ asrc,
+                                                const float* __restrict__ qk,
+                                                float4* __restrict__ es) {
+  constexpr int dh = C / H;
+  constexpr int CQ = C / 4;     // channel quads
+  constexpr int EPG = 64 / CQ;  // edges per group (one per slot)
+  constexpr int QH = dh / 4;    // quads per head
+  constexpr int kG = 8;         // groups requested together
+  static_assert(dh % 4 == 0, "a channel quad must lie in one head");
+  __shared__ int32_t sY[4][128];
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int q = lane / CQ, m = lane % CQ;
+  const int32_t i = xcd_block(blockIdx.x, gridDim.x) * 4 + wv;
+  if (i >= n) return;
+  const int hq = (4 * m) / dh;
   const float isd = rsqrtf((float)dh);
-  es[a] = make_float4(s[0] * isd, s[1] * isd, s[2] * isd, s[3] * isd);
+  const float4 qv = *reinterpret_cast<const float4*>(qk + (int64_t)i * 2 * C + 4 * m);
+  const int32_t a0 = arow[i], a1 = arow[i + 1];
+  for (int32_t b = a0; b < a1; b += 128) {
+    const int cnt = min(128, a1 - b);
+#pragma unroll
+    for (int h2 = 0; h2 < 2; h2++) {
+      const int l2 = lane + 64 * h2;
+      if (l2 < cnt) sY[wv][l2] = asrc[b + l2];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    for (int u = 0; u < cnt; u += kG * EPG) {
+      float4 kv[kG];
+#pragma unroll
+      for (int g = 0; g < kG; g++) {
+        const int e = min(u + g * EPG + q, cnt - 1);
+        kv[g] = *reinterpret_cast<const float4*>(qk + (int64_t)sY[wv][e] * 2 * C + C + 4 * m);
+      }
+#pragma unroll
+      for (int g = 0; g < kG; g++) {
+        float d = qv.x * kv[g].x + qv.y * kv[g].y + qv.z * kv[g].z + qv.w * kv[g].w;
+#pragma unroll
+        for (int o = 1; o < QH; o <<= 1) d += __shfl_xor(d, o, 64);
+        const int e = u + g * EPG + q;
+        if (m % QH == 0 && e < cnt) reinterpret_cast<float*>(es)[(int64_t)(b + e) * 4 + hq] = d * isd;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1498,6 +1574,7 @@ struct EFWS {
   float *WqkT, *W0T, *WlT;  // per layer transposed weights
   float *h, *qk, *m, *yg, *yl;
   int32_t *arow, *adst, *asrc, *aslot, *slot2act, *arev, *rev_own;
+  int32_t *crow, *canon;  // per row: offsets of the canonical edges (source > destination)
   float4* ageo;
   float *ew, *edw;
   float4* es;
@@ -1529,6 +1606,8 @@ static EFWS carve_ef(Carver& cv, const tess_model_desc& md, int32_t n, int64_t c
   w.slot2act = cv.take<int32_t>(ec);
   w.arev = cv.take<int32_t>(ec);
   w.rev_own = cv.take<int32_t>(ec);
+  w.crow = cv.take<int32_t>(nn + 1);
+  w.canon = cv.take<int32_t>(ec);
   w.ageo = cv.take<float4>(ec);
   w.ew = cv.take<float>(T * ec * 12);
   w.edw = cv.take<float>(T * ec * 12);
@@ -1608,12 +1687,14 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
       rev = w.rev_own;
     }
     k_active_count<<<gridn(n, 4), 256, 0, st>>>(n, pos, row_ptr, col_shift, box[0], box[1], box[2],
-                                                rc * rc, w.arow, rmin2_bits);
+                                                rc * rc, w.arow, w.crow, rmin2_bits);
     k_fill_i32<<<1, 64, 0, st>>>(w.arow + n, 1, 0);
+    k_fill_i32<<<1, 64, 0, st>>>(w.crow + n, 1, 0);
     TESS_HIP_CHECK(scan_exclusive_i32(w.arow, (int64_t)n + 1, w.scan_tmp, st));
+    TESS_HIP_CHECK(scan_exclusive_i32(w.crow, (int64_t)n + 1, w.scan_tmp, st));
     k_active_fill<<<gridn(n, 4), 256, 0, st>>>(n, pos, row_ptr, col_shift, box[0], box[1], box[2],
                                                rc * rc, w.arow, w.adst, w.asrc, w.aslot,
-                                               w.slot2act, w.ageo);
+                                               w.slot2act, w.ageo, w.crow, w.canon);
     k_active_rev<<<gridn(cap, 256), 256, 0, st>>>(w.arow + n, w.aslot, rev, w.slot2act, w.arev, cap);
     TESS_HIP_CHECK(hipGetLastError());
   } else {
@@ -1642,16 +1723,18 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
       if (cap > 0)
         TESS_TIMED("edge_prep", st,
                    k_edge_prep<LMAX, C, H, R, true><<<gridn(cap, 256), 256, 0, st>>>(
-                       w.arow + n, w.ageo, w.adst, w.asrc, lw[t].W1, lw[t].W2, qk, rc, ew, edw,
-                       es, cap, species, w.l0tab, S));
+                       w.crow + n, w.canon, w.arev, w.ageo, w.adst, w.asrc, lw[t].W1,
+                       lw[t].W2, qk, rc, ew, edw, es, cap, species, w.l0tab, S));
     } else {
       TESS_HIP_CHECK(
           gemm<EPI_STORE>(st, n, C, 2 * C, ht, feat0, w.WqkT + (int64_t)t * C * 2 * C, e0));
-      if (cap > 0)
+      if (cap > 0) {
         TESS_TIMED("edge_prep", st,
                    k_edge_prep<LMAX, C, H, R, false><<<gridn(cap, 256), 256, 0, st>>>(
-                       w.arow + n, w.ageo, w.adst, w.asrc, lw[t].W1, lw[t].W2, qk, rc, ew, edw,
-                       es, cap, species, w.l0tab, S));
+                       w.crow + n, w.canon, w.arev, w.ageo, w.adst, w.asrc, lw[t].W1,
+                       lw[t].W2, qk, rc, ew, edw, es, cap, species, w.l0tab, S));
+        k_logits<C, H><<<gridn(n, 4), 256, 0, st>>>(n, w.arow, w.asrc, qk, es);
+      }
     }
     if (t == 0)
       TESS_TIMED("edge_apply", st,
