@@ -1733,7 +1733,8 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
                    k_edge_prep<LMAX, C, H, R, false><<<gridn(cap, 256), 256, 0, st>>>(
                        w.crow + n, w.canon, w.arev, w.ageo, w.adst, w.asrc, lw[t].W1,
                        lw[t].W2, qk, rc, ew, edw, es, cap, species, w.l0tab, S));
-        k_logits<C, H><<<gridn(n, 4), 256, 0, st>>>(n, w.arow, w.asrc, qk, es);
+        TESS_TIMED("logits", st,
+                   k_logits<C, H><<<gridn(n, 4), 256, 0, st>>>(n, w.arow, w.asrc, qk, es));
       }
     }
     if (t == 0)
