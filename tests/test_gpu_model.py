@@ -62,6 +62,25 @@ def test_energy_forces_full_oracle(T, oracle_mod, wname):
     assert abs(g["e_atom"].sum() - g["energy"]) <= 1e-6 * abs(g["energy"])
 
 
+@pytest.mark.parametrize("shape", [(2, 16, 4, 32), (1, 32, 4, 32), (2, 64, 4, 64)])
+@pytest.mark.parametrize("layers", [1, 3])
+def test_energy_forces_every_shape(T, oracle_mod, shape, layers):
+    """Every compiled model shape (l_max, channels, heads, radial hidden) on a 1,500-atom
+    salt box, with one layer (first = last) and with three (first, inner, last layers each
+    take their own kernels)."""
+    l_max, C, H, R = shape
+    m = W.ModelSpec(n_species=4, n_layers=layers, channels=C, l_max=l_max, n_heads=H, n_rbf=8,
+                    radial_hidden=R)
+    wl = W.salt_box(1500, 1006, m, "salt1k5")
+    w = W.make_weights(wl.model, 2006)
+    g = _run(T, wl, w)
+    nb = oracle_mod.build_neighbors(wl.box, wl.pos, wl.species, wl.model.r_cut, wl.skin)
+    ref = oracle_mod.energy_forces(wl.model, w, wl.box, nb["pos"].astype(np.float64),
+                                   nb["species"], nb["row_ptr"], nb["col_shift"])
+    _assert_ef(g["energy"], g["forces"], ref["energy"], ref["forces"],
+               "shape %s T=%d" % (shape, layers))
+
+
 def _golden(name):
     path = os.path.join(GOLDEN, name + ".json")
     if not os.path.exists(path):
