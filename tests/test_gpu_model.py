@@ -62,7 +62,8 @@ def test_energy_forces_full_oracle(T, oracle_mod, wname):
     assert abs(g["e_atom"].sum() - g["energy"]) <= 1e-6 * abs(g["energy"])
 
 
-@pytest.mark.parametrize("shape", [(2, 16, 4, 32), (1, 32, 4, 32), (2, 64, 4, 64)])
+@pytest.mark.parametrize("shape", [(1, 16, 1, 32), (2, 16, 4, 32), (1, 32, 4, 32), (2, 32, 4, 32),
+                                   (2, 64, 4, 64)])
 @pytest.mark.parametrize("layers", [1, 3])
 def test_energy_forces_every_shape(T, oracle_mod, shape, layers):
     """Every compiled model shape (l_max, channels, heads, radial hidden) on a 1,500-atom
