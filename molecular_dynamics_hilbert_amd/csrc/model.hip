@@ -422,14 +422,15 @@ __global__ void __launch_bounds__(256) k_l0_logits(int S, const float* __restric
   }
 }
 
-// Per active edge and layer: radial weights w_p = W2 SiLU(W1 b), their r-derivative, and the
-// per-head logits s_h = <q_i^h, k_j^h>/sqrt(d). Lane = edge (64 consecutive active edges per
-// wave). Both layers of the radial MLP run on 4x4x1 MFMA blocks (block b = lanes 4b..4b+3,
+// Per neighbour pair and layer: radial weights w_p = W2 SiLU(W1 b) and their r-derivative,
+// written to both entries of the pair (they share |r|); first layer: also the logits of both
+// entries from the species table. Lane = pair (64 consecutive canonical entries per wave).
+// Both layers of the radial MLP run on 4x4x1 MFMA blocks (block b = lanes 4b..4b+3,
 // D_b[r][j] += A[r] B[j] with A from lane 4b+r and B from lane 4b+j): A is a weight picked by
-// lane & 3 (4 hidden units, resp. 4 paths, per block) and B is the lane's own edge value, so
-// lane 4b+j ends with its own edge's 4 hidden pre-activations (resp. 4 path weights) in its
-// 4 accumulator registers. The activation, the Bessel basis and the logits stay on the VALU,
-// one edge per lane. Scheduling barriers keep each group's MFMAs together: on this chip
+// lane & 3 (4 hidden units, resp. 4 paths, per block) and B is the lane's own pair value, so
+// lane 4b+j ends with its own pair's 4 hidden pre-activations (resp. 4 path weights) in its
+// 4 accumulator registers. The activation and the Bessel basis stay on the VALU, one pair per
+// lane. Scheduling barriers keep each group's MFMAs together: on this chip
 // MFMAs interleaved one by one with independent VALU work of the same wave issue slower than
 // the two run back to back. Weights are staged in LDS (W2 padded with zero rows to a multiple
 // of 4 paths, so the 12th slot of each edge's weight row is written as 0).
@@ -441,8 +442,7 @@ __global__ void __launch_bounds__(256) k_edge_prep(const int32_t* __restrict__ c
                                                    const int32_t* __restrict__ adst,
                                                    const int32_t* __restrict__ asrc,
                                                    const float* __restrict__ W1,
-                                                   const float* __restrict__ W2,
-                                                   const float* __restrict__ qk, float rc,
+                                                   const float* __restrict__ W2, float rc,
                                                    float* __restrict__ ew, float* __restrict__ edw,
                                                    float4* __restrict__ es, int64_t cap,
                                                    const int32_t* __restrict__ species,
@@ -530,16 +530,13 @@ __global__ void __launch_bounds__(256) k_edge_prep(const int32_t* __restrict__ c
     *reinterpret_cast<float4*>(ew + ar * 12 + 4 * pg) = wv;
     *reinterpret_cast<float4*>(edw + ar * 12 + 4 * pg) = dv;
   }
-  // logits of both directions: a = (i <- j) and rev(a) = (j <- i)
-  const int32_t i = adst[a], j = asrc[a];
   if constexpr (L0) {
-    // first layer: q and k depend on the species only, the logits come from their table
-    const int si = sp_index(species[i], S), sj = sp_index(species[j], S);
+    // first layer: q and k depend on the species only, the logits of both directions,
+    // a = (i <- j) and rev(a) = (j <- i), come from their table (other layers: k_logits)
+    const int si = sp_index(species[adst[a]], S), sj = sp_index(species[asrc[a]], S);
     es[a] = l0tab[si * S + sj];
     es[ar] = l0tab[sj * S + si];
-    return;
   }
-  (void)qk;  // the other layers' logits: k_logits
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1724,7 +1721,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
         TESS_TIMED("edge_prep", st,
                    k_edge_prep<LMAX, C, H, R, true><<<gridn(cap, 256), 256, 0, st>>>(
                        w.crow + n, w.canon, w.arev, w.ageo, w.adst, w.asrc, lw[t].W1,
-                       lw[t].W2, qk, rc, ew, edw, es, cap, species, w.l0tab, S));
+                       lw[t].W2, rc, ew, edw, es, cap, species, w.l0tab, S));
     } else {
       TESS_HIP_CHECK(
           gemm<EPI_STORE>(st, n, C, 2 * C, ht, feat0, w.WqkT + (int64_t)t * C * 2 * C, e0));
@@ -1732,7 +1729,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
         TESS_TIMED("edge_prep", st,
                    k_edge_prep<LMAX, C, H, R, false><<<gridn(cap, 256), 256, 0, st>>>(
                        w.crow + n, w.canon, w.arev, w.ageo, w.adst, w.asrc, lw[t].W1,
-                       lw[t].W2, qk, rc, ew, edw, es, cap, species, w.l0tab, S));
+                       lw[t].W2, rc, ew, edw, es, cap, species, w.l0tab, S));
         TESS_TIMED("logits", st,
                    k_logits<C, H><<<gridn(n, 4), 256, 0, st>>>(n, w.arow, w.asrc, qk, es));
       }
