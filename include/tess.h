@@ -11,7 +11,13 @@
  *  - All other array arguments are DEVICE pointers (e.g. torch tensors on cuda:0), owned by
  *    the caller, row-major, without padding. The library never allocates device memory: the
  *    caller passes a workspace of at least tess_workspace_bytes() bytes.
+ *  - The weights blob and the workspace must be 16-byte aligned (torch allocations are);
+ *    otherwise TESS_ERR_ARG (weights) or TESS_ERR_WORKSPACE (workspace).
  *  - `hip_stream` is a hipStream_t (NULL = default stream). Work is enqueued on it in order.
+ *    tess_energy_forces and tess_md_steps also run independent kernels of the pass on one
+ *    second stream per host thread and device, created by the library on first use; it forks
+ *    from and joins `hip_stream` through events, so the pass stays ordered on `hip_stream`
+ *    (and captures into one graph).
  *  - Return value: a tess_status. Argument, box and workspace errors are detected on the host
  *    before anything is enqueued. TESS_ERR_HIP reports a failed HIP call (the stream state is
  *    then undefined).

@@ -60,6 +60,9 @@ void timing_mark(const char* name, hipStream_t st, bool begin) {
 
 namespace {
 
+// 16-byte loads read the weights and the workspace
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 constexpr float kAccelConv = 9.648533e-3f;  // eV/A/amu -> A/fs^2
 
 // First half of a velocity-Verlet step: v += dt/2 F/m; x += dt v; flag |x - x_ref| > skin/2.
@@ -381,7 +384,7 @@ int32_t tess_build_neighbors(int32_t n, const float box[3], float r_cut, float s
     return TESS_ERR_ARG;
   if (!box_ok(box, r_cut, skin)) return TESS_ERR_BOX;
   Layout L = layout(reinterpret_cast<char*>(workspace), nullptr, n, edge_cap);
-  if (!workspace || ws_bytes < L.total) return TESS_ERR_WORKSPACE;
+  if (!workspace || !aligned16(workspace) || ws_bytes < L.total) return TESS_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
   *n_edges = 0;
   if (n == 0) {
@@ -398,12 +401,13 @@ int32_t tess_energy_forces(const tess_model_desc* d, const float* weights, int32
                            int64_t n_edges, double* energy, float* e_atom, float* forces,
                            void* workspace, int64_t ws_bytes, void* hip_stream) {
   if (!d || !ef_shape_supported(*d)) return TESS_ERR_ARG;
-  if (n < 0 || n >= (1 << 27) || n_edges < 0 || !box || !energy || !weights) return TESS_ERR_ARG;
+  if (n < 0 || n >= (1 << 27) || n_edges < 0 || !box || !energy || !weights || !aligned16(weights))
+    return TESS_ERR_ARG;
   if (n > 0 && (!pos || !species || !row_ptr || (n_edges > 0 && !col_shift))) return TESS_ERR_ARG;
   for (int a = 0; a < 3; a++)
     if (!(box[a] > 0.0f)) return TESS_ERR_BOX;
   Layout L = layout(reinterpret_cast<char*>(workspace), d, n, n_edges);
-  if (!workspace || ws_bytes < L.total) return TESS_ERR_WORKSPACE;
+  if (!workspace || !aligned16(workspace) || ws_bytes < L.total) return TESS_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
   if (n == 0) {
     TESS_HIP_CHECK(hipMemsetAsync(energy, 0, sizeof(double), st));
@@ -423,7 +427,8 @@ int32_t tess_md_steps_ex(const tess_model_desc* d, const float* weights, int32_t
                          const tess_md_options* opt_in, void* hip_stream) {
   if (!d || !ef_shape_supported(*d)) return TESS_ERR_ARG;
   if (n < 1 || n >= (1 << 27) || n_steps < 0 || rebuild_every < 1 || edge_cap < 0 || !box ||
-      !n_edges || !weights || !pos || !vel || !species || !mass_by_species || !perm_accum ||
+      !n_edges || !weights || !aligned16(weights) || !pos || !vel || !species ||
+      !mass_by_species || !perm_accum ||
       !forces || !row_ptr || !col_shift || !rev || !(dt_fs > 0.0f) || !(r_cut > 0.0f) ||
       !(skin >= 0.0f) || d->r_cut != r_cut || (flags & ~(TESS_MD_FORCES_VALID | TESS_MD_GRAPH)))
     return TESS_ERR_ARG;
@@ -436,7 +441,7 @@ int32_t tess_md_steps_ex(const tess_model_desc* d, const float* weights, int32_t
     return TESS_ERR_ARG;
   if (!box_ok(box, r_cut, skin)) return TESS_ERR_BOX;
   Layout L = layout(reinterpret_cast<char*>(workspace), d, n, edge_cap);
-  if (!workspace || ws_bytes < L.total) return TESS_ERR_WORKSPACE;
+  if (!workspace || !aligned16(workspace) || ws_bytes < L.total) return TESS_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
   const float half_skin2 = 0.25f * skin * skin;
   const bool forces_valid = (flags & TESS_MD_FORCES_VALID) != 0;

@@ -59,7 +59,7 @@ struct Epi {
 };
 
 // Block tile 128 rows x 64 columns, 4 waves of 32 x 64 (two 32x32 MFMA tiles each). The
-// block's K x 64 slice of Wt is staged in LDS once. Each lane loads its row of X with float4
+// block's K x 64 slice of Wt is staged in LDS once, while the block's X rows are in flight. Each lane loads its row of X with float4
 // loads: lanes 0-31 take k = 8s..8s+3 and lanes 32-63 k = 8s+4..8s+7, so MFMA step (s, q)
 // pairs k = 8s+q (first half-wave) with k = 8s+4+q (second half-wave), and the B operand
 // uses the same pairing. K must be a multiple of 8 and at most kGemmMaxK.
@@ -93,10 +93,6 @@ __global__ void __launch_bounds__(256) k_gemm(int64_t M, int O, const float* __r
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int64_t r0 = (int64_t)blockIdx.x * 128 + w * 32;
   const int o0 = blockIdx.y * 64;
-  for (int k = t; k < K * 64; k += 256) {
-    const int kk = k >> 6, oo = k & 63;
-    Ws[kk][oo] = (o0 + oo < O) ? Wt[(int64_t)kk * O + o0 + oo] : 0.0f;
-  }
   const int64_t row = r0 + (lane & 31);
   const bool row_ok = row < M;
   const int kh = (lane >> 5) * 4;
@@ -108,6 +104,17 @@ __global__ void __launch_bounds__(256) k_gemm(int64_t M, int O, const float* __r
   } else {
 #pragma unroll
     for (int s8 = 0; s8 < K / 8; s8++) xa[s8] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  }
+  // the block's K x 64 slice of Wt, staged after the X rows are requested (rows of Wt are O
+  // floats, O a multiple of 4, and the blob is 16-byte aligned)
+  for (int k = t; k < K * 16; k += 256) {
+    const int kk = k >> 4, oo = 4 * (k & 15);
+    float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (o0 + oo < O) v = *reinterpret_cast<const float4*>(Wt + (int64_t)kk * O + o0 + oo);
+    Ws[kk][oo] = v.x;
+    Ws[kk][oo + 1] = v.y;
+    Ws[kk][oo + 2] = v.z;
+    Ws[kk][oo + 3] = v.w;
   }
   // epilogue inputs of this lane's 32 elements (rows r0 + 8(v/4) + 4 half + v%4, columns
   // o0 + col and o0 + 32 + col), requested before the MFMA loop
@@ -1637,6 +1644,44 @@ struct LayerW {
   const float *Wq, *Wk, *W1, *W2, *W0, *Wl[3];
 };
 
+// A second stream per host thread and device for kernels of the pass that do not depend on
+// the work before them: the radial MLPs of layers 1..T-1 need only the geometry and run next
+// to the first layer. It forks from and joins the caller's stream through events, so the
+// caller sees one stream-ordered pass, and the fork/join become graph edges under stream
+// capture. Created on first use; if it cannot be created, every kernel runs on the caller's
+// stream in the same order.
+constexpr int kAuxEvents = 17;  // fork + one per layer (at most 16)
+struct AuxStream {
+  bool tried = false, ok = false;
+  hipStream_t s = nullptr;
+  hipEvent_t ev[kAuxEvents] = {};
+};
+AuxStream* aux_stream() {
+  constexpr int kMaxDev = 16;
+  thread_local AuxStream a[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  AuxStream& x = a[dev];
+  if (!x.tried) {
+    x.tried = true;
+    bool ok = hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking) == hipSuccess;
+    for (int k = 0; k < kAuxEvents && ok; k++)
+      ok = hipEventCreateWithFlags(&x.ev[k], hipEventDisableTiming) == hipSuccess;
+    x.ok = ok;
+    if (!ok) (void)hipGetLastError();
+  }
+  return x.ok ? &x : nullptr;
+}
+// `to` waits for everything enqueued so far on `from` (through event k of the pool).
+inline hipError_t stream_after(AuxStream* ax, int k, hipStream_t from, hipStream_t to) {
+  hipError_t e = hipEventRecord(ax->ev[k], from);
+  if (e != hipSuccess) return e;
+  return hipStreamWaitEvent(to, ax->ev[k], 0);
+}
+
 template <int LMAX, int C, int H, int R>
 int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const float box[3],
                const float* pos, const int32_t* species, const int32_t* row_ptr,
@@ -1698,6 +1743,21 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     k_fill_i32<<<gridn((int64_t)n + 1, 256), 256, 0, st>>>(w.arow, (int64_t)n + 1, 0);
   }
   const RowMap feat0{(int64_t)D * C, C, 0, 1};
+  // The radial MLPs of layers 1..T-1 depend only on the geometry: they run on the second
+  // stream while the first layer runs; layer t's contraction waits for event t.
+  AuxStream* ax = aux_stream();
+  const hipStream_t sa = ax ? ax->s : st;
+  if (ax && cap > 0 && T > 1) {
+    TESS_HIP_CHECK(stream_after(ax, 0, st, sa));
+    for (int t = 1; t < T; t++) {
+      TESS_TIMED("edge_prep", sa,
+                 k_edge_prep<LMAX, C, H, R, false><<<gridn(cap, 256), 256, 0, sa>>>(
+                     w.crow + n, w.canon, w.arev, w.ageo, w.adst, w.asrc, lw[t].W1, lw[t].W2, rc,
+                     w.ew + (int64_t)t * ecap * 12, w.edw + (int64_t)t * ecap * 12,
+                     w.es + (int64_t)t * ecap, cap, species, w.l0tab, S));
+      TESS_HIP_CHECK(hipEventRecord(ax->ev[t], sa));
+    }
+  }
   // ---------------- forward ----------------
   for (int t = 0; t < T; t++) {
     float* ht = w.h + (int64_t)t * NDC;
@@ -1726,12 +1786,14 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
       TESS_HIP_CHECK(
           gemm<EPI_STORE>(st, n, C, 2 * C, ht, feat0, w.WqkT + (int64_t)t * C * 2 * C, e0));
       if (cap > 0) {
-        TESS_TIMED("edge_prep", st,
-                   k_edge_prep<LMAX, C, H, R, false><<<gridn(cap, 256), 256, 0, st>>>(
-                       w.crow + n, w.canon, w.arev, w.ageo, w.adst, w.asrc, lw[t].W1,
-                       lw[t].W2, rc, ew, edw, es, cap, species, w.l0tab, S));
+        if (!ax)
+          TESS_TIMED("edge_prep", st,
+                     k_edge_prep<LMAX, C, H, R, false><<<gridn(cap, 256), 256, 0, st>>>(
+                         w.crow + n, w.canon, w.arev, w.ageo, w.adst, w.asrc, lw[t].W1,
+                         lw[t].W2, rc, ew, edw, es, cap, species, w.l0tab, S));
         TESS_TIMED("logits", st,
                    k_logits<C, H><<<gridn(n, 4), 256, 0, st>>>(n, w.arow, w.asrc, qk, es));
+        if (ax) TESS_HIP_CHECK(hipStreamWaitEvent(st, ax->ev[t], 0));
       }
     }
     if (t == 0)

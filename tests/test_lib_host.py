@@ -86,3 +86,29 @@ def test_md_options_rejected_host_side(T):
     o = T.MdOptions(T.THERMOSTAT_BERENDSEN, 300.0, 10.0, None, None)
     assert call(C.byref(o), ws_bytes=8) == T.ERR_WORKSPACE
     assert call(None, ws_bytes=8) == T.ERR_WORKSPACE
+
+
+def test_misaligned_weights_and_workspace_rejected(T):
+    """The weights blob and the workspace are read with 16-byte loads: a pointer that is not
+    16-byte aligned is refused on the host before anything is enqueued."""
+    L = T.lib()
+    wl = W.water648()
+    d = T.desc(wl.model)
+    box = (C.c_float * 3)(30.0, 30.0, 30.0)
+    fake = C.c_void_p(0x1000)
+    e = C.c_void_p(0x2000)
+
+    def ef(weights, ws):
+        return L.tess_energy_forces(C.byref(d), weights, 10, box, fake, fake, fake, fake, None,
+                                    0, e, None, None, ws, 1 << 40, None)
+
+    assert ef(C.c_void_p(0x1004), fake) == T.ERR_ARG
+    assert ef(fake, C.c_void_p(0x1008)) == T.ERR_WORKSPACE
+    ne = C.c_int64(0)
+    assert L.tess_build_neighbors(10, box, 5.75, 1.0, fake, fake, None, None, fake, fake, fake,
+                                  fake, None, 100, C.byref(ne), C.c_void_p(0x1001), 1 << 40,
+                                  None) == T.ERR_WORKSPACE
+    rc = float(wl.model.r_cut)
+    assert L.tess_md_steps_ex(C.byref(d), C.c_void_p(0x100c), 10, box, rc, 1.0, fake, fake, fake,
+                              fake, 0.5, 4, 20, 0, fake, fake, None, fake, fake, fake, 100,
+                              C.byref(ne), fake, 1 << 40, None, None) == T.ERR_ARG
