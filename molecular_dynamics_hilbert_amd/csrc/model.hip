@@ -62,7 +62,7 @@ struct Epi {
 // block's K x 64 slice of Wt is staged in LDS once, while the block's X rows are in flight. Each lane loads its row of X with float4
 // loads: lanes 0-31 take k = 8s..8s+3 and lanes 32-63 k = 8s+4..8s+7, so MFMA step (s, q)
 // pairs k = 8s+q (first half-wave) with k = 8s+4+q (second half-wave), and the B operand
-// uses the same pairing. K must be a multiple of 8 and at most kGemmMaxK.
+// uses the same pairing. K must be a multiple of 16 and at most kGemmMaxK.
 // Offsets of output row v of a lane (row r0 + 8(v/4) + 4(lane/32) + v%4) in y, h and the
 // gates; rows past M are clamped (and flagged) so that loads stay in bounds. One 32-bit
 // division by the rows-per-node count (row maps of y and h share it).
@@ -107,14 +107,24 @@ __global__ void __launch_bounds__(256) k_gemm(int64_t M, int O, const float* __r
   }
   // the block's K x 64 slice of Wt, staged after the X rows are requested (rows of Wt are O
   // floats, O a multiple of 4, and the blob is 16-byte aligned)
-  for (int k = t; k < K * 16; k += 256) {
-    const int kk = k >> 4, oo = 4 * (k & 15);
-    float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    if (o0 + oo < O) v = *reinterpret_cast<const float4*>(Wt + (int64_t)kk * O + o0 + oo);
-    Ws[kk][oo] = v.x;
-    Ws[kk][oo + 1] = v.y;
-    Ws[kk][oo + 2] = v.z;
-    Ws[kk][oo + 3] = v.w;
+  // (every load is requested before the first LDS write)
+  {
+    static_assert(K % 16 == 0, "K is a multiple of 16");
+    float4 wv[K / 16];
+#pragma unroll
+    for (int i = 0; i < K / 16; i++) {
+      const int k = t + 256 * i, kk = k >> 4, oo = 4 * (k & 15);
+      wv[i] = *reinterpret_cast<const float4*>(Wt + (int64_t)kk * O + (o0 + oo < O ? o0 + oo : 0));
+    }
+#pragma unroll
+    for (int i = 0; i < K / 16; i++) {
+      const int k = t + 256 * i, kk = k >> 4, oo = 4 * (k & 15);
+      const float4 v = o0 + oo < O ? wv[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      Ws[kk][oo] = v.x;
+      Ws[kk][oo + 1] = v.y;
+      Ws[kk][oo + 2] = v.z;
+      Ws[kk][oo + 3] = v.w;
+    }
   }
   // epilogue inputs of this lane's 32 elements (rows r0 + 8(v/4) + 4 half + v%4, columns
   // o0 + col and o0 + 32 + col), requested before the MFMA loop
@@ -1644,16 +1654,19 @@ struct LayerW {
   const float *Wq, *Wk, *W1, *W2, *W0, *Wl[3];
 };
 
-// A second stream per host thread and device for kernels of the pass that do not depend on
-// the work before them: the radial MLPs of layers 1..T-1 need only the geometry and run next
-// to the first layer. It forks from and joins the caller's stream through events, so the
-// caller sees one stream-ordered pass, and the fork/join become graph edges under stream
-// capture. Created on first use; if it cannot be created, every kernel runs on the caller's
-// stream in the same order.
-constexpr int kAuxEvents = 17;  // fork + one per layer (at most 16)
+// Two more streams per host thread and device for kernels of the pass that do not depend on
+// the work next to them: (1) the radial MLPs of layers 1..T-1 need only the geometry and run
+// next to the first layer; (2) layer t+1's q|k GEMM and logits need only the l = 0 features
+// that layer t's first update GEMM writes, and run next to that layer's l >= 1 updates; in the
+// backward, the l = 0 block of m_bar runs next to the l >= 1 blocks. The streams fork from
+// and join the caller's stream through events, so the caller sees one stream-ordered pass
+// and the fork/join become graph edges under stream capture. Created on first use; if they
+// cannot be created, every kernel runs on the caller's stream in the same order.
+constexpr int kAuxEvents = 20;  // 0: fork, 1..15: radial MLP of layer t done, 16..19 below
+constexpr int kEvFwdFork = 16, kEvFwdJoin = 17, kEvBwdFork = 18, kEvBwdJoin = 19;
 struct AuxStream {
   bool tried = false, ok = false;
-  hipStream_t s = nullptr;
+  hipStream_t s = nullptr, s2 = nullptr;
   hipEvent_t ev[kAuxEvents] = {};
 };
 AuxStream* aux_stream() {
@@ -1667,7 +1680,8 @@ AuxStream* aux_stream() {
   AuxStream& x = a[dev];
   if (!x.tried) {
     x.tried = true;
-    bool ok = hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking) == hipSuccess;
+    bool ok = hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking) == hipSuccess &&
+              hipStreamCreateWithFlags(&x.s2, hipStreamNonBlocking) == hipSuccess;
     for (int k = 0; k < kAuxEvents && ok; k++)
       ok = hipEventCreateWithFlags(&x.ev[k], hipEventDisableTiming) == hipSuccess;
     x.ok = ok;
@@ -1747,6 +1761,21 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
   // stream while the first layer runs; layer t's contraction waits for event t.
   AuxStream* ax = aux_stream();
   const hipStream_t sa = ax ? ax->s : st;
+  const hipStream_t sb = ax ? ax->s2 : st;
+  // q|k GEMM and logits of layer t (t >= 1) on stream `qs`
+  auto qk_logits = [&](int t, hipStream_t qs) -> int32_t {
+    Epi e0{};
+    e0.y = w.qk + (int64_t)t * n * 2 * C;
+    e0.ym = RowMap{2 * C, 0, 0, 1};
+    TESS_HIP_CHECK(gemm<EPI_STORE>(qs, n, C, 2 * C, w.h + (int64_t)t * NDC, feat0,
+                                   w.WqkT + (int64_t)t * C * 2 * C, e0));
+    if (cap > 0)
+      TESS_TIMED("logits", qs,
+                 k_logits<C, H><<<gridn(n, 4), 256, 0, qs>>>(n, w.arow, w.asrc, e0.y,
+                                                            w.es + (int64_t)t * ecap));
+    TESS_HIP_CHECK(hipGetLastError());
+    return TESS_OK;
+  };
   if (ax && cap > 0 && T > 1) {
     TESS_HIP_CHECK(stream_after(ax, 0, st, sa));
     for (int t = 1; t < T; t++) {
@@ -1762,7 +1791,6 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
   for (int t = 0; t < T; t++) {
     float* ht = w.h + (int64_t)t * NDC;
     float* hn = w.h + (int64_t)(t + 1) * NDC;
-    float* qk = w.qk + (int64_t)t * n * 2 * C;
     float4* Pt = w.P + (int64_t)t * ecap;
     float* mt = w.m + (int64_t)t * NDC;
     float* yg = w.yg + (int64_t)t * n * G;
@@ -1770,9 +1798,6 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     float* ew = w.ew + (int64_t)t * ecap * 12;
     float* edw = w.edw + (int64_t)t * ecap * 12;
     float4* es = w.es + (int64_t)t * ecap;
-    Epi e0{};
-    e0.y = qk;
-    e0.ym = RowMap{2 * C, 0, 0, 1};
     if (t == 0) {
       // first layer: logits from the per-species table (q and k of the first layer are not
       // needed anywhere else: the backward stops before dE/dh^0)
@@ -1782,19 +1807,19 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
                    k_edge_prep<LMAX, C, H, R, true><<<gridn(cap, 256), 256, 0, st>>>(
                        w.crow + n, w.canon, w.arev, w.ageo, w.adst, w.asrc, lw[t].W1,
                        lw[t].W2, rc, ew, edw, es, cap, species, w.l0tab, S));
+    } else if (ax) {
+      // q|k and logits were enqueued on the third stream after the previous layer's l = 0
+      // update; the radial MLP on the second stream at the start
+      TESS_HIP_CHECK(hipStreamWaitEvent(st, ax->ev[kEvFwdJoin], 0));
+      if (cap > 0) TESS_HIP_CHECK(hipStreamWaitEvent(st, ax->ev[t], 0));
     } else {
-      TESS_HIP_CHECK(
-          gemm<EPI_STORE>(st, n, C, 2 * C, ht, feat0, w.WqkT + (int64_t)t * C * 2 * C, e0));
-      if (cap > 0) {
-        if (!ax)
-          TESS_TIMED("edge_prep", st,
-                     k_edge_prep<LMAX, C, H, R, false><<<gridn(cap, 256), 256, 0, st>>>(
-                         w.crow + n, w.canon, w.arev, w.ageo, w.adst, w.asrc, lw[t].W1,
-                         lw[t].W2, rc, ew, edw, es, cap, species, w.l0tab, S));
-        TESS_TIMED("logits", st,
-                   k_logits<C, H><<<gridn(n, 4), 256, 0, st>>>(n, w.arow, w.asrc, qk, es));
-        if (ax) TESS_HIP_CHECK(hipStreamWaitEvent(st, ax->ev[t], 0));
-      }
+      if (cap > 0)
+        TESS_TIMED("edge_prep", st,
+                   k_edge_prep<LMAX, C, H, R, false><<<gridn(cap, 256), 256, 0, st>>>(
+                       w.crow + n, w.canon, w.arev, w.ageo, w.adst, w.asrc, lw[t].W1,
+                       lw[t].W2, rc, ew, edw, es, cap, species, w.l0tab, S));
+      const int32_t rq = qk_logits(t, st);
+      if (rq != TESS_OK) return rq;
     }
     if (t == 0)
       TESS_TIMED("edge_apply", st,
@@ -1825,6 +1850,13 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     const bool last = t == T - 1 && t > 0;
     TESS_HIP_CHECK(gemm<EPI_UPD0>(st, n, C, G, mt, feat0, w.W0T + (int64_t)t * C * G, eu,
                                   last ? C : 0));
+    if (ax && t + 1 < T) {
+      // the next layer's q|k and logits read only h^(t+1)'s l = 0 block, written above
+      TESS_HIP_CHECK(stream_after(ax, kEvFwdFork, st, sb));
+      const int32_t rq = qk_logits(t + 1, sb);
+      if (rq != TESS_OK) return rq;
+      TESS_HIP_CHECK(hipEventRecord(ax->ev[kEvFwdJoin], sb));
+    }
     for (int l = 1; l <= LMAX && !last; l++) {
       RowMap ml{(int64_t)D * C, C, l * l, 2 * l + 1};
       Epi el{};
@@ -1876,8 +1908,13 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     Epi em{};
     em.y = w.mbar;
     em.ym = feat0;
-    TESS_HIP_CHECK(gemm<EPI_STORE>(st, n, mb0 ? C : G, C, w.xcat, RowMap{G, 0, 0, 1}, lw[t].W0,
+    // the l = 0 block of m_bar and the l >= 1 blocks read and write disjoint data
+    const bool fork = ax && !mb0;
+    const hipStream_t s0 = fork ? sb : st;
+    if (fork) TESS_HIP_CHECK(stream_after(ax, kEvBwdFork, st, sb));
+    TESS_HIP_CHECK(gemm<EPI_STORE>(s0, n, mb0 ? C : G, C, w.xcat, RowMap{G, 0, 0, 1}, lw[t].W0,
                                    em));
+    if (fork) TESS_HIP_CHECK(hipEventRecord(ax->ev[kEvBwdJoin], sb));
     for (int l = 1; l <= LMAX && !mb0; l++) {
       RowMap ml{(int64_t)D * C, C, l * l, 2 * l + 1};
       Epi el{};
@@ -1885,6 +1922,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
       el.ym = ml;
       TESS_HIP_CHECK(gemm<EPI_STORE>(st, (int64_t)n * (2 * l + 1), C, C, w.ybl, ml, lw[t].Wl[l], el));
     }
+    if (fork) TESS_HIP_CHECK(hipStreamWaitEvent(st, ax->ev[kEvBwdJoin], 0));
     if (mb0)
       k_dst<LMAX, C, H, true><<<gridn(n, 4), 256, 0, st>>>(n, w.mbar, mt, w.Dst);
     else
