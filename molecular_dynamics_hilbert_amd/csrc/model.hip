@@ -1661,7 +1661,8 @@ struct LayerW {
 // backward, the l = 0 block of m_bar runs next to the l >= 1 blocks. The streams fork from
 // and join the caller's stream through events, so the caller sees one stream-ordered pass
 // and the fork/join become graph edges under stream capture. Created on first use; if they
-// cannot be created, every kernel runs on the caller's stream in the same order.
+// cannot be created (or the first call comes under capture), every kernel runs on the caller's
+// stream in the same order.
 constexpr int kAuxEvents = 20;  // 0: fork, 1..15: radial MLP of layer t done, 16..19 below
 constexpr int kEvFwdFork = 16, kEvFwdJoin = 17, kEvBwdFork = 18, kEvBwdJoin = 19;
 struct AuxStream {
@@ -1669,7 +1670,7 @@ struct AuxStream {
   hipStream_t s = nullptr, s2 = nullptr;
   hipEvent_t ev[kAuxEvents] = {};
 };
-AuxStream* aux_stream() {
+AuxStream* aux_stream(hipStream_t st) {
   constexpr int kMaxDev = 16;
   thread_local AuxStream a[kMaxDev];
   int dev = 0;
@@ -1679,6 +1680,14 @@ AuxStream* aux_stream() {
   }
   AuxStream& x = a[dev];
   if (!x.tried) {
+    // streams are created outside any stream capture (a capture in progress runs the pass on
+    // the caller's stream alone; a later call outside capture creates them)
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    if (cs != hipStreamCaptureStatusNone) return nullptr;
     x.tried = true;
     bool ok = hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking) == hipSuccess &&
               hipStreamCreateWithFlags(&x.s2, hipStreamNonBlocking) == hipSuccess;
@@ -1759,7 +1768,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
   const RowMap feat0{(int64_t)D * C, C, 0, 1};
   // The radial MLPs of layers 1..T-1 depend only on the geometry: they run on the second
   // stream while the first layer runs; layer t's contraction waits for event t.
-  AuxStream* ax = aux_stream();
+  AuxStream* ax = aux_stream(st);
   const hipStream_t sa = ax ? ax->s : st;
   const hipStream_t sb = ax ? ax->s2 : st;
   // q|k GEMM and logits of layer t (t >= 1) on stream `qs`

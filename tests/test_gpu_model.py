@@ -141,6 +141,33 @@ def test_repeatable_and_energy_only(T):
     assert c["energy"] == a["energy"]
 
 
+def test_energy_forces_graph_capture_replays(T):
+    """tess_energy_forces captured by the caller (torch CUDA graph, global capture mode) with
+    its second and third streams forked and joined inside the capture: every replay, with
+    eager work and synchronisation between replays, equals the eager pass bit for bit."""
+    import torch
+    wl = W.load("salt4k")
+    w = W.make_weights(wl.model, 2002)
+    ref = _run(T, wl, w)
+    s = T.System(wl, w)
+    s.rebuild()
+    s.energy_forces()  # eager call first: the library's streams exist before the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        s.energy_forces()
+    for k in range(4):
+        s.energy.zero_()
+        s.forces.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert float(s.energy.cpu()[0]) == ref["energy"], k
+        assert np.array_equal(s.forces.cpu().numpy().astype(np.float64), ref["forces"]), k
+        # eager work between replays
+        s.energy_forces(forces=False)
+        torch.cuda.synchronize()
+
+
 def test_skin_edges_contribute_nothing(T):
     """Pairs with r_c <= r < r_c+skin carry exactly zero: E and F from a skin-0 list equal
     those from the skin-1 list bit for bit (same active edges in the same order)."""
