@@ -646,7 +646,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((TRANS
     const int32_t* __restrict__ asrc, const int32_t* __restrict__ arev,
     const float* __restrict__ ew, const float4* __restrict__ es, const float* __restrict__ X,
     float rc, float* __restrict__ out, const float* __restrict__ base, float4* __restrict__ P,
-    const int32_t* __restrict__ species, const float* __restrict__ emb, int S) {
+    const int32_t* __restrict__ species, const float* __restrict__ emb, int S,
+    const float* __restrict__ base0) {
   constexpr int D = Dims<LMAX>::D;
   constexpr int DI = L0ONLY ? 1 : D;          // input components that can be non-zero
   constexpr int CQ = C / 4;                   // channel quads
@@ -892,7 +893,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((TRANS
     // lane 4bb + jj holds, for tile t and register r, channel 16 bb + 4 r + t of output
     // component 4 d + jj
     // the adjoint adds the residual path: out = base + contribution (every component of
-    // every row is written)
+    // every row is written); with base0 set, the base is base0[c] in component 0 and zero in
+    // the others (the readout's gradient, for the last layer)
     const int bb = lane >> 2;
     const int64_t ro = (int64_t)x * D * C;
 #pragma unroll
@@ -902,7 +904,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((TRANS
         const int64_t off = ro + (4 * d + jj) * C + 16 * bb + 4 * r;
         float4 v = make_float4(acc[0][d][r], acc[1][d][r], acc[2][d][r], acc[3][d][r]);
         if (TRANS) {
-          const float4 pv = *reinterpret_cast<const float4*>(base + off);
+          float4 pv = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+          if (!base0)
+            pv = *reinterpret_cast<const float4*>(base + off);
+          else if (4 * d + jj == 0)
+            pv = *reinterpret_cast<const float4*>(base0 + 16 * bb + 4 * r);
           v.x += pv.x; v.y += pv.y; v.z += pv.z; v.w += pv.w;
         }
         *reinterpret_cast<float4*>(out + off) = v;
@@ -910,7 +916,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((TRANS
     if constexpr (VC8) {
       const int64_t off = ro + 8 * C + 4 * m;
       float4 v = acc8;
-      if (TRANS) {
+      if (TRANS && !base0) {
         const float4 pv = *reinterpret_cast<const float4*>(base + off);
         v.x += pv.x; v.y += pv.y; v.z += pv.z; v.w += pv.w;
       }
@@ -1060,7 +1066,8 @@ __global__ void __launch_bounds__(256) k_energy_final(int32_t nb, const double* 
 template <int LMAX, bool MB0>
 __global__ void k_bwd_update(int32_t n, int C, const float* __restrict__ gbar,
                              const float* __restrict__ yg, const float* __restrict__ yl,
-                             float* __restrict__ xcat, float* __restrict__ ybl) {
+                             float* __restrict__ xcat, float* __restrict__ ybl,
+                             const float* __restrict__ wE) {
   constexpr int D = Dims<LMAX>::D;
   int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (k >= (int64_t)n * C) return;
@@ -1070,7 +1077,8 @@ __global__ void k_bwd_update(int32_t n, int C, const float* __restrict__ gbar,
   const float* gb = gbar + i * D * C + c;
   float y0 = yg[i * G + c];
   float sg0 = sigmoidf_(y0);
-  xcat[i * G + c] = gb[0] * sg0 * (1.0f + y0 * (1.0f - sg0));
+  // wE (last layer): dE/dh^T is the readout's w_E in component 0 (and zero elsewhere)
+  xcat[i * G + c] = (wE ? wE[c] : gb[0]) * sg0 * (1.0f + y0 * (1.0f - sg0));
   if constexpr (MB0) return;
 #pragma unroll
   for (int l = 1; l <= LMAX; l++) {
@@ -1834,17 +1842,17 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
       TESS_TIMED("edge_apply", st,
                  k_edge_contract<LMAX, C, H, true, false><<<gridn(n, 4), 256, 0, st>>>(
                      n, w.arow, w.ageo, w.asrc, w.arev, ew, es, ht, rc, mt, nullptr, Pt, species,
-                     emb, S));
+                     emb, S, nullptr));
     else if (t == T - 1)  // last layer: only m^0 is read (by the y^0 update)
       TESS_TIMED("edge_apply", st,
                  k_edge_contract<LMAX, C, H, false, false, true><<<gridn(n, 4), 256, 0, st>>>(
                      n, w.arow, w.ageo, w.asrc, w.arev, ew, es, ht, rc, mt, nullptr, Pt, species,
-                     emb, S));
+                     emb, S, nullptr));
     else
       TESS_TIMED("edge_apply", st,
                  k_edge_contract<LMAX, C, H, false, false><<<gridn(n, 4), 256, 0, st>>>(
                      n, w.arow, w.ageo, w.asrc, w.arev, ew, es, ht, rc, mt, nullptr, Pt, species,
-                     emb, S));
+                     emb, S, nullptr));
     TESS_HIP_CHECK(hipGetLastError());
     Epi eu{};
     eu.y = yg;
@@ -1892,7 +1900,9 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
   // ---------------- backward ----------------
   float* gbar = w.gbar;
   float* hbar = w.hbar;
-  k_gbar_init<<<gridn(NDC, 256), 256, 0, st>>>(n, C, D, wE, gbar);
+  // dE/dh^T: w_E in the l = 0 channels. With more than one layer, the last layer's kernels
+  // read w_E directly (only its l = 0 part is non-zero); a single layer reads the buffer.
+  if (T == 1) k_gbar_init<<<gridn(NDC, 256), 256, 0, st>>>(n, C, D, wE, gbar);
   for (int t = T - 1; t >= 0; t--) {
     const float* ht = w.h + (int64_t)t * NDC;
     const float* qk = w.qk + (int64_t)t * n * 2 * C;
@@ -1906,10 +1916,10 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     const bool mb0 = t == T - 1 && t > 0;
     if (mb0)
       k_bwd_update<LMAX, true><<<gridn((int64_t)n * C, 256), 256, 0, st>>>(n, C, gbar, yg, yl,
-                                                                         w.xcat, w.ybl);
+                                                                         w.xcat, w.ybl, wE);
     else
-      k_bwd_update<LMAX, false><<<gridn((int64_t)n * C, 256), 256, 0, st>>>(n, C, gbar, yg, yl,
-                                                                          w.xcat, w.ybl);
+      k_bwd_update<LMAX, false><<<gridn((int64_t)n * C, 256), 256, 0, st>>>(
+          n, C, gbar, yg, yl, w.xcat, w.ybl, nullptr);
     // The energy reads only the l = 0 channels of the last features, so at the last layer
     // dE/dh^(l>=1) = 0: the gate adjoints and the l >= 1 components of m_bar vanish. That layer
     // (when it is not also the first) forms only m_bar's l = 0 component and its edge kernels
@@ -1956,16 +1966,17 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     }
     TESS_HIP_CHECK(hipGetLastError());
     if (t > 0) {
-      if (mb0)  // only m_bar's l = 0 component enters the adjoint contraction
+      if (mb0)  // only m_bar's l = 0 component enters the adjoint contraction; the residual
+                // input is the readout's gradient w_E in component 0
         TESS_TIMED("edge_tapply", st,
                    k_edge_contract<LMAX, C, H, true, true><<<gridn(n, 4), 256, 0, st>>>(
-                       n, w.arow, w.ageo, w.asrc, w.arev, ew, es, w.mbar, rc, hbar, gbar, Pt,
-                       species, emb, S));
+                       n, w.arow, w.ageo, w.asrc, w.arev, ew, es, w.mbar, rc, hbar, nullptr, Pt,
+                       species, emb, S, wE));
       else
         TESS_TIMED("edge_tapply", st,
                    k_edge_contract<LMAX, C, H, false, true><<<gridn(n, 4), 256, 0, st>>>(
                        n, w.arow, w.ageo, w.asrc, w.arev, ew, es, w.mbar, rc, hbar, gbar, Pt,
-                       species, emb, S));
+                       species, emb, S, nullptr));
       k_qk_bar<C, H><<<gridn(n, 4), 256, 0, st>>>(n, w.arow, w.asrc, w.arev, w.sbar, qk,
                                                  w.qkbar);
       Epi ea{};
