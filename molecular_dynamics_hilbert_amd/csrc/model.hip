@@ -295,6 +295,10 @@ __global__ void __launch_bounds__(256) k_active_count(int32_t n, const float* __
                                                       uint32_t* __restrict__ rmin2_bits) {
   int32_t i = blockIdx.x * 4 + (threadIdx.x >> 6);
   int lane = threadIdx.x & 63;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {  // entry n of both count arrays (the scans' totals)
+    acnt[n] = 0;
+    ccnt[n] = 0;
+  }
   if (i >= n) return;
   int cnt = 0, ccn = 0;
   float mn = INFINITY;
@@ -1646,7 +1650,7 @@ static EFWS carve_ef(Carver& cv, const tess_model_desc& md, int32_t n, int64_t c
   w.sbar = cv.take<float4>(ec);
   w.l0tab = cv.take<float4>(16 * 16);
   w.epart = cv.take<double>(nn / 256 + 2);
-  w.scan_tmp = cv.take<int32_t>(nn / 4096 + 4);
+  w.scan_tmp = cv.take<int32_t>(2 * (nn / 4096 + 2));  // two arrays of n + 1 counts
   return w;
 }
 
@@ -1761,10 +1765,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     }
     k_active_count<<<gridn(n, 4), 256, 0, st>>>(n, pos, row_ptr, col_shift, box[0], box[1], box[2],
                                                 rc * rc, w.arow, w.crow, rmin2_bits);
-    k_fill_i32<<<1, 64, 0, st>>>(w.arow + n, 1, 0);
-    k_fill_i32<<<1, 64, 0, st>>>(w.crow + n, 1, 0);
-    TESS_HIP_CHECK(scan_exclusive_i32(w.arow, (int64_t)n + 1, w.scan_tmp, st));
-    TESS_HIP_CHECK(scan_exclusive_i32(w.crow, (int64_t)n + 1, w.scan_tmp, st));
+    TESS_HIP_CHECK(scan_exclusive_i32_pair(w.arow, w.crow, (int64_t)n + 1, w.scan_tmp, st));
     k_active_fill<<<gridn(n, 4), 256, 0, st>>>(n, pos, row_ptr, col_shift, box[0], box[1], box[2],
                                                rc * rc, w.arow, w.adst, w.asrc, w.aslot,
                                                w.slot2act, w.ageo, w.crow, w.canon);

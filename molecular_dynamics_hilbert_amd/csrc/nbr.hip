@@ -452,20 +452,28 @@ __device__ __forceinline__ int32_t block_exclusive_scan_256(int32_t v, int32_t* 
   return off + inc - v;
 }
 
-__global__ void __launch_bounds__(256) k_scan_partial(const int32_t* __restrict__ d, int64_t n,
+// Two arrays of the same length can be scanned by the same launches: blockIdx.y (partial,
+// final) or blockIdx.x (sums) selects the array, and its tile sums sit nb entries apart.
+struct ScanPair {
+  int32_t* d[2];
+};
+
+__global__ void __launch_bounds__(256) k_scan_partial(ScanPair sp, int64_t n,
                                                       int32_t* __restrict__ sums) {
   __shared__ int32_t sh[4];
+  const int32_t* __restrict__ d = sp.d[blockIdx.y];
   int64_t base = (int64_t)blockIdx.x * kScanTile + threadIdx.x * 16;
   int32_t s = 0;
   for (int k = 0; k < 16; k++)
     if (base + k < n) s += d[base + k];
   int32_t tot;
   block_exclusive_scan_256(s, sh, &tot);
-  if (threadIdx.x == 0) sums[blockIdx.x] = tot;
+  if (threadIdx.x == 0) sums[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = tot;
 }
 
-__global__ void __launch_bounds__(256) k_scan_sums(int32_t* __restrict__ sums, int32_t nb) {
+__global__ void __launch_bounds__(256) k_scan_sums(int32_t* __restrict__ sums_all, int32_t nb) {
   __shared__ int32_t sh[4];
+  int32_t* __restrict__ sums = sums_all + (int64_t)blockIdx.x * nb;
   int32_t carry = 0;
   for (int32_t b0 = 0; b0 < nb; b0 += 256) {
     int32_t k = b0 + threadIdx.x;
@@ -478,9 +486,10 @@ __global__ void __launch_bounds__(256) k_scan_sums(int32_t* __restrict__ sums, i
   }
 }
 
-__global__ void __launch_bounds__(256) k_scan_final(int32_t* __restrict__ d, int64_t n,
+__global__ void __launch_bounds__(256) k_scan_final(ScanPair sp, int64_t n,
                                                     const int32_t* __restrict__ sums) {
   __shared__ int32_t sh[4];
+  int32_t* __restrict__ d = sp.d[blockIdx.y];
   int64_t base = (int64_t)blockIdx.x * kScanTile + threadIdx.x * 16;
   int32_t v[16];
   int32_t s = 0;
@@ -489,7 +498,8 @@ __global__ void __launch_bounds__(256) k_scan_final(int32_t* __restrict__ d, int
     s += v[k];
   }
   int32_t tot;
-  int32_t run = block_exclusive_scan_256(s, sh, &tot) + sums[blockIdx.x];
+  int32_t run = block_exclusive_scan_256(s, sh, &tot) +
+                sums[(int64_t)blockIdx.y * gridDim.x + blockIdx.x];
   for (int k = 0; k < 16; k++) {
     if (base + k < n) d[base + k] = run;
     run += v[k];
@@ -501,11 +511,18 @@ inline int32_t grid(int64_t n, int b) { return (int32_t)((n + b - 1) / b); }
 }  // namespace
 
 hipError_t scan_exclusive_i32(int32_t* data, int64_t n, int32_t* partial, hipStream_t s) {
+  return scan_exclusive_i32_pair(data, nullptr, n, partial, s);
+}
+
+hipError_t scan_exclusive_i32_pair(int32_t* a, int32_t* b, int64_t n, int32_t* partial,
+                                   hipStream_t s) {
   int32_t nb = grid(n, kScanTile);
   if (nb == 0) return hipSuccess;
-  k_scan_partial<<<nb, 256, 0, s>>>(data, n, partial);
-  k_scan_sums<<<1, 256, 0, s>>>(partial, nb);
-  k_scan_final<<<nb, 256, 0, s>>>(data, n, partial);
+  const unsigned na = b ? 2u : 1u;
+  ScanPair sp{{a, b ? b : a}};
+  k_scan_partial<<<dim3(nb, na), 256, 0, s>>>(sp, n, partial);
+  k_scan_sums<<<na, 256, 0, s>>>(partial, nb);
+  k_scan_final<<<dim3(nb, na), 256, 0, s>>>(sp, n, partial);
   return hipGetLastError();
 }
 

@@ -233,9 +233,13 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Exclusive scan of int32 counts in place (single workgroup, any length). Host wrapper in
-// nbr.hip.
-hipError_t scan_exclusive_i32(int32_t* data, int64_t n, int32_t* total_out, hipStream_t s);
+// Exclusive scan of int32 counts in place, any length: tile sums, a scan of the tile sums,
+// then the tiles; `partial` holds ceil(n/4096) entries. Host wrappers in nbr.hip.
+hipError_t scan_exclusive_i32(int32_t* data, int64_t n, int32_t* partial, hipStream_t s);
+// Two arrays of length n scanned by the same three launches; `partial` holds 2 x ceil(n/4096)
+// entries.
+hipError_t scan_exclusive_i32_pair(int32_t* a, int32_t* b, int64_t n, int32_t* partial,
+                                   hipStream_t s);
 
 }  // namespace tess
 
