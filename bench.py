@@ -28,10 +28,9 @@ sys.path.insert(0, ROOT)
 METRIC = "atom-steps/s (E+F, 4-layer l<=2) at 60K atoms on 1 GPU; neighbor rebuild ms"
 PEAK_FP32_VECTOR_TFLOPS = 157.3  # MI355X fp32 vector, 256 CUs x 2.4 GHz (packed issue)
 PEAK_FP32_MFMA_TFLOPS = 157.3    # MI355X dense fp32 matrix cores
-# the edge contractions run their channel sums on the matrix cores; the gradient and the
-# radial MLP's activations are vector-ALU work
-BOUND = {"edge_apply": "mfma", "edge_tapply": "mfma", "edge_grad": "alu", "edge_grad_last": "alu",
-         "edge_prep": "alu"}
+# the edge contractions run their channel sums on the matrix cores; the gradients are
+# vector-ALU work
+BOUND = {"edge_apply": "mfma", "edge_tapply": "mfma", "edge_grad": "alu", "edge_grad_last": "alu"}
 PEAK_HBM_GBS = 8000.0
 
 
@@ -45,23 +44,19 @@ def edge_kernel_flops(spec, n_active: int) -> dict:
       edge_grad  : Abar^h = sum_c mbar (x) h_j -> C*D*D MAC per edge (first layer: C*D)
       edge_grad_last: the same at the last layer, one row of Abar -> C*D MAC per edge
       edge_tapply: A_e^T mbar -> C*D*D MAC per edge (layers 1..T-1; the last: C*D)
-      edge_prep  : radial MLP and its r-derivative, 2*(K*R + P*R) MAC per pair of entries
-                   (i <- j), (j <- i), which share |r|
       logits     : <q_i, k_j> -> C MAC per edge (layers after the first; the first layer's
                    come from a per-species table)"""
-    C, T, K, R = spec.channels, spec.n_layers, spec.n_rbf, spec.radial_hidden
+    C, T = spec.channels, spec.n_layers
     D = (spec.l_max + 1) ** 2
-    P = spec.n_paths
     full, one = C * D * D, C * D
     mac = {"edge_apply": 0, "edge_grad": 0, "edge_grad_last": 0, "edge_tapply": 0,
-           "edge_prep": 0, "logits": 0}
+           "logits": 0}
     for t in range(T):
         first, last = t == 0, t == T - 1 and t > 0
         mac["edge_apply"] += one if (first or last) else full
         mac["edge_grad_last" if last else "edge_grad"] += one if (first or last) else full
         if t > 0:
             mac["edge_tapply"] += one if last else full
-        mac["edge_prep"] += K * R + P * R  # 2*(K*R + P*R) per pair = per two edges
         mac["logits"] += 0 if first else C
     return {k: 2.0 * n_active * v for k, v in mac.items()}
 
@@ -167,7 +162,7 @@ def run(args):
     md(max(args.warmup, 1), False, args.graph)
     torch.cuda.synchronize()
     skin_flags[0] = 0
-    names = ("edge_prep", "logits", "edge_apply", "edge_grad", "edge_grad_last", "edge_tapply",
+    names = ("edge_radial", "logits", "edge_apply", "edge_grad", "edge_grad_last", "edge_tapply",
              "node_gemm", "radix_scatter", "nbr_count", "nbr_fill")
     # profile pass (same length): HIP events around every instrumented kernel, giving the
     # per-kernel times and the dominant edge kernel
@@ -176,7 +171,7 @@ def run(args):
     torch.cuda.synchronize()
     kern = {k: T.timing_read(k) for k in names}
     T.timing_enable(False)
-    dom = max(("edge_apply", "edge_grad", "edge_grad_last", "edge_tapply", "edge_prep"),
+    dom = max(("edge_apply", "edge_grad", "edge_grad_last", "edge_tapply"),
               key=lambda k: kern[k][0])
     skin_flags[0] = 0
     # timed region: exactly `steps` MD steps, inputs resident in HBM. Only the dominant kernel

@@ -188,7 +188,7 @@ int32_t tess_set_curve(int32_t curve);
 
 /* Optional kernel timing for benchmarks (not part of the method). tess_timing_enable(1)
  * clears the counters and, until tess_timing_enable(0), records a pair of HIP events on the
- * launching stream around each launch of the instrumented kernels ("edge_prep", "logits",
+ * launching stream around each launch of the instrumented kernels ("edge_radial", "logits",
  * "edge_apply", "edge_grad", "edge_grad_last", "edge_tapply", "node_gemm", "radix_scatter",
  * "nbr_count", "nbr_fill"). tess_timing_read waits for those events and returns the summed
  * milliseconds and the launch count of one kernel. Host memory only; not thread-safe across
