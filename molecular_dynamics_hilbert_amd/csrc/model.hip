@@ -462,66 +462,93 @@ __global__ void __launch_bounds__(256) k_radial_table(const float* __restrict__ 
   }
 }
 
-// Radial weights w and dw/dr of every layer for each active edge from the table, written at
-// [layer][path][edge] (path-major, row stride ews); with l0tab, also the first layer's logits
-// from the species table. The
-// distances are random, so the table is read from LDS: persistent blocks (one per CU) take
-// contiguous edge ranges, stage one layer's table (98 KB) at a time and interpolate every
-// edge of their range from it (the per-edge reads are scattered over the table; from global
-// memory each would touch its own cache lines).
+// Radial weights w and dw/dr of layers t_begin..t_end-1 for each active edge from the table, written at
+// [layer][path][edge] (path-major rows of ews floats, ews a multiple of 64); with l0tab, also
+// the first layer's logits from the species table. The distances are random, so the table is
+// read from LDS: persistent blocks (one per CU) take contiguous ranges of whole groups of 4
+// edges, stage one layer's table (98 KB) at a time and interpolate every edge of their range
+// from it. A thread takes 4 consecutive edges at a time, so each output row gets one 16-byte
+// store per thread (a wave writes 1 KB of a row); slots past the active count in the last
+// group get the value at r = 0 (never read).
 constexpr int kRadThreads = 1024;
 constexpr int kRadBlocks = 256;  // one per compute unit (the table fills most of a CU's LDS)
 __global__ void __launch_bounds__(kRadThreads) k_edge_radial(
     const int32_t* __restrict__ arow_n, const float4* __restrict__ ageo,
-    const float* __restrict__ rtab, int T, int np, float rc, float* __restrict__ ew,
+    const float* __restrict__ rtab, int t_begin, int t_end, int np, float rc, float* __restrict__ ew,
     float* __restrict__ edw, int64_t lstride, int64_t ews, int64_t cap,
-    const int32_t* __restrict__ adst,
-    const int32_t* __restrict__ asrc, const int32_t* __restrict__ species,
-    const float4* __restrict__ l0tab, int S, float4* __restrict__ es) {
+    const int32_t* __restrict__ adst, const int32_t* __restrict__ asrc,
+    const int32_t* __restrict__ species, const float4* __restrict__ l0tab, int S,
+    float4* __restrict__ es) {
   __shared__ float4 stab[(kRadKnots + 1) * 6];
   const int64_t n_act = min((int64_t)*arow_n, cap);
-  const int64_t per = (n_act + gridDim.x - 1) / gridDim.x;
-  const int64_t a0 = (int64_t)blockIdx.x * per, a1 = min(a0 + per, n_act);
+  const int64_t ngr = (n_act + 3) / 4;  // groups of 4 edges
+  const int64_t per = (ngr + gridDim.x - 1) / gridDim.x;
+  const int64_t g0 = (int64_t)blockIdx.x * per, g1 = min(g0 + per, ngr);
   const float hk = rc / (float)kRadKnots, ih = (float)kRadKnots / rc;
-  for (int t = 0; t < T; t++) {
-    if (t > 0) __syncthreads();
+  for (int t = t_begin; t < t_end; t++) {
+    if (t > t_begin) __syncthreads();
     const float4* src = reinterpret_cast<const float4*>(rtab + (int64_t)t * (kRadKnots + 1) * 24);
     for (int k = threadIdx.x; k < (kRadKnots + 1) * 6; k += kRadThreads) stab[k] = src[k];
     __syncthreads();
-    for (int64_t a = a0 + threadIdx.x; a < a1; a += kRadThreads) {
-      const float x = ageo[a].w * ih;
-      const int i = min(max((int)x, 0), kRadKnots - 1);
-      const float tt = x - (float)i, t2 = tt * tt, t3 = t2 * tt;
-      // cubic Hermite basis on [r_i, r_i + h] and its r-derivative
-      const float h00 = 2.0f * t3 - 3.0f * t2 + 1.0f, h10 = (t3 - 2.0f * t2 + tt) * hk;
-      const float h01 = 3.0f * t2 - 2.0f * t3, h11 = (t3 - t2) * hk;
-      const float d00 = 6.0f * (t2 - tt) * ih, d10 = 3.0f * t2 - 4.0f * tt + 1.0f;
-      const float d01 = -d00, d11 = 3.0f * t2 - 2.0f * tt;
-      const float4* k0 = stab + i * 6;
-      const float4* k1 = k0 + 6;
+    for (int64_t g = g0 + threadIdx.x; g < g1; g += kRadThreads) {
+      const int64_t a = 4 * g;
+      // cubic Hermite basis on [r_i, r_i + h] of each of the 4 edges, and its r-derivative
+      float hb[4][8];
+      int ib[4];
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const float r = a + e < n_act ? ageo[a + e].w : 0.0f;
+        const float x = r * ih;
+        const int i = min(max((int)x, 0), kRadKnots - 1);
+        const float tt = x - (float)i, t2 = tt * tt, t3 = t2 * tt;
+        ib[e] = i;
+        hb[e][0] = 2.0f * t3 - 3.0f * t2 + 1.0f;
+        hb[e][1] = (t3 - 2.0f * t2 + tt) * hk;
+        hb[e][2] = 3.0f * t2 - 2.0f * t3;
+        hb[e][3] = (t3 - t2) * hk;
+        hb[e][4] = 6.0f * (t2 - tt) * ih;
+        hb[e][5] = 3.0f * t2 - 4.0f * tt + 1.0f;
+        hb[e][6] = -hb[e][4];
+        hb[e][7] = 3.0f * t2 - 2.0f * tt;
+      }
+      // paths in groups of 4: one 16-byte store per output row per thread
 #pragma unroll
       for (int q = 0; q < 3; q++) {
-        const float4 w0 = k0[q], g0 = k0[3 + q], w1 = k1[q], g1 = k1[3 + q];
-        const float wv[4] = {h00 * w0.x + h10 * g0.x + h01 * w1.x + h11 * g1.x,
-                             h00 * w0.y + h10 * g0.y + h01 * w1.y + h11 * g1.y,
-                             h00 * w0.z + h10 * g0.z + h01 * w1.z + h11 * g1.z,
-                             h00 * w0.w + h10 * g0.w + h01 * w1.w + h11 * g1.w};
-        const float dv[4] = {d00 * w0.x + d10 * g0.x + d01 * w1.x + d11 * g1.x,
-                             d00 * w0.y + d10 * g0.y + d01 * w1.y + d11 * g1.y,
-                             d00 * w0.z + d10 * g0.z + d01 * w1.z + d11 * g1.z,
-                             d00 * w0.w + d10 * g0.w + d01 * w1.w + d11 * g1.w};
-        // path-major rows: consecutive edges of a wave write consecutive words
+        float wv[4][4], dv[4][4];
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-          if (4 * q + e < np) {
-            ew[t * lstride + (int64_t)(4 * q + e) * ews + a] = wv[e];
-            edw[t * lstride + (int64_t)(4 * q + e) * ews + a] = dv[e];
+          const float4* k0 = stab + ib[e] * 6;
+          const float4 w0 = k0[q], g0v = k0[3 + q], w1 = k0[6 + q], g1v = k0[9 + q];
+          const float* h = hb[e];
+          wv[e][0] = h[0] * w0.x + h[1] * g0v.x + h[2] * w1.x + h[3] * g1v.x;
+          wv[e][1] = h[0] * w0.y + h[1] * g0v.y + h[2] * w1.y + h[3] * g1v.y;
+          wv[e][2] = h[0] * w0.z + h[1] * g0v.z + h[2] * w1.z + h[3] * g1v.z;
+          wv[e][3] = h[0] * w0.w + h[1] * g0v.w + h[2] * w1.w + h[3] * g1v.w;
+          dv[e][0] = h[4] * w0.x + h[5] * g0v.x + h[6] * w1.x + h[7] * g1v.x;
+          dv[e][1] = h[4] * w0.y + h[5] * g0v.y + h[6] * w1.y + h[7] * g1v.y;
+          dv[e][2] = h[4] * w0.z + h[5] * g0v.z + h[6] * w1.z + h[7] * g1v.z;
+          dv[e][3] = h[4] * w0.w + h[5] * g0v.w + h[6] * w1.w + h[7] * g1v.w;
+        }
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+          const int p = 4 * q + c;
+          if (p < np) {
+            *reinterpret_cast<float4*>(ew + t * lstride + p * ews + a) =
+                make_float4(wv[0][c], wv[1][c], wv[2][c], wv[3][c]);
+            *reinterpret_cast<float4*>(edw + t * lstride + p * ews + a) =
+                make_float4(dv[0][c], dv[1][c], dv[2][c], dv[3][c]);
           }
         }
       }
       if (t == 0 && l0tab) {
-        const int si = sp_index(species[adst[a]], S), sj = sp_index(species[asrc[a]], S);
-        es[a] = l0tab[si * S + sj];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          if (a + e < n_act) {
+            const int si = sp_index(species[adst[a + e]], S);
+            const int sj = sp_index(species[asrc[a + e]], S);
+            es[a + e] = l0tab[si * S + sj];
+          }
+        }
       }
     }
   }
@@ -1612,6 +1639,9 @@ struct EFWS {
   int32_t* scan_tmp;
 };
 
+// Row stride of the path-major radial-weight arrays: the edge capacity rounded up to 64.
+inline int64_t ews_of(int64_t ecap) { return (ecap + 63) & ~int64_t(63); }
+
 static EFWS carve_ef(Carver& cv, const tess_model_desc& md, int32_t n, int64_t cap) {
   EFWS w{};
   const int64_t C = md.channels, Lm = md.l_max, T = md.n_layers, H = md.n_heads;
@@ -1633,8 +1663,8 @@ static EFWS carve_ef(Carver& cv, const tess_model_desc& md, int32_t n, int64_t c
   w.arev = cv.take<int32_t>(ec);
   w.rev_own = cv.take<int32_t>(ec);
   w.ageo = cv.take<float4>(ec);
-  w.ew = cv.take<float>(T * ec * 12);
-  w.edw = cv.take<float>(T * ec * 12);
+  w.ew = cv.take<float>(T * ews_of(ec) * 12);
+  w.edw = cv.take<float>(T * ews_of(ec) * 12);
   w.es = cv.take<float4>(T * ec);
   w.P = cv.take<float4>(T * ec);
   w.gbar = cv.take<float>(nn * D * C);
@@ -1665,20 +1695,18 @@ struct LayerW {
   const float *Wq, *Wk, *W1, *W2, *W0, *Wl[3];
 };
 
-// Two more streams per host thread and device for kernels of the pass that do not depend on
-// the work next to them: (1) the radial MLPs of layers 1..T-1 need only the geometry and run
-// next to the first layer; (2) layer t+1's q|k GEMM and logits need only the l = 0 features
-// that layer t's first update GEMM writes, and run next to that layer's l >= 1 updates; in the
-// backward, the l = 0 block of m_bar runs next to the l >= 1 blocks. The streams fork from
-// and join the caller's stream through events, so the caller sees one stream-ordered pass
-// and the fork/join become graph edges under stream capture. Created on first use; if they
-// cannot be created (or the first call comes under capture), every kernel runs on the caller's
-// stream in the same order.
-constexpr int kAuxEvents = 20;  // 0: fork, 1..15: radial MLP of layer t done, 16..19 below
-constexpr int kEvFwdFork = 16, kEvFwdJoin = 17, kEvBwdFork = 18, kEvBwdJoin = 19;
+// A second stream per host thread and device for kernels of the pass that do not depend on
+// the work next to them: layer t+1's q|k GEMM and logits need only the l = 0 features that
+// layer t's first update GEMM writes, and run next to that layer's l >= 1 updates; in the
+// backward, the l = 0 block of m_bar runs next to the l >= 1 blocks. The stream forks from
+// and joins the caller's stream through events, so the caller sees one stream-ordered pass
+// and the fork/join become graph edges under stream capture. Created on first use; if it
+// cannot be created (or the first call comes under capture), every kernel runs on the
+// caller's stream in the same order.
+constexpr int kEvFwdFork = 0, kEvFwdJoin = 1, kEvBwdFork = 2, kEvBwdJoin = 3, kAuxEvents = 4;
 struct AuxStream {
   bool tried = false, ok = false;
-  hipStream_t s = nullptr, s2 = nullptr;
+  hipStream_t s = nullptr;
   hipEvent_t ev[kAuxEvents] = {};
 };
 AuxStream* aux_stream(hipStream_t st) {
@@ -1691,8 +1719,8 @@ AuxStream* aux_stream(hipStream_t st) {
   }
   AuxStream& x = a[dev];
   if (!x.tried) {
-    // streams are created outside any stream capture (a capture in progress runs the pass on
-    // the caller's stream alone; a later call outside capture creates them)
+    // the stream is created outside any stream capture (a capture in progress runs the pass
+    // on the caller's stream alone; a later call outside capture creates it)
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(st, &cs) != hipSuccess) {
       (void)hipGetLastError();
@@ -1700,8 +1728,7 @@ AuxStream* aux_stream(hipStream_t st) {
     }
     if (cs != hipStreamCaptureStatusNone) return nullptr;
     x.tried = true;
-    bool ok = hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking) == hipSuccess &&
-              hipStreamCreateWithFlags(&x.s2, hipStreamNonBlocking) == hipSuccess;
+    bool ok = hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking) == hipSuccess;
     for (int k = 0; k < kAuxEvents && ok; k++)
       ok = hipEventCreateWithFlags(&x.ev[k], hipEventDisableTiming) == hipSuccess;
     x.ok = ok;
@@ -1728,6 +1755,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
   const int T = md.n_layers, S = md.n_species, K = md.n_rbf;
   const float rc = md.r_cut;
   const int64_t cap = n_edges > 0 ? n_edges : 0;  // threads per edge kernel
+  const int64_t ews = ews_of(ecap > 0 ? ecap : 1);  // row stride of the radial-weight arrays
   // ecap: edge capacity the workspace was laid out for (strides of per-layer edge arrays)
   // weight offsets in the blob
   std::vector<LayerW> lw(T);
@@ -1778,7 +1806,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
   }
   const RowMap feat0{(int64_t)D * C, C, 0, 1};
   AuxStream* ax = aux_stream(st);
-  const hipStream_t sb = ax ? ax->s2 : st;
+  const hipStream_t sb = ax ? ax->s : st;
   // q|k GEMM and logits of layer t (t >= 1) on stream `qs`
   auto qk_logits = [&](int t, hipStream_t qs) -> int32_t {
     Epi e0{};
@@ -1800,8 +1828,8 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
   if (cap > 0)
     TESS_TIMED("edge_radial", st,
                k_edge_radial<<<kRadBlocks, kRadThreads, 0, st>>>(
-                   w.arow + n, w.ageo, w.rtab, T, P, rc, w.ew, w.edw, ecap * 12, ecap, cap, w.adst,
-                   w.asrc, species, w.l0tab, S, w.es));
+                   w.arow + n, w.ageo, w.rtab, 0, T, P, rc, w.ew, w.edw, ews * 12, ews, cap,
+                   w.adst, w.asrc, species, w.l0tab, S, w.es));
   TESS_HIP_CHECK(hipGetLastError());
   // ---------------- forward ----------------
   for (int t = 0; t < T; t++) {
@@ -1811,8 +1839,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     float* mt = w.m + (int64_t)t * NDC;
     float* yg = w.yg + (int64_t)t * n * G;
     float* yl = w.yl + (int64_t)t * NDC;
-    float* ew = w.ew + (int64_t)t * ecap * 12;
-    float* edw = w.edw + (int64_t)t * ecap * 12;
+    float* ew = w.ew + (int64_t)t * ews * 12;
     float4* es = w.es + (int64_t)t * ecap;
     if (t > 0) {
       if (ax) {
@@ -1828,17 +1855,17 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
       TESS_TIMED("edge_apply", st,
                  k_edge_contract<LMAX, C, H, true, false><<<gridn(n, 4), 256, 0, st>>>(
                      n, w.arow, w.ageo, w.asrc, w.arev, ew, es, ht, rc, mt, nullptr, Pt, species,
-                     emb, S, nullptr, ecap));
+                     emb, S, nullptr, ews));
     else if (t == T - 1)  // last layer: only m^0 is read (by the y^0 update)
       TESS_TIMED("edge_apply", st,
                  k_edge_contract<LMAX, C, H, false, false, true><<<gridn(n, 4), 256, 0, st>>>(
                      n, w.arow, w.ageo, w.asrc, w.arev, ew, es, ht, rc, mt, nullptr, Pt, species,
-                     emb, S, nullptr, ecap));
+                     emb, S, nullptr, ews));
     else
       TESS_TIMED("edge_apply", st,
                  k_edge_contract<LMAX, C, H, false, false><<<gridn(n, 4), 256, 0, st>>>(
                      n, w.arow, w.ageo, w.asrc, w.arev, ew, es, ht, rc, mt, nullptr, Pt, species,
-                     emb, S, nullptr, ecap));
+                     emb, S, nullptr, ews));
     TESS_HIP_CHECK(hipGetLastError());
     Epi eu{};
     eu.y = yg;
@@ -1896,8 +1923,8 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     const float* mt = w.m + (int64_t)t * NDC;
     const float* yg = w.yg + (int64_t)t * n * G;
     const float* yl = w.yl + (int64_t)t * NDC;
-    const float* ew = w.ew + (int64_t)t * ecap * 12;
-    const float* edw = w.edw + (int64_t)t * ecap * 12;
+    const float* ew = w.ew + (int64_t)t * ews * 12;
+    const float* edw = w.edw + (int64_t)t * ews * 12;
     const float4* es = w.es + (int64_t)t * ecap;
     const bool mb0 = t == T - 1 && t > 0;
     if (mb0)
@@ -1938,17 +1965,17 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
         TESS_TIMED("edge_grad", st,
                    k_edge_grad<LMAX, C, H, true><<<gb, 256, 0, st>>>(
                        w.arow + n, w.ageo, w.adst, w.asrc, ew, edw, Pt, w.Dst, w.mbar, ht, rc,
-                       w.sbar, w.gacc, t != T - 1, cap, ecap, species, emb, S));
+                       w.sbar, w.gacc, t != T - 1, cap, ews, species, emb, S));
       else if (mb0)
         TESS_TIMED("edge_grad_last", st,
                    k_edge_grad_last<LMAX, C, H><<<gb, 256, 0, st>>>(
                        w.arow + n, w.ageo, w.adst, w.asrc, w.arev, ew, edw, Pt, w.Dst, w.mbar, ht,
-                       rc, w.sbar, w.gacc, t != T - 1, cap, ecap));
+                       rc, w.sbar, w.gacc, t != T - 1, cap, ews));
       else
         TESS_TIMED("edge_grad", st,
                    k_edge_grad<LMAX, C, H, false><<<gb, 256, 0, st>>>(
                        w.arow + n, w.ageo, w.adst, w.asrc, ew, edw, Pt, w.Dst, w.mbar, ht, rc,
-                       w.sbar, w.gacc, t != T - 1, cap, ecap, species, emb, S));
+                       w.sbar, w.gacc, t != T - 1, cap, ews, species, emb, S));
     }
     TESS_HIP_CHECK(hipGetLastError());
     if (t > 0) {
@@ -1957,12 +1984,12 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
         TESS_TIMED("edge_tapply", st,
                    k_edge_contract<LMAX, C, H, true, true><<<gridn(n, 4), 256, 0, st>>>(
                        n, w.arow, w.ageo, w.asrc, w.arev, ew, es, w.mbar, rc, hbar, nullptr, Pt,
-                       species, emb, S, wE, ecap));
+                       species, emb, S, wE, ews));
       else
         TESS_TIMED("edge_tapply", st,
                    k_edge_contract<LMAX, C, H, false, true><<<gridn(n, 4), 256, 0, st>>>(
                        n, w.arow, w.ageo, w.asrc, w.arev, ew, es, w.mbar, rc, hbar, gbar, Pt,
-                       species, emb, S, nullptr, ecap));
+                       species, emb, S, nullptr, ews));
       k_qk_bar<C, H><<<gridn(n, 4), 256, 0, st>>>(n, w.arow, w.asrc, w.arev, w.sbar, qk,
                                                  w.qkbar);
       Epi ea{};
