@@ -6,17 +6,19 @@
 // Data layout in HBM (fp32): node features [N][D][C] (component-major per node, channels
 // contiguous, so a wave reading one component of one node reads 4C contiguous bytes);
 // q|k per node [N][2C]; per active edge (r < r_cut, destination-major) geometry float4
-// (r_vec, |r|), radial weights w[12], dw/dr[12] and logits s[4] per layer.
+// (r_vec, |r|) and, per layer, path-major rows of radial weights w_p and dw_p/dr, and logits
+// s[4].
 //
-// Kernels per layer (forward): MFMA GEMM q|k; edge_prep (one thread per edge: Bessel basis,
-// radial MLP and its r-derivative, logits); edge contraction (one wave per destination row:
-// softmax statistics, coupling matrices A_e into LDS, then alpha * A_e h_j summed over the
-// row's edges on 4x4x1 MFMA blocks); MFMA GEMMs of the gated residual update with fused
-// epilogues. Backward: elementwise update adjoint + MFMA GEMMs; edge_grad (one lane per edge
-// and head: per-head sum over channels of mbar_i (x) h_j contracted through the coupling
-// adjoint, giving the logit adjoint and dE/dr_vec); the transposed edge contraction (one wave
-// per row: h_bar via A^T, k_bar, q_bar); MFMA GEMM for the q/k projections; force assembly
-// through the reverse-edge index.
+// Once per pass: the radial MLP of every layer tabulated over r (fp64 knots) and interpolated
+// for every active edge (cubic Hermite, C^1). Kernels per layer (forward): MFMA GEMM q|k and
+// the logits kernel; edge contraction (one wave per destination row: softmax statistics,
+// coupling matrices A_e into LDS, then alpha * A_e h_j summed over the row's edges on 4x4x1
+// MFMA blocks); MFMA GEMMs of the gated residual update with fused epilogues. Backward:
+// elementwise update adjoint + MFMA GEMMs; edge_grad (one lane per edge and head: per-head
+// sum over channels of mbar_i (x) h_j contracted through the coupling adjoint, giving the
+// logit adjoint and dE/dr_vec); the transposed edge contraction (one wave per row: h_bar via
+// A^T); the q/k adjoints (k_qk_bar) and their MFMA GEMM; force assembly through the
+// reverse-edge index.
 #include "tess_common.h"
 
 #include <vector>
