@@ -1698,14 +1698,16 @@ struct LayerW {
 };
 
 // A second stream per host thread and device for kernels of the pass that do not depend on
-// the work next to them: layer t+1's q|k GEMM and logits need only the l = 0 features that
+// the work next to them: the radial-weight table needs only the weights and is built next to
+// the active-edge list; layer t+1's q|k GEMM and logits need only the l = 0 features that
 // layer t's first update GEMM writes, and run next to that layer's l >= 1 updates; in the
 // backward, the l = 0 block of m_bar runs next to the l >= 1 blocks. The stream forks from
 // and joins the caller's stream through events, so the caller sees one stream-ordered pass
 // and the fork/join become graph edges under stream capture. Created on first use; if it
 // cannot be created (or the first call comes under capture), every kernel runs on the
 // caller's stream in the same order.
-constexpr int kEvFwdFork = 0, kEvFwdJoin = 1, kEvBwdFork = 2, kEvBwdJoin = 3, kAuxEvents = 4;
+constexpr int kEvFwdFork = 0, kEvFwdJoin = 1, kEvBwdFork = 2, kEvBwdJoin = 3, kEvTabFork = 4,
+              kEvTabDone = 5, kAuxEvents = 6;
 struct AuxStream {
   bool tried = false, ok = false;
   hipStream_t s = nullptr;
@@ -1780,10 +1782,16 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     k_prep_weights<LMAX, C, R><<<dim3(gridn(NEL, 256), T), 256, 0, st>>>(weights, S, K, w.WqkT,
                                                                          w.W0T, w.WlT);
   }
-  // radial-weight table of every layer
-  k_radial_table<P><<<dim3(gridn(kRadKnots + 1, 256), T), 256, 0, st>>>(
+  // The library's second stream (see aux_stream).
+  AuxStream* ax = aux_stream(st);
+  const hipStream_t sb = ax ? ax->s : st;
+  // radial-weight table of every layer: it depends on the weights only and runs on the second
+  // stream next to the active-edge list (joined before the interpolation)
+  if (ax) TESS_HIP_CHECK(stream_after(ax, kEvTabFork, st, sb));
+  k_radial_table<P><<<dim3(gridn(kRadKnots + 1, 256), T), 256, 0, sb>>>(
       lw[0].W1, (int64_t)(2 * C * C + R * K + P * R + G * C + LMAX * C * C), R, rc, w.rtab);
   TESS_HIP_CHECK(hipGetLastError());
+  if (ax) TESS_HIP_CHECK(hipEventRecord(ax->ev[kEvTabDone], sb));
   const int64_t NDC = (int64_t)n * D * C;
   // embedding
   k_embed<<<gridn((int64_t)n * C, 256), 256, 0, st>>>(n, C, D, S, species, emb, w.h);
@@ -1807,8 +1815,6 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     k_fill_i32<<<gridn((int64_t)n + 1, 256), 256, 0, st>>>(w.arow, (int64_t)n + 1, 0);
   }
   const RowMap feat0{(int64_t)D * C, C, 0, 1};
-  AuxStream* ax = aux_stream(st);
-  const hipStream_t sb = ax ? ax->s : st;
   // q|k GEMM and logits of layer t (t >= 1) on stream `qs`
   auto qk_logits = [&](int t, hipStream_t qs) -> int32_t {
     Epi e0{};
@@ -1827,6 +1833,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
   // anywhere else: the backward stops before dE/dh^0); then the radial weights of every layer
   // and the first layer's logits for each active edge
   k_l0_logits<C, H><<<1, 256, 0, st>>>(S, emb, lw[0].Wq, lw[0].Wk, w.l0tab);
+  if (ax) TESS_HIP_CHECK(hipStreamWaitEvent(st, ax->ev[kEvTabDone], 0));
   if (cap > 0)
     TESS_TIMED("edge_radial", st,
                k_edge_radial<<<kRadBlocks, kRadThreads, 0, st>>>(
