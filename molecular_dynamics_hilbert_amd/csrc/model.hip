@@ -326,7 +326,8 @@ __global__ void __launch_bounds__(256) k_active_fill(int32_t n, const float* __r
                                                      int32_t* __restrict__ asrc,
                                                      int32_t* __restrict__ aslot,
                                                      int32_t* __restrict__ slot2act,
-                                                     float4* __restrict__ ageo) {
+                                                     float4* __restrict__ ageo,
+                                                     float* __restrict__ ar) {
   int32_t i = blockIdx.x * 4 + (threadIdx.x >> 6);
   int lane = threadIdx.x & 63;
   if (i >= n) return;
@@ -348,7 +349,9 @@ __global__ void __launch_bounds__(256) k_active_fill(int32_t n, const float* __r
       adst[a] = i;
       asrc[a] = j;
       aslot[a] = e;
-      ageo[a] = make_float4(r.x, r.y, r.z, sqrtf(r.w));
+      const float rr = sqrtf(r.w);
+      ageo[a] = make_float4(r.x, r.y, r.z, rr);
+      ar[a] = rr;
       slot2act[e] = a;
     } else if (ok) {
       slot2act[e] = -1;
@@ -474,9 +477,10 @@ __global__ void __launch_bounds__(256) k_radial_table(const float* __restrict__ 
 // group get the value at r = 0 (never read).
 constexpr int kRadThreads = 1024;
 constexpr int kRadBlocks = 256;  // one per compute unit (the table fills most of a CU's LDS)
+template <int NP>
 __global__ void __launch_bounds__(kRadThreads) k_edge_radial(
-    const int32_t* __restrict__ arow_n, const float4* __restrict__ ageo,
-    const float* __restrict__ rtab, int t_begin, int t_end, int np, float rc, float* __restrict__ ew,
+    const int32_t* __restrict__ arow_n, const float* __restrict__ ar,
+    const float* __restrict__ rtab, int t_begin, int t_end, float rc, float* __restrict__ ew,
     float* __restrict__ edw, int64_t lstride, int64_t ews, int64_t cap,
     const int32_t* __restrict__ adst, const int32_t* __restrict__ asrc,
     const int32_t* __restrict__ species, const float4* __restrict__ l0tab, int S,
@@ -492,14 +496,20 @@ __global__ void __launch_bounds__(kRadThreads) k_edge_radial(
     const float4* src = reinterpret_cast<const float4*>(rtab + (int64_t)t * (kRadKnots + 1) * 24);
     for (int k = threadIdx.x; k < (kRadKnots + 1) * 6; k += kRadThreads) stab[k] = src[k];
     __syncthreads();
-    for (int64_t g = g0 + threadIdx.x; g < g1; g += kRadThreads) {
+    // |r| of the thread's next group of 4 edges is requested before the current one is used
+    int64_t g = g0 + threadIdx.x;
+    float4 rn = g < g1 ? *reinterpret_cast<const float4*>(ar + 4 * g) : make_float4(0, 0, 0, 0);
+    for (; g < g1; g += kRadThreads) {
       const int64_t a = 4 * g;
+      const float4 r4 = rn;
+      if (g + kRadThreads < g1) rn = *reinterpret_cast<const float4*>(ar + 4 * (g + kRadThreads));
+      const float rv[4] = {r4.x, r4.y, r4.z, r4.w};
       // cubic Hermite basis on [r_i, r_i + h] of each of the 4 edges, and its r-derivative
       float hb[4][8];
       int ib[4];
 #pragma unroll
       for (int e = 0; e < 4; e++) {
-        const float r = a + e < n_act ? ageo[a + e].w : 0.0f;
+        const float r = a + e < n_act ? rv[e] : 0.0f;
         const float x = r * ih;
         const int i = min(max((int)x, 0), kRadKnots - 1);
         const float tt = x - (float)i, t2 = tt * tt, t3 = t2 * tt;
@@ -514,8 +524,10 @@ __global__ void __launch_bounds__(kRadThreads) k_edge_radial(
         hb[e][7] = 3.0f * t2 - 2.0f * tt;
       }
       // paths in groups of 4: one 16-byte store per output row per thread
+      float* pw = ew + t * lstride + a;
+      float* pd = edw + t * lstride + a;
 #pragma unroll
-      for (int q = 0; q < 3; q++) {
+      for (int q = 0; q < (NP + 3) / 4; q++) {
         float wv[4][4], dv[4][4];
 #pragma unroll
         for (int e = 0; e < 4; e++) {
@@ -533,12 +545,11 @@ __global__ void __launch_bounds__(kRadThreads) k_edge_radial(
         }
 #pragma unroll
         for (int c = 0; c < 4; c++) {
-          const int p = 4 * q + c;
-          if (p < np) {
-            *reinterpret_cast<float4*>(ew + t * lstride + p * ews + a) =
-                make_float4(wv[0][c], wv[1][c], wv[2][c], wv[3][c]);
-            *reinterpret_cast<float4*>(edw + t * lstride + p * ews + a) =
-                make_float4(dv[0][c], dv[1][c], dv[2][c], dv[3][c]);
+          if (4 * q + c < NP) {
+            *reinterpret_cast<float4*>(pw) = make_float4(wv[0][c], wv[1][c], wv[2][c], wv[3][c]);
+            *reinterpret_cast<float4*>(pd) = make_float4(dv[0][c], dv[1][c], dv[2][c], dv[3][c]);
+            pw += ews;
+            pd += ews;
           }
         }
       }
@@ -1630,6 +1641,7 @@ struct EFWS {
   float *h, *qk, *m, *yg, *yl;
   int32_t *arow, *adst, *asrc, *aslot, *slot2act, *arev, *rev_own;
   float4* ageo;
+  float* ar;  // |r| of each active edge (a copy of ageo's w, read 4 edges per 16-byte load)
   float *ew, *edw;
   float4* es;
   float4* P;  // per layer and active edge: softmax probability of each head
@@ -1665,6 +1677,7 @@ static EFWS carve_ef(Carver& cv, const tess_model_desc& md, int32_t n, int64_t c
   w.arev = cv.take<int32_t>(ec);
   w.rev_own = cv.take<int32_t>(ec);
   w.ageo = cv.take<float4>(ec);
+  w.ar = cv.take<float>(ews_of(ec));
   w.ew = cv.take<float>(T * ews_of(ec) * 12);
   w.edw = cv.take<float>(T * ews_of(ec) * 12);
   w.es = cv.take<float4>(T * ec);
@@ -1808,7 +1821,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     TESS_HIP_CHECK(scan_exclusive_i32(w.arow, (int64_t)n + 1, w.scan_tmp, st));
     k_active_fill<<<gridn(n, 4), 256, 0, st>>>(n, pos, row_ptr, col_shift, box[0], box[1], box[2],
                                                rc * rc, w.arow, w.adst, w.asrc, w.aslot,
-                                               w.slot2act, w.ageo);
+                                               w.slot2act, w.ageo, w.ar);
     k_active_rev<<<gridn(cap, 256), 256, 0, st>>>(w.arow + n, w.aslot, rev, w.slot2act, w.arev, cap);
     TESS_HIP_CHECK(hipGetLastError());
   } else {
@@ -1836,8 +1849,8 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
   if (ax) TESS_HIP_CHECK(hipStreamWaitEvent(st, ax->ev[kEvTabDone], 0));
   if (cap > 0)
     TESS_TIMED("edge_radial", st,
-               k_edge_radial<<<kRadBlocks, kRadThreads, 0, st>>>(
-                   w.arow + n, w.ageo, w.rtab, 0, T, P, rc, w.ew, w.edw, ews * 12, ews, cap,
+               k_edge_radial<P><<<kRadBlocks, kRadThreads, 0, st>>>(
+                   w.arow + n, w.ar, w.rtab, 0, T, rc, w.ew, w.edw, ews * 12, ews, cap,
                    w.adst, w.asrc, species, w.l0tab, S, w.es));
   TESS_HIP_CHECK(hipGetLastError());
   // ---------------- forward ----------------
