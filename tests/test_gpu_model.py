@@ -62,6 +62,23 @@ def test_energy_forces_full_oracle(T, oracle_mod, wname):
     assert abs(g["e_atom"].sum() - g["energy"]) <= 1e-6 * abs(g["energy"])
 
 
+def test_energy_forces_dense_rows(T, oracle_mod):
+    """2,000 atoms at 0.25 atoms/A^3 (box 20 A) with the 4-layer 64-channel model: about 200
+    neighbours within r_c and 320 candidates per atom, so every row spans several chunks of
+    the contractions (32 / 28 edges), several 128-edge stagings of the logit and q/k-adjoint
+    kernels, and rows longer than a wave; full comparison with the oracle."""
+    wl = W.salt_box(2000, 1007, W.big_model(), "dense2k", box_edge=20.0)
+    w = W.make_weights(wl.model, 2003)
+    g = _run(T, wl, w)
+    rp = g["sys"].row_ptr.cpu().numpy()
+    assert np.diff(rp).max() > 256  # candidate rows longer than four waves of 64
+    nb = oracle_mod.build_neighbors(wl.box, wl.pos, wl.species, wl.model.r_cut, wl.skin)
+    ref = oracle_mod.energy_forces(wl.model, w, wl.box, nb["pos"].astype(np.float64),
+                                   nb["species"], nb["row_ptr"], nb["col_shift"])
+    _assert_ef(g["energy"], g["forces"], ref["energy"], ref["forces"], "dense2k")
+    assert np.all(np.abs(g["e_atom"] - ref["e_atom"]) <= 1e-5 * (1 + np.abs(ref["e_atom"])))
+
+
 @pytest.mark.parametrize("shape", [(1, 16, 1, 32), (2, 16, 4, 32), (1, 32, 4, 32), (2, 32, 4, 32),
                                    (2, 64, 4, 64)])
 @pytest.mark.parametrize("layers", [1, 3])
