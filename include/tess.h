@@ -15,9 +15,11 @@
  *    otherwise TESS_ERR_ARG (weights) or TESS_ERR_WORKSPACE (workspace).
  *  - `hip_stream` is a hipStream_t (NULL = default stream). Work is enqueued on it in order.
  *    tess_energy_forces and tess_md_steps also run independent kernels of the pass on one
- *    second stream per host thread and device, created by the library on first use; it forks
- *    from and joins `hip_stream` through events, so the pass stays ordered on `hip_stream`
- *    (and captures into one graph).
+ *    second stream per host thread and device, created by the library on its first call
+ *    outside stream capture and kept until the process ends (default priority, non-blocking);
+ *    it forks from and joins `hip_stream` through events, so the pass stays ordered on
+ *    `hip_stream` (and captures into one graph). A call that is the thread's first on a
+ *    device and runs under capture uses `hip_stream` alone.
  *  - Return value: a tess_status. Argument, box and workspace errors are detected on the host
  *    before anything is enqueued. TESS_ERR_HIP reports a failed HIP call (the stream state is
  *    then undefined).
