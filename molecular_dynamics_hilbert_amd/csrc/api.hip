@@ -47,12 +47,12 @@ void timing_mark(const char* name, hipStream_t st, bool begin) {
   std::lock_guard<std::mutex> g(t.mu);
   hipEvent_t e;
   if (hipEventCreate(&e) != hipSuccess) return;
-  hipEventRecord(e, st);
+  (void)hipEventRecord(e, st);
   if (begin) {
     t.open[name] = e;
   } else {
     auto it = t.open.find(name);
-    if (it == t.open.end()) { hipEventDestroy(e); return; }
+    if (it == t.open.end()) { (void)hipEventDestroy(e); return; }
     t.ev[name].push_back({it->second, e});
     t.open.erase(it);
   }
@@ -268,7 +268,7 @@ int32_t md_interval_graph(const tess_model_desc* d, const float* weights, int32_
   std::lock_guard<std::mutex> g(c.mu);
   if (!(c.valid && c.key == key)) {
     if (c.valid) {
-      hipGraphExecDestroy(c.exec);
+      (void)hipGraphExecDestroy(c.exec);
       c.valid = false;
     }
     if (hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal) != hipSuccess) {
@@ -280,12 +280,12 @@ int32_t md_interval_graph(const tess_model_desc* d, const float* weights, int32_
     hipGraph_t graph = nullptr;
     const hipError_t ec = hipStreamEndCapture(st, &graph);
     if (rc != TESS_OK || ec != hipSuccess || !graph) {
-      if (graph) hipGraphDestroy(graph);
+      if (graph) (void)hipGraphDestroy(graph);
       (void)hipGetLastError();
       return rc != TESS_OK ? rc : TESS_ERR_HIP;
     }
     const hipError_t ei = hipGraphInstantiate(&c.exec, graph, nullptr, nullptr, 0);
-    hipGraphDestroy(graph);
+    (void)hipGraphDestroy(graph);
     if (ei != hipSuccess) return TESS_ERR_HIP;
     c.key = key;
     c.valid = true;
@@ -304,9 +304,12 @@ int32_t tess_timing_enable(int32_t on) {
   TimingState& t = timing();
   std::lock_guard<std::mutex> g(t.mu);
   for (auto& kv : t.ev)
-    for (auto& pr : kv.second) { hipEventDestroy(pr.first); hipEventDestroy(pr.second); }
+    for (auto& pr : kv.second) {
+      (void)hipEventDestroy(pr.first);
+      (void)hipEventDestroy(pr.second);
+    }
   t.ev.clear();
-  for (auto& kv : t.open) hipEventDestroy(kv.second);
+  for (auto& kv : t.open) (void)hipEventDestroy(kv.second);
   t.open.clear();
   t.on = on != 0;
   return TESS_OK;

@@ -92,6 +92,7 @@ constexpr int kGemmMaxK = 192;
 template <int EPI, int K>
 __global__ void __launch_bounds__(256) k_gemm(int64_t M, int O, const float* __restrict__ X,
                                               RowMap xm, const float* __restrict__ Wt, Epi ep) {
+  static_assert(K % 16 == 0 && K <= kGemmMaxK, "K is a multiple of 16, at most kGemmMaxK");
   __shared__ float Ws[K][64 + 1];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int64_t r0 = (int64_t)blockIdx.x * 128 + w * 32;
@@ -112,7 +113,6 @@ __global__ void __launch_bounds__(256) k_gemm(int64_t M, int O, const float* __r
   // floats, O a multiple of 4, and the blob is 16-byte aligned)
   // (every load is requested before the first LDS write)
   {
-    static_assert(K % 16 == 0, "K is a multiple of 16");
     float4 wv[K / 16];
 #pragma unroll
     for (int i = 0; i < K / 16; i++) {
@@ -1076,7 +1076,7 @@ __global__ void __launch_bounds__(256) k_readout(int32_t n, int C, int D, const 
   sh[threadIdx.x] = v;
   __syncthreads();
   for (int s = 128; s > 0; s >>= 1) {
-    if (threadIdx.x < s) sh[threadIdx.x] += sh[threadIdx.x + s];
+    if ((int)threadIdx.x < s) sh[threadIdx.x] += sh[threadIdx.x + s];
     __syncthreads();
   }
   if (threadIdx.x == 0) part[blockIdx.x] = sh[0];
@@ -1090,7 +1090,7 @@ __global__ void __launch_bounds__(256) k_energy_final(int32_t nb, const double* 
   sh[threadIdx.x] = v;
   __syncthreads();
   for (int s = 128; s > 0; s >>= 1) {
-    if (threadIdx.x < s) sh[threadIdx.x] += sh[threadIdx.x + s];
+    if ((int)threadIdx.x < s) sh[threadIdx.x] += sh[threadIdx.x + s];
     __syncthreads();
   }
   if (threadIdx.x == 0) energy[0] = sh[0];

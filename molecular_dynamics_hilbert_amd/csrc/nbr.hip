@@ -245,6 +245,8 @@ __global__ void __launch_bounds__(64) k_pairs(int32_t n, CellGrid g, double rcs2
                                               int32_t* __restrict__ misc) {
   __shared__ int32_t vstart[27], vcode[27], vpre[28];
   __shared__ uint32_t buf[FILL ? kMaxRow : 1];
+  (void)n;  // one block per atom: the grid is n blocks
+  if constexpr (FILL) (void)misc;
   const int32_t i = blockIdx.x;
   const int lane = threadIdx.x;
   const double xi0 = (double)pos[3 * i], xi1 = (double)pos[3 * i + 1], xi2 = (double)pos[3 * i + 2];
