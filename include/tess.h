@@ -82,6 +82,8 @@ int64_t tess_workspace_bytes(const tess_model_desc* desc, int32_t n_atoms, int64
  *          code = 9(sx+1) + 3(sy+1) + (sz+1) the image shift s in {-1,0,1}^3
  *  out     rev[edge_cap] nullable; rev[e] = slot of the reverse pair (j <- i, -s)
  *  out     *n_edges (HOST) number of pairs; on TESS_ERR_CAPACITY the required count
+ *          (a count above 2^31 - 1, which the int32 row offsets cannot hold, is also reported
+ *          as TESS_ERR_CAPACITY with the true count: no edge_cap satisfies it)
  * Synchronises the stream once (to read the pair count). On TESS_ERR_CAPACITY / TESS_ERR_ROW
  * the positions and permutation outputs are valid but col_shift and rev are not. */
 int32_t tess_build_neighbors(int32_t n, const float box[3], float r_cut, float skin,

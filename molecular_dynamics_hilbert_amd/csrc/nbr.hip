@@ -377,16 +377,31 @@ __global__ void __launch_bounds__(64) k_pairs(int32_t n, CellGrid g, double rcs2
   }
 }
 
-// Longest row of a scanned CSR: block maxima, one atomic per block.
+// Longest row and total pair count of a scanned CSR: block reductions, one atomic of each
+// per block. The scan adds in 32 bits, so a total beyond the int32 range of row_ptr wraps
+// there; each row's count is still the difference of its (wrapped) bounds, and their 64-bit
+// sum is the true total.
 __global__ void __launch_bounds__(256) k_max_row(int32_t n, const int32_t* __restrict__ row_ptr,
-                                                 int32_t* __restrict__ out) {
+                                                 int32_t* __restrict__ out,
+                                                 unsigned long long* __restrict__ total) {
   int32_t i = blockIdx.x * 256 + threadIdx.x;
-  int v = i < n ? row_ptr[i + 1] - row_ptr[i] : 0;
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+  int v = i < n ? (int)((uint32_t)row_ptr[i + 1] - (uint32_t)row_ptr[i]) : 0;
+  unsigned long long s = (unsigned long long)v;
+  for (int o = 32; o >= 1; o >>= 1) {
+    v = max(v, __shfl_xor(v, o, 64));
+    s += __shfl_xor(s, o, 64);
+  }
   __shared__ int32_t sh[4];
-  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __shared__ unsigned long long ss[4];
+  if ((threadIdx.x & 63) == 0) {
+    sh[threadIdx.x >> 6] = v;
+    ss[threadIdx.x >> 6] = s;
+  }
   __syncthreads();
-  if (threadIdx.x == 0) atomicMax(out, max(max(sh[0], sh[1]), max(sh[2], sh[3])));
+  if (threadIdx.x == 0) {
+    atomicMax(out, max(max(sh[0], sh[1]), max(sh[2], sh[3])));
+    atomicAdd(total, ss[0] + ss[1] + ss[2] + ss[3]);
+  }
 }
 
 // rev[e] for every pair of row i: position of (j <- i, 26 - code) in row j (rows are sorted
@@ -624,15 +639,20 @@ int32_t build_neighbors_impl(int32_t n, const float box[3], float r_cut, float s
                                               ws.cell_atoms, row_ptr, nullptr, ws.misc));
   TESS_HIP_CHECK(hipGetLastError());
   TESS_HIP_CHECK(scan_exclusive_i32(row_ptr, (int64_t)n + 1, ws.scan_tmp, st));
-  k_max_row<<<grid(n, 256), 256, 0, st>>>(n, row_ptr, ws.misc);
+  // misc[0]: longest row; misc[4..5]: 64-bit pair total (the block is 256-byte aligned)
+  unsigned long long* total = reinterpret_cast<unsigned long long*>(ws.misc + 4);
+  k_max_row<<<grid(n, 256), 256, 0, st>>>(n, row_ptr, ws.misc, total);
   TESS_HIP_CHECK(hipGetLastError());
-  int32_t host[2] = {0, 0};
-  TESS_HIP_CHECK(hipMemcpyAsync(&host[0], row_ptr + n, sizeof(int32_t), hipMemcpyDeviceToHost, st));
-  TESS_HIP_CHECK(hipMemcpyAsync(&host[1], ws.misc, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+  int32_t max_row = 0;
+  unsigned long long pairs = 0;
+  TESS_HIP_CHECK(hipMemcpyAsync(&max_row, ws.misc, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+  TESS_HIP_CHECK(hipMemcpyAsync(&pairs, total, sizeof(pairs), hipMemcpyDeviceToHost, st));
   TESS_HIP_CHECK(hipStreamSynchronize(st));
-  *n_edges = host[0];
-  if (host[1] > kMaxRow) return TESS_ERR_ROW;
-  if ((int64_t)host[0] > edge_cap) return TESS_ERR_CAPACITY;
+  *n_edges = (int64_t)pairs;
+  if (max_row > kMaxRow) return TESS_ERR_ROW;
+  // a total that row_ptr (int32) cannot hold is reported like a capacity shortfall, with the
+  // true count; no edge_cap satisfies it
+  if ((int64_t)pairs > edge_cap || pairs > (unsigned long long)INT32_MAX) return TESS_ERR_CAPACITY;
   TESS_TIMED("nbr_fill", st,
              k_pairs<true><<<n, 64, 0, st>>>(n, g, rcs2, pos, ws.cell_id, ws.cell_start,
                                              ws.cell_atoms, row_ptr, col_shift, ws.misc));

@@ -242,6 +242,8 @@ class System:
                                      ws0, check=False)
             if st not in (OK, ERR_CAPACITY):
                 raise TessError(st, "tess_build_neighbors")
+            if ne > 2**31 - 1:  # beyond what the int32 row offsets can hold
+                raise TessError(ERR_CAPACITY, "tess_build_neighbors (%d pairs)" % ne)
             edge_cap = max(1, int(1.15 * ne) + 64)
         self.edge_cap = edge_cap
         self.col_shift = torch.empty(edge_cap, dtype=torch.int32, device=device)

@@ -153,3 +153,24 @@ def test_errors_capacity_box_row(T, oracle_mod):
     box, pos, sp = W.random_small_box(2600, 14.0, 3)
     g = _gpu_rebuild(T, box, pos, sp, cap=4000000)
     assert g["status"] == T.ERR_ROW
+
+
+def test_pair_total_beyond_int32_reported(T):
+    # Simple cubic lattice (spacing 1 A, 133^3 atoms) with r_c + skin = 6.04 A: every atom's
+    # candidates are the 924 lattice vectors with 1 <= |v|^2 <= 36 (brute-force count below),
+    # 2,173,836,588 pairs in all, more than int32 row offsets hold. The rebuild reports the exact
+    # count as a capacity shortfall and returns before the fill pass (the pair buffer here has
+    # one entry).
+    L, rc, skin = 133, 5.0, 1.04
+    rcs2 = float(np.float32(rc) + np.float32(skin)) ** 2
+    v = np.arange(-7, 8)
+    d2 = (v[:, None, None] ** 2 + v[None, :, None] ** 2 + v[None, None, :] ** 2).ravel()
+    per_atom = int(((d2 > 0) & (d2 < rcs2)).sum())
+    assert per_atom == 924
+    g = np.arange(L, dtype=np.float32)
+    x, y, z = np.meshgrid(g, g, g, indexing="ij")
+    pos = np.stack([x.ravel(), y.ravel(), z.ravel()], 1)
+    box = np.full(3, float(L), np.float32)
+    out = _gpu_rebuild(T, box, pos, np.zeros(L ** 3, np.int32), cap=1, rc=rc, skin=skin)
+    assert out["status"] == T.ERR_CAPACITY
+    assert out["n_edges"] == L ** 3 * per_atom > 2 ** 31 - 1
