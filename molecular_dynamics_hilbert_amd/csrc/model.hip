@@ -976,7 +976,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((TRANS
 // channel quad m): each 16-byte load covers 4 channels, so one wave request brings whole q|k
 // rows of several neighbours. Eight groups of edges are requested before any is used; past
 // the row's end a slot repeats the last edge with weight 0. The slots' partial sums are added
-// at the end.
+// at the end. swapped: sbar of edge e is stored at slot rev(e) (the last layer's edge gradient
+// writes it so), and the two reads of each pair exchange.
 // ---------------------------------------------------------------------------------------
 template <int C, int H>
 __global__ void __launch_bounds__(256) k_qk_bar(int32_t n, const int32_t* __restrict__ arow,
@@ -984,7 +985,7 @@ __global__ void __launch_bounds__(256) k_qk_bar(int32_t n, const int32_t* __rest
                                                 const int32_t* __restrict__ arev,
                                                 const float4* __restrict__ sbar,
                                                 const float* __restrict__ qk,
-                                                float* __restrict__ qkbar) {
+                                                float* __restrict__ qkbar, bool swapped) {
   constexpr int dh = C / H;
   constexpr int CQ = C / 4;     // channel quads
   constexpr int EPG = 64 / CQ;  // edges per group (one per slot)
@@ -1008,8 +1009,9 @@ __global__ void __launch_bounds__(256) k_qk_bar(int32_t n, const int32_t* __rest
       if (l2 < cnt) {
         const int32_t e = b + l2;
         sY[wv][l2] = asrc[e];
-        sS[wv][l2] = sbar[arev[e]];
-        sD[wv][l2] = sbar[e];
+        const int32_t er = arev[e];
+        sS[wv][l2] = sbar[swapped ? e : er];
+        sD[wv][l2] = sbar[swapped ? er : e];
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -1475,8 +1477,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
 // per block and only mbar_i's l = 0 head slice (64 B per lane) is gathered, instead of the
 // 2.3 KB of h_j per edge of the destination-major form. The geometry of e is -r_vec(a') and
 // its radial weights are those of a' (both bit-exact, |r| is the same); the softmax
-// probability, D_i and the outputs sbar, g are read or written at e. The sums run in the same
-// order as in k_edge_grad, so the results are identical to its single-row form.
+// probability and D_i are read at e. The outputs are written at a' = rev(e), so that the lanes'
+// stores are consecutive: sbar_e goes to slot a' (the q/k adjoints of this layer read the two
+// slots of each pair the other way round), and -g_e is added to slot a' of the per-edge
+// gradient sum. The forces use that sum only as g_a - g_rev(a) per pair, which is unchanged.
+// The per-edge sums run in the same order as in k_edge_grad, so sbar and g are identical to its
+// single-row form.
 template <int LMAX, int C, int H>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) k_edge_grad_last(
     const int32_t* __restrict__ arow_n, const float4* __restrict__ ageo,
@@ -1580,9 +1586,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
 #pragma unroll
         for (int d = 0; d < 9; d++) Yb[d] = quad_sum(Yb[d]);
         ubar = quad_sum(ubar);
-        reinterpret_cast<float*>(sbar)[e * 4 + hh] = sb;
+        reinterpret_cast<float*>(sbar)[a * 4 + hh] = sb;
       } else {
-        sbar[e] = make_float4(sb, 0.0f, 0.0f, 0.0f);
+        sbar[a] = make_float4(sb, 0.0f, 0.0f, 0.0f);
       }
       if (hh == 0) {
         float dEdr = ubar * du;
@@ -1594,12 +1600,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
         float gx = dEdr * nx + (gy[0] - ng * nx) * ir;
         float gyv = dEdr * ny + (gy[1] - ng * ny) * ir;
         float gz = dEdr * nz + (gy[2] - ng * nz) * ir;
+        float b0x = 0.0f, b0y = 0.0f, b0z = 0.0f;
         if (accumulate) {
-          gx += gacc[e * 3]; gyv += gacc[e * 3 + 1]; gz += gacc[e * 3 + 2];
+          b0x = gacc[a * 3]; b0y = gacc[a * 3 + 1]; b0z = gacc[a * 3 + 2];
         }
-        gacc[e * 3] = gx;
-        gacc[e * 3 + 1] = gyv;
-        gacc[e * 3 + 2] = gz;
+        gacc[a * 3] = b0x - gx;
+        gacc[a * 3 + 1] = b0y - gyv;
+        gacc[a * 3 + 2] = b0z - gz;
       }
     }
   }
@@ -2012,8 +2019,9 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
                    k_edge_contract<LMAX, C, H, false, true><<<gridn(n, 4), 256, 0, st>>>(
                        n, w.arow, w.ageo, w.asrc, w.arev, ew, es, w.mbar, rc, hbar, gbar, Pt,
                        species, emb, S, nullptr, ews));
+      // the last layer's source-major edge gradient stores sbar of edge e at slot rev(e)
       k_qk_bar<C, H><<<gridn(n, 4), 256, 0, st>>>(n, w.arow, w.asrc, w.arev, w.sbar, qk,
-                                                 w.qkbar);
+                                                 w.qkbar, mb0);
       Epi ea{};
       ea.y = hbar;
       ea.ym = feat0;
