@@ -280,6 +280,70 @@ def test_cube_rotations_periodic(oracle_mod):
         assert np.abs(Fr - F @ Rm.T).max() < 1e-6
 
 
+def _sub_cluster(wl, radius, L=50.0):
+    """Atoms of `wl` within `radius` (minimum image) of its box centre, moved into an
+    L-edge box (no periodic image inside the cutoff: every shift code is 13)."""
+    x = wl.pos.astype(np.float64)
+    Lw = wl.box.astype(np.float64)
+    d = x - Lw / 2
+    d -= Lw * np.round(d / Lw)
+    sel = np.where((d * d).sum(1) < radius * radius)[0]
+    pos = d[sel] + L / 2
+    sub = W.Workload(wl.name + "_cluster", np.full(3, L, np.float32), pos.astype(np.float32),
+                     wl.species[sel], wl.species_names, wl.model)
+    return sub
+
+
+@pytest.mark.parametrize("case", [("salt4k", 9.0, 2002), ("salt60k", 7.5, 2003)])
+def test_rotation_invariance_lmax2_cluster(oracle_mod, case):
+    """l_max = 2 models (salt4k's two layers; the four-layer 64-channel model of the large
+    workloads): every l = 2 path, the gated l = 2 update and their adjoints enter E and F.
+    Under random SO(3) rotations of an isolated cluster (same pair list) E is invariant and
+    F rotates with it, in fp64. A mistake that mixes m-components of a degree in any way
+    other than a rotation does (a cyclic m-shift, a sign, a transposed block) breaks this."""
+    name, radius, seed = case
+    wl = _sub_cluster(W.load(name), radius)
+    assert wl.model.l_max == 2 and wl.model.n_layers >= 2
+    nb, w, out = _system(oracle_mod, wl, seed=seed)
+    assert np.all((nb["col_shift"] >> 27) == 13)
+    x = nb["pos"].astype(np.float64)
+    c = x.mean(0)
+    E0, F0 = out["energy"], out["forces"]
+    assert np.abs(F0).max() > 1e-3  # forces are not trivially zero
+    for s in range(3):
+        R = Rotation.random(random_state=200 + s).as_matrix()
+        xr = (x - c) @ R.T + c
+        outr = oracle_mod.energy_forces(wl.model, w, wl.box, xr, nb["species"], nb["row_ptr"],
+                                        nb["col_shift"])
+        assert abs(outr["energy"] - E0) < 1e-12 * abs(E0), (outr["energy"], E0)
+        assert np.abs(outr["forces"] - F0 @ R.T).max() < 1e-12 * max(1.0, np.abs(F0).max())
+
+
+def test_cube_rotations_periodic_lmax2(oracle_mod):
+    """The 24 proper rotations of a cube map the periodic salt4k box (l_max = 2, two layers)
+    onto itself; through a full rebuild from the rotated fp32 coordinates E is unchanged
+    and every atom's force rotates (up to the fp32 rounding of the rotated input)."""
+    import itertools
+    wl = W.load("salt4k")
+    nb, w, out = _system(oracle_mod, wl, seed=2002)
+    F = np.empty((wl.n, 3)); F[nb["perm"]] = out["forces"]
+    L = float(wl.box[0])
+    mats = []
+    for perm in itertools.permutations(range(3)):
+        for signs in itertools.product((1, -1), repeat=3):
+            Rm = np.zeros((3, 3))
+            for a in range(3):
+                Rm[a, perm[a]] = signs[a]
+            if np.linalg.det(Rm) > 0:
+                mats.append(Rm)
+    for Rm in (mats[3], mats[8], mats[17]):
+        pr = (wl.pos.astype(np.float64) @ Rm.T) % L
+        nbr, _, outr = _system(oracle_mod, wl, seed=2002, pos=pr.astype(np.float32))
+        assert abs(outr["energy"] - out["energy"]) < 1e-6 * abs(out["energy"])
+        Fr = np.empty((wl.n, 3)); Fr[nbr["perm"]] = outr["forces"]
+        assert np.abs(Fr - F @ Rm.T).max() < 1e-6 * max(1.0, np.abs(F).max())
+
+
 def test_skin_invariance_exact(oracle_mod):
     """Edges with r_c <= r < r_c+skin contribute exactly zero: E and F from the skin-0 list
     equal those from the skin-1 list bit for bit."""
