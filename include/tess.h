@@ -23,6 +23,15 @@
  *  - Return value: a tess_status. Argument, box and workspace errors are detected on the host
  *    before anything is enqueued. TESS_ERR_HIP reports a failed HIP call (the stream state is
  *    then undefined).
+ *  - Device status word: the first 4 bytes of the workspace. Kernels record problems they
+ *    find on the device there (asynchronously): a species index outside [0, n_species) seen
+ *    by the energy pass, and a non-finite position (neighbour build), energy or force (energy
+ *    pass). The next synchronising call on that workspace -- tess_check_status,
+ *    tess_build_neighbors or tess_md_steps -- returns TESS_ERR_SPECIES (first) or
+ *    TESS_ERR_NONFINITE and clears the word. A fresh workspace must start with that word zero
+ *    (zero-filled memory, or one tess_check_status call). The Tessera abstract reports runs
+ *    with no broken bonds or anomalously close pairs; this is the device-side check that a
+ *    run has not blown up.
  *  - Supported model shapes (kernels are compiled per shape): n_rbf == 8, n_species <= 16,
  *    n_layers <= 16 and (l_max, channels, n_heads, radial_hidden) one of (1, 16, 1, 32),
  *    (1, 32, 4, 32), (2, 16, 4, 32), (2, 32, 4, 32), (2, 64, 4, 64). Others: TESS_ERR_ARG.
@@ -44,8 +53,9 @@ typedef enum {
   TESS_ERR_WORKSPACE = -4, /* workspace smaller than tess_workspace_bytes() */
   TESS_ERR_HIP = -5,       /* a HIP runtime call failed */
   TESS_ERR_SKIN = -6,      /* an atom moved more than skin/2 since the last rebuild */
-  TESS_ERR_SPECIES = -7,   /* species index outside [0, n_species) */
-  TESS_ERR_ROW = -8        /* an atom has more than 1024 candidate neighbours */
+  TESS_ERR_SPECIES = -7,   /* species index outside [0, n_species) (device status word) */
+  TESS_ERR_NONFINITE = -8, /* non-finite position, energy or force (device status word) */
+  TESS_ERR_ROW = -9        /* an atom has more than 1024 candidate neighbours */
 } tess_status;
 
 /* Model hyper-parameters. Paths P follow from l_max (4 for l_max 1, 11 for l_max 2). */
@@ -54,8 +64,14 @@ typedef struct {
   float r_cut;
 } tess_model_desc;
 
-int32_t tess_abi_version(void);
+int32_t tess_abi_version(void); /* 2 */
 const char* tess_status_string(int32_t status);
+
+/* tess_check_status -- synchronises `hip_stream`, reads and clears the device status word of
+ * `workspace` (any workspace of tess_workspace_bytes(); at least 4 bytes, 16-byte aligned).
+ * Returns TESS_OK, TESS_ERR_SPECIES or TESS_ERR_NONFINITE (TESS_ERR_WORKSPACE for a bad
+ * pointer or size). */
+int32_t tess_check_status(void* workspace, int64_t ws_bytes, void* hip_stream);
 
 /* Number of fp32 weights. Blob order (row-major [out][in], y = W x): Emb[S][C]; for each
  * layer W_q[C][C], W_k[C][C], W1[R][K], W2[P][R], W_lin0[C(1+l_max)][C], then W_lin^l[C][C]
@@ -84,8 +100,11 @@ int64_t tess_workspace_bytes(const tess_model_desc* desc, int32_t n_atoms, int64
  *  out     *n_edges (HOST) number of pairs; on TESS_ERR_CAPACITY the required count
  *          (a count above 2^31 - 1, which the int32 row offsets cannot hold, is also reported
  *          as TESS_ERR_CAPACITY with the true count: no edge_cap satisfies it)
- * Synchronises the stream once (to read the pair count). On TESS_ERR_CAPACITY / TESS_ERR_ROW
- * the positions and permutation outputs are valid but col_shift and rev are not. */
+ * Synchronises the stream once (to read the pair count and the device status word). On
+ * TESS_ERR_CAPACITY / TESS_ERR_ROW the positions and permutation outputs are valid but
+ * col_shift and rev are not. A set status word (a non-finite input coordinate, or a problem
+ * left by an earlier energy pass on this workspace) is returned as TESS_ERR_NONFINITE /
+ * TESS_ERR_SPECIES and cleared; col_shift and rev are then not written. */
 int32_t tess_build_neighbors(int32_t n, const float box[3], float r_cut, float skin,
                              float* pos, int32_t* species, float* vel, float* ref_pos,
                              int32_t* perm, uint32_t* hkey, int32_t* row_ptr,
@@ -106,8 +125,10 @@ int32_t tess_build_neighbors(int32_t n, const float box[3], float r_cut, float s
  *  out energy   device double[1]; e_atom device float[n] (nullable);
  *      forces   device float[n][3] (nullable: energy only, no backward pass).
  * Fully asynchronous (no host synchronisation). Species outside [0, n_species) are clamped
- * into that range where they index the weights (the results are then meaningless, but no
- * access leaves the weights); validate species on the host first if they are not trusted. */
+ * into that range where they index the weights (no access leaves the weights) and set
+ * TESS_ERR_SPECIES in the workspace's device status word; a non-finite energy or force sets
+ * TESS_ERR_NONFINITE there. Both are reported by the next synchronising call
+ * (tess_check_status, tess_build_neighbors, tess_md_steps). */
 int32_t tess_energy_forces(const tess_model_desc* desc, const float* weights, int32_t n,
                            const float box[3], const float* pos, const int32_t* species,
                            const int32_t* row_ptr, const uint32_t* col_shift,
@@ -130,13 +151,20 @@ int32_t tess_energy_forces(const tess_model_desc* desc, const float* weights, in
  *  out    epot_trace device double[n_steps] (nullable); row_ptr/col_shift/rev as in
  *         tess_build_neighbors; *n_edges (HOST) pairs of the last rebuild
  * Synchronises once per rebuild. If an atom moved more than skin/2 from its position at
- * the last rebuild, the call finishes that interval and returns TESS_ERR_SKIN.
+ * the last rebuild, the call finishes that interval and returns TESS_ERR_SKIN. At the same
+ * synchronisation it reads the device status word: a species outside [0, n_species) or a
+ * non-finite position, energy or force stops the run with TESS_ERR_SPECIES /
+ * TESS_ERR_NONFINITE (reported before TESS_ERR_SKIN; masses are read at the species index
+ * clamped into range, so no access leaves mass_by_species).
  * flags: TESS_MD_FORCES_VALID; TESS_MD_GRAPH captures the steps of a rebuild interval into a
  * HIP graph once and replays it for later intervals and calls with identical arguments
- * (pointers, sizes, step count, dt, box, model); results are identical to eager launches.
- * It is ignored on the NULL stream and while kernel timing is enabled. One graph is cached
- * per process (a call with other arguments re-captures it); calls that use the flag must not
- * run concurrently from several threads. Other flag bits: TESS_ERR_ARG. */
+ * (pointers, sizes, step count, dt, skin, box, model, thermostat, which traces are
+ * requested); results are identical to eager launches. Traces are staged in the workspace
+ * and copied out after each replay, so their offsets do not force a re-capture. It is
+ * ignored on the NULL stream, while kernel timing is enabled and for rebuild_every > 256.
+ * One graph is cached per process (a call with other arguments re-captures it); calls that
+ * use the flag must not run concurrently from several threads. Other flag bits:
+ * TESS_ERR_ARG. */
 int32_t tess_md_steps(const tess_model_desc* desc, const float* weights, int32_t n,
                       const float box[3], float r_cut, float skin, float* pos, float* vel,
                       int32_t* species, const float* mass_by_species, float dt_fs,

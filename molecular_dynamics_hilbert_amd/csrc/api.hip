@@ -66,14 +66,19 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 constexpr float kAccelConv = 9.648533e-3f;  // eV/A/amu -> A/fs^2
 
 // First half of a velocity-Verlet step: v += dt/2 F/m; x += dt v; flag |x - x_ref| > skin/2.
+// Species index of mass_by_species, clamped to [0, S) (an out-of-range species is reported
+// by the energy pass through the status word; the clamp keeps every access in bounds).
+__device__ __forceinline__ int32_t mass_index(int32_t s, int32_t S) { return min(max(s, 0), S - 1); }
+
 __global__ void k_vv_kick_drift(int32_t n, float dt, const float* __restrict__ F,
                                 const int32_t* __restrict__ species,
-                                const float* __restrict__ mass, float* __restrict__ pos,
-                                float* __restrict__ vel, const float* __restrict__ ref,
-                                float half_skin2, int32_t* __restrict__ flag) {
+                                const float* __restrict__ mass, int32_t S,
+                                float* __restrict__ pos, float* __restrict__ vel,
+                                const float* __restrict__ ref, float half_skin2,
+                                int32_t* __restrict__ flag) {
   int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
-  float im = kAccelConv / mass[species[i]];
+  float im = kAccelConv / mass[mass_index(species[i], S)];
   float d2 = 0.0f;
 #pragma unroll
   for (int a = 0; a < 3; a++) {
@@ -90,10 +95,10 @@ __global__ void k_vv_kick_drift(int32_t n, float dt, const float* __restrict__ F
 // Second half: v += dt/2 F/m.
 __global__ void k_vv_kick(int32_t n, float dt, const float* __restrict__ F,
                           const int32_t* __restrict__ species, const float* __restrict__ mass,
-                          float* __restrict__ vel) {
+                          int32_t S, float* __restrict__ vel) {
   int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
-  float im = kAccelConv / mass[species[i]];
+  float im = kAccelConv / mass[mass_index(species[i], S)];
 #pragma unroll
   for (int a = 0; a < 3; a++) vel[3 * i + a] += 0.5f * dt * F[3 * i + a] * im;
 }
@@ -112,13 +117,13 @@ __device__ __forceinline__ double block_sum_256(double v) {
 __global__ void __launch_bounds__(256) k_vv_kick_ke(int32_t n, float dt,
                                                     const float* __restrict__ F,
                                                     const int32_t* __restrict__ species,
-                                                    const float* __restrict__ mass,
+                                                    const float* __restrict__ mass, int32_t S,
                                                     float* __restrict__ vel,
                                                     double* __restrict__ part) {
   int32_t i = blockIdx.x * 256 + threadIdx.x;
   double mv2 = 0.0;
   if (i < n) {
-    const float m = mass[species[i]];
+    const float m = mass[mass_index(species[i], S)];
     const float im = kAccelConv / m;
     double v2 = 0.0;
 #pragma unroll
@@ -174,10 +179,29 @@ __global__ void __launch_bounds__(256) k_md_thermo(int32_t n, int32_t nparts,
 }
 
 __global__ void k_set_u32(uint32_t* __restrict__ p, uint32_t v) { *p = v; }
+__global__ void k_zero_f64(double* __restrict__ p) { *p = 0.0; }
+
+// After a replayed interval: the traces of its k steps, written by the graph into the
+// workspace's staging arrays, are copied to the caller's trace arrays (NULL: not requested).
+__global__ void k_copy_traces(int32_t k, const double* __restrict__ ep_in,
+                              double* __restrict__ ep_out, const double* __restrict__ ke_in,
+                              double* __restrict__ ke_out, const float* __restrict__ rm_in,
+                              float* __restrict__ rm_out) {
+  const int32_t j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= k) return;
+  if (ep_out) ep_out[j] = ep_in[j];
+  if (ke_out) ke_out[j] = ke_in[j];
+  if (rm_out) rm_out[j] = rm_in[j];
+}
 
 inline int32_t gridn(int64_t n, int b) { return (int32_t)((n + b - 1) / b); }
 
+// Steps per interval whose traces a replayed graph stages in the workspace (longer
+// intervals run eagerly).
+constexpr int32_t kTraceStage = 256;
+
 struct Layout {
+  int32_t* status;  // device status word (first word of the workspace)
   NbrWS nbr;
   char* ef;
   int64_t ef_bytes;
@@ -188,12 +212,15 @@ struct Layout {
   double* epot;
   double* ke_part;      // kinetic-energy sums, one per block of 256 atoms
   uint32_t* rmin2_bits;  // shortest squared pair distance of the step (float bits)
+  double *epot_stage, *ke_stage;  // per-step traces of a replayed interval
+  float* rmin_stage;
   int64_t total;
 };
 
 Layout layout(char* base, const tess_model_desc* md, int32_t n, int64_t cap) {
   Layout L{};
   Carver cv{base, 0};
+  L.status = cv.take<int32_t>(64);
   L.nbr = carve_nbr(cv, n);
   int64_t nn = n > 0 ? n : 1;
   L.ref_pos = cv.take<float>(3 * nn);
@@ -202,6 +229,9 @@ Layout layout(char* base, const tess_model_desc* md, int32_t n, int64_t cap) {
   L.epot = cv.take<double>(4);
   L.ke_part = cv.take<double>(gridn(nn, 256));
   L.rmin2_bits = cv.take<uint32_t>(64);
+  L.epot_stage = cv.take<double>(kTraceStage);
+  L.ke_stage = cv.take<double>(kTraceStage);
+  L.rmin_stage = cv.take<float>(kTraceStage);
   if (md) {
     L.ef_bytes = ef_workspace_bytes(*md, n, cap);
     L.ef = cv.take<char>(L.ef_bytes);
@@ -224,13 +254,17 @@ using namespace tess;
 
 // ---- graph replay of a rebuild interval (TESS_MD_GRAPH) ----------------------------------
 // The k velocity-Verlet steps between two rebuilds are captured once into a HIP graph and
-// replayed for every later interval with the same arguments (pointers, sizes, step count,
-// time step, box, model). One cached graph per process; a different key re-captures it.
+// replayed for every later interval with the same arguments. The key holds everything the
+// captured launches bake in: device pointers, sizes, the step count, the time step, the box,
+// the model, the skin threshold and the thermostat; the per-step traces are written by the
+// graph into fixed staging arrays of the workspace (copied out after each replay), so the
+// trace pointers of an interval are not part of the key. One cached graph per process; a
+// different key re-captures it.
 namespace {
 struct GraphKey {
-  const void* p[14];
-  int64_t i[7];
-  float f[7];
+  const void* p[10];
+  int64_t i[10];
+  float f[8];
   bool operator==(const GraphKey& o) const { return std::memcmp(this, &o, sizeof(*this)) == 0; }
 };
 struct GraphCache {
@@ -247,23 +281,25 @@ GraphCache& graph_cache() {
 template <class StepFn>
 int32_t md_interval_graph(const tess_model_desc* d, const float* weights, int32_t n,
                           const float box[3], float* pos, float* vel, int32_t* species,
-                          const float* mass, float dt, float* forces, double* epot0,
+                          const float* mass, float dt, float half_skin2, float* forces,
                           int32_t* row_ptr, uint32_t* col_shift, int32_t* rev, int64_t edge_cap,
-                          void* ws, const tess_md_options& opt, double* ke0, float* rmin0,
-                          int32_t k, hipStream_t st, StepFn step, bool* done) {
+                          void* ws, const tess_md_options& opt, bool has_epot, int32_t k,
+                          hipStream_t st, StepFn step, bool* done) {
   GraphKey key;
   std::memset(&key, 0, sizeof(key));
   // the model description and the box are host arrays: their values are part of the key
-  const void* ps[14] = {weights, pos, vel, species, mass, forces, epot0, row_ptr, col_shift,
-                        rev, ws, ke0, rmin0, nullptr};
-  for (int a = 0; a < 14; a++) key.p[a] = ps[a];
+  const void* ps[10] = {weights, pos, vel, species, mass, forces, row_ptr, col_shift, rev, ws};
+  for (int a = 0; a < 10; a++) key.p[a] = ps[a];
   key.i[0] = n; key.i[1] = edge_cap; key.i[2] = k;
   key.i[3] = d->n_species; key.i[4] = d->n_layers;
   key.i[5] = ((int64_t)d->channels << 40) | ((int64_t)d->radial_hidden << 24) |
              ((int64_t)d->n_rbf << 16) | ((int64_t)d->l_max << 8) | d->n_heads;
   key.i[6] = opt.thermostat;
+  key.i[7] = has_epot;
+  key.i[8] = opt.ke_trace != nullptr;
+  key.i[9] = opt.rmin_trace != nullptr;
   key.f[0] = dt; key.f[1] = box[0]; key.f[2] = box[1]; key.f[3] = box[2]; key.f[4] = d->r_cut;
-  key.f[5] = opt.t_target_K; key.f[6] = opt.tau_fs;
+  key.f[5] = opt.t_target_K; key.f[6] = opt.tau_fs; key.f[7] = half_skin2;
   GraphCache& c = graph_cache();
   std::lock_guard<std::mutex> g(c.mu);
   if (!(c.valid && c.key == key)) {
@@ -294,11 +330,25 @@ int32_t md_interval_graph(const tess_model_desc* d, const float* weights, int32_
   *done = true;
   return TESS_OK;
 }
+
+// Reads the status word and the skin flag (one synchronisation); returns the status error,
+// else TESS_ERR_SKIN if the flag is set, else TESS_OK. A reported status is cleared.
+int32_t md_sync_check(const Layout& L, hipStream_t st) {
+  int32_t f = 0, bits = 0;
+  TESS_HIP_CHECK(hipMemcpyAsync(&f, L.flag, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+  TESS_HIP_CHECK(hipMemcpyAsync(&bits, L.status, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+  TESS_HIP_CHECK(hipStreamSynchronize(st));
+  if (bits) {
+    TESS_HIP_CHECK(hipMemsetAsync(L.status, 0, sizeof(int32_t), st));
+    return status_error(bits);
+  }
+  return f ? TESS_ERR_SKIN : TESS_OK;
+}
 }  // namespace
 
 extern "C" {
 
-int32_t tess_abi_version(void) { return 1; }
+int32_t tess_abi_version(void) { return 2; }
 
 int32_t tess_timing_enable(int32_t on) {
   TimingState& t = timing();
@@ -356,6 +406,7 @@ const char* tess_status_string(int32_t s) {
     case TESS_ERR_HIP: return "HIP runtime error";
     case TESS_ERR_SKIN: return "an atom moved more than skin/2 since the last rebuild";
     case TESS_ERR_SPECIES: return "species index out of range";
+    case TESS_ERR_NONFINITE: return "non-finite position, energy or force";
     case TESS_ERR_ROW: return "an atom has more than 1024 candidate neighbours";
     default: return "unknown status";
   }
@@ -395,7 +446,20 @@ int32_t tess_build_neighbors(int32_t n, const float box[3], float r_cut, float s
     return TESS_OK;
   }
   return build_neighbors_impl(n, box, r_cut, skin, pos, species, vel, ref_pos, nullptr, nullptr,
-                              perm, hkey, row_ptr, col_shift, rev, edge_cap, n_edges, L.nbr, st);
+                              perm, hkey, row_ptr, col_shift, rev, edge_cap, n_edges, L.nbr,
+                              L.status, st);
+}
+
+int32_t tess_check_status(void* workspace, int64_t ws_bytes, void* hip_stream) {
+  if (!workspace || !aligned16(workspace) || ws_bytes < (int64_t)sizeof(int32_t))
+    return TESS_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  int32_t* status = reinterpret_cast<int32_t*>(workspace);  // first word of every layout
+  int32_t bits = 0;
+  TESS_HIP_CHECK(hipMemcpyAsync(&bits, status, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+  TESS_HIP_CHECK(hipStreamSynchronize(st));
+  if (bits) TESS_HIP_CHECK(hipMemsetAsync(status, 0, sizeof(int32_t), st));
+  return status_error(bits);
 }
 
 int32_t tess_energy_forces(const tess_model_desc* d, const float* weights, int32_t n,
@@ -412,12 +476,13 @@ int32_t tess_energy_forces(const tess_model_desc* d, const float* weights, int32
   Layout L = layout(reinterpret_cast<char*>(workspace), d, n, n_edges);
   if (!workspace || !aligned16(workspace) || ws_bytes < L.total) return TESS_ERR_WORKSPACE;
   hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
-  if (n == 0) {
-    TESS_HIP_CHECK(hipMemsetAsync(energy, 0, sizeof(double), st));
+  if (n == 0) {  // a kernel rather than a memset node, so the call stays capturable
+    k_zero_f64<<<1, 1, 0, st>>>(energy);
+    TESS_HIP_CHECK(hipGetLastError());
     return TESS_OK;
   }
   return ef_dispatch(*d, weights, n, box, pos, species, row_ptr, col_shift, rev, n_edges, n_edges,
-                     energy, e_atom, forces, L.ef, L.ef_bytes, st);
+                     energy, e_atom, forces, L.ef, L.ef_bytes, L.status, st);
 }
 
 int32_t tess_md_steps_ex(const tess_model_desc* d, const float* weights, int32_t n,
@@ -461,72 +526,79 @@ int32_t tess_md_steps_ex(const tess_model_desc* d, const float* weights, int32_t
     TESS_HIP_CHECK(hipGetLastError());
   }
   // one velocity-Verlet step; `grid_edges` sizes the edge-kernel grids (the kernels stop at
-  // the device-side active-edge count, so any value >= the pair count gives the same result)
-  auto step = [&](int32_t s, int64_t grid_edges) -> int32_t {
-    k_vv_kick_drift<<<nb, 256, 0, st>>>(n, dt_fs, forces, species, mass_by_species, pos, vel,
+  // the device-side active-edge count, so any value >= the pair count gives the same result);
+  // ep/ke/rm receive the step's traces (ke/rm nullable)
+  const int32_t S = d->n_species;
+  auto step = [&](int64_t grid_edges, double* ep, double* ke, float* rm) -> int32_t {
+    k_vv_kick_drift<<<nb, 256, 0, st>>>(n, dt_fs, forces, species, mass_by_species, S, pos, vel,
                                         L.ref_pos, half_skin2, L.flag);
     TESS_HIP_CHECK(hipGetLastError());
     int32_t rc = ef_dispatch(*d, weights, n, box, pos, species, row_ptr, col_shift, rev,
-                             grid_edges, edge_cap, epot_trace ? epot_trace + s : L.epot, nullptr,
-                             forces, L.ef, L.ef_bytes, st,
-                             opt.rmin_trace ? L.rmin2_bits : nullptr);
+                             grid_edges, edge_cap, ep, nullptr, forces, L.ef, L.ef_bytes,
+                             L.status, st, opt.rmin_trace ? L.rmin2_bits : nullptr);
     if (rc != TESS_OK) return rc;
     if (need_ke)
-      k_vv_kick_ke<<<nb, 256, 0, st>>>(n, dt_fs, forces, species, mass_by_species, vel,
+      k_vv_kick_ke<<<nb, 256, 0, st>>>(n, dt_fs, forces, species, mass_by_species, S, vel,
                                        L.ke_part);
     else
-      k_vv_kick<<<nb, 256, 0, st>>>(n, dt_fs, forces, species, mass_by_species, vel);
+      k_vv_kick<<<nb, 256, 0, st>>>(n, dt_fs, forces, species, mass_by_species, S, vel);
     TESS_HIP_CHECK(hipGetLastError());
     if (end_kernel) {
       k_md_thermo<<<berendsen ? nb : 1, 256, 0, st>>>(
           n, need_ke ? nb : 0, L.ke_part, berendsen ? 1 : 0,
           berendsen ? (double)dt_fs / (double)opt.tau_fs : 0.0, (double)opt.t_target_K, vel,
-          opt.ke_trace ? opt.ke_trace + s : nullptr, L.rmin2_bits,
-          opt.rmin_trace ? opt.rmin_trace + s : nullptr);
+          ke, L.rmin2_bits, rm);
       TESS_HIP_CHECK(hipGetLastError());
     }
     return TESS_OK;
   };
   for (int32_t s = 0; s < n_steps;) {
     if (s > 0) {
-      int32_t f = 0;
-      TESS_HIP_CHECK(hipMemcpyAsync(&f, L.flag, sizeof(int32_t), hipMemcpyDeviceToHost, st));
-      TESS_HIP_CHECK(hipStreamSynchronize(st));
-      if (f) return TESS_ERR_SKIN;
+      const int32_t rc0 = md_sync_check(L, st);
+      if (rc0 != TESS_OK) return rc0;
     }
     int32_t rc = build_neighbors_impl(n, box, r_cut, skin, pos, species, vel, L.ref_pos,
                                       (forces_valid || s > 0) ? forces : nullptr, perm_accum,
                                       L.perm, nullptr, row_ptr, col_shift, rev, edge_cap, &ne,
-                                      L.nbr, st);
+                                      L.nbr, L.status, st);
     *n_edges = ne;
     if (rc != TESS_OK) return rc;
     if (s == 0 && !forces_valid) {
       rc = ef_dispatch(*d, weights, n, box, pos, species, row_ptr, col_shift, rev, ne, edge_cap,
-                       L.epot, nullptr, forces, L.ef, L.ef_bytes, st);
+                       L.epot, nullptr, forces, L.ef, L.ef_bytes, L.status, st);
       if (rc != TESS_OK) return rc;
     }
     const int32_t k = n_steps - s < rebuild_every ? n_steps - s : rebuild_every;
     bool done = false;
-    if (use_graph) {
-      rc = md_interval_graph(d, weights, n, box, pos, vel, species, mass_by_species, dt_fs,
-                             forces, epot_trace ? epot_trace + s : L.epot, row_ptr, col_shift,
-                             rev, edge_cap, workspace, opt,
-                             opt.ke_trace ? opt.ke_trace + s : nullptr,
-                             opt.rmin_trace ? opt.rmin_trace + s : nullptr, k, st,
-                             [&](int32_t j) { return step(s + j, edge_cap); }, &done);
+    if (use_graph && k <= kTraceStage) {
+      // the graph writes the traces into the workspace's staging arrays (fixed addresses)
+      rc = md_interval_graph(
+          d, weights, n, box, pos, vel, species, mass_by_species, dt_fs, half_skin2, forces,
+          row_ptr, col_shift, rev, edge_cap, workspace, opt, epot_trace != nullptr, k, st,
+          [&](int32_t j) {
+            return step(edge_cap, L.epot_stage + j, opt.ke_trace ? L.ke_stage + j : nullptr,
+                        opt.rmin_trace ? L.rmin_stage + j : nullptr);
+          },
+          &done);
       if (rc != TESS_OK) return rc;
+      if (done && (epot_trace || opt.ke_trace || opt.rmin_trace)) {
+        k_copy_traces<<<gridn(k, 256), 256, 0, st>>>(
+            k, L.epot_stage, epot_trace ? epot_trace + s : nullptr, L.ke_stage,
+            opt.ke_trace ? opt.ke_trace + s : nullptr, L.rmin_stage,
+            opt.rmin_trace ? opt.rmin_trace + s : nullptr);
+        TESS_HIP_CHECK(hipGetLastError());
+      }
     }
     if (!done)
       for (int32_t j = 0; j < k; j++) {
-        rc = step(s + j, ne);
+        rc = step(ne, epot_trace ? epot_trace + s + j : L.epot,
+                  opt.ke_trace ? opt.ke_trace + s + j : nullptr,
+                  opt.rmin_trace ? opt.rmin_trace + s + j : nullptr);
         if (rc != TESS_OK) return rc;
       }
     s += k;
   }
-  int32_t f = 0;
-  TESS_HIP_CHECK(hipMemcpyAsync(&f, L.flag, sizeof(int32_t), hipMemcpyDeviceToHost, st));
-  TESS_HIP_CHECK(hipStreamSynchronize(st));
-  return f ? TESS_ERR_SKIN : TESS_OK;
+  return md_sync_check(L, st);
 }
 
 int32_t tess_md_steps(const tess_model_desc* d, const float* weights, int32_t n, const float box[3],

@@ -264,13 +264,18 @@ __global__ void k_prep_weights(const float* __restrict__ weights, int S, int K,
 // outside the weights.
 __device__ __forceinline__ int sp_index(int32_t s, int S) { return min(max(s, 0), S - 1); }
 
+// An index out of range also sets kStatusSpecies in the status word (reported by the next
+// synchronising call).
 __global__ void k_embed(int32_t n, int C, int D, int S, const int32_t* __restrict__ species,
-                        const float* __restrict__ emb, float* __restrict__ h) {
+                        const float* __restrict__ emb, float* __restrict__ h,
+                        int32_t* __restrict__ status) {
   int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (k >= (int64_t)n * C) return;
   int64_t i = k / C;
   int c = (int)(k - i * C);
-  h[i * D * C + c] = emb[sp_index(species[i], S) * C + c];
+  const int32_t s = species[i];
+  if (c == 0 && (s < 0 || s >= S)) atomicOr(status, kStatusSpecies);
+  h[i * D * C + c] = emb[sp_index(s, S) * C + c];
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1084,8 +1089,10 @@ __global__ void __launch_bounds__(256) k_readout(int32_t n, int C, int D, const 
   if (threadIdx.x == 0) part[blockIdx.x] = sh[0];
 }
 
+// A non-finite total (some E_i is not finite) sets kStatusNonFinite in the status word.
 __global__ void __launch_bounds__(256) k_energy_final(int32_t nb, const double* __restrict__ part,
-                                                      double* __restrict__ energy) {
+                                                      double* __restrict__ energy,
+                                                      int32_t* __restrict__ status) {
   __shared__ double sh[256];
   double v = 0.0;
   for (int32_t k = threadIdx.x; k < nb; k += 256) v += part[k];
@@ -1095,7 +1102,10 @@ __global__ void __launch_bounds__(256) k_energy_final(int32_t nb, const double* 
     if ((int)threadIdx.x < s) sh[threadIdx.x] += sh[threadIdx.x + s];
     __syncthreads();
   }
-  if (threadIdx.x == 0) energy[0] = sh[0];
+  if (threadIdx.x == 0) {
+    energy[0] = sh[0];
+    if (!isfinite(sh[0])) atomicOr(status, kStatusNonFinite);
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1613,11 +1623,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
 }
 
 // F_x = sum over the row's active edges a of (g_a - g_rev(a)); one wave per row, lanes over
-// edges, a fixed-order wave sum (deterministic).
+// edges, a fixed-order wave sum (deterministic). A non-finite force sets kStatusNonFinite.
 __global__ void __launch_bounds__(256) k_forces(int32_t n, const int32_t* __restrict__ arow,
                                                 const int32_t* __restrict__ arev,
                                                 const float* __restrict__ gacc,
-                                                float* __restrict__ F) {
+                                                float* __restrict__ F,
+                                                int32_t* __restrict__ status) {
   const int32_t x = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (x >= n) return;
@@ -1635,6 +1646,7 @@ __global__ void __launch_bounds__(256) k_forces(int32_t n, const int32_t* __rest
     F[3 * (int64_t)x] = f0;
     F[3 * (int64_t)x + 1] = f1;
     F[3 * (int64_t)x + 2] = f2;
+    if (!(isfinite(f0) && isfinite(f1) && isfinite(f2))) atomicOr(status, kStatusNonFinite);
   }
 }
 
@@ -1771,8 +1783,8 @@ template <int LMAX, int C, int H, int R>
 int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const float box[3],
                const float* pos, const int32_t* species, const int32_t* row_ptr,
                const uint32_t* col_shift, const int32_t* rev_in, int64_t n_edges, int64_t ecap,
-               double* energy, float* e_atom, float* forces, const EFWS& w, hipStream_t st,
-               uint32_t* rmin2_bits) {
+               double* energy, float* e_atom, float* forces, const EFWS& w, int32_t* status,
+               hipStream_t st, uint32_t* rmin2_bits) {
   constexpr int D = Dims<LMAX>::D;
   constexpr int P = Dims<LMAX>::P;
   constexpr int G = C * (1 + LMAX);
@@ -1814,7 +1826,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
   if (ax) TESS_HIP_CHECK(hipEventRecord(ax->ev[kEvTabDone], sb));
   const int64_t NDC = (int64_t)n * D * C;
   // embedding
-  k_embed<<<gridn((int64_t)n * C, 256), 256, 0, st>>>(n, C, D, S, species, emb, w.h);
+  k_embed<<<gridn((int64_t)n * C, 256), 256, 0, st>>>(n, C, D, S, species, emb, w.h, status);
   // active edges
   const int32_t* rev = rev_in;
   if (cap > 0) {
@@ -1936,7 +1948,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
   const float* hT = w.h + (int64_t)T * NDC;
   int32_t nb = gridn(n, 256);
   if (nb > 0) k_readout<<<nb, 256, 0, st>>>(n, C, D, hT, wE, e_atom, w.epart);
-  k_energy_final<<<1, 256, 0, st>>>(nb, w.epart, energy);
+  k_energy_final<<<1, 256, 0, st>>>(nb, w.epart, energy, status);
   TESS_HIP_CHECK(hipGetLastError());
   if (!forces) return TESS_OK;
   // ---------------- backward ----------------
@@ -2032,7 +2044,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     }
   }
   if (cap > 0) {
-    k_forces<<<gridn(n, 4), 256, 0, st>>>(n, w.arow, w.arev, w.gacc, forces);
+    k_forces<<<gridn(n, 4), 256, 0, st>>>(n, w.arow, w.arev, w.gacc, forces, status);
   } else if (n > 0) {
     k_fill_f32<<<gridn(3 * (int64_t)n, 256), 256, 0, st>>>(forces, 3 * (int64_t)n, 0.0f);
   }
@@ -2056,7 +2068,7 @@ int32_t ef_dispatch(const tess_model_desc& md, const float* weights, int32_t n, 
                     const float* pos, const int32_t* species, const int32_t* row_ptr,
                     const uint32_t* col_shift, const int32_t* rev, int64_t n_edges,
                     int64_t ecap, double* energy, float* e_atom, float* forces, char* ws,
-                    int64_t ws_bytes, hipStream_t st, uint32_t* rmin2_bits) {
+                    int64_t ws_bytes, int32_t* status, hipStream_t st, uint32_t* rmin2_bits) {
   Carver cv{ws, 0};
   EFWS w = carve_ef(cv, md, n, ecap);
   if (cv.off > ws_bytes) return TESS_ERR_WORKSPACE;
@@ -2064,7 +2076,8 @@ int32_t ef_dispatch(const tess_model_desc& md, const float* weights, int32_t n, 
 #define TESS_EF_CASE(L_, C_, H_, R_)                                                          \
   if (l == L_ && c == C_ && h == H_ && r == R_)                                               \
     return ef_run<L_, C_, H_, R_>(md, weights, n, box, pos, species, row_ptr, col_shift, rev, \
-                                  n_edges, ecap, energy, e_atom, forces, w, st, rmin2_bits);
+                                  n_edges, ecap, energy, e_atom, forces, w, status, st,       \
+                                  rmin2_bits);
   TESS_EF_CASE(1, 16, 1, 32)
   TESS_EF_CASE(2, 32, 4, 32)
   TESS_EF_CASE(2, 64, 4, 64)

@@ -86,9 +86,13 @@ __global__ void k_wrap_key(int32_t n, int curve, double Lx, double Ly, double Lz
                            float* __restrict__ pos_w, uint32_t* __restrict__ key,
                            int32_t* __restrict__ idx, int32_t* __restrict__ sp_tmp,
                            float* __restrict__ v_tmp, float* __restrict__ f_tmp,
-                           int32_t* __restrict__ pa_tmp) {
+                           int32_t* __restrict__ pa_tmp, int32_t* __restrict__ status) {
   int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
+  // a non-finite coordinate is reported through the status word (its key and cell are then
+  // meaningless but stay in range: the quantisation and the cell index clamp)
+  if (!(isfinite(pos[3 * i]) && isfinite(pos[3 * i + 1]) && isfinite(pos[3 * i + 2])))
+    atomicOr(status, kStatusNonFinite);
   float x = wrap_coord(pos[3 * i + 0], Lx);
   float y = wrap_coord(pos[3 * i + 1], Ly);
   float z = wrap_coord(pos[3 * i + 2], Lz);
@@ -581,7 +585,7 @@ int32_t build_neighbors_impl(int32_t n, const float box[3], float r_cut, float s
                              int32_t* perm_accum, int32_t* perm, uint32_t* hkey,
                              int32_t* row_ptr, uint32_t* col_shift, int32_t* rev,
                              int64_t edge_cap, int64_t* n_edges, const NbrWS& ws,
-                             hipStream_t st) {
+                             int32_t* status, hipStream_t st) {
   const double L[3] = {(double)box[0], (double)box[1], (double)box[2]};
   const double rcs = (double)r_cut + (double)skin;
   const double rcs2 = rcs * rcs;
@@ -589,7 +593,7 @@ int32_t build_neighbors_impl(int32_t n, const float box[3], float r_cut, float s
   k_wrap_key<<<grid(n, 256), 256, 0, st>>>(n, sort_curve(), L[0], L[1], L[2], pos, species,
                                            vel, forces,
                                            perm_accum, ws.pos_w, ws.key[0], ws.idx[0], ws.sp_tmp,
-                                           ws.v_tmp, ws.f_tmp, ws.pa_tmp);
+                                           ws.v_tmp, ws.f_tmp, ws.pa_tmp, status);
   TESS_HIP_CHECK(hipGetLastError());
   // 2. stable radix sort, 4 x 8 bits (keys have 30 bits)
   int32_t nblk = grid(n, kTile);
@@ -643,12 +647,17 @@ int32_t build_neighbors_impl(int32_t n, const float box[3], float r_cut, float s
   unsigned long long* total = reinterpret_cast<unsigned long long*>(ws.misc + 4);
   k_max_row<<<grid(n, 256), 256, 0, st>>>(n, row_ptr, ws.misc, total);
   TESS_HIP_CHECK(hipGetLastError());
-  int32_t max_row = 0;
+  int32_t max_row = 0, bits = 0;
   unsigned long long pairs = 0;
   TESS_HIP_CHECK(hipMemcpyAsync(&max_row, ws.misc, sizeof(int32_t), hipMemcpyDeviceToHost, st));
   TESS_HIP_CHECK(hipMemcpyAsync(&pairs, total, sizeof(pairs), hipMemcpyDeviceToHost, st));
+  TESS_HIP_CHECK(hipMemcpyAsync(&bits, status, sizeof(int32_t), hipMemcpyDeviceToHost, st));
   TESS_HIP_CHECK(hipStreamSynchronize(st));
   *n_edges = (int64_t)pairs;
+  if (bits) {  // reported here and cleared (a pending bit may come from an earlier pass)
+    TESS_HIP_CHECK(hipMemsetAsync(status, 0, sizeof(int32_t), st));
+    return status_error(bits);
+  }
   if (max_row > kMaxRow) return TESS_ERR_ROW;
   // a total that row_ptr (int32) cannot hold is reported like a capacity shortfall, with the
   // true count; no edge_cap satisfies it

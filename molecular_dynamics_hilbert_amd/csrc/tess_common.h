@@ -258,6 +258,17 @@ struct Carver {
   }
 };
 
+// Device status word: the first word of every workspace. Kernels OR in bits for problems
+// they detect on the device; the next synchronising call on the workspace reports and clears
+// them (tess_check_status, tess_build_neighbors, tess_md_steps).
+constexpr int32_t kStatusSpecies = 1;    // a species index outside [0, n_species)
+constexpr int32_t kStatusNonFinite = 2;  // a non-finite position, energy or force
+// Error code of a status word (species first), TESS_OK for 0.
+inline int32_t status_error(int32_t bits) {
+  return (bits & kStatusSpecies) ? TESS_ERR_SPECIES
+                                 : ((bits & kStatusNonFinite) ? TESS_ERR_NONFINITE : TESS_OK);
+}
+
 // Neighbour-build scratch (a prefix of every workspace).
 struct NbrWS {
   float* pos_w;       // [3n] wrapped positions (pre-sort order)
@@ -280,12 +291,16 @@ NbrWS carve_nbr(Carver& c, int32_t n);
 
 // Internal rebuild used by tess_build_neighbors and tess_md_steps. Optional extra arrays
 // are permuted along (forces [n][3], perm_accum [n]).
+// `status` is the workspace's device status word (see below): the wrap kernel sets
+// kStatusNonFinite for a non-finite coordinate, and the call reads the word at its one
+// synchronisation and returns TESS_ERR_SPECIES / TESS_ERR_NONFINITE (clearing it) when a bit
+// is set, before the fill pass.
 int32_t build_neighbors_impl(int32_t n, const float box[3], float r_cut, float skin,
                              float* pos, int32_t* species, float* vel, float* ref_pos,
                              float* forces, int32_t* perm_accum, int32_t* perm, uint32_t* hkey,
                              int32_t* row_ptr, uint32_t* col_shift, int32_t* rev,
                              int64_t edge_cap, int64_t* n_edges, const NbrWS& ws,
-                             hipStream_t stream);
+                             int32_t* status, hipStream_t stream);
 // Reverse-pair index of a sorted CSR (rev[e] = slot of (j <- i, -s)).
 hipError_t rev_index(int32_t n, const int32_t* row_ptr, const uint32_t* col, int32_t* rev,
                      hipStream_t s);
@@ -298,7 +313,8 @@ int32_t ef_dispatch(const tess_model_desc& md, const float* weights, int32_t n, 
                     const float* pos, const int32_t* species, const int32_t* row_ptr,
                     const uint32_t* col_shift, const int32_t* rev, int64_t n_edges,
                     int64_t ecap, double* energy, float* e_atom, float* forces, char* ws,
-                    int64_t ws_bytes, hipStream_t st, uint32_t* rmin2_bits = nullptr);
+                    int64_t ws_bytes, int32_t* status, hipStream_t st,
+                    uint32_t* rmin2_bits = nullptr);
 }  // namespace tess
 
 #define TESS_HIP_CHECK(expr)                       \

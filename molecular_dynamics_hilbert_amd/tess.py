@@ -17,8 +17,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtess.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "tess.h")
 
-OK, ERR_ARG, ERR_BOX, ERR_CAPACITY, ERR_WORKSPACE, ERR_HIP, ERR_SKIN, ERR_SPECIES, ERR_ROW = (
-    0, -1, -2, -3, -4, -5, -6, -7, -8)
+(OK, ERR_ARG, ERR_BOX, ERR_CAPACITY, ERR_WORKSPACE, ERR_HIP, ERR_SKIN, ERR_SPECIES,
+ ERR_NONFINITE, ERR_ROW) = (0, -1, -2, -3, -4, -5, -6, -7, -8, -9)
 MD_FORCES_VALID = 1
 MD_GRAPH = 2
 
@@ -80,6 +80,8 @@ def lib() -> C.CDLL:
         L.tess_timing_only.argtypes = [C.c_char_p]
         L.tess_set_curve.restype = i32
         L.tess_set_curve.argtypes = [i32]
+        L.tess_check_status.restype = i32
+        L.tess_check_status.argtypes = [p, i64, p]
         _lib = L
     return _lib
 
@@ -151,10 +153,23 @@ def _stream():
 
 
 def workspace(spec, n: int, edge_cap: int, device="cuda") -> torch.Tensor:
+    """A workspace of tess_workspace_bytes() bytes whose device status word (its first
+    word) starts at zero."""
     nb = workspace_bytes(spec, n, edge_cap)
     if nb < 0:
         raise TessError(ERR_ARG, "tess_workspace_bytes")
-    return torch.empty(nb, dtype=torch.uint8, device=device)
+    ws = torch.empty(nb, dtype=torch.uint8, device=device)
+    ws[:256].zero_()
+    return ws
+
+
+def check_status(ws, check=True) -> int:
+    """tess_check_status: synchronise the current stream, report and clear the workspace's
+    device status word."""
+    st = lib().tess_check_status(_p(ws), int(ws.numel()), _stream())
+    if check and st != OK:
+        raise TessError(st, "tess_check_status")
+    return st
 
 
 def build_neighbors(box, r_cut, skin, pos, species, perm, row_ptr, col_shift, ws, vel=None,

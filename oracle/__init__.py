@@ -47,6 +47,7 @@ def lib():
         _lib = C.CDLL(build())
         L = _lib
         p = C.c_void_p
+        L.tor_num_threads.restype = C.c_int32
         L.tor_wrap1.restype = C.c_float
         L.tor_wrap1.argtypes = [C.c_float, C.c_double]
         L.tor_hilbert_key3.restype = C.c_uint32
@@ -158,6 +159,11 @@ def flagged_pairs(box, pos, r_cut, skin, band=1e-5):
     fj = np.zeros(max(cnt, 1), np.int32)
     lib().tor_flagged_pairs(n, _ptr(_box(box)), _ptr(pos), r_cut, skin, band, cnt, _ptr(fi), _ptr(fj))
     return fi[:cnt], fj[:cnt]
+
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP loops use."""
+    return int(lib().tor_num_threads())
 
 
 def build_neighbors(box, pos, species, r_cut, skin, vel=None):

@@ -29,6 +29,9 @@
 
 int32_t tor_abi_version(void) { return 1; }
 
+/* Threads the oracle's parallel loops use (OpenMP's current maximum). */
+int32_t tor_num_threads(void) { return (int32_t)omp_get_max_threads(); }
+
 /* ------------------------------------------------------------------------------------
  * Step 1 -- wrap (Tessera abstract: fixed shapes between rebuilds; periodic box).
  * Reading: t = x/L, f = floor(t), x_w = x - f*L with each operation rounded separately in

@@ -28,6 +28,8 @@ typedef struct {
 } tor_model;
 
 int32_t tor_abi_version(void);
+/* Threads used by the oracle's parallel loops. */
+int32_t tor_num_threads(void);
 
 /* Wrap one fp32 coordinate into [0, L] in fp64 and round back to fp32. */
 float tor_wrap1(float x, double L);

@@ -31,7 +31,7 @@ def test_single_hip_runtime(T):
 
 
 def test_counts_and_status(T):
-    assert T.lib().tess_abi_version() == 1
+    assert T.lib().tess_abi_version() == 2
     for wl in (W.water648(), W.salt4k()):
         assert T.weights_count(wl.model) == W.weight_count(wl.model)
     assert T.weights_count(W.big_model()) == W.weight_count(W.big_model())
