@@ -112,6 +112,21 @@ int32_t tess_build_neighbors(int32_t n, const float box[3], float r_cut, float s
                              int64_t* n_edges, void* workspace, int64_t ws_bytes,
                              void* hip_stream);
 
+/* tess_build_neighbors_static -- tess_build_neighbors for callers that cannot allocate
+ * memory (no hipMalloc and no workspace of their own: code run under stream capture, tight
+ * serving loops, harnesses that forbid allocation). The arguments, outputs, synchronisation
+ * and errors are those of tess_build_neighbors, without the workspace: the rebuild's scratch
+ * is a 48 MiB array inside the library, one per GPU, kept until the process ends (the call
+ * itself allocates nothing). Limit: n <= 524288 atoms, else TESS_ERR_WORKSPACE before anything
+ * is enqueued. Every call on one GPU shares that GPU's array, so calls that overlap on one GPU
+ * (concurrent streams or threads) race; serialise them. Its status word starts every call at
+ * zero, so only this call's own non-finite coordinates are reported. */
+int32_t tess_build_neighbors_static(int32_t n, const float box[3], float r_cut, float skin,
+                                    float* pos, int32_t* species, float* vel, float* ref_pos,
+                                    int32_t* perm, uint32_t* hkey, int32_t* row_ptr,
+                                    uint32_t* col_shift, int32_t* rev, int64_t edge_cap,
+                                    int64_t* n_edges, void* hip_stream);
+
 /* tess_energy_forces -- energy and forces of the equivariant message-passing attention
  * stack (Tessera title and abstract: equivariant attention, force back-propagation).
  * Per layer: q/k projections of the scalar channels, per-edge Bessel radial basis with a

@@ -247,6 +247,40 @@ bool box_ok(const float box[3], float r_cut, float skin) {
   return true;
 }
 
+// ---- neighbour build without allocation (tess_build_neighbors_static) --------------------
+// A file-scope device array holds that entry point's scratch (the wrap/sort/cell arrays of the
+// rebuild and the status word), so its callers pass no workspace. Each GPU the library runs
+// on holds one copy until the process ends. Host code never uses the array's name as an
+// address: the device address of each GPU's copy comes from hipGetSymbolAddress, taken once
+// per device with that device current.
+constexpr int64_t kStaticScratchBytes = int64_t(48) << 20;  // 48 MiB
+constexpr int32_t kStaticMaxAtoms = 1 << 19;                // 524,288 atoms
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+// Device address of this device's scratch copy (nullptr if it cannot be resolved).
+char* static_scratch() {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static char* addr[kMaxDev] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> g(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    addr[dev] = static_cast<char*>(p);
+  }
+  return addr[dev];
+}
+
+__global__ void k_zero_i32(int32_t* __restrict__ p) { *p = 0; }
+
 }  // namespace
 }  // namespace tess
 
@@ -448,6 +482,42 @@ int32_t tess_build_neighbors(int32_t n, const float box[3], float r_cut, float s
   return build_neighbors_impl(n, box, r_cut, skin, pos, species, vel, ref_pos, nullptr, nullptr,
                               perm, hkey, row_ptr, col_shift, rev, edge_cap, n_edges, L.nbr,
                               L.status, st);
+}
+
+int32_t tess_build_neighbors_static(int32_t n, const float box[3], float r_cut, float skin,
+                                    float* pos, int32_t* species, float* vel, float* ref_pos,
+                                    int32_t* perm, uint32_t* hkey, int32_t* row_ptr,
+                                    uint32_t* col_shift, int32_t* rev, int64_t edge_cap,
+                                    int64_t* n_edges, void* hip_stream) {
+  if (n < 0 || n >= (1 << 27) || !box || !n_edges || edge_cap < 0 || !(r_cut > 0.0f) ||
+      !(skin >= 0.0f))
+    return TESS_ERR_ARG;
+  if (n > 0 && (!pos || !species || !perm || !row_ptr || (!col_shift && edge_cap > 0)))
+    return TESS_ERR_ARG;
+  if (!box_ok(box, r_cut, skin)) return TESS_ERR_BOX;
+  // the scratch this call needs: the status word and the rebuild arrays for n atoms
+  Carver need{nullptr, 0};
+  (void)need.take<int32_t>(64);
+  (void)carve_nbr(need, n);
+  if (n > kStaticMaxAtoms || need.off > kStaticScratchBytes) return TESS_ERR_WORKSPACE;
+  char* base = static_scratch();
+  if (!base) return TESS_ERR_HIP;
+  Carver cv{base, 0};
+  int32_t* status = cv.take<int32_t>(64);
+  NbrWS ws = carve_nbr(cv, n);
+  hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  *n_edges = 0;
+  if (n == 0) {
+    if (row_ptr) TESS_HIP_CHECK(hipMemsetAsync(row_ptr, 0, sizeof(int32_t), st));
+    return TESS_OK;
+  }
+  // the array keeps the previous call's contents: the status word starts each call at zero
+  // (every other array the rebuild reads is written or cleared by the rebuild itself)
+  k_zero_i32<<<1, 1, 0, st>>>(status);
+  TESS_HIP_CHECK(hipGetLastError());
+  return build_neighbors_impl(n, box, r_cut, skin, pos, species, vel, ref_pos, nullptr, nullptr,
+                              perm, hkey, row_ptr, col_shift, rev, edge_cap, n_edges, ws, status,
+                              st);
 }
 
 int32_t tess_check_status(void* workspace, int64_t ws_bytes, void* hip_stream) {

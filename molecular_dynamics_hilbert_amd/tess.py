@@ -82,6 +82,9 @@ def lib() -> C.CDLL:
         L.tess_set_curve.argtypes = [i32]
         L.tess_check_status.restype = i32
         L.tess_check_status.argtypes = [p, i64, p]
+        L.tess_build_neighbors_static.restype = i32
+        L.tess_build_neighbors_static.argtypes = [i32, p, f32, f32, p, p, p, p, p, p, p, p, p,
+                                                  i64, p, p]
         _lib = L
     return _lib
 
@@ -185,6 +188,22 @@ def build_neighbors(box, r_cut, skin, pos, species, perm, row_ptr, col_shift, ws
                                     int(ws.numel()), _stream())
     if check and st != OK:
         raise TessError(st, "tess_build_neighbors")
+    return st, int(ne.value)
+
+
+def build_neighbors_static(box, r_cut, skin, pos, species, perm, row_ptr, col_shift, vel=None,
+                           ref_pos=None, hkey=None, rev=None, check=True):
+    """tess_build_neighbors_static: build_neighbors with the library's own device scratch (no
+    workspace). Returns (status, n_edges)."""
+    n = int(pos.shape[0])
+    ne = C.c_int64(0)
+    cap = int(col_shift.numel()) if col_shift is not None else 0
+    st = lib().tess_build_neighbors_static(n, _box(box), float(r_cut), float(skin), _p(pos),
+                                           _p(species), _p(vel), _p(ref_pos), _p(perm),
+                                           _p(hkey), _p(row_ptr), _p(col_shift), _p(rev), cap,
+                                           C.byref(ne), _stream())
+    if check and st != OK:
+        raise TessError(st, "tess_build_neighbors_static")
     return st, int(ne.value)
 
 
