@@ -5,10 +5,12 @@
 //   1. wrap + 30-bit Hilbert key per atom (fp64, every operation rounded on its own),
 //   2. stable LSD radix sort of (key, index), 4 passes of 8 bits; each 1024-key tile ranks
 //      its keys with wave ballots (64 lanes) so equal digits keep their index order,
-//   3. cell binning (cells at least (r_cut+skin)(1+1e-6) wide),
-//   4. per atom one wave scans the 27 neighbouring cells; the fp64 pair test decides, the
-//      wave compacts passing pairs with ballot + popcount, and a bitonic sort in LDS puts each
-//      row in ascending (j, shift) order. Count pass, scan, fill pass.
+//   3. cell binning (cells at least (r_cut+skin)(1+1e-6) wide) into a cell-sorted copy of
+//      the positions,
+//   4. one block per cell stages its 27-cell stencil in LDS (sorted by (j, shift) for the
+//      fill), and its waves test the cell's atoms against it: the fp64 pair test decides, the
+//      wave compacts passing pairs with ballot + popcount, in row order. Count pass, scan,
+//      fill pass.
 // Decisions that must match the fp64 reference bit for bit are written with FP contraction
 // off.
 #include "tess_common.h"
@@ -226,55 +228,160 @@ __global__ void k_cell_count(int32_t n, CellGrid g, const float* __restrict__ po
   atomicAdd(&cnt[c], 1);
 }
 
+// Cell-sorted copy of the atoms: atoms[slot] = i and cpos[slot] = (x_i, y_i, z_i, bits of i),
+// so a cell's atoms and their positions are contiguous (one 16-byte load per candidate).
 __global__ void k_cell_fill(int32_t n, const int32_t* __restrict__ cell_id,
                             const int32_t* __restrict__ cell_start, int32_t* __restrict__ fill,
-                            int32_t* __restrict__ atoms) {
+                            int32_t* __restrict__ atoms, const float* __restrict__ pos,
+                            float4* __restrict__ cpos) {
   int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   int c = cell_id[i];
-  int slot = atomicAdd(&fill[c], 1);
-  atoms[cell_start[c] + slot] = i;
+  int slot = cell_start[c] + atomicAdd(&fill[c], 1);
+  atoms[slot] = i;
+  cpos[slot] = make_float4(pos[3 * i], pos[3 * i + 1], pos[3 * i + 2], __int_as_float(i));
 }
 
-// One wave (one 64-thread block) per atom. FILL = false counts, FILL = true writes the
-// sorted row.
-template <bool FILL>
-__global__ void __launch_bounds__(64) k_pairs(int32_t n, CellGrid g, double rcs2,
-                                              const float* __restrict__ pos,
-                                              const int32_t* __restrict__ cell_id,
-                                              const int32_t* __restrict__ cell_start,
-                                              const int32_t* __restrict__ cell_atoms,
-                                              int32_t* __restrict__ row_ptr,
-                                              uint32_t* __restrict__ col_shift,
-                                              int32_t* __restrict__ misc) {
-  __shared__ int32_t vstart[27], vcode[27], vpre[28];
-  __shared__ uint32_t buf[FILL ? kMaxRow : 1];
-  (void)n;  // one block per atom: the grid is n blocks
-  if constexpr (FILL) (void)misc;
-  const int32_t i = blockIdx.x;
-  const int lane = threadIdx.x;
-  const double xi0 = (double)pos[3 * i], xi1 = (double)pos[3 * i + 1], xi2 = (double)pos[3 * i + 2];
-  int32_t csize = 0;
-  if (lane < 27) {
-    int c = cell_id[i];
-    int cz = c % g.nc[2], cy = (c / g.nc[2]) % g.nc[1], cx = c / (g.nc[1] * g.nc[2]);
-    int d[3] = {lane / 9 - 1, (lane / 3) % 3 - 1, lane % 3 - 1};
-    int cc[3] = {cx + d[0], cy + d[1], cz + d[2]};
-    int s[3];
-    for (int a = 0; a < 3; a++) {
-      s[a] = 0;
-      if (cc[a] < 0) { cc[a] += g.nc[a]; s[a] = -1; }
-      else if (cc[a] >= g.nc[a]) { cc[a] -= g.nc[a]; s[a] = 1; }
-    }
-    int cell = (cc[0] * g.nc[1] + cc[1]) * g.nc[2] + cc[2];
-    const int32_t c0 = cell_start[cell];
-    vstart[lane] = c0;
-    vcode[lane] = 9 * (s[0] + 1) + 3 * (s[1] + 1) + (s[2] + 1);
-    csize = cell_start[cell + 1] - c0;
+// Stencil cell v (0..26) of cell c: the neighbour cell's index and the image-shift code
+// 9(sx+1) + 3(sy+1) + (sz+1) of its wrap.
+__device__ __forceinline__ void stencil_cell(int c, int v, const CellGrid& g, int& cell,
+                                             int& code) {
+  const int cz = c % g.nc[2], cy = (c / g.nc[2]) % g.nc[1], cx = c / (g.nc[1] * g.nc[2]);
+  const int d[3] = {v / 9 - 1, (v / 3) % 3 - 1, v % 3 - 1};
+  int cc[3] = {cx + d[0], cy + d[1], cz + d[2]};
+  int sh[3];
+  for (int a = 0; a < 3; a++) {
+    sh[a] = 0;
+    if (cc[a] < 0) { cc[a] += g.nc[a]; sh[a] = -1; }
+    else if (cc[a] >= g.nc[a]) { cc[a] -= g.nc[a]; sh[a] = 1; }
   }
-  // inclusive prefix of the 27 cell sizes across lanes (wave scan), vpre[v] = start of cell v
-  {
-    int32_t inc = csize;
+  cell = (cc[0] * g.nc[1] + cc[1]) * g.nc[2] + cc[2];
+  code = 9 * (sh[0] + 1) + 3 * (sh[1] + 1) + (sh[2] + 1);
+}
+
+// The fp64 pair test (operation order fixed, contraction off): candidate at fp32 (x, y, z)
+// with shift code `code` against atom i at (xi0, xi1, xi2).
+__device__ __forceinline__ bool pair_pass(float x, float y, float z, int code, double xi0,
+                                          double xi1, double xi2, const CellGrid& g,
+                                          double rcs2) {
+  const double s0 = (double)(code / 9 - 1), s1 = (double)((code / 3) % 3 - 1),
+               s2 = (double)(code % 3 - 1);
+  const double r0 = ((double)x - xi0) + s0 * g.L[0];
+  const double r1 = ((double)y - xi1) + s1 * g.L[1];
+  const double r2 = ((double)z - xi2) + s2 * g.L[2];
+  double rr = r0 * r0 + r1 * r1;
+  rr = rr + r2 * r2;
+  return rr < rcs2;
+}
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// Pair search of one atom by one wave with the candidates read from global memory
+// (cell-sorted positions; stencil cells vstart/vcode/vpre in LDS), for cells whose stencil
+// holds more candidates than the LDS stage. FILL = false returns the count; FILL = true
+// writes the row sorted by (j, code) through the wave's LDS buffer `buf` (kMaxRow entries).
+template <bool FILL>
+__device__ int atom_row_global(int32_t i, int lane, const CellGrid& g, double rcs2,
+                               const float4* __restrict__ cpos, const int32_t* vstart,
+                               const int32_t* vcode, const int32_t* vpre,
+                               const int32_t* __restrict__ row_ptr,
+                               uint32_t* __restrict__ col_shift, uint32_t* buf,
+                               const float* __restrict__ pos) {
+  const double xi0 = (double)pos[3 * i], xi1 = (double)pos[3 * i + 1], xi2 = (double)pos[3 * i + 2];
+  const int total = vpre[27];
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int count = 0;
+  for (int q0 = 0; q0 < total; q0 += 64) {
+    const int q = q0 + lane;
+    const bool ok = q < total;
+    int lo = 0, hi = 27;  // stencil cell v with vpre[v] <= q < vpre[v+1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (vpre[mid] <= q) lo = mid; else hi = mid;
+    }
+    const float4 p = cpos[ok ? vstart[lo] + (q - vpre[lo]) : 0];
+    const int32_t j = __float_as_int(p.w);
+    const int code = vcode[lo];
+    const bool pass = ok && pair_pass(p.x, p.y, p.z, code, xi0, xi1, xi2, g, rcs2) &&
+                      !(j == i && code == 13);
+    const uint64_t m = __ballot(pass);
+    if (FILL) {
+      const int slot = count + __popcll(m & lt);
+      if (pass && slot < kMaxRow) buf[slot] = ((uint32_t)j << 5) | (uint32_t)code;
+    }
+    count += __popcll(m);
+  }
+  if (!FILL || count > kMaxRow) return count;  // long rows are rejected before the fill
+  const int64_t o = row_ptr[i];
+  wave_sync_lds();
+  int p2 = 1;
+  while (p2 < count) p2 <<= 1;
+  for (int k = count + lane; k < p2; k += 64) buf[k] = 0xFFFFFFFFu;
+  wave_sync_lds();
+  for (int k = 2; k <= p2; k <<= 1) {
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      for (int u = lane; u < (p2 >> 1); u += 64) {
+        const int a = 2 * jj * (u / jj) + (u % jj);
+        const int b = a + jj;
+        const uint32_t va = buf[a], vb = buf[b];
+        const bool up = (a & k) == 0;
+        if ((va > vb) == up) { buf[a] = vb; buf[b] = va; }
+      }
+      wave_sync_lds();
+    }
+  }
+  for (int k = lane; k < count; k += 64) {
+    const uint32_t e = buf[k];
+    col_shift[o + k] = (e >> 5) | ((e & 31u) << 27);
+  }
+  wave_sync_lds();
+  return count;
+}
+
+// Pair search with LDS-staged cell stencils: one 256-thread block per cell (the second level
+// of the three-level search). The block stages the candidates of the cell's 27-cell stencil
+// (position and entry j<<5|code, one 16-byte load each) in LDS once; the fill pass also sorts
+// them by (j, code) with a bitonic sort, so the ballot compaction of each atom's passing
+// candidates comes out in the row's order and is written to the CSR directly. The four waves
+// take the cell's atoms in turn and test them against the staged candidates in fp64 (the
+// third level). A stencil with more than kCellCap candidates (small or dense boxes) is read
+// from global memory per atom instead. FILL = false writes each atom's count to row_ptr[i].
+constexpr int kCellCap = 2048;
+template <bool FILL>
+__global__ void __launch_bounds__(256) k_cell_pairs(CellGrid g, double rcs2,
+                                                    const float* __restrict__ pos,
+                                                    const float4* __restrict__ cpos,
+                                                    const int32_t* __restrict__ cell_start,
+                                                    const int32_t* __restrict__ cell_atoms,
+                                                    int32_t* __restrict__ row_ptr,
+                                                    uint32_t* __restrict__ col_shift) {
+  __shared__ int32_t vstart[27], vcode[27], vpre[28];
+  // staged candidates (float4) and, for the fill, the sort keys (entry << 32 | index); the
+  // global-memory path reuses the space as four per-wave row buffers
+  constexpr int kBytes = kCellCap * 16 + (FILL ? kCellCap * 8 : 0);
+  static_assert(kBytes >= 4 * kMaxRow * 4, "row buffers fit the staging area");
+  __shared__ __align__(16) char smem[kBytes];
+  float4* spos = reinterpret_cast<float4*>(smem);
+  uint64_t* skey = reinterpret_cast<uint64_t*>(smem + kCellCap * 16);
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int c = (int)xcd_block(blockIdx.x, gridDim.x);
+  const int32_t a0 = cell_start[c], a1 = cell_start[c + 1];
+  if (a0 == a1) return;  // empty cell (the whole block returns)
+  if (t < 64) {
+    int32_t sz = 0;
+    if (lane < 27) {
+      int cell, code;
+      stencil_cell(c, lane, g, cell, code);
+      const int32_t s0 = cell_start[cell];
+      vstart[lane] = s0;
+      vcode[lane] = code;
+      sz = cell_start[cell + 1] - s0;
+    }
+    int32_t inc = sz;  // inclusive prefix of the 27 sizes across lanes
 #pragma unroll
     for (int o = 1; o < 32; o <<= 1) {
       const int32_t y = __shfl_up(inc, o, 64);
@@ -285,99 +392,75 @@ __global__ void __launch_bounds__(64) k_pairs(int32_t n, CellGrid g, double rcs2
   }
   __syncthreads();
   const int total = vpre[27];
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int count = 0;
-  // Candidates q0 + lane and q0 + 64 + lane are tested together (two independent load
-  // chains per lane); their ballots are consumed in candidate order.
-  for (int q0 = 0; q0 < total; q0 += 128) {
-    bool pass[2] = {false, false};
-    uint32_t entry[2] = {0u, 0u};
-    int32_t jv[2];
-    int vv[2];
-    bool ok[2];
-#pragma unroll
-    for (int h = 0; h < 2; h++) {
-      const int q = q0 + 64 * h + lane;
-      ok[h] = q < total;
-      int lo = 0, hi = 27;  // find v with vpre[v] <= q < vpre[v+1]
+  if (total > kCellCap) {  // uniform across the block
+    uint32_t* buf = reinterpret_cast<uint32_t*>(smem) + wv * kMaxRow;
+    for (int32_t k = a0 + wv; k < a1; k += 4) {
+      const int32_t i = cell_atoms[k];
+      const int cnt = atom_row_global<FILL>(i, lane, g, rcs2, cpos, vstart, vcode, vpre, row_ptr,
+                                            col_shift, buf, pos);
+      if (!FILL && lane == 0) row_ptr[i] = cnt;
+    }
+    return;
+  }
+  // stage candidate q of stencil cell v (vpre[v] <= q < vpre[v+1]); pad the keys to a power
+  // of two for the sort
+  int p2 = 1;
+  while (p2 < total) p2 <<= 1;
+  for (int q = t; q < (FILL ? p2 : total); q += 256) {
+    if (q < total) {
+      int lo = 0, hi = 27;
       while (hi - lo > 1) {
-        int mid = (lo + hi) >> 1;
+        const int mid = (lo + hi) >> 1;
         if (vpre[mid] <= q) lo = mid; else hi = mid;
       }
-      vv[h] = lo;
-      jv[h] = ok[h] ? cell_atoms[vstart[lo] + (q - vpre[lo])] : i;
+      const float4 p = cpos[vstart[lo] + (q - vpre[lo])];
+      const uint32_t entry = ((uint32_t)__float_as_int(p.w) << 5) | (uint32_t)vcode[lo];
+      spos[q] = make_float4(p.x, p.y, p.z, __uint_as_float(entry));
+      if (FILL) skey[q] = ((uint64_t)entry << 32) | (uint32_t)q;
+    } else if (FILL) {
+      skey[q] = ~0ull;
     }
-#pragma unroll
-    for (int h = 0; h < 2; h++) {
-      const int32_t j = jv[h];
-      const int code = vcode[vv[h]];
-      double s0 = (double)(code / 9 - 1), s1 = (double)((code / 3) % 3 - 1),
-             s2 = (double)(code % 3 - 1);
-      double r0 = ((double)pos[3 * j] - xi0) + s0 * g.L[0];
-      double r1 = ((double)pos[3 * j + 1] - xi1) + s1 * g.L[1];
-      double r2 = ((double)pos[3 * j + 2] - xi2) + s2 * g.L[2];
-      double rr = r0 * r0 + r1 * r1;
-      rr = rr + r2 * r2;
-      pass[h] = ok[h] && (rr < rcs2) && !(j == i && code == 13);
-      entry[h] = ((uint32_t)j << 5) | (uint32_t)code;
+  }
+  __syncthreads();
+  if (FILL) {  // bitonic sort of the keys (the entries of one stencil are distinct)
+    for (int k = 2; k <= p2; k <<= 1) {
+      for (int jj = k >> 1; jj > 0; jj >>= 1) {
+        for (int u = t; u < (p2 >> 1); u += 256) {
+          const int a = 2 * jj * (u / jj) + (u % jj);
+          const int b = a + jj;
+          const uint64_t va = skey[a], vb = skey[b];
+          const bool up = (a & k) == 0;
+          if ((va > vb) == up) { skey[a] = vb; skey[b] = va; }
+        }
+        __syncthreads();
+      }
     }
-#pragma unroll
-    for (int h = 0; h < 2; h++) {
-      uint64_t m = __ballot(pass[h]);
-      if (FILL) {
-        int slot = count + __popcll(m & lt);
-        if (pass[h] && slot < kMaxRow) buf[slot] = entry[h];
+  }
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int32_t k = a0 + wv; k < a1; k += 4) {
+    const int32_t i = cell_atoms[k];
+    const double xi0 = (double)pos[3 * i], xi1 = (double)pos[3 * i + 1],
+                 xi2 = (double)pos[3 * i + 2];
+    int count = 0;
+    const int64_t o = FILL ? (int64_t)row_ptr[i] : 0;
+    for (int q0 = 0; q0 < total; q0 += 64) {
+      const int q = q0 + lane;
+      const bool ok = q < total;
+      const int qs = ok ? (FILL ? (int)(uint32_t)skey[q] : q) : 0;
+      const float4 p = spos[qs];
+      const uint32_t entry = __float_as_uint(p.w);
+      const int32_t j = (int32_t)(entry >> 5);
+      const int code = (int)(entry & 31u);
+      const bool pass = ok && pair_pass(p.x, p.y, p.z, code, xi0, xi1, xi2, g, rcs2) &&
+                        !(j == i && code == 13);
+      const uint64_t m = __ballot(pass);
+      if (FILL && pass) {
+        const int slot = count + __popcll(m & lt);
+        if (slot < kMaxRow) col_shift[o + slot] = (uint32_t)j | ((uint32_t)code << 27);
       }
       count += __popcll(m);
     }
-  }
-  if (!FILL) {
-    if (lane == 0) row_ptr[i] = count;
-    return;
-  }
-  if (count > kMaxRow) return;  // rejected on the host before this pass runs
-  int64_t o = row_ptr[i];
-  __syncthreads();
-  if (count <= 256) {
-    // rank sort: keys within a row are distinct, so an entry's position is the number of
-    // smaller keys (the wave reads every key once, a broadcast LDS read per key)
-    uint32_t mine[4];
-    int rank[4];
-#pragma unroll
-    for (int u = 0; u < 4; u++) {
-      mine[u] = lane + 64 * u < count ? buf[lane + 64 * u] : 0xFFFFFFFFu;
-      rank[u] = 0;
-    }
-    for (int k = 0; k < count; k++) {
-      const uint32_t y = buf[k];
-#pragma unroll
-      for (int u = 0; u < 4; u++) rank[u] += y < mine[u] ? 1 : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; u++)
-      if (lane + 64 * u < count)
-        col_shift[o + rank[u]] = (mine[u] >> 5) | ((mine[u] & 31u) << 27);
-    return;
-  }
-  int p2 = 1;
-  while (p2 < count) p2 <<= 1;
-  for (int k = count + lane; k < p2; k += 64) buf[k] = 0xFFFFFFFFu;
-  __syncthreads();
-  for (int k = 2; k <= p2; k <<= 1) {
-    for (int jj = k >> 1; jj > 0; jj >>= 1) {
-      for (int t = lane; t < (p2 >> 1); t += 64) {
-        int a = 2 * jj * (t / jj) + (t % jj);
-        int b = a + jj;
-        uint32_t va = buf[a], vb = buf[b];
-        bool up = (a & k) == 0;
-        if ((va > vb) == up) { buf[a] = vb; buf[b] = va; }
-      }
-      __syncthreads();
-    }
-  }
-  for (int k = lane; k < count; k += 64) {
-    uint32_t e = buf[k];
-    col_shift[o + k] = (e >> 5) | ((e & 31u) << 27);
+    if (!FILL && lane == 0) row_ptr[i] = count;
   }
 }
 
@@ -572,6 +655,7 @@ NbrWS carve_nbr(Carver& c, int32_t n) {
   w.cell_start = c.take<int32_t>(w.ncell_cap + 1);
   w.cell_fill = c.take<int32_t>(w.ncell_cap);
   w.cell_atoms = c.take<int32_t>(nn);
+  w.cell_pos = c.take<float4>(nn);
   w.cell_id = c.take<int32_t>(nn);
   int64_t scan_len = (256 * nblk + 1 > w.ncell_cap + 1 ? 256 * nblk + 1 : w.ncell_cap + 1);
   if (nn + 1 > scan_len) scan_len = nn + 1;
@@ -634,13 +718,13 @@ int32_t build_neighbors_impl(int32_t n, const float box[3], float r_cut, float s
   k_cell_count<<<grid(n, 256), 256, 0, st>>>(n, g, pos, ws.cell_id, ws.cell_start);
   TESS_HIP_CHECK(scan_exclusive_i32(ws.cell_start, ncell + 1, ws.scan_tmp, st));
   k_cell_fill<<<grid(n, 256), 256, 0, st>>>(n, ws.cell_id, ws.cell_start, ws.cell_fill,
-                                            ws.cell_atoms);
+                                            ws.cell_atoms, pos, ws.cell_pos);
   TESS_HIP_CHECK(hipGetLastError());
   // 4. pairs: count, scan, check, fill
   TESS_HIP_CHECK(hipMemsetAsync(row_ptr + n, 0, sizeof(int32_t), st));
   TESS_TIMED("nbr_count", st,
-             k_pairs<false><<<n, 64, 0, st>>>(n, g, rcs2, pos, ws.cell_id, ws.cell_start,
-                                              ws.cell_atoms, row_ptr, nullptr, ws.misc));
+             k_cell_pairs<false><<<(unsigned)ncell, 256, 0, st>>>(
+                 g, rcs2, pos, ws.cell_pos, ws.cell_start, ws.cell_atoms, row_ptr, nullptr));
   TESS_HIP_CHECK(hipGetLastError());
   TESS_HIP_CHECK(scan_exclusive_i32(row_ptr, (int64_t)n + 1, ws.scan_tmp, st));
   // misc[0]: longest row; misc[4..5]: 64-bit pair total (the block is 256-byte aligned)
@@ -663,8 +747,8 @@ int32_t build_neighbors_impl(int32_t n, const float box[3], float r_cut, float s
   // true count; no edge_cap satisfies it
   if ((int64_t)pairs > edge_cap || pairs > (unsigned long long)INT32_MAX) return TESS_ERR_CAPACITY;
   TESS_TIMED("nbr_fill", st,
-             k_pairs<true><<<n, 64, 0, st>>>(n, g, rcs2, pos, ws.cell_id, ws.cell_start,
-                                             ws.cell_atoms, row_ptr, col_shift, ws.misc));
+             k_cell_pairs<true><<<(unsigned)ncell, 256, 0, st>>>(
+                 g, rcs2, pos, ws.cell_pos, ws.cell_start, ws.cell_atoms, row_ptr, col_shift));
   TESS_HIP_CHECK(hipGetLastError());
   if (rev) {
     k_rev<<<grid(n, 4), 256, 0, st>>>(n, row_ptr, col_shift, rev);

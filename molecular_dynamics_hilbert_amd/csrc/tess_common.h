@@ -281,7 +281,8 @@ struct NbrWS {
   float* f_tmp;       // [3n]
   int32_t* cell_start;  // [ncell_cap + 1]
   int32_t* cell_fill;   // [ncell_cap]
-  int32_t* cell_atoms;  // [n]
+  int32_t* cell_atoms;  // [n] atom indices grouped by cell
+  float4* cell_pos;     // [n] their positions (and index bits), grouped by cell
   int32_t* cell_id;     // [n]
   int32_t* scan_tmp;    // [scan partial sums]
   int32_t* misc;        // [16]: [0] max row length, [1] pair count low word
