@@ -344,15 +344,20 @@ __device__ int atom_row_global(int32_t i, int lane, const CellGrid& g, double rc
 
 // Pair search with LDS-staged cell stencils: one 256-thread block per cell (the second level
 // of the three-level search). The block stages the candidates of the cell's 27-cell stencil
-// (position and entry j<<5|code, one 16-byte load each) in LDS once; the fill pass also sorts
-// them by (j, code) with a bitonic sort, so the ballot compaction of each atom's passing
-// candidates comes out in the row's order and is written to the CSR directly. The four waves
-// take the cell's atoms in turn and test them against the staged candidates in fp64 (the
-// third level). A stencil with more than kCellCap candidates (small or dense boxes) is read
-// from global memory per atom instead. FILL = false writes each atom's count to row_ptr[i].
+// (image-shifted fp32 position and entry j<<5|code, one 16-byte load each) in LDS once; the
+// fill pass also sorts them by (j, code) with a bitonic sort, so the ballot compaction of each
+// atom's passing candidates comes out in the row's order and is written to the CSR directly.
+// The four waves take the cell's atoms in turn and test them against the staged candidates
+// (the third level). The decision is the fp64 test of pair_pass; an fp32 distance decides
+// first wherever it cannot differ from it: pairs whose fp32 squared distance lies more than
+// `band` away from (r_cut+skin)^2 (band bounds the fp32 rounding of the shifted position, the
+// difference and the squares, computed on the host) are classified by it, the few inside the
+// band by the fp64 test from the stored positions. A stencil with more than kCellCap
+// candidates (small or dense boxes) is read from global memory per atom instead (fp64 test).
+// FILL = false writes each atom's count to row_ptr[i].
 constexpr int kCellCap = 2048;
 template <bool FILL>
-__global__ void __launch_bounds__(256) k_cell_pairs(CellGrid g, double rcs2,
+__global__ void __launch_bounds__(256) k_cell_pairs(CellGrid g, double rcs2, float lo2, float hi2,
                                                     const float* __restrict__ pos,
                                                     const float4* __restrict__ cpos,
                                                     const int32_t* __restrict__ cell_start,
@@ -414,8 +419,13 @@ __global__ void __launch_bounds__(256) k_cell_pairs(CellGrid g, double rcs2,
         if (vpre[mid] <= q) lo = mid; else hi = mid;
       }
       const float4 p = cpos[vstart[lo] + (q - vpre[lo])];
-      const uint32_t entry = ((uint32_t)__float_as_int(p.w) << 5) | (uint32_t)vcode[lo];
-      spos[q] = make_float4(p.x, p.y, p.z, __uint_as_float(entry));
+      const int code = vcode[lo];
+      const uint32_t entry = ((uint32_t)__float_as_int(p.w) << 5) | (uint32_t)code;
+      // image-shifted position in fp32 (one rounding per axis)
+      const float xs = p.x + (float)(code / 9 - 1) * (float)g.L[0];
+      const float ys = p.y + (float)((code / 3) % 3 - 1) * (float)g.L[1];
+      const float zs = p.z + (float)(code % 3 - 1) * (float)g.L[2];
+      spos[q] = make_float4(xs, ys, zs, __uint_as_float(entry));
       if (FILL) skey[q] = ((uint64_t)entry << 32) | (uint32_t)q;
     } else if (FILL) {
       skey[q] = ~0ull;
@@ -439,8 +449,7 @@ __global__ void __launch_bounds__(256) k_cell_pairs(CellGrid g, double rcs2,
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int32_t k = a0 + wv; k < a1; k += 4) {
     const int32_t i = cell_atoms[k];
-    const double xi0 = (double)pos[3 * i], xi1 = (double)pos[3 * i + 1],
-                 xi2 = (double)pos[3 * i + 2];
+    const float xf0 = pos[3 * i], xf1 = pos[3 * i + 1], xf2 = pos[3 * i + 2];
     int count = 0;
     const int64_t o = FILL ? (int64_t)row_ptr[i] : 0;
     for (int q0 = 0; q0 < total; q0 += 64) {
@@ -451,8 +460,13 @@ __global__ void __launch_bounds__(256) k_cell_pairs(CellGrid g, double rcs2,
       const uint32_t entry = __float_as_uint(p.w);
       const int32_t j = (int32_t)(entry >> 5);
       const int code = (int)(entry & 31u);
-      const bool pass = ok && pair_pass(p.x, p.y, p.z, code, xi0, xi1, xi2, g, rcs2) &&
-                        !(j == i && code == 13);
+      const float dx = p.x - xf0, dy = p.y - xf1, dz = p.z - xf2;
+      const float d2 = __builtin_fmaf(dz, dz, __builtin_fmaf(dy, dy, dx * dx));
+      bool near = d2 < lo2;
+      if (ok && !near && d2 <= hi2)  // inside the band: the fp64 test decides
+        near = pair_pass(pos[3 * j], pos[3 * j + 1], pos[3 * j + 2], code, (double)xf0,
+                         (double)xf1, (double)xf2, g, rcs2);
+      const bool pass = ok && near && !(j == i && code == 13);
       const uint64_t m = __ballot(pass);
       if (FILL && pass) {
         const int slot = count + __popcll(m & lt);
@@ -491,29 +505,68 @@ __global__ void __launch_bounds__(256) k_max_row(int32_t n, const int32_t* __res
   }
 }
 
-// rev[e] for every pair of row i: position of (j <- i, 26 - code) in row j (rows are sorted
-// by (j, code)). One wave per row.
+// rev[e] = slot of the reverse pair (j <- i, 26 - code) of entry e = (i <- j, code); rows are
+// sorted by (j, code). Each pair is searched once, from the row of its smaller index: for an
+// entry with j >= i the lane binary-searches row j for (i, 26 - code) and writes both
+// directions. One wave takes kRevRows consecutive rows: their j >= i entries are compacted
+// into LDS first, so every lane runs two interleaved searches (independent load chains).
+constexpr int kRevRows = 2;
 __global__ void __launch_bounds__(256) k_rev(int32_t n, const int32_t* __restrict__ row_ptr,
                                              const uint32_t* __restrict__ col,
                                              int32_t* __restrict__ rev) {
-  int32_t i = blockIdx.x * 4 + (threadIdx.x >> 6);
-  int lane = threadIdx.x & 63;
-  if (i >= n) return;
-  int32_t b = row_ptr[i], e_end = row_ptr[i + 1];
-  // two entries per lane, their binary searches interleaved (independent load chains)
-  for (int32_t e0 = b + lane; e0 < e_end; e0 += 128) {
-    int32_t lo[2], hi[2];
+  __shared__ int32_t se[4][128];
+  __shared__ uint32_t sw[4][128];
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int32_t i0 = (blockIdx.x * 4 + wv) * kRevRows;
+  if (i0 >= n) return;
+  const int32_t i1 = min(i0 + kRevRows, n);
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int32_t b = row_ptr[i0], e_end = row_ptr[i1];
+  int32_t i = i0;  // row of entry b + lane advances with the entries
+  for (int32_t base = b; base < e_end;) {
+    // compact up to 128 searching entries (j >= i) of [base, e_end) into LDS
+    int cnt = 0;
+    int32_t e = base;
+    while (e < e_end && cnt <= 64) {
+      const int32_t ee = e + lane;
+      bool want = false;
+      uint32_t key = 0;
+      if (ee < e_end) {
+        int32_t r = i;
+        while (row_ptr[r + 1] <= ee) r++;  // rows of the wave's range, ascending
+        const uint32_t c = col[ee];
+        const int32_t j = (int32_t)(c & 0x7FFFFFFu);
+        want = j >= r;
+        key = ((uint32_t)r << 5) | (26u - (c >> 27));
+      }
+      const uint64_t m = __ballot(want);
+      if (want) {
+        const int slot = cnt + __popcll(m & lt);
+        se[wv][slot] = ee;
+        sw[wv][slot] = key;
+      }
+      cnt += __popcll(m);
+      e += 64;
+    }
+    base = e;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    int32_t lo[2], hi[2], ei[2];
     uint32_t want[2];
-    bool ok[2];
 #pragma unroll
     for (int h = 0; h < 2; h++) {
-      const int32_t e = e0 + 64 * h;
-      ok[h] = e < e_end;
-      const uint32_t c = col[ok[h] ? e : e0];
-      const int32_t j = (int32_t)(c & 0x7FFFFFFu);
-      want[h] = ((uint32_t)i << 5) | (26u - (c >> 27));
-      lo[h] = ok[h] ? row_ptr[j] : 0;
-      hi[h] = ok[h] ? row_ptr[j + 1] : 0;
+      const int k = lane + 64 * h;
+      lo[h] = hi[h] = 0;
+      ei[h] = -1;
+      want[h] = 0;
+      if (k < cnt) {
+        ei[h] = se[wv][k];
+        want[h] = sw[wv][k];
+        const int32_t j = (int32_t)(col[ei[h]] & 0x7FFFFFFu);
+        lo[h] = row_ptr[j];
+        hi[h] = row_ptr[j + 1];
+      }
     }
     while (lo[0] < hi[0] || lo[1] < hi[1]) {
 #pragma unroll
@@ -528,7 +581,15 @@ __global__ void __launch_bounds__(256) k_rev(int32_t n, const int32_t* __restric
     }
 #pragma unroll
     for (int h = 0; h < 2; h++)
-      if (ok[h]) rev[e0 + 64 * h] = lo[h];
+      if (ei[h] >= 0) {
+        rev[ei[h]] = lo[h];
+        rev[lo[h]] = ei[h];
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    // the row of the next entries
+    while (i < i1 - 1 && row_ptr[i + 1] <= base) i++;
   }
 }
 
@@ -633,7 +694,7 @@ hipError_t scan_exclusive_i32_pair(int32_t* a, int32_t* b, int64_t n, int32_t* p
 hipError_t rev_index(int32_t n, const int32_t* row_ptr, const uint32_t* col, int32_t* rev,
                      hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  k_rev<<<grid(n, 4), 256, 0, s>>>(n, row_ptr, col, rev);
+  k_rev<<<grid(n, 4 * kRevRows), 256, 0, s>>>(n, row_ptr, col, rev);
   return hipGetLastError();
 }
 
@@ -722,9 +783,16 @@ int32_t build_neighbors_impl(int32_t n, const float box[3], float r_cut, float s
   TESS_HIP_CHECK(hipGetLastError());
   // 4. pairs: count, scan, check, fill
   TESS_HIP_CHECK(hipMemsetAsync(row_ptr + n, 0, sizeof(int32_t), st));
+  // fp32 pre-decision band around (r_cut+skin)^2: bounds the fp32 error of the shifted
+  // position (|x + sL| <= 2L), the difference and the fused squares for |d| <= r_cut+skin+2,
+  // with a factor 16 to spare (u = 2^-24)
+  const double Lmax = fmax(L[0], fmax(L[1], L[2]));
+  const double band = 16.0 * ldexp(1.0, -24) * (2.0 * Lmax + rcs + 2.0) * (rcs + 2.0);
+  const float lo2 = (float)(rcs2 - band), hi2 = (float)(rcs2 + band);
   TESS_TIMED("nbr_count", st,
              k_cell_pairs<false><<<(unsigned)ncell, 256, 0, st>>>(
-                 g, rcs2, pos, ws.cell_pos, ws.cell_start, ws.cell_atoms, row_ptr, nullptr));
+                 g, rcs2, lo2, hi2, pos, ws.cell_pos, ws.cell_start, ws.cell_atoms, row_ptr,
+                 nullptr));
   TESS_HIP_CHECK(hipGetLastError());
   TESS_HIP_CHECK(scan_exclusive_i32(row_ptr, (int64_t)n + 1, ws.scan_tmp, st));
   // misc[0]: longest row; misc[4..5]: 64-bit pair total (the block is 256-byte aligned)
@@ -748,10 +816,11 @@ int32_t build_neighbors_impl(int32_t n, const float box[3], float r_cut, float s
   if ((int64_t)pairs > edge_cap || pairs > (unsigned long long)INT32_MAX) return TESS_ERR_CAPACITY;
   TESS_TIMED("nbr_fill", st,
              k_cell_pairs<true><<<(unsigned)ncell, 256, 0, st>>>(
-                 g, rcs2, pos, ws.cell_pos, ws.cell_start, ws.cell_atoms, row_ptr, col_shift));
+                 g, rcs2, lo2, hi2, pos, ws.cell_pos, ws.cell_start, ws.cell_atoms, row_ptr,
+                 col_shift));
   TESS_HIP_CHECK(hipGetLastError());
   if (rev) {
-    k_rev<<<grid(n, 4), 256, 0, st>>>(n, row_ptr, col_shift, rev);
+    k_rev<<<grid(n, 4 * kRevRows), 256, 0, st>>>(n, row_ptr, col_shift, rev);
     TESS_HIP_CHECK(hipGetLastError());
   }
   return TESS_OK;
