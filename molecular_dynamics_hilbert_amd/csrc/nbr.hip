@@ -517,7 +517,9 @@ __global__ void __launch_bounds__(256) k_rev(int32_t n, const int32_t* __restric
   __shared__ int32_t se[4][128];
   __shared__ uint32_t sw[4][128];
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int32_t i0 = (blockIdx.x * 4 + wv) * kRevRows;
+  // XCD-aware block order: each XCD walks one contiguous range of rows, whose target rows
+  // (spatial neighbours, nearby in curve order) then share that XCD's L2
+  const int32_t i0 = ((int32_t)xcd_block(blockIdx.x, gridDim.x) * 4 + wv) * kRevRows;
   if (i0 >= n) return;
   const int32_t i1 = min(i0 + kRevRows, n);
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));

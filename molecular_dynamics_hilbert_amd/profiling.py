@@ -112,8 +112,35 @@ def write_summaries(stats_csv: str, fetch_csv: str, write_csv: str, kernel_key: 
         f.write("\n".join(md) + "\n")
 
 
+REBUILD_KERNELS = ("k_wrap_key", "k_radix_hist", "k_radix_scatter", "k_scan_partial", "k_scan_sums",
+                   "k_scan_final", "k_permute", "k_cell_count", "k_cell_fill", "k_cell_pairs",
+                   "k_max_row", "k_rev")
+
+
+def rebuild_md(stats_csv: str, workload: str, command: str, calls_per_rebuild: dict = None) -> str:
+    """Kernel statistics of the neighbour-rebuild kernels alone."""
+    rows = [r for r in csv.DictReader(open(stats_csv))
+            if short_name(r["Name"]).split("<")[0] in REBUILD_KERNELS]
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    out = ["# Neighbour rebuild at %s: rocprofv3 kernel statistics" % workload, "",
+           "Command (run from the repository root):", "", "    " + command, "",
+           "| kernel | calls | avg us | min us | max us |", "|---|---:|---:|---:|---:|"]
+    for r in rows:
+        out.append("| %s | %s | %.1f | %.1f | %.1f |" % (
+            short_name(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3,
+            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+    out += ["", "Source digest: %s." % source_digest()]
+    return "\n".join(out) + "\n"
+
+
 def main(argv):
-    if argv[0] == "stats":
+    if argv[0] == "rebuild":
+        # rebuild <stats_csv> <workload> <out_md> <command...>
+        md = rebuild_md(argv[1], argv[2], " ".join(argv[4:]))
+        with open(argv[3], "w") as f:
+            f.write(md)
+        print(md)
+    elif argv[0] == "stats":
         print(kernel_stats_md(argv[1]))
     elif argv[0] == "summarize":
         # summarize <prof_dir> <pmc_fetch_dir> <pmc_write_dir> <kernel_key> <kernel_name> <workload> <copy_mib>
