@@ -26,9 +26,12 @@
  *  - Device status word: the first 4 bytes of the workspace. Kernels record problems they
  *    find on the device there (asynchronously): a species index outside [0, n_species) seen
  *    by the energy pass, and a non-finite position (neighbour build), energy or force (energy
- *    pass). The next synchronising call on that workspace -- tess_check_status,
- *    tess_build_neighbors or tess_md_steps -- returns TESS_ERR_SPECIES (first) or
- *    TESS_ERR_NONFINITE and clears the word. A fresh workspace must start with that word zero
+ *    pass), and a radial network whose interpolation table deviates from it by more than
+ *    1e-6 of max|w| or 1e-4 of max|dw/dr| at the knot intervals' midpoints (energy pass; the
+ *    radial weights are interpolated from a per-call table of 1,024 intervals on [0, r_cut]).
+ *    The next synchronising call on that workspace -- tess_check_status,
+ *    tess_build_neighbors or tess_md_steps -- returns TESS_ERR_SPECIES (first),
+ *    TESS_ERR_NONFINITE or TESS_ERR_RADIAL and clears the word. A fresh workspace must start with that word zero
  *    (zero-filled memory, or one tess_check_status call). The Tessera abstract reports runs
  *    with no broken bonds or anomalously close pairs; this is the device-side check that a
  *    run has not blown up.
@@ -55,7 +58,8 @@ typedef enum {
   TESS_ERR_SKIN = -6,      /* an atom moved more than skin/2 since the last rebuild */
   TESS_ERR_SPECIES = -7,   /* species index outside [0, n_species) (device status word) */
   TESS_ERR_NONFINITE = -8, /* non-finite position, energy or force (device status word) */
-  TESS_ERR_ROW = -9        /* an atom has more than 1024 candidate neighbours */
+  TESS_ERR_ROW = -9,       /* an atom has more than 1024 candidate neighbours */
+  TESS_ERR_RADIAL = -10    /* radial network too rough for the interpolation table (status word) */
 } tess_status;
 
 /* Model hyper-parameters. Paths P follow from l_max (4 for l_max 1, 11 for l_max 2). */
@@ -69,8 +73,8 @@ const char* tess_status_string(int32_t status);
 
 /* tess_check_status -- synchronises `hip_stream`, reads and clears the device status word of
  * `workspace` (any workspace of tess_workspace_bytes(); at least 4 bytes, 16-byte aligned).
- * Returns TESS_OK, TESS_ERR_SPECIES or TESS_ERR_NONFINITE (TESS_ERR_WORKSPACE for a bad
- * pointer or size). */
+ * Returns TESS_OK, TESS_ERR_SPECIES, TESS_ERR_NONFINITE or TESS_ERR_RADIAL
+ * (TESS_ERR_WORKSPACE for a bad pointer or size). */
 int32_t tess_check_status(void* workspace, int64_t ws_bytes, void* hip_stream);
 
 /* Number of fp32 weights. Blob order (row-major [out][in], y = W x): Emb[S][C]; for each

@@ -442,6 +442,7 @@ const char* tess_status_string(int32_t s) {
     case TESS_ERR_SPECIES: return "species index out of range";
     case TESS_ERR_NONFINITE: return "non-finite position, energy or force";
     case TESS_ERR_ROW: return "an atom has more than 1024 candidate neighbours";
+    case TESS_ERR_RADIAL: return "radial network too rough for the interpolation table";
     default: return "unknown status";
   }
 }

@@ -418,16 +418,11 @@ __device__ __forceinline__ void radial8(float r, float rc, RadialOut& o) {
 // against the MLP at 2e5 random distances), about fp32 rounding.
 // Table layout: [layer][knot][24]: w_0..w_11 (zero past P), then dw_0..dw_11.
 // ---------------------------------------------------------------------------------------
+// The radial MLP of one layer and its r-derivative in fp64 at distance r (r = 0: the basis
+// takes its limit).
 template <int P>
-__global__ void __launch_bounds__(256) k_radial_table(const float* __restrict__ W1_0,
-                                                      int64_t lstride, int R, float rc,
-                                                      float* __restrict__ tab) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;  // knot
-  const int t = blockIdx.y;                             // layer
-  if (i > kRadKnots) return;
-  const float* W1 = W1_0 + (int64_t)t * lstride;  // [R][8]
-  const float* W2 = W1 + (int64_t)R * 8;          // [P][R]
-  const double rcd = (double)rc, r = (double)i * (rcd / kRadKnots);
+__device__ void radial_mlp_fp64(const float* __restrict__ W1, const float* __restrict__ W2,
+                                int R, double rcd, double r, double* w, double* dw) {
   const double wk = 3.14159265358979323846 / rcd, pref = sqrt(2.0 / rcd);
   const double u = 0.5 * (cos(wk * r) + 1.0), du = -0.5 * wk * sin(wk * r);
   double b[8], db[8];
@@ -435,7 +430,7 @@ __global__ void __launch_bounds__(256) k_radial_table(const float* __restrict__ 
   for (int k = 0; k < 8; k++) {
     const double a = (double)(k + 1) * wk;
     double B, dB;
-    if (i == 0) {  // sin(a r)/r -> a, and its derivative -> 0
+    if (r == 0.0) {  // sin(a r)/r -> a, and its derivative -> 0
       B = pref * a;
       dB = 0.0;
     } else {
@@ -446,7 +441,6 @@ __global__ void __launch_bounds__(256) k_radial_table(const float* __restrict__ 
     b[k] = u * B;
     db[k] = du * B + u * dB;
   }
-  double w[P], dw[P];
 #pragma unroll
   for (int p = 0; p < P; p++) { w[p] = 0.0; dw[p] = 0.0; }
   for (int h = 0; h < R; h++) {
@@ -464,12 +458,79 @@ __global__ void __launch_bounds__(256) k_radial_table(const float* __restrict__ 
       dw[p] += (double)W2[p * R + h] * dact;
     }
   }
+}
+
+template <int P>
+__global__ void __launch_bounds__(256) k_radial_table(const float* __restrict__ W1_0,
+                                                      int64_t lstride, int R, float rc,
+                                                      float* __restrict__ tab) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;  // knot
+  const int t = blockIdx.y;                             // layer
+  if (i > kRadKnots) return;
+  const float* W1 = W1_0 + (int64_t)t * lstride;  // [R][8]
+  const float* W2 = W1 + (int64_t)R * 8;          // [P][R]
+  const double rcd = (double)rc;
+  double w[P], dw[P];
+  radial_mlp_fp64<P>(W1, W2, R, rcd, (double)i * (rcd / kRadKnots), w, dw);
   float* o = tab + ((int64_t)t * (kRadKnots + 1) + i) * 24;
 #pragma unroll
   for (int p = 0; p < 12; p++) {
     o[p] = p < P ? (float)w[p] : 0.0f;
     o[12 + p] = p < P ? (float)dw[p] : 0.0f;
   }
+}
+
+// Guard of the table: at the midpoint of every interval the exact MLP (fp64) is compared with
+// the Hermite interpolant of the stored (fp32) knots, evaluated in fp64. Per layer the largest
+// deviations of w and dw/dr and the largest |w|, |dw/dr| there are kept as float bits
+// (non-negative floats order like their bit patterns) in acc[4 t .. 4 t + 3].
+template <int P>
+__global__ void __launch_bounds__(256) k_radial_check(const float* __restrict__ W1_0,
+                                                      int64_t lstride, int R, float rc,
+                                                      const float* __restrict__ tab,
+                                                      uint32_t* __restrict__ acc) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;  // interval
+  const int t = blockIdx.y;                             // layer
+  float ew = 0.0f, ed = 0.0f, mw = 0.0f, md = 0.0f;
+  if (i < kRadKnots) {
+    const float* W1 = W1_0 + (int64_t)t * lstride;
+    const float* W2 = W1 + (int64_t)R * 8;
+    const double rcd = (double)rc, h = rcd / kRadKnots;
+    double w[P], dw[P];
+    radial_mlp_fp64<P>(W1, W2, R, rcd, ((double)i + 0.5) * h, w, dw);
+    const float* k0 = tab + ((int64_t)t * (kRadKnots + 1) + i) * 24;
+    const float* k1 = k0 + 24;
+    // cubic Hermite at t = 1/2: w = (w0 + w1)/2 + h (g0 - g1)/8; dw = 1.5 (w1 - w0)/h - (g0 + g1)/4
+#pragma unroll
+    for (int p = 0; p < P; p++) {
+      const double w0 = k0[p], w1 = k1[p], g0 = k0[12 + p], g1 = k1[12 + p];
+      const double wi = 0.5 * (w0 + w1) + 0.125 * h * (g0 - g1);
+      const double di = 1.5 * (w1 - w0) / h - 0.25 * (g0 + g1);
+      ew = fmaxf(ew, (float)fabs(wi - w[p]));
+      ed = fmaxf(ed, (float)fabs(di - dw[p]));
+      mw = fmaxf(mw, (float)fabs(w[p]));
+      md = fmaxf(md, (float)fabs(dw[p]));
+    }
+  }
+  ew = wave_max(ew); ed = wave_max(ed); mw = wave_max(mw); md = wave_max(md);
+  if ((threadIdx.x & 63) == 0) {
+    atomicMax(acc + 4 * t, __float_as_uint(ew));
+    atomicMax(acc + 4 * t + 1, __float_as_uint(ed));
+    atomicMax(acc + 4 * t + 2, __float_as_uint(mw));
+    atomicMax(acc + 4 * t + 3, __float_as_uint(md));
+  }
+}
+
+// Flags kStatusRadial when some layer's midpoint deviation exceeds 1e-6 of max|w| or 1e-4 of
+// max|dw/dr| (for the random-init models: about 6e-10 and 2e-7), i.e. when the radial network
+// is too rough for the table's knot spacing. One thread per layer.
+__global__ void k_radial_verdict(int T, const uint32_t* __restrict__ acc,
+                                 int32_t* __restrict__ status) {
+  const int t = threadIdx.x;
+  if (t >= T) return;
+  const float ew = __uint_as_float(acc[4 * t]), ed = __uint_as_float(acc[4 * t + 1]);
+  const float mw = __uint_as_float(acc[4 * t + 2]), md = __uint_as_float(acc[4 * t + 3]);
+  if (!(ew <= 1e-6f * mw) || !(ed <= 1e-4f * md)) atomicOr(status, kStatusRadial);
 }
 
 // Radial weights w and dw/dr of layers t_begin..t_end-1 for each active edge from the table, written at
@@ -1668,6 +1729,7 @@ struct EFWS {
   float4* sbar;
   float4* l0tab;  // first layer: logits of every (destination species, source species) pair
   float* rtab;    // per layer: radial weights and their r-derivatives at the table's knots
+  uint32_t* rchk;  // per layer: the table guard's deviations and scales (float bits)
   double* epart;
   int32_t* scan_tmp;
 };
@@ -1712,6 +1774,7 @@ static EFWS carve_ef(Carver& cv, const tess_model_desc& md, int32_t n, int64_t c
   w.sbar = cv.take<float4>(ec);
   w.l0tab = cv.take<float4>(16 * 16);
   w.rtab = cv.take<float>(T * (kRadKnots + 1) * 24);
+  w.rchk = cv.take<uint32_t>(4 * T);
   w.epart = cv.take<double>(nn / 256 + 2);
   w.scan_tmp = cv.take<int32_t>(nn / 4096 + 4);
   return w;
@@ -1739,7 +1802,7 @@ struct LayerW {
 // cannot be created (or the first call comes under capture), every kernel runs on the
 // caller's stream in the same order.
 constexpr int kEvFwdFork = 0, kEvFwdJoin = 1, kEvBwdFork = 2, kEvBwdJoin = 3, kEvTabFork = 4,
-              kEvTabDone = 5, kAuxEvents = 6;
+              kEvTabDone = 5, kEvChkDone = 6, kAuxEvents = 7;
 struct AuxStream {
   bool tried = false, ok = false;
   hipStream_t s = nullptr;
@@ -1820,10 +1883,19 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
   // radial-weight table of every layer: it depends on the weights only and runs on the second
   // stream next to the active-edge list (joined before the interpolation)
   if (ax) TESS_HIP_CHECK(stream_after(ax, kEvTabFork, st, sb));
-  k_radial_table<P><<<dim3(gridn(kRadKnots + 1, 256), T), 256, 0, sb>>>(
-      lw[0].W1, (int64_t)(2 * C * C + R * K + P * R + G * C + LMAX * C * C), R, rc, w.rtab);
+  const int64_t lstride = (int64_t)(2 * C * C + R * K + P * R + G * C + LMAX * C * C);
+  k_radial_table<P><<<dim3(gridn(kRadKnots + 1, 256), T), 256, 0, sb>>>(lw[0].W1, lstride, R,
+                                                                        rc, w.rtab);
   TESS_HIP_CHECK(hipGetLastError());
   if (ax) TESS_HIP_CHECK(hipEventRecord(ax->ev[kEvTabDone], sb));
+  // the table's guard runs behind it on the same stream, next to the forward pass (joined
+  // before the energy is summed)
+  k_fill_i32<<<1, 64, 0, sb>>>(reinterpret_cast<int32_t*>(w.rchk), 4 * T, 0);
+  k_radial_check<P><<<dim3(gridn(kRadKnots, 256), T), 256, 0, sb>>>(lw[0].W1, lstride, R, rc,
+                                                                    w.rtab, w.rchk);
+  k_radial_verdict<<<1, 64, 0, sb>>>(T, w.rchk, status);
+  TESS_HIP_CHECK(hipGetLastError());
+  if (ax) TESS_HIP_CHECK(hipEventRecord(ax->ev[kEvChkDone], sb));
   const int64_t NDC = (int64_t)n * D * C;
   // embedding
   k_embed<<<gridn((int64_t)n * C, 256), 256, 0, st>>>(n, C, D, S, species, emb, w.h, status);
@@ -1948,6 +2020,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
   const float* hT = w.h + (int64_t)T * NDC;
   int32_t nb = gridn(n, 256);
   if (nb > 0) k_readout<<<nb, 256, 0, st>>>(n, C, D, hT, wE, e_atom, w.epart);
+  if (ax) TESS_HIP_CHECK(hipStreamWaitEvent(st, ax->ev[kEvChkDone], 0));
   k_energy_final<<<1, 256, 0, st>>>(nb, w.epart, energy, status);
   TESS_HIP_CHECK(hipGetLastError());
   if (!forces) return TESS_OK;

@@ -263,10 +263,13 @@ struct Carver {
 // them (tess_check_status, tess_build_neighbors, tess_md_steps).
 constexpr int32_t kStatusSpecies = 1;    // a species index outside [0, n_species)
 constexpr int32_t kStatusNonFinite = 2;  // a non-finite position, energy or force
-// Error code of a status word (species first), TESS_OK for 0.
+constexpr int32_t kStatusRadial = 4;     // radial MLP too rough for the interpolation table
+// Error code of a status word (species first, then non-finite values), TESS_OK for 0.
 inline int32_t status_error(int32_t bits) {
   return (bits & kStatusSpecies) ? TESS_ERR_SPECIES
-                                 : ((bits & kStatusNonFinite) ? TESS_ERR_NONFINITE : TESS_OK);
+         : (bits & kStatusNonFinite) ? TESS_ERR_NONFINITE
+         : (bits & kStatusRadial) ? TESS_ERR_RADIAL
+                                  : TESS_OK;
 }
 
 // Neighbour-build scratch (a prefix of every workspace).

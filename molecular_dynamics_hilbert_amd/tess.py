@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libtess.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "tess.h")
 
 (OK, ERR_ARG, ERR_BOX, ERR_CAPACITY, ERR_WORKSPACE, ERR_HIP, ERR_SKIN, ERR_SPECIES,
- ERR_NONFINITE, ERR_ROW) = (0, -1, -2, -3, -4, -5, -6, -7, -8, -9)
+ ERR_NONFINITE, ERR_ROW, ERR_RADIAL) = (0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10)
 MD_FORCES_VALID = 1
 MD_GRAPH = 2
 

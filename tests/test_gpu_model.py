@@ -355,3 +355,33 @@ def test_status_word_species_and_nonfinite(T):
     assert st == T.ERR_NONFINITE
     assert T.check_status(s.ws, check=False) == T.OK
     torch.cuda.synchronize()
+
+
+def _scale_w1(spec, w, scale):
+    """Weights with every layer's first radial matrix W1 scaled (sharper radial functions)."""
+    w = w.copy()
+    S, C, T, R, K = spec.n_species, spec.channels, spec.n_layers, spec.radial_hidden, 8
+    P = 11 if spec.l_max == 2 else 4
+    G = C * (1 + spec.l_max)
+    off = S * C
+    for _ in range(T):
+        off += 2 * C * C
+        w[off:off + R * K] *= scale
+        off += R * K + P * R + G * C + spec.l_max * C * C
+    return w
+
+
+def test_radial_table_sharper_weights_and_guard(T, oracle_mod):
+    """W1 scaled by 4: the interpolated radial weights still give oracle parity and the table
+    guard stays quiet; scaled by 32 the guard reports TESS_ERR_RADIAL."""
+    wl = W.load("salt4k")
+    w4 = _scale_w1(wl.model, W.make_weights(wl.model, 2002), 4.0)
+    g = _run(T, wl, w4)
+    assert T.check_status(g["sys"].ws, check=False) == T.OK
+    nb = oracle_mod.build_neighbors(wl.box, wl.pos, wl.species, wl.model.r_cut, wl.skin)
+    ref = oracle_mod.energy_forces(wl.model, w4, wl.box, nb["pos"].astype(np.float64),
+                                   nb["species"], nb["row_ptr"], nb["col_shift"])
+    _assert_ef(g["energy"], g["forces"], ref["energy"], ref["forces"], "salt4k W1x4")
+    w32 = _scale_w1(wl.model, W.make_weights(wl.model, 2002), 32.0)
+    g = _run(T, wl, w32)
+    assert T.check_status(g["sys"].ws, check=False) == T.ERR_RADIAL

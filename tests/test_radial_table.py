@@ -93,3 +93,30 @@ def test_interpolant_is_c1_at_the_knots():
     assert np.abs(dwl - dwr).max() <= 1e-6 * np.abs(dwk).max()
     # w and dw/dr vanish at r_c (envelope), so the table ends smoothly at the cutoff
     assert np.abs(wk[-1]).max() <= 1e-12 * np.abs(wk).max()
+
+
+def _midpoint_deviation(W1, W2, rc):
+    """The library's table guard in numpy: fp32-stored knots, Hermite at the interval
+    midpoints (fp64) against the MLP; deviations relative to the midpoints' max |w|, |dw/dr|."""
+    h = rc / NK
+    knots = np.arange(NK + 1) * h
+    mids = (np.arange(NK) + 0.5) * h
+    wk, dwk = _mlp(knots, W1, W2, rc)
+    wk, dwk = wk.astype(np.float32).astype(np.float64), dwk.astype(np.float32).astype(np.float64)
+    wi, dwi = _hermite(mids, wk, dwk, h)
+    we, dwe = _mlp(mids, W1, W2, rc)
+    return np.abs(wi - we).max() / np.abs(we).max(), np.abs(dwi - dwe).max() / np.abs(dwe).max()
+
+
+def test_table_guard_thresholds():
+    """The guard flags a layer whose midpoint deviation exceeds 1e-6 of max|w| or 1e-4 of
+    max|dw/dr|. The benchmark's weights, and the same with W1 scaled by 4 (sharper radial
+    functions; the GPU parity test uses them), stay inside (the stored fp32 knots dominate:
+    about 5e-8 and 1e-5); W1 scaled by 32 is flagged."""
+    spec = W.big_model()
+    w = W.make_weights(spec, 2003)
+    rc = float(spec.r_cut)
+    for scale, inside in ((1.0, True), (4.0, True), (32.0, False)):
+        dev = [_midpoint_deviation(W1 * scale, W2, rc) for W1, W2 in _layers(spec, w)]
+        ok = all(a <= 1e-6 and b <= 1e-4 for a, b in dev)
+        assert ok == inside, (scale, dev)
