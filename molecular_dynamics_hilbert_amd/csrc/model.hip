@@ -62,31 +62,17 @@ struct Epi {
 };
 
 // Block tile 128 rows x 64 columns, 4 waves of 32 x 64 (two 32x32 MFMA tiles each). The
-// block's K x 64 slice of Wt is staged in LDS once, while the block's X rows are in flight. Each lane loads its row of X with float4
-// loads: lanes 0-31 take k = 8s..8s+3 and lanes 32-63 k = 8s+4..8s+7, so MFMA step (s, q)
-// pairs k = 8s+q (first half-wave) with k = 8s+4+q (second half-wave), and the B operand
-// uses the same pairing. K must be a multiple of 16 and at most kGemmMaxK.
-// Offsets of output row v of a lane (row r0 + 8(v/4) + 4(lane/32) + v%4) in y, h and the
-// gates; rows past M are clamped (and flagged) so that loads stay in bounds. One 32-bit
-// division by the rows-per-node count (row maps of y and h share it).
-struct EpiRow {
-  int64_t yb, hb, gb;
-  bool ok;
-};
-__device__ __forceinline__ EpiRow epi_row(const Epi& ep, int64_t r0, int v, int lane, int64_t M) {
-  const int64_t r = r0 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-  EpiRow e;
-  e.ok = r < M;
-  const uint32_t rr = (uint32_t)(e.ok ? r : M - 1);
-  const uint32_t rpn = (uint32_t)ep.ym.rpn;
-  const uint32_t nd = rr / rpn;
-  const int32_t kc = (int32_t)(rr - nd * rpn);
-  e.yb = (int64_t)nd * ep.ym.nstride + (int64_t)(ep.ym.c0 + kc) * ep.ym.cstride;
-  e.hb = (int64_t)nd * ep.hm.nstride + (int64_t)(ep.hm.c0 + kc) * ep.hm.cstride;
-  e.gb = (int64_t)nd * ep.gstride + ep.goff;
-  return e;
-}
-
+// block's K x 64 slice of Wt is staged in LDS once, while the block's X rows are in flight.
+// The MFMAs form the transposed tile (Wt^T X^T), so that a lane ends with 16 columns of ONE
+// output row, in four runs of 4 consecutive columns: the epilogue then reads its inputs and
+// writes its outputs as float4 at one row offset per lane (a layout with a column per lane
+// would need 4x as many scalar memory instructions and a row offset per element). Each lane
+// loads its row of X with float4 loads: lanes 0-31 take k = 8s..8s+3 and lanes 32-63
+// k = 8s+4..8s+7, so MFMA step (s, q) pairs k = 8s+q (first half-wave) with k = 8s+4+q
+// (second half-wave), and the Wt operand uses the same pairing. K must be a multiple of 16
+// and at most kGemmMaxK; O, the row maps' strides and offsets, the gate stride and offset and
+// cdim are multiples of 4 and the arrays 16-byte aligned (checked by the launcher, except the
+// alignment of the base pointers, which are workspace or weight-blob carvings).
 constexpr int kGemmMaxK = 192;
 
 template <int EPI, int K>
@@ -95,11 +81,11 @@ __global__ void __launch_bounds__(256) k_gemm(int64_t M, int O, const float* __r
   static_assert(K % 16 == 0 && K <= kGemmMaxK, "K is a multiple of 16, at most kGemmMaxK");
   __shared__ float Ws[K][64 + 1];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int64_t r0 = (int64_t)blockIdx.x * 128 + w * 32;
+  const int col = lane & 31, hf = lane >> 5;
+  const int64_t row = (int64_t)blockIdx.x * 128 + w * 32 + col;
   const int o0 = blockIdx.y * 64;
-  const int64_t row = r0 + (lane & 31);
   const bool row_ok = row < M;
-  const int kh = (lane >> 5) * 4;
+  const int kh = hf * 4;
   float4 xa[K / 8];
   if (row_ok) {
     const float* xr = X + row_off(xm, row);
@@ -129,32 +115,35 @@ __global__ void __launch_bounds__(256) k_gemm(int64_t M, int O, const float* __r
       Ws[kk][oo + 3] = v.w;
     }
   }
-  // epilogue inputs of this lane's 32 elements (rows r0 + 8(v/4) + 4 half + v%4, columns
-  // o0 + col and o0 + 32 + col), requested before the MFMA loop
-  const int col = lane & 31;
-  bool ook[2], hok[2];
+  // this lane's output row (clamped past M so that the loads below stay in bounds): its
+  // offsets in y, h and the gates, with one 32-bit division by the rows-per-node count (the
+  // row maps of y and h share it)
+  const uint32_t rr = (uint32_t)(row_ok ? row : M - 1);
+  const uint32_t rpn = (uint32_t)ep.ym.rpn;
+  const uint32_t nd = rr / rpn;
+  const int32_t kc = (int32_t)(rr - nd * rpn);
+  const int64_t yb = (int64_t)nd * ep.ym.nstride + (int64_t)(ep.ym.c0 + kc) * ep.ym.cstride;
+  const int64_t hb = (int64_t)nd * ep.hm.nstride + (int64_t)(ep.hm.c0 + kc) * ep.hm.cstride;
+  const int64_t gb = (int64_t)nd * ep.gstride + ep.goff;
+  // epilogue inputs at columns o0 + 32 nt + 8 g + 4 hf .. + 3, requested before the MFMA
+  // loop from clamped columns (a load under a branch would be waited for inside the branch);
+  // values of columns outside the output are never used
+  float4 in0[2][4], in1[2][4];
 #pragma unroll
-  for (int nt = 0; nt < 2; nt++) {
-    ook[nt] = o0 + 32 * nt + col < O;
-    hok[nt] = ook[nt] && (EPI != EPI_UPD0 || o0 + 32 * nt + col < ep.cdim);
-  }
-  float in0[16][2], in1[16][2];
+  for (int nt = 0; nt < 2; nt++)
 #pragma unroll
-  for (int v = 0; v < 16; v++) {
-    const EpiRow er = epi_row(ep, r0, v, lane, M);
-#pragma unroll
-    for (int nt = 0; nt < 2; nt++) {
-      // unconditional loads from clamped columns (a load under a branch would be waited for
-      // inside the branch); values of columns outside the output are never used
-      const int o = o0 + 32 * nt + col;
-      in0[v][nt] = 0.0f;
-      in1[v][nt] = 0.0f;
-      if (EPI == EPI_ADD) in0[v][nt] = ep.y[er.yb + (ook[nt] ? o : 0)];
+    for (int g = 0; g < 4; g++) {
+      const int oc = o0 + 32 * nt + 8 * g + 4 * hf;
+      const bool ok = oc < O;
+      const bool hok = ok && (EPI != EPI_UPD0 || oc < ep.cdim);
+      in0[nt][g] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      in1[nt][g] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (EPI == EPI_ADD) in0[nt][g] = *reinterpret_cast<const float4*>(ep.y + yb + (ok ? oc : 0));
       if (EPI == EPI_UPD0 || EPI == EPI_UPDL)  // a NULL residual input reads as zero
-        in0[v][nt] = ep.hin ? ep.hin[er.hb + (hok[nt] ? o : 0)] : 0.0f;
-      if (EPI == EPI_UPDL) in1[v][nt] = ep.gates[er.gb + (ook[nt] ? o : 0)];
+        if (ep.hin) in0[nt][g] = *reinterpret_cast<const float4*>(ep.hin + hb + (hok ? oc : 0));
+      if (EPI == EPI_UPDL)
+        in1[nt][g] = *reinterpret_cast<const float4*>(ep.gates + gb + (ok ? oc : 0));
     }
-  }
   __syncthreads();
   floatx16 acc0, acc1;
 #pragma unroll
@@ -165,36 +154,41 @@ __global__ void __launch_bounds__(256) k_gemm(int64_t M, int O, const float* __r
 #pragma unroll
     for (int q = 0; q < 4; q++) {
       const int k = 8 * s8 + q + kh;
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av[q], Ws[k][col], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av[q], Ws[k][32 + col], acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(Ws[k][col], av[q], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(Ws[k][32 + col], av[q], acc1, 0, 0, 0);
     }
   }
-  // Epilogue: the inputs loaded before the MFMA loop, then one store per element. The row
-  // offsets are recomputed here rather than kept live across the MFMA loop (the empty asm
-  // hides r0 from common-subexpression elimination).
-  int64_t r0s = r0;
-  asm volatile("" : "+v"(r0s));
+  // Epilogue: register v = 4 g + s of tile nt holds column o0 + 32 nt + 8 g + 4 hf + s of this
+  // lane's row.
+  if (!row_ok) return;
 #pragma unroll
-  for (int v = 0; v < 16; v++) {
-    const EpiRow er = epi_row(ep, r0s, v, lane, M);
+  for (int nt = 0; nt < 2; nt++)
 #pragma unroll
-    for (int nt = 0; nt < 2; nt++) {
-      const int o = o0 + 32 * nt + col;
-      const float val = nt == 0 ? acc0[v] : acc1[v];
-      if (!er.ok || !ook[nt]) continue;
+    for (int g = 0; g < 4; g++) {
+      const int oc = o0 + 32 * nt + 8 * g + 4 * hf;
+      if (oc >= O) continue;
+      const floatx16& a = nt == 0 ? acc0 : acc1;
+      const float4 v = make_float4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
+      float4* yp = reinterpret_cast<float4*>(ep.y + yb + oc);
+      const float4 x0 = in0[nt][g];
       if (EPI == EPI_STORE) {
-        ep.y[er.yb + o] = val;
+        *yp = v;
       } else if (EPI == EPI_ADD) {
-        ep.y[er.yb + o] = in0[v][nt] + val;
+        *yp = make_float4(x0.x + v.x, x0.y + v.y, x0.z + v.z, x0.w + v.w);
       } else if (EPI == EPI_UPD0) {
-        ep.y[er.yb + o] = val;
-        if (hok[nt]) ep.hout[er.hb + o] = in0[v][nt] + val * sigmoidf_(val);
+        *yp = v;
+        if (oc < ep.cdim)
+          *reinterpret_cast<float4*>(ep.hout + hb + oc) =
+              make_float4(x0.x + v.x * sigmoidf_(v.x), x0.y + v.y * sigmoidf_(v.y),
+                          x0.z + v.z * sigmoidf_(v.z), x0.w + v.w * sigmoidf_(v.w));
       } else {  // EPI_UPDL
-        ep.y[er.yb + o] = val;
-        ep.hout[er.hb + o] = in0[v][nt] + sigmoidf_(in1[v][nt]) * val;
+        const float4 x1 = in1[nt][g];
+        *yp = v;
+        *reinterpret_cast<float4*>(ep.hout + hb + oc) =
+            make_float4(x0.x + sigmoidf_(x1.x) * v.x, x0.y + sigmoidf_(x1.y) * v.y,
+                        x0.z + sigmoidf_(x1.z) * v.z, x0.w + sigmoidf_(x1.w) * v.w);
       }
     }
-  }
 }
 
 // o_first: when > 0, only output columns [0, o_first) are computed (O stays the row length of
@@ -203,6 +197,12 @@ template <int EPI>
 hipError_t gemm(hipStream_t st, int64_t M, int K, int O, const float* X, RowMap xm,
                 const float* Wt, const Epi& ep, int o_first = 0) {
   if (M <= 0) return hipSuccess;
+  // the kernel moves rows of Wt, y, h and the gates in float4 pieces
+  auto q4 = [](int64_t v) { return (v & 3) == 0; };
+  auto map4 = [&](const RowMap& m) { return q4(m.nstride) && q4((int64_t)m.c0 * m.cstride) && q4(m.cstride); };
+  if (!q4(O) || !map4(ep.ym) || (EPI >= EPI_UPD0 && (!map4(ep.hm) || !q4(ep.cdim))) ||
+      (EPI == EPI_UPDL && (!q4(ep.gstride) || !q4(ep.goff))))
+    return hipErrorInvalidValue;
   dim3 g((unsigned)((M + 127) / 128), (unsigned)(((o_first > 0 ? o_first : O) + 63) / 64));
   switch (K) {
     case 16: TESS_TIMED("node_gemm", st, k_gemm<EPI, 16><<<g, 256, 0, st>>>(M, O, X, xm, Wt, ep)); break;
