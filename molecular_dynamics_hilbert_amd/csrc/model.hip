@@ -890,64 +890,40 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((TRANS
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     prefetch(b + kChunk);
     // Groups of EPG edges; past the chunk's end a lane re-reads the last edge with alpha = 0.
-    // Two register sets of features alternate so that the next group is in flight during this
-    // group's MFMAs.
     const int ngroups = (cnt + EPG - 1) / EPG;
-    auto fetch = [&](int E, float4* xo, float& ao, int& eo) {
+    // edge slot of group E for this lane (clamped to the chunk) and its weight alpha
+    auto slot = [&](int E, float& ao) {
       const int e0 = E * EPG + q;
       const int e = e0 < cnt ? e0 : cnt - 1;
       ao = e0 < cnt ? sAl[wv][e][hl] : 0.0f;
-      eo = e;
-      if constexpr (EMB) {
-        xo[0] = sEmb[sSp[wv][e] * (C / 4) + m];
-      } else {
-        const float* Xy = X + (int64_t)sJ[wv][e] * D * C + 4 * m;
-#pragma unroll
-        for (int k = 0; k < DI; k++) xo[k] = *reinterpret_cast<const float4*>(Xy + k * C);
-      }
+      return e;
     };
     // alpha depends on (edge, head of the channel). When a head spans 16 channels, the four
     // rows of an MFMA block (channels 16(b%4)+4i+s) share one head, which is also the head of
     // the lane supplying the block's B value, so alpha scales B; otherwise it scales A.
     constexpr bool AL_ON_B = dh % 16 == 0;
-    auto mma = [&](const float4* xi, float ai, int e) {
+    // the contribution of input component k of edge slot e (features xk, weight ai)
+    auto mma_k = [&](int k, const float4 xk, float ai, int e) {
       const float* Ae = sA[wv][e];
       if constexpr (OUT0) {
-#pragma unroll
-        for (int k = 0; k < DI; k++) {
-          const float b = ai * Ae[k];
-          acc0.x = __builtin_fmaf(b, xi[k].x, acc0.x);
-          acc0.y = __builtin_fmaf(b, xi[k].y, acc0.y);
-          acc0.z = __builtin_fmaf(b, xi[k].z, acc0.z);
-          acc0.w = __builtin_fmaf(b, xi[k].w, acc0.w);
-        }
-        return;
-      }
-      float bv[DI][NDG], b8v[DI];
-#pragma unroll
-      for (int k = 0; k < DI; k++) {
-#pragma unroll
-        for (int d = 0; d < NDG; d++) bv[k][d] = 0.0f;
-        b8v[k] = 0.0f;
-      }
-#pragma unroll
-      for (int k = 0; k < DI; k++) {
-        {
-#pragma unroll
-          for (int d = 0; d < NDG; d++) bv[k][d] = Ae[(4 * d + jj) * DI + k];
-          if constexpr (VC8) b8v[k] = Ae[8 * DI + k];
-        }
+        const float b = ai * Ae[k];
+        acc0.x = __builtin_fmaf(b, xk.x, acc0.x);
+        acc0.y = __builtin_fmaf(b, xk.y, acc0.y);
+        acc0.z = __builtin_fmaf(b, xk.z, acc0.z);
+        acc0.w = __builtin_fmaf(b, xk.w, acc0.w);
+      } else {
         const float sa = AL_ON_B ? 1.0f : ai;
-        const float xs[4] = {sa * xi[k].x, sa * xi[k].y, sa * xi[k].z, sa * xi[k].w};
+        const float xs[4] = {sa * xk.x, sa * xk.y, sa * xk.z, sa * xk.w};
 #pragma unroll
         for (int d = 0; d < NDG; d++) {
-          const float bk = AL_ON_B ? ai * bv[k][d] : bv[k][d];
+          const float bv = Ae[(4 * d + jj) * DI + k];
+          const float bk = AL_ON_B ? ai * bv : bv;
 #pragma unroll
           for (int t = 0; t < 4; t++)
             acc[t][d] = __builtin_amdgcn_mfma_f32_4x4x1f32(xs[t], bk, acc[t][d], 0, 0, 0);
         }
         if constexpr (VC8) {
-          const float b8 = AL_ON_B ? ai * b8v[k] : b8v[k];
+          const float b8 = AL_ON_B ? ai * Ae[8 * DI + k] : Ae[8 * DI + k];
           acc8.x = __builtin_fmaf(b8, xs[0], acc8.x);
           acc8.y = __builtin_fmaf(b8, xs[1], acc8.y);
           acc8.z = __builtin_fmaf(b8, xs[2], acc8.z);
@@ -955,16 +931,40 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((TRANS
         }
       }
     };
-    float4 xa[DI], xb[DI];
-    float ala, alb;
-    int ea, eb;
-    fetch(0, xa, ala, ea);
-    for (int E = 0; E < ngroups; E += 2) {
-      fetch(E + 1, xb, alb, eb);
-      mma(xa, ala, ea);
-      if (E + 1 >= ngroups) break;
-      fetch(E + 2, xa, ala, ea);
-      mma(xb, alb, eb);
+    if constexpr (EMB) {
+      // first layer: one input component, read from the LDS copy of the embedding
+      for (int E = 0; E < ngroups; E++) {
+        float al;
+        const int e = slot(E, al);
+        mma_k(0, sEmb[sSp[wv][e] * (C / 4) + m], al, e);
+      }
+    } else {
+      // Rolling prefetch: each feature register is reloaded with the next group's component
+      // as soon as the current group's MFMAs for that component have been issued, so a
+      // group's gathers are in flight during the previous group's work without a second
+      // register set (the chunk's first group is loaded before the loop).
+      float4 xr[DI];
+      float al;
+      int e = slot(0, al);
+      {
+        const float* X0 = X + (int64_t)sJ[wv][e] * D * C + 4 * m;
+#pragma unroll
+        for (int k = 0; k < DI; k++) xr[k] = *reinterpret_cast<const float4*>(X0 + k * C);
+      }
+      for (int E = 0; E + 1 < ngroups; E++) {
+        float aln;
+        const int en = slot(E + 1, aln);
+        const float* Xn = X + (int64_t)sJ[wv][en] * D * C + 4 * m;
+#pragma unroll
+        for (int k = 0; k < DI; k++) {
+          mma_k(k, xr[k], al, e);
+          xr[k] = *reinterpret_cast<const float4*>(Xn + k * C);
+        }
+        e = en;
+        al = aln;
+      }
+#pragma unroll
+      for (int k = 0; k < DI; k++) mma_k(k, xr[k], al, e);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
