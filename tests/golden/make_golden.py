@@ -16,7 +16,11 @@ within R - n_layers * r_cut of the centre and the forces of every atom within DE
 equal those of the periodic system. Half of the centres lie within 2 A of one, two or three
 periodic faces of the box (so their clusters cross the periodic boundary), half are random.
 
-usage: python tests/golden/make_golden.py [salt60k capsid39k salt500k]
+salt60k_md runs the oracle's velocity-Verlet integrator on the whole salt60k box (start at
+50 K, readout weights scaled by 30, MD_STEPS steps inside one rebuild interval) and stores
+every atom's final position and velocity and the potential-energy trace.
+
+usage: python tests/golden/make_golden.py [salt60k capsid39k salt500k salt60k_md]
 """
 from __future__ import annotations
 
@@ -137,10 +141,41 @@ def clustered(name: str):
     return meta, arrays
 
 
+MD_STEPS = 4
+MD_SCALE = 30.0   # readout weights scale, as in the small MD parity runs
+MD_TEMP = 50.0    # K
+
+
+def md_trajectory(name: str):
+    base = name[:-3]
+    wl = W.load(base)
+    w = W.make_weights(wl.model, WEIGHT_SEED[base])
+    w[-wl.model.channels:] *= MD_SCALE
+    vseed = 3000 + WEIGHT_SEED[base] % 1000
+    vel = W.maxwell_velocities(wl.species, wl.masses(), MD_TEMP, vseed)
+    t0 = time.time()
+    o = oracle.md_steps(wl.model, w, wl.box, wl.model.r_cut, wl.skin, wl.pos, vel, wl.species,
+                        wl.masses(), wl.dt_fs, MD_STEPS, 20)
+    assert o["status"] == 0
+    pa = np.asarray(o["perm_accum"])
+    x = np.empty((wl.n, 3)); x[pa] = o["pos"]
+    v = np.empty((wl.n, 3)); v[pa] = o["vel"]
+    meta = dict(workload=name, digest=digest(wl, w), weight_seed=WEIGHT_SEED[base],
+                readout_scale=MD_SCALE, temperature_K=MD_TEMP, velocity_seed=vseed,
+                n_steps=MD_STEPS, rebuild_every=20, epot=[float(e) for e in o["epot"]],
+                oracle_seconds=time.time() - t0,
+                method="oracle velocity Verlet on the whole periodic box; final positions and "
+                       "velocities of every atom by original id")
+    return meta, dict(pos=x, vel=v, epot=np.asarray(o["epot"]))
+
+
 def main(names):
     for name in names:
         t = time.time()
-        meta, arrays = clustered(name) if name == "salt500k" else full_system(name)
+        if name.endswith("_md"):
+            meta, arrays = md_trajectory(name)
+        else:
+            meta, arrays = clustered(name) if name == "salt500k" else full_system(name)
         with open(os.path.join(HERE, name + ".json"), "w") as f:
             json.dump(meta, f)
         np.savez_compressed(os.path.join(HERE, name + ".npz"), **arrays)

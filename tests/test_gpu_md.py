@@ -92,6 +92,42 @@ def test_md_salt4k_short(T, oracle_mod):
     _compare(T, oracle_mod, "salt4k", 6, 3, 2002)
 
 
+def test_md_salt60k_stored_oracle(T):
+    """The whole 60,000-atom box: every atom's position and velocity after the oracle's
+    velocity-Verlet steps (stored by tests/golden/make_golden.py from oracle/ only), and the
+    potential-energy trace, against tess_md_steps on the same start state."""
+    import json
+    import os
+    from tests.golden.make_golden import digest
+    here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    jp, zp = os.path.join(here, "salt60k_md.json"), os.path.join(here, "salt60k_md.npz")
+    if not (os.path.exists(jp) and os.path.exists(zp)):
+        pytest.skip("no stored oracle trajectory (run tests/golden/make_golden.py salt60k_md)")
+    with open(jp) as f:
+        gold = json.load(f)
+    with np.load(zp) as z:  # no pickles
+        arr = {k: z[k] for k in z.files}
+    wl = W.load("salt60k")
+    w = W.make_weights(wl.model, gold["weight_seed"])
+    w[-wl.model.channels:] *= gold["readout_scale"]
+    assert digest(wl, w) == gold["digest"], "input generator changed since the values were stored"
+    vel = W.maxwell_velocities(wl.species, wl.masses(), gold["temperature_K"],
+                               gold["velocity_seed"])
+    g = _gpu_md(T, wl, w, vel, gold["n_steps"], gold["rebuild_every"])
+    assert g["status"] == 0
+    assert np.array_equal(np.sort(g["pa"]), np.arange(wl.n))
+    xg = np.empty((wl.n, 3)); xg[g["pa"]] = g["pos"]
+    vg = np.empty((wl.n, 3)); vg[g["pa"]] = g["vel"]
+    L = wl.box.astype(np.float64)
+    dx = xg - arr["pos"]
+    dx -= L * np.round(dx / L)
+    print("salt60k md steps=%d max|dx|=%.2e max|dv|=%.2e" % (
+        gold["n_steps"], np.abs(dx).max(), np.abs(vg - arr["vel"]).max()), flush=True)
+    assert np.abs(dx).max() <= 1e-4
+    assert np.abs(vg - arr["vel"]).max() <= 1e-5
+    assert np.all(np.abs(g["epot"] - arr["epot"]) <= 1e-5 * np.abs(arr["epot"]))
+
+
 def test_md_traces_nve_water(T, oracle_mod):
     """Kinetic-energy and shortest-pair-distance traces (tess_md_steps_ex, no thermostat)
     against the oracle's; two intervals with a rebuild between them."""
