@@ -271,6 +271,19 @@ def run(args):
                 "traffic": _traffic(dom, args.workload),
                 "avg_launch_ms": dom_ms / max(dom_cnt, 1), "launches": dom_cnt,
                 "flops_per_ef_pass": flops[dom]}
+    # the same figures for every edge kernel (times from the profile pass, where each
+    # instrumented kernel carries events; the dominant kernel's above come from the timed region)
+    edge_rooflines = {}
+    for k in ("edge_apply", "edge_grad", "edge_grad_last", "edge_tapply"):
+        k_ms, k_cnt = kern[k]
+        if k_ms <= 0:
+            continue
+        a = flops[k] * ef_calls / (k_ms * 1e-3) / 1e12
+        pk = PEAK_FP32_MFMA_TFLOPS if BOUND[k] == "mfma" else PEAK_FP32_VECTOR_TFLOPS
+        edge_rooflines[k] = {"bound": BOUND[k], "achieved": round(a, 3), "peak": pk,
+                             "unit": "TFLOP/s", "frac": round(a / pk, 4),
+                             "traffic": _traffic(k, args.workload),
+                             "avg_launch_ms": round(k_ms / max(k_cnt, 1), 4), "launches": k_cnt}
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "atom-steps/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -288,6 +301,7 @@ def run(args):
         "rebuild_ms": round(statistics.median(rb), 4),
         "ef_ms": round(statistics.median(ef), 4),
         "roofline": roofline,
+        "edge_rooflines": edge_rooflines,
         "kernels_ms": {k: round(v["avg_ms"], 4) for k, v in rows.items()},
         "large_system": None if args.no_large else large_system(),
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(),
