@@ -356,6 +356,7 @@ __device__ int atom_row_global(int32_t i, int lane, const CellGrid& g, double rc
 // candidates (small or dense boxes) is read from global memory per atom instead (fp64 test).
 // FILL = false writes each atom's count to row_ptr[i].
 constexpr int kCellCap = 2048;
+constexpr int kCellAtoms = 4;  // atoms a wave tests against each candidate it reads
 template <bool FILL>
 __global__ void __launch_bounds__(256) k_cell_pairs(CellGrid g, double rcs2, float lo2, float hi2,
                                                     const float* __restrict__ pos,
@@ -408,18 +409,34 @@ __global__ void __launch_bounds__(256) k_cell_pairs(CellGrid g, double rcs2, flo
     return;
   }
   // stage candidate q of stencil cell v (vpre[v] <= q < vpre[v+1]); pad the keys to a power
-  // of two for the sort
+  // of two for the sort. A thread's candidates (at most kCellCap / 256) first find their
+  // stencil cells, then request their positions together.
   int p2 = 1;
   while (p2 < total) p2 <<= 1;
-  for (int q = t; q < (FILL ? p2 : total); q += 256) {
+  constexpr int kPer = kCellCap / 256;
+  int sv[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; r++) {
+    const int q = t + 256 * r;
+    int lo = 0, hi = 27;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (vpre[mid] <= q) lo = mid; else hi = mid;
+    }
+    sv[r] = lo;
+  }
+  float4 sp[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; r++) {
+    const int q = t + 256 * r;
+    sp[r] = q < total ? cpos[vstart[sv[r]] + (q - vpre[sv[r]])] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int r = 0; r < kPer; r++) {
+    const int q = t + 256 * r;
     if (q < total) {
-      int lo = 0, hi = 27;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (vpre[mid] <= q) lo = mid; else hi = mid;
-      }
-      const float4 p = cpos[vstart[lo] + (q - vpre[lo])];
-      const int code = vcode[lo];
+      const float4 p = sp[r];
+      const int code = vcode[sv[r]];
       const uint32_t entry = ((uint32_t)__float_as_int(p.w) << 5) | (uint32_t)code;
       // image-shifted position in fp32 (one rounding per axis)
       const float xs = p.x + (float)(code / 9 - 1) * (float)g.L[0];
@@ -427,7 +444,7 @@ __global__ void __launch_bounds__(256) k_cell_pairs(CellGrid g, double rcs2, flo
       const float zs = p.z + (float)(code % 3 - 1) * (float)g.L[2];
       spos[q] = make_float4(xs, ys, zs, __uint_as_float(entry));
       if (FILL) skey[q] = ((uint64_t)entry << 32) | (uint32_t)q;
-    } else if (FILL) {
+    } else if (FILL && q < p2) {
       skey[q] = ~0ull;
     }
   }
@@ -446,12 +463,25 @@ __global__ void __launch_bounds__(256) k_cell_pairs(CellGrid g, double rcs2, flo
       }
     }
   }
+  // Each wave takes kCellAtoms of the cell's atoms at a time: every staged candidate read
+  // from LDS is tested against all of them.
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int32_t k = a0 + wv; k < a1; k += 4) {
-    const int32_t i = cell_atoms[k];
-    const float xf0 = pos[3 * i], xf1 = pos[3 * i + 1], xf2 = pos[3 * i + 2];
-    int count = 0;
-    const int64_t o = FILL ? (int64_t)row_ptr[i] : 0;
+  for (int32_t k0 = a0 + wv * kCellAtoms; k0 < a1; k0 += 4 * kCellAtoms) {
+    int32_t ia[kCellAtoms];
+    float xf[kCellAtoms][3];
+    int count[kCellAtoms];
+    int64_t o[kCellAtoms];
+#pragma unroll
+    for (int u = 0; u < kCellAtoms; u++) {
+      // atoms past the cell's end repeat its first atom (wave-uniform; never written)
+      const int32_t i = cell_atoms[k0 + u < a1 ? k0 + u : a0];
+      ia[u] = i;
+      xf[u][0] = pos[3 * i];
+      xf[u][1] = pos[3 * i + 1];
+      xf[u][2] = pos[3 * i + 2];
+      count[u] = 0;
+      o[u] = FILL ? (int64_t)row_ptr[i] : 0;
+    }
     for (int q0 = 0; q0 < total; q0 += 64) {
       const int q = q0 + lane;
       const bool ok = q < total;
@@ -460,21 +490,29 @@ __global__ void __launch_bounds__(256) k_cell_pairs(CellGrid g, double rcs2, flo
       const uint32_t entry = __float_as_uint(p.w);
       const int32_t j = (int32_t)(entry >> 5);
       const int code = (int)(entry & 31u);
-      const float dx = p.x - xf0, dy = p.y - xf1, dz = p.z - xf2;
-      const float d2 = __builtin_fmaf(dz, dz, __builtin_fmaf(dy, dy, dx * dx));
-      bool near = d2 < lo2;
-      if (ok && !near && d2 <= hi2)  // inside the band: the fp64 test decides
-        near = pair_pass(pos[3 * j], pos[3 * j + 1], pos[3 * j + 2], code, (double)xf0,
-                         (double)xf1, (double)xf2, g, rcs2);
-      const bool pass = ok && near && !(j == i && code == 13);
-      const uint64_t m = __ballot(pass);
-      if (FILL && pass) {
-        const int slot = count + __popcll(m & lt);
-        if (slot < kMaxRow) col_shift[o + slot] = (uint32_t)j | ((uint32_t)code << 27);
+#pragma unroll
+      for (int u = 0; u < kCellAtoms; u++) {
+        if (k0 + u >= a1) break;  // wave-uniform
+        const float dx = p.x - xf[u][0], dy = p.y - xf[u][1], dz = p.z - xf[u][2];
+        const float d2 = __builtin_fmaf(dz, dz, __builtin_fmaf(dy, dy, dx * dx));
+        bool near = d2 < lo2;
+        if (ok && !near && d2 <= hi2)  // inside the band: the fp64 test decides
+          near = pair_pass(pos[3 * j], pos[3 * j + 1], pos[3 * j + 2], code, (double)xf[u][0],
+                           (double)xf[u][1], (double)xf[u][2], g, rcs2);
+        const bool pass = ok && near && !(j == ia[u] && code == 13);
+        const uint64_t m = __ballot(pass);
+        if (FILL && pass) {
+          const int slot = count[u] + __popcll(m & lt);
+          if (slot < kMaxRow) col_shift[o[u] + slot] = (uint32_t)j | ((uint32_t)code << 27);
+        }
+        count[u] += __popcll(m);
       }
-      count += __popcll(m);
     }
-    if (!FILL && lane == 0) row_ptr[i] = count;
+    if (!FILL && lane == 0) {
+#pragma unroll
+      for (int u = 0; u < kCellAtoms; u++)
+        if (k0 + u < a1) row_ptr[ia[u]] = count[u];
+    }
   }
 }
 
