@@ -41,7 +41,7 @@ from molecular_dynamics_hilbert_amd import workloads as W  # noqa: E402
 
 WEIGHT_SEED = {"water648": 2001, "salt4k": 2002, "salt60k": 2003, "capsid39k": 2004,
                "salt500k": 2005}
-N_CLUSTERS = 32   # salt500k cluster centres (half near periodic faces)
+N_CLUSTERS = 64   # salt500k cluster centres (half near periodic faces), all distinct
 DELTA = 2.0       # A: force atoms lie within DELTA of a cluster's centre
 
 
@@ -99,7 +99,9 @@ def face_centres(x, L, rng, k):
     out = []
     for t in range(k):
         want = 1 + t % 3
-        pool = np.where(cnt == want)[0]
+        pool = np.setdiff1d(np.where(cnt == want)[0], out)
+        if pool.size == 0:  # few atoms lie near a corner: take any face atom not yet taken
+            pool = np.setdiff1d(np.where(cnt >= 1)[0], out)
         out.append(int(rng.choice(pool)))
     return out
 
@@ -115,7 +117,8 @@ def clustered(name: str):
     L = wl.box.astype(np.float64)
     rng = np.random.default_rng(78)
     centres = face_centres(x, L, rng, N_CLUSTERS // 2)
-    centres += [int(c) for c in rng.choice(wl.n, N_CLUSTERS - len(centres), replace=False)]
+    rest = np.setdiff1d(np.arange(wl.n), centres)
+    centres += [int(c) for c in rng.choice(rest, N_CLUSTERS - len(centres), replace=False)]
     e_ids, e_vals, f_ids, f_vals, sizes = [], [], [], [], []
     seen_e, seen_f = set(), set()
     t0 = time.time()
