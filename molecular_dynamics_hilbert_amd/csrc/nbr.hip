@@ -342,6 +342,102 @@ __device__ int atom_row_global(int32_t i, int lane, const CellGrid& g, double rc
   return count;
 }
 
+// Candidates a cell block stages in LDS (16 bytes each). 2016 rather than 2048 keeps the
+// block's LDS (with the stencil tables) within 32 KiB, so five blocks fit a CU.
+constexpr int kCellCap = 2016;
+
+// Sorts the block's staged candidates by their entry (j << 5 | shift code) and leaves them
+// in that order in spos[0, total). On entry, thread t holds candidate q = t + 256 r in sp[r]
+// (r < kPer; position in .xyz, the entry's bits in .w) and spos is free; total <= 256 * EPT.
+// The keys (entry << 32 | q) are sorted by an ascending bitonic network in registers: position
+// a = t*EPT + r lives in thread t, so a compare-exchange at distance jj < EPT stays in the
+// thread, one with EPT <= jj < 64*EPT crosses lanes of a wave (a lane shuffle), and only the
+// three stages with partners in another wave exchange through LDS (spos as scratch). The
+// candidates are then written to spos unsorted and gathered into sorted order.
+template <int J, int EPT>
+__device__ __forceinline__ void bitonic_in_thread(uint64_t (&x)[EPT], int base, int k) {
+#pragma unroll
+  for (int r = 0; r < EPT; r++)
+    if ((r & J) == 0) {
+      const bool up = ((base + r) & k) == 0;
+      const uint64_t a = x[r], b = x[r | J];
+      const bool swap = (a > b) == up;
+      x[r] = swap ? b : a;
+      x[r | J] = swap ? a : b;
+    }
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+template <int EPT, int kPer>
+__device__ __forceinline__ void sort_staged(float4* spos, const float4 (&sp)[kPer], int total,
+                                            int t) {
+  static_assert(EPT <= kPer, "every key slot has a staged candidate slot");
+  constexpr int N = 256 * EPT;
+  const int base = t * EPT;
+  uint64_t x[EPT];
+#pragma unroll
+  for (int r = 0; r < EPT; r++) {
+    const int q = t + 256 * r;
+    x[r] = q < total ? ((uint64_t)__float_as_uint(sp[r].w) << 32) | (uint32_t)q : ~0ull;
+  }
+  uint64_t* xbuf = reinterpret_cast<uint64_t*>(spos);  // N * 8 bytes <= half of spos
+  for (int k = 2; k <= N; k <<= 1) {
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      if (jj >= 64 * EPT) {  // block-uniform
+        __syncthreads();     // earlier readers of xbuf are done
+#pragma unroll
+        for (int r = 0; r < EPT; r++) xbuf[base + r] = x[r];
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < EPT; r++) {
+          const int a = base + r;
+          const uint64_t y = xbuf[a ^ jj];
+          const bool keep_min = ((a & jj) == 0) == ((a & k) == 0);
+          x[r] = keep_min ? (x[r] < y ? x[r] : y) : (x[r] < y ? y : x[r]);
+        }
+      } else if (jj >= EPT) {
+        const int m = jj / EPT;  // lane distance (a power of two below 64)
+#pragma unroll
+        for (int r = 0; r < EPT; r++) {
+          const int a = base + r;
+          const uint64_t y = shfl_xor_u64(x[r], m);
+          const bool keep_min = ((a & jj) == 0) == ((a & k) == 0);
+          x[r] = keep_min ? (x[r] < y ? x[r] : y) : (x[r] < y ? y : x[r]);
+        }
+      } else if (jj == 1) {
+        bitonic_in_thread<1, EPT>(x, base, k);
+      } else if (jj == 2) {
+        bitonic_in_thread<2, EPT>(x, base, k);
+      } else {
+        if constexpr (EPT > 4) bitonic_in_thread<4, EPT>(x, base, k);
+      }
+    }
+  }
+  __syncthreads();  // the last exchange reads are done
+#pragma unroll
+  for (int r = 0; r < kPer; r++) {
+    const int q = t + 256 * r;
+    if (q < total) spos[q] = sp[r];
+  }
+  __syncthreads();
+  // (a native 4-vector keeps the gathered values in registers)
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  f32x4* sv4 = reinterpret_cast<f32x4*>(spos);
+  f32x4 v[EPT];
+#pragma unroll
+  for (int r = 0; r < EPT; r++) v[r] = sv4[base + r < total ? (uint32_t)x[r] : 0u];
+  __syncthreads();
+  // positions in [total, kCellCap) take filler that the pair loop never reads
+#pragma unroll
+  for (int r = 0; r < EPT; r++)
+    if (base + r < kCellCap) sv4[base + r] = v[r];
+}
+
 // Pair search with LDS-staged cell stencils: one 256-thread block per cell (the second level
 // of the three-level search). The block stages the candidates of the cell's 27-cell stencil
 // (image-shifted fp32 position and entry j<<5|code, one 16-byte load each) in LDS once; the
@@ -355,7 +451,6 @@ __device__ int atom_row_global(int32_t i, int lane, const CellGrid& g, double rc
 // band by the fp64 test from the stored positions. A stencil with more than kCellCap
 // candidates (small or dense boxes) is read from global memory per atom instead (fp64 test).
 // FILL = false writes each atom's count to row_ptr[i].
-constexpr int kCellCap = 2048;
 constexpr int kCellAtoms = 4;  // atoms a wave tests against each candidate it reads
 template <bool FILL>
 __global__ void __launch_bounds__(256) k_cell_pairs(CellGrid g, double rcs2, float lo2, float hi2,
@@ -366,13 +461,12 @@ __global__ void __launch_bounds__(256) k_cell_pairs(CellGrid g, double rcs2, flo
                                                     int32_t* __restrict__ row_ptr,
                                                     uint32_t* __restrict__ col_shift) {
   __shared__ int32_t vstart[27], vcode[27], vpre[28];
-  // staged candidates (float4) and, for the fill, the sort keys (entry << 32 | index); the
-  // global-memory path reuses the space as four per-wave row buffers
-  constexpr int kBytes = kCellCap * 16 + (FILL ? kCellCap * 8 : 0);
+  // staged candidates (float4; for the fill in (j, shift) order); the global-memory path
+  // reuses the space as four per-wave row buffers
+  constexpr int kBytes = kCellCap * 16;
   static_assert(kBytes >= 4 * kMaxRow * 4, "row buffers fit the staging area");
   __shared__ __align__(16) char smem[kBytes];
   float4* spos = reinterpret_cast<float4*>(smem);
-  uint64_t* skey = reinterpret_cast<uint64_t*>(smem + kCellCap * 16);
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int c = (int)xcd_block(blockIdx.x, gridDim.x);
   const int32_t a0 = cell_start[c], a1 = cell_start[c + 1];
@@ -408,12 +502,10 @@ __global__ void __launch_bounds__(256) k_cell_pairs(CellGrid g, double rcs2, flo
     }
     return;
   }
-  // stage candidate q of stencil cell v (vpre[v] <= q < vpre[v+1]); pad the keys to a power
-  // of two for the sort. A thread's candidates (at most kCellCap / 256) first find their
-  // stencil cells, then request their positions together.
-  int p2 = 1;
-  while (p2 < total) p2 <<= 1;
-  constexpr int kPer = kCellCap / 256;
+  // stage candidate q of stencil cell v (vpre[v] <= q < vpre[v+1]). A thread's candidates
+  // (at most kPer) first find their stencil cells, then request their positions
+  // together.
+  constexpr int kPer = (kCellCap + 255) / 256;
   int sv[kPer];
 #pragma unroll
   for (int r = 0; r < kPer; r++) {
@@ -442,27 +534,15 @@ __global__ void __launch_bounds__(256) k_cell_pairs(CellGrid g, double rcs2, flo
       const float xs = p.x + (float)(code / 9 - 1) * (float)g.L[0];
       const float ys = p.y + (float)((code / 3) % 3 - 1) * (float)g.L[1];
       const float zs = p.z + (float)(code % 3 - 1) * (float)g.L[2];
-      spos[q] = make_float4(xs, ys, zs, __uint_as_float(entry));
-      if (FILL) skey[q] = ((uint64_t)entry << 32) | (uint32_t)q;
-    } else if (FILL && q < p2) {
-      skey[q] = ~0ull;
+      sp[r] = make_float4(xs, ys, zs, __uint_as_float(entry));
+      if (!FILL) spos[q] = sp[r];
     }
+  }
+  if (FILL) {  // the entries of one stencil are distinct; block-uniform choice
+    if (total <= 1024) sort_staged<4>(spos, sp, total, t);
+    else sort_staged<8>(spos, sp, total, t);
   }
   __syncthreads();
-  if (FILL) {  // bitonic sort of the keys (the entries of one stencil are distinct)
-    for (int k = 2; k <= p2; k <<= 1) {
-      for (int jj = k >> 1; jj > 0; jj >>= 1) {
-        for (int u = t; u < (p2 >> 1); u += 256) {
-          const int a = 2 * jj * (u / jj) + (u % jj);
-          const int b = a + jj;
-          const uint64_t va = skey[a], vb = skey[b];
-          const bool up = (a & k) == 0;
-          if ((va > vb) == up) { skey[a] = vb; skey[b] = va; }
-        }
-        __syncthreads();
-      }
-    }
-  }
   // Each wave takes kCellAtoms of the cell's atoms at a time: every staged candidate read
   // from LDS is tested against all of them.
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -485,8 +565,7 @@ __global__ void __launch_bounds__(256) k_cell_pairs(CellGrid g, double rcs2, flo
     for (int q0 = 0; q0 < total; q0 += 64) {
       const int q = q0 + lane;
       const bool ok = q < total;
-      const int qs = ok ? (FILL ? (int)(uint32_t)skey[q] : q) : 0;
-      const float4 p = spos[qs];
+      const float4 p = spos[ok ? q : 0];
       const uint32_t entry = __float_as_uint(p.w);
       const int32_t j = (int32_t)(entry >> 5);
       const int code = (int)(entry & 31u);
@@ -516,16 +595,22 @@ __global__ void __launch_bounds__(256) k_cell_pairs(CellGrid g, double rcs2, flo
   }
 }
 
-// Longest row and total pair count of a scanned CSR: block reductions, one atomic of each
-// per block. The scan adds in 32 bits, so a total beyond the int32 range of row_ptr wraps
-// there; each row's count is still the difference of its (wrapped) bounds, and their 64-bit
-// sum is the true total.
+// Longest row and total pair count of a scanned CSR: grid-stride over the rows, block
+// reductions, one atomic of each per block (at most kMaxRowBlocks blocks, so the atomics on
+// the one result line stay few). The scan adds in 32 bits, so a total beyond the int32 range
+// of row_ptr wraps there; each row's count is still the difference of its (wrapped) bounds,
+// and their 64-bit sum is the true total.
+constexpr int kMaxRowBlocks = 256;
 __global__ void __launch_bounds__(256) k_max_row(int32_t n, const int32_t* __restrict__ row_ptr,
                                                  int32_t* __restrict__ out,
                                                  unsigned long long* __restrict__ total) {
-  int32_t i = blockIdx.x * 256 + threadIdx.x;
-  int v = i < n ? (int)((uint32_t)row_ptr[i + 1] - (uint32_t)row_ptr[i]) : 0;
-  unsigned long long s = (unsigned long long)v;
+  int v = 0;
+  unsigned long long s = 0;
+  for (int32_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
+    const int c = (int)((uint32_t)row_ptr[i + 1] - (uint32_t)row_ptr[i]);
+    v = max(v, c);
+    s += (unsigned long long)c;
+  }
   for (int o = 32; o >= 1; o >>= 1) {
     v = max(v, __shfl_xor(v, o, 64));
     s += __shfl_xor(s, o, 64);
@@ -543,17 +628,35 @@ __global__ void __launch_bounds__(256) k_max_row(int32_t n, const int32_t* __res
   }
 }
 
-// rev[e] = slot of the reverse pair (j <- i, 26 - code) of entry e = (i <- j, code); rows are
-// sorted by (j, code). Each pair is searched once, from the row of its smaller index: for an
-// entry with j >= i the lane binary-searches row j for (i, 26 - code) and writes both
-// directions. One wave takes kRevRows consecutive rows: their j >= i entries are compacted
+// rev[e] = slot of the reverse pair (j <- i, 26 - code) of entry e = (i <- j, code). Rows are
+// sorted by (j, code) with distinct entries, and the pair test is symmetric, so the reverse
+// entry is in row j. Each pair is searched once, from the row of its smaller index: for an
+// entry with j >= i the lane searches row j for (i, 26 - code) and writes both directions.
+// One wave takes kRevRows consecutive rows: their j >= i entries (index, key, j) are compacted
 // into LDS first, so every lane runs two interleaved searches (independent load chains).
+// The search reads runs of four consecutive entries (one 16-byte request each, always inside
+// row j): three runs spread over the open range per round cut it about four-fold, so a row of
+// ~130 entries takes two or three dependent rounds instead of the eight probes of a binary
+// search. A key that a row lacks (impossible for a symmetric list) ends its search unwritten.
 constexpr int kRevRows = 2;
+
+__device__ __forceinline__ uint32_t rev_sort_key(uint32_t c) {
+  return ((c & 0x7FFFFFFu) << 5) | (c >> 27);
+}
+
+// four consecutive col entries from a 4-byte-aligned address
+__device__ __forceinline__ uint4 load_run4(const uint32_t* p) {
+  uint4 v;
+  __builtin_memcpy(&v, p, sizeof(v));
+  return v;
+}
+
 __global__ void __launch_bounds__(256) k_rev(int32_t n, const int32_t* __restrict__ row_ptr,
                                              const uint32_t* __restrict__ col,
                                              int32_t* __restrict__ rev) {
   __shared__ int32_t se[4][128];
   __shared__ uint32_t sw[4][128];
+  __shared__ int32_t sj[4][128];
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   // XCD-aware block order: each XCD walks one contiguous range of rows, whose target rows
   // (spatial neighbours, nearby in curve order) then share that XCD's L2
@@ -571,11 +674,12 @@ __global__ void __launch_bounds__(256) k_rev(int32_t n, const int32_t* __restric
       const int32_t ee = e + lane;
       bool want = false;
       uint32_t key = 0;
+      int32_t j = 0;
       if (ee < e_end) {
         int32_t r = i;
         while (row_ptr[r + 1] <= ee) r++;  // rows of the wave's range, ascending
         const uint32_t c = col[ee];
-        const int32_t j = (int32_t)(c & 0x7FFFFFFu);
+        j = (int32_t)(c & 0x7FFFFFFu);
         want = j >= r;
         key = ((uint32_t)r << 5) | (26u - (c >> 27));
       }
@@ -584,6 +688,7 @@ __global__ void __launch_bounds__(256) k_rev(int32_t n, const int32_t* __restric
         const int slot = cnt + __popcll(m & lt);
         se[wv][slot] = ee;
         sw[wv][slot] = key;
+        sj[wv][slot] = j;
       }
       cnt += __popcll(m);
       e += 64;
@@ -592,44 +697,325 @@ __global__ void __launch_bounds__(256) k_rev(int32_t n, const int32_t* __restric
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    int32_t lo[2], hi[2], ei[2];
-    uint32_t want[2];
+    // search state: the open range [lo, hi) of row [rs, re); found = slot, -1 searching,
+    // -2 no search (or a key the row lacks)
+    int32_t lo[2], hi[2], rs[2], re[2], ei[2], found[2];
+    uint32_t w[2];
 #pragma unroll
     for (int h = 0; h < 2; h++) {
       const int k = lane + 64 * h;
-      lo[h] = hi[h] = 0;
       ei[h] = -1;
-      want[h] = 0;
+      found[h] = -2;
+      w[h] = 0;
+      lo[h] = hi[h] = rs[h] = re[h] = 0;
       if (k < cnt) {
         ei[h] = se[wv][k];
-        want[h] = sw[wv][k];
-        const int32_t j = (int32_t)(col[ei[h]] & 0x7FFFFFFu);
-        lo[h] = row_ptr[j];
-        hi[h] = row_ptr[j + 1];
-      }
-    }
-    while (lo[0] < hi[0] || lo[1] < hi[1]) {
-#pragma unroll
-      for (int h = 0; h < 2; h++) {
-        if (lo[h] < hi[h]) {
-          const int32_t mid = (lo[h] + hi[h]) >> 1;
-          const uint32_t cm = col[mid];
-          const uint32_t km = ((cm & 0x7FFFFFFu) << 5) | (cm >> 27);
-          if (km < want[h]) lo[h] = mid + 1; else hi[h] = mid;
-        }
+        w[h] = sw[wv][k];
+        const int32_t j = sj[wv][k];
+        rs[h] = lo[h] = row_ptr[j];
+        re[h] = hi[h] = row_ptr[j + 1];
+        found[h] = -1;
       }
     }
 #pragma unroll
     for (int h = 0; h < 2; h++)
-      if (ei[h] >= 0) {
-        rev[ei[h]] = lo[h];
-        rev[lo[h]] = ei[h];
+      if (found[h] == -1 && re[h] - rs[h] < 4) {  // short row: read its entries one by one
+        found[h] = -2;
+        for (int32_t k = rs[h]; k < re[h]; k++)
+          if (rev_sort_key(col[k]) == w[h]) found[h] = k;
+      }
+    while (found[0] == -1 || found[1] == -1) {
+      uint4 run[2][3];
+      int32_t c0[2][3];
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        if (found[h] != -1) continue;
+        const int32_t len = hi[h] - lo[h];
+#pragma unroll
+        for (int m = 0; m < 3; m++) {
+          // runs inside [lo, hi) while it is longer than 4, else one run covering it; every
+          // run lies in [rs, re) (re - rs >= 4)
+          int32_t c = len > 4 ? lo[h] + ((m + 1) * len) / 4 - 2 : min(lo[h], re[h] - 4);
+          if (len > 4) c = max(lo[h], min(c, hi[h] - 4));
+          c0[h][m] = c;
+          run[h][m] = load_run4(col + c);
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        if (found[h] != -1) continue;
+        int32_t nlo = lo[h], nhi = hi[h];
+        int32_t f = -1;
+        bool lacks = false;
+#pragma unroll
+        for (int m = 0; m < 3; m++) {
+          const uint32_t k0 = rev_sort_key(run[h][m].x), k1 = rev_sort_key(run[h][m].y),
+                         k2 = rev_sort_key(run[h][m].z), k3 = rev_sort_key(run[h][m].w);
+          const int32_t c = c0[h][m];
+          if (w[h] < k0) nhi = min(nhi, c);
+          else if (w[h] > k3) nlo = max(nlo, c + 4);
+          else if (w[h] == k0) f = c;
+          else if (w[h] == k1) f = c + 1;
+          else if (w[h] == k2) f = c + 2;
+          else if (w[h] == k3) f = c + 3;
+          else lacks = true;
+        }
+        if (f >= 0) found[h] = f;
+        else if (lacks || nlo >= nhi || hi[h] - lo[h] <= 4) found[h] = -2;
+        lo[h] = nlo;
+        hi[h] = nhi;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; h++)
+      if (found[h] >= 0) {
+        rev[ei[h]] = found[h];
+        rev[found[h]] = ei[h];
       }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     // the row of the next entries
     while (i < i1 - 1 && row_ptr[i + 1] <= base) i++;
+  }
+}
+
+// Reverse index by row groups, for boxes at least 2 (r_cut + skin) wide on every axis: there a
+// row holds at most one image of any atom, so its entries have distinct indices. A block takes
+// kRevGroup consecutive rows [g, g + R). Their reverse entries in a target row j are the
+// entries of row j with index in [g, g + R), which are consecutive there: for an entry
+// e = (i <- j), rev[e] = lower_bound(row j, g) + #{rows i' in [g, i) that hold j}. So each
+// distinct target row is searched once per group (about one search per eight entries for
+// groups of 32 rows at water density), and every store rev[e] is contiguous. An LDS hash table
+// maps each distinct target j to its search result and a mask of the group's rows holding it
+// (OR-ed in any order, so the result does not depend on thread order). The group's entries
+// (target and row) are first staged in LDS with independent loads, so neither pass over them
+// waits on global memory. A group with more entries than the stage holds is split, and one
+// whose table gets crowded (a probe chain of kRevMaxProbe) is redone in halves; a single row
+// (at most kMaxRow = kRevSlots entries) always fits.
+constexpr int kRevGroup = 32;
+constexpr int kRevSlots = 1024;
+constexpr int kRevMaxProbe = 64;   // probe chain that marks a group's table as crowded
+constexpr int kRevEntries = 4608;  // entries of a group staged in LDS (32 rows of ~144)
+static_assert(kRevEntries >= kMaxRow, "one row always fits the stage");
+static_assert(kRevSlots >= kMaxRow, "one row's distinct targets always fit the table");
+constexpr uint32_t kRevEmpty = 0xFFFFFFFFu;
+
+__device__ __forceinline__ uint32_t rev_hash(uint32_t j) {
+  return (j * 0x9E3779B1u) >> (32 - 10);  // kRevSlots = 2^10
+}
+
+// first position p in [rs, re] of the sorted row whose sort key is >= w, reading one run of
+// four entries per round (the middle of the open range, or one run covering it once it is at
+// most four long); NS independent searches advance in lockstep (act = false: none). One run
+// per round keeps the number of memory instructions low (each costs the data-return path
+// about the same whatever it carries), at the price of a few more rounds.
+template <int NS>
+__device__ __forceinline__ void lower_bound_runs(const uint32_t* __restrict__ col,
+                                                 const bool (&act)[NS], const int32_t (&rs)[NS],
+                                                 const int32_t (&re)[NS], uint32_t w,
+                                                 int32_t (&out)[NS]) {
+  int32_t lo[NS], hi[NS];
+  bool live[NS];
+#pragma unroll
+  for (int h = 0; h < NS; h++) {
+    lo[h] = rs[h];
+    hi[h] = re[h];
+    out[h] = rs[h];
+    live[h] = act[h] && rs[h] < re[h];
+    if (live[h] && re[h] - rs[h] < 4) {  // short row: count its entries below w
+      int32_t p = rs[h];
+      for (int32_t k = rs[h]; k < re[h]; k++)
+        if (rev_sort_key(col[k]) < w) p = k + 1;
+      out[h] = p;
+      live[h] = false;
+    }
+  }
+  for (;;) {
+    bool any = false;
+#pragma unroll
+    for (int h = 0; h < NS; h++) any |= live[h];
+    if (!any) break;
+    uint4 run[NS];
+    int32_t c0[NS];
+#pragma unroll
+    for (int h = 0; h < NS; h++) {
+      if (!live[h]) continue;
+      const int32_t len = hi[h] - lo[h];
+      // inside [lo, hi) while it is longer than 4, else covering it; always inside [rs, re)
+      // (re - rs >= 4)
+      c0[h] = len > 4 ? lo[h] + (len - 4) / 2 : min(lo[h], re[h] - 4);
+      run[h] = load_run4(col + c0[h]);
+    }
+#pragma unroll
+    for (int h = 0; h < NS; h++) {
+      if (!live[h]) continue;
+      const bool covering = hi[h] - lo[h] <= 4;
+      const int32_t q = (rev_sort_key(run[h].x) < w) + (rev_sort_key(run[h].y) < w) +
+                        (rev_sort_key(run[h].z) < w) + (rev_sort_key(run[h].w) < w);
+      const int32_t c = c0[h];
+      // q > 0: every key before c + q is below w; q < 4: the key at c + q is not
+      if (q > 0) lo[h] = max(lo[h], c + q);
+      if (q < 4) hi[h] = min(hi[h], c + q);
+      // a covering run pins the answer; otherwise the range shrank strictly
+      if (covering || lo[h] >= hi[h]) {
+        out[h] = lo[h];
+        live[h] = false;
+      }
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) k_rev_grouped(int32_t n,
+                                                     const int32_t* __restrict__ row_ptr,
+                                                     const uint32_t* __restrict__ col,
+                                                     int32_t* __restrict__ rev) {
+  __shared__ uint32_t tkey[kRevSlots];
+  __shared__ uint32_t tmask[kRevSlots];
+  __shared__ int32_t tbase[kRevSlots];
+  __shared__ __align__(16) uint32_t sc[kRevEntries];  // the group's targets j, entry order
+  __shared__ __align__(16) uint8_t srow[kRevEntries];  // their rows, offsets from the first
+  __shared__ int16_t slist[kRevSlots];                 // occupied table slots
+  __shared__ int32_t srp[kRevGroup + 1];
+  __shared__ int32_t swsum[4];
+  __shared__ int32_t sflag;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  // XCD-aware block order: consecutive groups (spatial neighbours) share an XCD's L2
+  const int32_t g0 = (int32_t)xcd_block(blockIdx.x, gridDim.x) * kRevGroup;
+  if (g0 >= n) return;
+  const int32_t g1 = min(g0 + kRevGroup, n);
+  if (t <= g1 - g0) srp[t] = row_ptr[g0 + t];
+  __syncthreads();
+  int rcap = kRevGroup;
+  int32_t ga = g0;
+  while (ga < g1) {
+    const int ra = (int)(ga - g0);
+    int R = min(rcap, (int)(g1 - ga));
+    while (R > 1 && srp[ra + R] - srp[ra] > kRevEntries) R >>= 1;  // block-uniform
+    const int32_t e0 = srp[ra];
+    const int ne = (int)(srp[ra + R] - e0);  // <= kRevEntries (one row: <= kMaxRow)
+    // stage the group's targets, four consecutive entries per thread and load, and their rows;
+    // clear the table
+    for (int k = 4 * t; k < ne; k += 4 * 256) {
+      uint4 v;
+      if (k + 4 <= ne) {
+        v = load_run4(col + e0 + k);
+      } else {
+        v.x = col[e0 + k];
+        v.y = k + 1 < ne ? col[e0 + k + 1] : 0u;
+        v.z = k + 2 < ne ? col[e0 + k + 2] : 0u;
+        v.w = 0u;
+      }
+      const uint32_t m = 0x7FFFFFFu;
+      *reinterpret_cast<uint4*>(&sc[k]) = make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+    }
+    for (int r = 0; r < R; r++)
+      for (int k = (int)(srp[ra + r] - e0) + t; k < (int)(srp[ra + r + 1] - e0); k += 256)
+        srow[k] = (uint8_t)r;
+    for (int k = t; k < kRevSlots; k += 256) {
+      tkey[k] = kRevEmpty;
+      tmask[k] = 0u;
+    }
+    if (t == 0) sflag = 0;
+    __syncthreads();
+    // 1. distinct targets and the group rows holding each
+    for (int k = t; k < ne; k += 256) {
+      const uint32_t j = sc[k];
+      uint32_t h = rev_hash(j);
+      bool placed = false;
+      // a group of several rows gives up on a long probe chain (a crowded table); a single
+      // row may probe the whole table, where it always fits
+      const int max_probe = R > 1 ? kRevMaxProbe : kRevSlots;
+      for (int probe = 0; probe < max_probe; probe++) {
+        const uint32_t old = atomicCAS(&tkey[h], kRevEmpty, j);
+        if (old == kRevEmpty || old == j) {
+          placed = true;
+          break;
+        }
+        h = (h + 1) & (kRevSlots - 1);
+      }
+      if (!placed) {
+        sflag = 1;
+        break;
+      }
+      atomicOr(&tmask[h], 1u << srow[k]);
+    }
+    __syncthreads();
+    const bool over = sflag != 0;
+    if (over) {  // block-uniform: redo the group in halves
+      rcap = R > 1 ? R / 2 : 1;
+      __syncthreads();  // every thread has read sflag before the next attempt resets it
+      continue;
+    }
+    // 2. list the occupied slots (thread t holds slots 4t .. 4t+3), then one search per
+    //    distinct target: where its entries of index >= ga begin
+    {
+      uint32_t occ = 0;
+#pragma unroll
+      for (int u = 0; u < 4; u++) occ |= (tkey[4 * t + u] != kRevEmpty ? 1u : 0u) << u;
+      int cnt = __popc(occ), inc = cnt;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += y;
+      }
+      if (lane == 63) swsum[wv] = inc;
+      __syncthreads();
+      int off = inc - cnt;
+      for (int k = 0; k < wv; k++) off += swsum[k];
+#pragma unroll
+      for (int u = 0; u < 4; u++)
+        if (occ & (1u << u)) slist[off++] = (int16_t)(4 * t + u);
+    }
+    __syncthreads();
+    const int nd = swsum[0] + swsum[1] + swsum[2] + swsum[3];
+    for (int b0 = 0; b0 < nd; b0 += 2 * 256) {
+      bool act[2];
+      int32_t rs[2], re[2], out[2], slot[2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; s2++) {
+        const int k = b0 + 256 * s2 + t;
+        act[s2] = k < nd;
+        slot[s2] = act[s2] ? slist[k] : 0;
+        rs[s2] = re[s2] = 0;
+        if (act[s2]) {
+          int2 b;
+          __builtin_memcpy(&b, row_ptr + tkey[slot[s2]], sizeof(b));  // row_ptr[j], [j+1]
+          rs[s2] = b.x;
+          re[s2] = b.y;
+        }
+      }
+      lower_bound_runs<2>(col, act, rs, re, (uint32_t)ga << 5, out);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; s2++)
+        if (act[s2]) tbase[slot[s2]] = out[s2];
+    }
+    __syncthreads();
+    // 3. every entry's reverse slot, four consecutive entries per thread and store
+    for (int k = 4 * t; k < ne; k += 4 * 256) {
+      const uint4 j4 = *reinterpret_cast<const uint4*>(&sc[k]);
+      const uint32_t r4 = *reinterpret_cast<const uint32_t*>(&srow[k]);
+      const uint32_t jj[4] = {j4.x, j4.y, j4.z, j4.w};
+      int32_t v[4];
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        v[u] = 0;
+        if (k + u < ne) {
+          uint32_t h = rev_hash(jj[u]);
+          while (tkey[h] != jj[u]) h = (h + 1) & (kRevSlots - 1);  // present after pass 1
+          const uint32_t below = (1u << ((r4 >> (8 * u)) & 0xFFu)) - 1u;
+          v[u] = tbase[h] + __popc(tmask[h] & below);
+        }
+      }
+      if (k + 4 <= ne) {
+        const int4 o = make_int4(v[0], v[1], v[2], v[3]);
+        __builtin_memcpy(rev + e0 + k, &o, sizeof(o));
+      } else {
+        for (int u = 0; u < 4 && k + u < ne; u++) rev[e0 + k + u] = v[u];
+      }
+    }
+    __syncthreads();
+    ga += R;
   }
 }
 
@@ -837,7 +1223,8 @@ int32_t build_neighbors_impl(int32_t n, const float box[3], float r_cut, float s
   TESS_HIP_CHECK(scan_exclusive_i32(row_ptr, (int64_t)n + 1, ws.scan_tmp, st));
   // misc[0]: longest row; misc[4..5]: 64-bit pair total (the block is 256-byte aligned)
   unsigned long long* total = reinterpret_cast<unsigned long long*>(ws.misc + 4);
-  k_max_row<<<grid(n, 256), 256, 0, st>>>(n, row_ptr, ws.misc, total);
+  k_max_row<<<(unsigned)min(grid(n, 256), kMaxRowBlocks), 256, 0, st>>>(n, row_ptr, ws.misc,
+                                                                         total);
   TESS_HIP_CHECK(hipGetLastError());
   int32_t max_row = 0, bits = 0;
   unsigned long long pairs = 0;
@@ -860,7 +1247,11 @@ int32_t build_neighbors_impl(int32_t n, const float box[3], float r_cut, float s
                  col_shift));
   TESS_HIP_CHECK(hipGetLastError());
   if (rev) {
-    k_rev<<<grid(n, 4 * kRevRows), 256, 0, st>>>(n, row_ptr, col_shift, rev);
+    // row groups need distinct indices per row: every box edge at least 2 (r_cut + skin)
+    if (fmin(L[0], fmin(L[1], L[2])) >= 2.0 * rcs * (1.0 + 1e-6))
+      k_rev_grouped<<<grid(n, kRevGroup), 256, 0, st>>>(n, row_ptr, col_shift, rev);
+    else
+      k_rev<<<grid(n, 4 * kRevRows), 256, 0, st>>>(n, row_ptr, col_shift, rev);
     TESS_HIP_CHECK(hipGetLastError());
   }
   return TESS_OK;

@@ -114,7 +114,7 @@ def write_summaries(stats_csv: str, fetch_csv: str, write_csv: str, kernel_key: 
 
 REBUILD_KERNELS = ("k_wrap_key", "k_radix_hist", "k_radix_scatter", "k_scan_partial", "k_scan_sums",
                    "k_scan_final", "k_permute", "k_cell_count", "k_cell_fill", "k_cell_pairs",
-                   "k_max_row", "k_rev")
+                   "k_max_row", "k_rev", "k_rev_grouped")
 
 
 def rebuild_md(stats_csv: str, workload: str, command: str, calls_per_rebuild: dict = None) -> str:

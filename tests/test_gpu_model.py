@@ -167,6 +167,24 @@ def test_repeatable_and_energy_only(T):
     assert c["energy"] == a["energy"]
 
 
+def test_reverse_index_built_inside_energy_pass(T):
+    """Without a caller reverse index the energy pass builds its own (a search per entry in
+    the target row); the rebuild's (one search per distinct target row of a group of rows)
+    must be the same index, so energy and forces agree bit for bit."""
+    import torch
+    wl = W.load("salt4k")
+    w = W.make_weights(wl.model, 2002)
+    a = _run(T, wl, w)
+    s = a["sys"]
+    f2 = torch.zeros_like(s.forces)
+    e2 = torch.zeros_like(s.energy)
+    T.energy_forces(s.spec, s.weights, s.box, s.pos, s.species, s.row_ptr, s.col_shift, None,
+                    s.n_edges, e2, s.ws, forces=f2)
+    torch.cuda.synchronize()
+    assert float(e2.cpu()[0]) == a["energy"]
+    assert np.array_equal(f2.cpu().numpy().astype(np.float64), a["forces"])
+
+
 def test_energy_forces_graph_capture_replays(T):
     """tess_energy_forces captured by the caller (torch CUDA graph, global capture mode) with
     its second and third streams forked and joined inside the capture: every replay, with
