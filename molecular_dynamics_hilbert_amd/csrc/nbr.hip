@@ -351,9 +351,10 @@ constexpr int kCellCap = 2016;
 // (r < kPer; position in .xyz, the entry's bits in .w) and spos is free; total <= 256 * EPT.
 // The keys (entry << 32 | q) are sorted by an ascending bitonic network in registers: position
 // a = t*EPT + r lives in thread t, so a compare-exchange at distance jj < EPT stays in the
-// thread, one with EPT <= jj < 64*EPT crosses lanes of a wave (a lane shuffle), and only the
-// three stages with partners in another wave exchange through LDS (spos as scratch). The
-// candidates are then written to spos unsorted and gathered into sorted order.
+// thread, one with EPT <= jj < 64*EPT crosses lanes of a wave (DPP moves, or a lane shuffle
+// for lanes 16 and 32 apart), and only the three stages with partners in another wave
+// exchange through LDS (spos as scratch). The candidates are then written to spos unsorted
+// and gathered into sorted order.
 template <int J, int EPT>
 __device__ __forceinline__ void bitonic_in_thread(uint64_t (&x)[EPT], int base, int k) {
 #pragma unroll
@@ -367,9 +368,27 @@ __device__ __forceinline__ void bitonic_in_thread(uint64_t (&x)[EPT], int base, 
     }
 }
 
+// The value of lane (lane ^ m) for m a power of two below 64. Distances 1, 2, 4 and 8 stay
+// in the VALU as DPP moves: quad permutations [1,0,3,2] and [2,3,0,1]; a half-row mirror
+// (lane ^ 7) followed by the quad reversal (lane ^ 3) for 4; a rotation by 8 within a row of
+// 16 lanes for 8. Distances 16 and 32 use ds_bpermute, which goes through the LDS unit.
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v, int m) {
+  const int x = (int)v;
+  switch (m) {
+    case 1: return (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);
+    case 2: return (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);
+    case 4: {
+      const int t = __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);
+      return (uint32_t)__builtin_amdgcn_update_dpp(0, t, 0x1B, 0xF, 0xF, false);
+    }
+    case 8: return (uint32_t)__builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false);
+    default: return (uint32_t)__shfl_xor(x, m, 64);
+  }
+}
+
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
-  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
+  const uint32_t lo = lane_xor_u32((uint32_t)v, m);
+  const uint32_t hi = lane_xor_u32((uint32_t)(v >> 32), m);
   return ((uint64_t)hi << 32) | lo;
 }
 
@@ -386,7 +405,10 @@ __device__ __forceinline__ void sort_staged(float4* spos, const float4 (&sp)[kPe
     x[r] = q < total ? ((uint64_t)__float_as_uint(sp[r].w) << 32) | (uint32_t)q : ~0ull;
   }
   uint64_t* xbuf = reinterpret_cast<uint64_t*>(spos);  // N * 8 bytes <= half of spos
+  // fully unrolled: every stage's distances are compile-time constants
+#pragma unroll
   for (int k = 2; k <= N; k <<= 1) {
+#pragma unroll
     for (int jj = k >> 1; jj > 0; jj >>= 1) {
       if (jj >= 64 * EPT) {  // block-uniform
         __syncthreads();     // earlier readers of xbuf are done
@@ -430,7 +452,8 @@ __device__ __forceinline__ void sort_staged(float4* spos, const float4 (&sp)[kPe
   f32x4* sv4 = reinterpret_cast<f32x4*>(spos);
   f32x4 v[EPT];
 #pragma unroll
-  for (int r = 0; r < EPT; r++) v[r] = sv4[base + r < total ? (uint32_t)x[r] : 0u];
+  for (int r = 0; r < EPT; r++)  // (the clamp only guards the LDS index)
+    v[r] = sv4[base + r < total ? min((uint32_t)x[r], (uint32_t)(total - 1)) : 0u];
   __syncthreads();
   // positions in [total, kCellCap) take filler that the pair loop never reads
 #pragma unroll
@@ -467,7 +490,10 @@ __global__ void __launch_bounds__(256) k_cell_pairs(CellGrid g, double rcs2, flo
   static_assert(kBytes >= 4 * kMaxRow * 4, "row buffers fit the staging area");
   __shared__ __align__(16) char smem[kBytes];
   float4* spos = reinterpret_cast<float4*>(smem);
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  // the wave index, known to the compiler as wave-uniform (keeps the per-atom conditions and
+  // counts scalar)
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
   const int c = (int)xcd_block(blockIdx.x, gridDim.x);
   const int32_t a0 = cell_start[c], a1 = cell_start[c + 1];
   if (a0 == a1) return;  // empty cell (the whole block returns)
@@ -545,7 +571,6 @@ __global__ void __launch_bounds__(256) k_cell_pairs(CellGrid g, double rcs2, flo
   __syncthreads();
   // Each wave takes kCellAtoms of the cell's atoms at a time: every staged candidate read
   // from LDS is tested against all of them.
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int32_t k0 = a0 + wv * kCellAtoms; k0 < a1; k0 += 4 * kCellAtoms) {
     int32_t ia[kCellAtoms];
     float xf[kCellAtoms][3];
@@ -562,26 +587,54 @@ __global__ void __launch_bounds__(256) k_cell_pairs(CellGrid g, double rcs2, flo
       count[u] = 0;
       o[u] = FILL ? (int64_t)row_ptr[i] : 0;
     }
+    float4 pn = spos[lane < total ? lane : 0];  // the first batch's candidate
     for (int q0 = 0; q0 < total; q0 += 64) {
       const int q = q0 + lane;
       const bool ok = q < total;
-      const float4 p = spos[ok ? q : 0];
+      const float4 p = pn;
+      if (q0 + 64 < total) {  // wave-uniform: request the next batch's candidate now
+        const int qn = q + 64;
+        pn = spos[qn < total ? qn : 0];
+      }
       const uint32_t entry = __float_as_uint(p.w);
       const int32_t j = (int32_t)(entry >> 5);
       const int code = (int)(entry & 31u);
+      // the decisions as wave masks (one compare each): near in fp32 and the atom itself (same
+      // index, zero shift); the rounding band is checked once per batch
+      const uint64_t m_ok = __ballot(ok);
+      const uint64_t m_self = __ballot(code == 13);
+      float d2v[kCellAtoms];
+      uint64_t m_near[kCellAtoms];
+      uint64_t m_band = 0;
 #pragma unroll
       for (int u = 0; u < kCellAtoms; u++) {
-        if (k0 + u >= a1) break;  // wave-uniform
         const float dx = p.x - xf[u][0], dy = p.y - xf[u][1], dz = p.z - xf[u][2];
-        const float d2 = __builtin_fmaf(dz, dz, __builtin_fmaf(dy, dy, dx * dx));
-        bool near = d2 < lo2;
-        if (ok && !near && d2 <= hi2)  // inside the band: the fp64 test decides
-          near = pair_pass(pos[3 * j], pos[3 * j + 1], pos[3 * j + 2], code, (double)xf[u][0],
+        d2v[u] = __builtin_fmaf(dz, dz, __builtin_fmaf(dy, dy, dx * dx));
+        m_near[u] = __ballot(d2v[u] < lo2);
+        m_band |= __ballot(d2v[u] >= lo2) & __ballot(d2v[u] <= hi2);
+      }
+      // inside the band the fp64 test decides; one branch per batch keeps its fp64 shift
+      // terms (shared by the atoms) out of the common path
+      if ((m_band & m_ok) != 0ull) {  // wave-uniform, rare
+#pragma unroll
+        for (int u = 0; u < kCellAtoms; u++) {
+          if (k0 + u >= a1) break;  // wave-uniform
+          bool in = false;
+          if (ok && d2v[u] >= lo2 && d2v[u] <= hi2)
+            in = pair_pass(pos[3 * j], pos[3 * j + 1], pos[3 * j + 2], code, (double)xf[u][0],
                            (double)xf[u][1], (double)xf[u][2], g, rcs2);
-        const bool pass = ok && near && !(j == ia[u] && code == 13);
-        const uint64_t m = __ballot(pass);
-        if (FILL && pass) {
-          const int slot = count[u] + __popcll(m & lt);
+          m_near[u] |= __ballot(in);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kCellAtoms; u++) {
+        // atoms past the cell's end (repeats of its first atom) are never written or counted
+        const uint64_t m = k0 + u < a1 ? m_near[u] & m_ok & ~(m_self & __ballot(j == ia[u]))
+                                       : 0ull;
+        if (FILL && ((m >> lane) & 1ull)) {
+          const int slot = count[u] + (int)__builtin_amdgcn_mbcnt_hi(
+                                          (uint32_t)(m >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
           if (slot < kMaxRow) col_shift[o[u] + slot] = (uint32_t)j | ((uint32_t)code << 27);
         }
         count[u] += __popcll(m);
