@@ -1903,7 +1903,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
   const int32_t* rev = rev_in;
   if (cap > 0) {
     if (!rev) {
-      // reverse index through a binary search in each row (rows are sorted)
+      // reverse index: each pair searched once in its target row (rows are sorted)
       TESS_HIP_CHECK(rev_index(n, row_ptr, col_shift, w.rev_own, st));
       rev = w.rev_own;
     }
