@@ -88,8 +88,20 @@ __global__ void k_wrap_key(int32_t n, int curve, double Lx, double Ly, double Lz
                            float* __restrict__ pos_w, uint32_t* __restrict__ key,
                            int32_t* __restrict__ idx, int32_t* __restrict__ sp_tmp,
                            float* __restrict__ v_tmp, float* __restrict__ f_tmp,
-                           int32_t* __restrict__ pa_tmp, int32_t* __restrict__ status) {
+                           int32_t* __restrict__ pa_tmp, int32_t* __restrict__ status,
+                           int32_t* __restrict__ cell_start, int32_t* __restrict__ cell_fill,
+                           int64_t ncell, int32_t* __restrict__ misc,
+                           int32_t* __restrict__ row_end) {
   int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  // counters of the later stages start at zero: cell counts (ncell + 1, the last one for the
+  // scan's total), cell fill counters, the row statistics and the last row offset
+  const int64_t nclr = ncell + 1 > 16 ? ncell + 1 : 16;
+  for (int64_t j = i; j < nclr; j += (int64_t)gridDim.x * blockDim.x) {
+    if (j <= ncell) cell_start[j] = 0;
+    if (j < ncell) cell_fill[j] = 0;
+    if (j < 16) misc[j] = 0;
+  }
+  if (i == 0) *row_end = 0;
   if (i >= n) return;
   // a non-finite coordinate is reported through the status word (its key and cell are then
   // meaningless but stay in range: the quantisation and the cell index clamp)
@@ -182,6 +194,37 @@ __global__ void __launch_bounds__(256) k_radix_scatter(const uint32_t* __restric
   }
 }
 
+struct CellGrid {
+  int nc[3];
+  double L[3];
+};
+
+__device__ __forceinline__ int cell_coord(float x, int nc, double L) {
+  int v = (int)floor((double)x * (double)nc / L);
+  return v < 0 ? 0 : (v >= nc ? nc - 1 : v);
+}
+
+// atomicAdd(&cnt[c], 1) for every active lane, one atomic per distinct c in the wave; returns
+// the lane's slot (the counter's old value plus the rank among the lanes with the same c,
+// ranks in lane order)
+__device__ __forceinline__ int32_t wave_aggregated_add(int32_t* __restrict__ cnt, int c) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint64_t left = __ballot(1);
+  int32_t slot = 0;
+  while (left) {
+    const int lead = __builtin_ctzll(left);
+    const int cl = __builtin_amdgcn_readlane(c, lead);
+    const uint64_t m = __ballot(c == cl) & left;
+    int32_t b = 0;
+    if (lane == lead) b = atomicAdd(&cnt[cl], __popcll(m));
+    b = __builtin_amdgcn_readlane(b, lead);
+    if (c == cl) slot = b + __popcll(m & lt);
+    left &= ~m;
+  }
+  return slot;
+}
+
 __global__ void k_permute(int32_t n, const int32_t* __restrict__ idx, const uint32_t* __restrict__ key,
                           const float* __restrict__ pos_w, const int32_t* __restrict__ sp_tmp,
                           const float* __restrict__ v_tmp, const float* __restrict__ f_tmp,
@@ -189,12 +232,19 @@ __global__ void k_permute(int32_t n, const int32_t* __restrict__ idx, const uint
                           int32_t* __restrict__ species, float* __restrict__ vel,
                           float* __restrict__ forces, int32_t* __restrict__ pa,
                           float* __restrict__ ref_pos, int32_t* __restrict__ perm,
-                          uint32_t* __restrict__ hkey) {
+                          uint32_t* __restrict__ hkey, CellGrid g,
+                          int32_t* __restrict__ cell_id, int32_t* __restrict__ cell_cnt) {
   int32_t k = blockIdx.x * blockDim.x + threadIdx.x;
   if (k >= n) return;
   int32_t o = idx[k];
   float x = pos_w[3 * o], y = pos_w[3 * o + 1], z = pos_w[3 * o + 2];
   pos[3 * k] = x; pos[3 * k + 1] = y; pos[3 * k + 2] = z;
+  // cell of the sorted atom, counted with one atomic per distinct cell of the wave
+  // (consecutive atoms along the curve mostly share a cell)
+  const int c = (cell_coord(x, g.nc[0], g.L[0]) * g.nc[1] + cell_coord(y, g.nc[1], g.L[1])) *
+                    g.nc[2] + cell_coord(z, g.nc[2], g.L[2]);
+  cell_id[k] = c;
+  (void)wave_aggregated_add(cell_cnt, c);
   if (ref_pos) { ref_pos[3 * k] = x; ref_pos[3 * k + 1] = y; ref_pos[3 * k + 2] = z; }
   species[k] = sp_tmp[o];
   if (vel)
@@ -206,28 +256,6 @@ __global__ void k_permute(int32_t n, const int32_t* __restrict__ idx, const uint
   if (hkey) hkey[k] = key[k];
 }
 
-struct CellGrid {
-  int nc[3];
-  double L[3];
-};
-
-__device__ __forceinline__ int cell_coord(float x, int nc, double L) {
-  int v = (int)floor((double)x * (double)nc / L);
-  return v < 0 ? 0 : (v >= nc ? nc - 1 : v);
-}
-
-__global__ void k_cell_count(int32_t n, CellGrid g, const float* __restrict__ pos,
-                             int32_t* __restrict__ cell_id, int32_t* __restrict__ cnt) {
-  int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  int cx = cell_coord(pos[3 * i], g.nc[0], g.L[0]);
-  int cy = cell_coord(pos[3 * i + 1], g.nc[1], g.L[1]);
-  int cz = cell_coord(pos[3 * i + 2], g.nc[2], g.L[2]);
-  int c = (cx * g.nc[1] + cy) * g.nc[2] + cz;
-  cell_id[i] = c;
-  atomicAdd(&cnt[c], 1);
-}
-
 // Cell-sorted copy of the atoms: atoms[slot] = i and cpos[slot] = (x_i, y_i, z_i, bits of i),
 // so a cell's atoms and their positions are contiguous (one 16-byte load per candidate).
 __global__ void k_cell_fill(int32_t n, const int32_t* __restrict__ cell_id,
@@ -236,8 +264,8 @@ __global__ void k_cell_fill(int32_t n, const int32_t* __restrict__ cell_id,
                             float4* __restrict__ cpos) {
   int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
-  int c = cell_id[i];
-  int slot = cell_start[c] + atomicAdd(&fill[c], 1);
+  const int c = cell_id[i];
+  const int slot = cell_start[c] + wave_aggregated_add(fill, c);
   atoms[slot] = i;
   cpos[slot] = make_float4(pos[3 * i], pos[3 * i + 1], pos[3 * i + 2], __int_as_float(i));
 }
@@ -648,39 +676,6 @@ __global__ void __launch_bounds__(256) k_cell_pairs(CellGrid g, double rcs2, flo
   }
 }
 
-// Longest row and total pair count of a scanned CSR: grid-stride over the rows, block
-// reductions, one atomic of each per block (at most kMaxRowBlocks blocks, so the atomics on
-// the one result line stay few). The scan adds in 32 bits, so a total beyond the int32 range
-// of row_ptr wraps there; each row's count is still the difference of its (wrapped) bounds,
-// and their 64-bit sum is the true total.
-constexpr int kMaxRowBlocks = 256;
-__global__ void __launch_bounds__(256) k_max_row(int32_t n, const int32_t* __restrict__ row_ptr,
-                                                 int32_t* __restrict__ out,
-                                                 unsigned long long* __restrict__ total) {
-  int v = 0;
-  unsigned long long s = 0;
-  for (int32_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
-    const int c = (int)((uint32_t)row_ptr[i + 1] - (uint32_t)row_ptr[i]);
-    v = max(v, c);
-    s += (unsigned long long)c;
-  }
-  for (int o = 32; o >= 1; o >>= 1) {
-    v = max(v, __shfl_xor(v, o, 64));
-    s += __shfl_xor(s, o, 64);
-  }
-  __shared__ int32_t sh[4];
-  __shared__ unsigned long long ss[4];
-  if ((threadIdx.x & 63) == 0) {
-    sh[threadIdx.x >> 6] = v;
-    ss[threadIdx.x >> 6] = s;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    atomicMax(out, max(max(sh[0], sh[1]), max(sh[2], sh[3])));
-    atomicAdd(total, ss[0] + ss[1] + ss[2] + ss[3]);
-  }
-}
-
 // rev[e] = slot of the reverse pair (j <- i, 26 - code) of entry e = (i <- j, code). Rows are
 // sorted by (j, code) with distinct entries, and the pair test is symmetric, so the reverse
 // entry is in row j. Each pair is searched once, from the row of its smaller index: for an
@@ -1073,100 +1068,234 @@ __global__ void __launch_bounds__(256) k_rev_grouped(int32_t n,
 }
 
 // ---- scan -----------------------------------------------------------------------------
-constexpr int kScanTile = 4096;  // 256 threads x 16
+// Exclusive scan of int32 counts in place. Up to kScanOneMax entries one block of 1024
+// threads does it in one launch (all values loaded first, then four 16,384-entry chunks scanned
+// with a running carry); longer arrays take two launches (tile sums, then each tile adds the
+// sum of the tile sums before it, which it reduces itself), and beyond kScanCarryTiles tiles a
+// third launch scans the tile sums. Optionally the same launches report the largest count and
+// the 64-bit total of the counts (stats[0], stats[2..3]).
+constexpr int kScanTile = 4096;          // 256 threads x 16 (multi-block tiles)
+constexpr int kScanOneChunk = 16384;     // 1024 threads x 16
+constexpr int kScanOneMax = 4 * kScanOneChunk;
+constexpr int kScanCarryTiles = 4096;
 
-__device__ __forceinline__ int32_t block_exclusive_scan_256(int32_t v, int32_t* sh, int32_t* total) {
-  int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  int32_t inc = v;
+__device__ __forceinline__ int32_t wave_inclusive_scan(int32_t v) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    int32_t y = __shfl_up(inc, o, 64);
-    if (lane >= o) inc += y;
+    int32_t y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
   }
+  return v;
+}
+
+template <int NW>
+__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* sh, int32_t* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int32_t inc = wave_inclusive_scan(v);
   if (lane == 63) sh[w] = inc;
   __syncthreads();
   int32_t off = 0, tot = 0;
 #pragma unroll
-  for (int k = 0; k < 4; k++) {
-    if (k < w) off += sh[k];
-    tot += sh[k];
+  for (int k = 0; k < NW; k++) {
+    const int32_t x = sh[k];
+    off += k < w ? x : 0;
+    tot += x;
   }
   __syncthreads();
   *total = tot;
   return off + inc - v;
 }
 
-// Two arrays of the same length can be scanned by the same launches: blockIdx.y (partial,
-// final) or blockIdx.x (sums) selects the array, and its tile sums sit nb entries apart.
-struct ScanPair {
-  int32_t* d[2];
-};
-
-__global__ void __launch_bounds__(256) k_scan_partial(ScanPair sp, int64_t n,
-                                                      int32_t* __restrict__ sums) {
-  __shared__ int32_t sh[4];
-  const int32_t* __restrict__ d = sp.d[blockIdx.y];
-  int64_t base = (int64_t)blockIdx.x * kScanTile + threadIdx.x * 16;
-  int32_t s = 0;
-  for (int k = 0; k < 16; k++)
-    if (base + k < n) s += d[base + k];
-  int32_t tot;
-  block_exclusive_scan_256(s, sh, &tot);
-  if (threadIdx.x == 0) sums[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = tot;
+// Largest value and 64-bit sum over the block, written by thread 0 (`atomic`: combined with
+// what other blocks wrote; the targets then start at zero).
+template <int NW>
+__device__ __forceinline__ void block_stats(int32_t mx, unsigned long long sm, int32_t* stats,
+                                            bool atomic) {
+  __shared__ int32_t smx[NW];
+  __shared__ unsigned long long ssm[NW];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    mx = max(mx, __shfl_xor(mx, o, 64));
+    sm += __shfl_xor(sm, o, 64);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    smx[threadIdx.x >> 6] = mx;
+    ssm[threadIdx.x >> 6] = sm;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    mx = smx[0];
+    sm = ssm[0];
+    for (int k = 1; k < NW; k++) {
+      mx = max(mx, smx[k]);
+      sm += ssm[k];
+    }
+    unsigned long long* tot = reinterpret_cast<unsigned long long*>(stats + 2);
+    if (atomic) {
+      atomicMax(stats, mx);
+      atomicAdd(tot, sm);
+    } else {
+      stats[0] = mx;
+      *tot = sm;
+    }
+  }
 }
 
-__global__ void __launch_bounds__(256) k_scan_sums(int32_t* __restrict__ sums_all, int32_t nb) {
+// 16 consecutive entries from p (entries at or beyond n read as 0); 16-byte loads where the
+// address allows
+__device__ __forceinline__ void load16(const int32_t* __restrict__ d, int64_t base, int64_t n,
+                                       int32_t v[16]) {
+  if (base + 16 <= n && ((reinterpret_cast<uintptr_t>(d + base) & 15) == 0)) {
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const int4 x = *reinterpret_cast<const int4*>(d + base + 4 * q);
+      v[4 * q] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 16; k++) v[k] = (base + k < n) ? d[base + k] : 0;
+  }
+}
+
+__device__ __forceinline__ void store16(int32_t* __restrict__ d, int64_t base, int64_t n,
+                                        const int32_t v[16]) {
+  if (base + 16 <= n && ((reinterpret_cast<uintptr_t>(d + base) & 15) == 0)) {
+#pragma unroll
+    for (int q = 0; q < 4; q++)
+      *reinterpret_cast<int4*>(d + base + 4 * q) =
+          make_int4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 16; k++)
+      if (base + k < n) d[base + k] = v[k];
+  }
+}
+
+__global__ void __launch_bounds__(1024) k_scan_one(int32_t* __restrict__ d, int32_t n,
+                                                   int32_t* __restrict__ stats) {
+  __shared__ int32_t sh[16];
+  constexpr int kChunks = kScanOneMax / kScanOneChunk;
+  int32_t v[kChunks][16];
+  const int nch = (n + kScanOneChunk - 1) / kScanOneChunk;
+#pragma unroll
+  for (int c = 0; c < kChunks; c++)
+    if (c < nch) load16(d, (int64_t)c * kScanOneChunk + threadIdx.x * 16, n, v[c]);
+  int32_t mx = 0;
+  unsigned long long sm = 0;
+  int32_t carry = 0;
+#pragma unroll
+  for (int c = 0; c < kChunks; c++) {
+    if (c < nch) {
+      int32_t s = 0;
+#pragma unroll
+      for (int k = 0; k < 16; k++) {
+        s += v[c][k];
+        mx = max(mx, v[c][k]);
+        sm += (unsigned long long)(uint32_t)v[c][k];
+      }
+      int32_t tot;
+      int32_t run = block_exclusive_scan<16>(s, sh, &tot) + carry;
+      carry += tot;
+#pragma unroll
+      for (int k = 0; k < 16; k++) {
+        const int32_t x = v[c][k];
+        v[c][k] = run;
+        run += x;
+      }
+      store16(d, (int64_t)c * kScanOneChunk + threadIdx.x * 16, n, v[c]);
+    }
+  }
+  if (stats) block_stats<16>(mx, sm, stats, false);
+}
+
+__global__ void __launch_bounds__(256) k_scan_partial(const int32_t* __restrict__ d, int64_t n,
+                                                      int32_t* __restrict__ sums,
+                                                      int32_t* __restrict__ stats) {
+  int32_t v[16];
+  load16(d, (int64_t)blockIdx.x * kScanTile + threadIdx.x * 16, n, v);
+  int32_t s = 0, mx = 0;
+  unsigned long long sm = 0;
+#pragma unroll
+  for (int k = 0; k < 16; k++) {
+    s += v[k];
+    mx = max(mx, v[k]);
+    sm += (unsigned long long)(uint32_t)v[k];
+  }
+  // block sum (wrapping in 32 bits like the scan itself)
+  s = wave_inclusive_scan(s);
   __shared__ int32_t sh[4];
-  int32_t* __restrict__ sums = sums_all + (int64_t)blockIdx.x * nb;
+  if ((threadIdx.x & 63) == 63) sh[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) sums[blockIdx.x] = sh[0] + sh[1] + sh[2] + sh[3];
+  if (stats) block_stats<4>(mx, sm, stats, true);
+}
+
+__global__ void __launch_bounds__(256) k_scan_sums(int32_t* __restrict__ sums, int32_t nb) {
+  __shared__ int32_t sh[4];
   int32_t carry = 0;
   for (int32_t b0 = 0; b0 < nb; b0 += 256) {
     int32_t k = b0 + threadIdx.x;
     int32_t v = k < nb ? sums[k] : 0;
     int32_t tot;
-    int32_t ex = block_exclusive_scan_256(v, sh, &tot);
+    int32_t ex = block_exclusive_scan<4>(v, sh, &tot);
     if (k < nb) sums[k] = carry + ex;
     carry += tot;
-    __syncthreads();
   }
 }
 
-__global__ void __launch_bounds__(256) k_scan_final(ScanPair sp, int64_t n,
+// CARRY: the tile's offset is the sum of the tile sums before it (reduced here); otherwise
+// `sums` already holds the scanned tile sums.
+template <bool CARRY>
+__global__ void __launch_bounds__(256) k_scan_final(int32_t* __restrict__ d, int64_t n,
                                                     const int32_t* __restrict__ sums) {
   __shared__ int32_t sh[4];
-  int32_t* __restrict__ d = sp.d[blockIdx.y];
-  int64_t base = (int64_t)blockIdx.x * kScanTile + threadIdx.x * 16;
+  int32_t carry;
+  if (CARRY) {
+    int32_t c = 0;
+    for (int32_t b = threadIdx.x; b < (int32_t)blockIdx.x; b += 256) c += sums[b];
+    int32_t tot;
+    (void)block_exclusive_scan<4>(c, sh, &tot);
+    carry = tot;
+  } else {
+    carry = sums[blockIdx.x];
+  }
+  const int64_t base = (int64_t)blockIdx.x * kScanTile + threadIdx.x * 16;
   int32_t v[16];
+  load16(d, base, n, v);
   int32_t s = 0;
-  for (int k = 0; k < 16; k++) {
-    v[k] = (base + k < n) ? d[base + k] : 0;
-    s += v[k];
-  }
+#pragma unroll
+  for (int k = 0; k < 16; k++) s += v[k];
   int32_t tot;
-  int32_t run = block_exclusive_scan_256(s, sh, &tot) +
-                sums[(int64_t)blockIdx.y * gridDim.x + blockIdx.x];
+  int32_t run = block_exclusive_scan<4>(s, sh, &tot) + carry;
+#pragma unroll
   for (int k = 0; k < 16; k++) {
-    if (base + k < n) d[base + k] = run;
-    run += v[k];
+    const int32_t x = v[k];
+    v[k] = run;
+    run += x;
   }
+  store16(d, base, n, v);
 }
 
 inline int32_t grid(int64_t n, int b) { return (int32_t)((n + b - 1) / b); }
 
 }  // namespace
 
-hipError_t scan_exclusive_i32(int32_t* data, int64_t n, int32_t* partial, hipStream_t s) {
-  return scan_exclusive_i32_pair(data, nullptr, n, partial, s);
-}
-
-hipError_t scan_exclusive_i32_pair(int32_t* a, int32_t* b, int64_t n, int32_t* partial,
-                                   hipStream_t s) {
-  int32_t nb = grid(n, kScanTile);
-  if (nb == 0) return hipSuccess;
-  const unsigned na = b ? 2u : 1u;
-  ScanPair sp{{a, b ? b : a}};
-  k_scan_partial<<<dim3(nb, na), 256, 0, s>>>(sp, n, partial);
-  k_scan_sums<<<na, 256, 0, s>>>(partial, nb);
-  k_scan_final<<<dim3(nb, na), 256, 0, s>>>(sp, n, partial);
+hipError_t scan_exclusive_i32(int32_t* data, int64_t n, int32_t* partial, hipStream_t s,
+                              int32_t* stats) {
+  if (n <= 0) return hipSuccess;
+  if (n <= kScanOneMax) {
+    k_scan_one<<<1, 1024, 0, s>>>(data, (int32_t)n, stats);
+    return hipGetLastError();
+  }
+  const int64_t nb = (n + kScanTile - 1) / kScanTile;
+  k_scan_partial<<<(unsigned)nb, 256, 0, s>>>(data, n, partial, stats);
+  if (nb <= kScanCarryTiles) {
+    k_scan_final<true><<<(unsigned)nb, 256, 0, s>>>(data, n, partial);
+  } else {
+    k_scan_sums<<<1, 256, 0, s>>>(partial, (int32_t)nb);
+    k_scan_final<false><<<(unsigned)nb, 256, 0, s>>>(data, n, partial);
+  }
   return hipGetLastError();
 }
 
@@ -1213,11 +1342,26 @@ int32_t build_neighbors_impl(int32_t n, const float box[3], float r_cut, float s
   const double L[3] = {(double)box[0], (double)box[1], (double)box[2]};
   const double rcs = (double)r_cut + (double)skin;
   const double rcs2 = rcs * rcs;
-  // 1. wrap + keys
+  // cell grid: cells at least (r_cut+skin)(1+1e-6) wide, at most ncell_cap of them
+  CellGrid g;
+  int64_t ncell = 1;
+  for (int a = 0; a < 3; a++) {
+    g.L[a] = L[a];
+    int k = (int)floor(L[a] / (rcs * (1.0 + 1e-6)));
+    g.nc[a] = k < 1 ? 1 : k;
+  }
+  for (;;) {
+    ncell = (int64_t)g.nc[0] * g.nc[1] * g.nc[2];
+    if (ncell <= ws.ncell_cap) break;
+    int a = (g.nc[0] >= g.nc[1] && g.nc[0] >= g.nc[2]) ? 0 : (g.nc[1] >= g.nc[2] ? 1 : 2);
+    g.nc[a]--;
+  }
+  // 1. wrap + keys (and the counters of the later stages cleared)
   k_wrap_key<<<grid(n, 256), 256, 0, st>>>(n, sort_curve(), L[0], L[1], L[2], pos, species,
                                            vel, forces,
                                            perm_accum, ws.pos_w, ws.key[0], ws.idx[0], ws.sp_tmp,
-                                           ws.v_tmp, ws.f_tmp, ws.pa_tmp, status);
+                                           ws.v_tmp, ws.f_tmp, ws.pa_tmp, status, ws.cell_start,
+                                           ws.cell_fill, ncell, ws.misc, row_ptr + n);
   TESS_HIP_CHECK(hipGetLastError());
   // 2. stable radix sort, 4 x 8 bits (keys have 30 bits)
   int32_t nblk = grid(n, kTile);
@@ -1232,36 +1376,19 @@ int32_t build_neighbors_impl(int32_t n, const float box[3], float r_cut, float s
     TESS_HIP_CHECK(hipGetLastError());
     cur ^= 1;
   }
-  // permute every per-atom array into sorted order
+  // permute every per-atom array into sorted order, and count the atoms of each cell
   k_permute<<<grid(n, 256), 256, 0, st>>>(n, ws.idx[cur], ws.key[cur], ws.pos_w, ws.sp_tmp,
                                           vel ? ws.v_tmp : nullptr, forces ? ws.f_tmp : nullptr,
                                           perm_accum ? ws.pa_tmp : nullptr, pos, species, vel,
-                                          forces, perm_accum, ref_pos, perm, hkey);
+                                          forces, perm_accum, ref_pos, perm, hkey, g, ws.cell_id,
+                                          ws.cell_start);
   TESS_HIP_CHECK(hipGetLastError());
   // 3. cells
-  CellGrid g;
-  int64_t ncell = 1;
-  for (int a = 0; a < 3; a++) {
-    g.L[a] = L[a];
-    int k = (int)floor(L[a] / (rcs * (1.0 + 1e-6)));
-    g.nc[a] = k < 1 ? 1 : k;
-  }
-  for (;;) {
-    ncell = (int64_t)g.nc[0] * g.nc[1] * g.nc[2];
-    if (ncell <= ws.ncell_cap) break;
-    int a = (g.nc[0] >= g.nc[1] && g.nc[0] >= g.nc[2]) ? 0 : (g.nc[1] >= g.nc[2] ? 1 : 2);
-    g.nc[a]--;
-  }
-  TESS_HIP_CHECK(hipMemsetAsync(ws.cell_start, 0, sizeof(int32_t) * (ncell + 1), st));
-  TESS_HIP_CHECK(hipMemsetAsync(ws.cell_fill, 0, sizeof(int32_t) * ncell, st));
-  TESS_HIP_CHECK(hipMemsetAsync(ws.misc, 0, sizeof(int32_t) * 16, st));
-  k_cell_count<<<grid(n, 256), 256, 0, st>>>(n, g, pos, ws.cell_id, ws.cell_start);
   TESS_HIP_CHECK(scan_exclusive_i32(ws.cell_start, ncell + 1, ws.scan_tmp, st));
   k_cell_fill<<<grid(n, 256), 256, 0, st>>>(n, ws.cell_id, ws.cell_start, ws.cell_fill,
                                             ws.cell_atoms, pos, ws.cell_pos);
   TESS_HIP_CHECK(hipGetLastError());
   // 4. pairs: count, scan, check, fill
-  TESS_HIP_CHECK(hipMemsetAsync(row_ptr + n, 0, sizeof(int32_t), st));
   // fp32 pre-decision band around (r_cut+skin)^2: bounds the fp32 error of the shifted
   // position (|x + sL| <= 2L), the difference and the fused squares for |d| <= r_cut+skin+2,
   // with a factor 16 to spare (u = 2^-24)
@@ -1273,12 +1400,11 @@ int32_t build_neighbors_impl(int32_t n, const float box[3], float r_cut, float s
                  g, rcs2, lo2, hi2, pos, ws.cell_pos, ws.cell_start, ws.cell_atoms, row_ptr,
                  nullptr));
   TESS_HIP_CHECK(hipGetLastError());
-  TESS_HIP_CHECK(scan_exclusive_i32(row_ptr, (int64_t)n + 1, ws.scan_tmp, st));
-  // misc[0]: longest row; misc[4..5]: 64-bit pair total (the block is 256-byte aligned)
-  unsigned long long* total = reinterpret_cast<unsigned long long*>(ws.misc + 4);
-  k_max_row<<<(unsigned)min(grid(n, 256), kMaxRowBlocks), 256, 0, st>>>(n, row_ptr, ws.misc,
-                                                                         total);
-  TESS_HIP_CHECK(hipGetLastError());
+  // the scan also writes the longest row (misc[0]) and the 64-bit pair total (misc[2..3]):
+  // it adds in 32 bits, so a total beyond the int32 range of row_ptr wraps there, while each
+  // row's count is still the difference of its (wrapped) bounds and the 64-bit sum is exact
+  TESS_HIP_CHECK(scan_exclusive_i32(row_ptr, (int64_t)n + 1, ws.scan_tmp, st, ws.misc));
+  unsigned long long* total = reinterpret_cast<unsigned long long*>(ws.misc + 2);
   int32_t max_row = 0, bits = 0;
   unsigned long long pairs = 0;
   TESS_HIP_CHECK(hipMemcpyAsync(&max_row, ws.misc, sizeof(int32_t), hipMemcpyDeviceToHost, st));

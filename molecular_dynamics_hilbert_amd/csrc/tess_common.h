@@ -233,13 +233,12 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Exclusive scan of int32 counts in place, any length: tile sums, a scan of the tile sums,
-// then the tiles; `partial` holds ceil(n/4096) entries. Host wrappers in nbr.hip.
-hipError_t scan_exclusive_i32(int32_t* data, int64_t n, int32_t* partial, hipStream_t s);
-// Two arrays of length n scanned by the same three launches; `partial` holds 2 x ceil(n/4096)
-// entries.
-hipError_t scan_exclusive_i32_pair(int32_t* a, int32_t* b, int64_t n, int32_t* partial,
-                                   hipStream_t s);
+// Exclusive scan of int32 counts in place, any length (one launch up to 65,536 entries, else
+// two, or three beyond 2^24); `partial` holds ceil(n/4096) entries. With `stats` (zeroed by the
+// caller when n > 65,536) the launches also write the largest count to stats[0] and the
+// 64-bit total of the counts to stats[2..3] (8-byte aligned). Host wrapper in nbr.hip.
+hipError_t scan_exclusive_i32(int32_t* data, int64_t n, int32_t* partial, hipStream_t s,
+                              int32_t* stats = nullptr);
 
 }  // namespace tess
 
@@ -288,7 +287,7 @@ struct NbrWS {
   float4* cell_pos;     // [n] their positions (and index bits), grouped by cell
   int32_t* cell_id;     // [n]
   int32_t* scan_tmp;    // [scan partial sums]
-  int32_t* misc;        // [16]: [0] max row length, [1] pair count low word
+  int32_t* misc;        // [16]: [0] max row length, [2..3] 64-bit pair count
   int64_t ncell_cap;
 };
 NbrWS carve_nbr(Carver& c, int32_t n);
