@@ -374,25 +374,36 @@ __device__ int atom_row_global(int32_t i, int lane, const CellGrid& g, double rc
 // block's LDS (with the stencil tables) within 32 KiB, so five blocks fit a CU.
 constexpr int kCellCap = 2016;
 
-// Sorts the block's staged candidates by their entry (j << 5 | shift code) and leaves them
-// in that order in spos[0, total). On entry, thread t holds candidate q = t + 256 r in sp[r]
-// (r < kPer; position in .xyz, the entry's bits in .w) and spos is free; total <= 256 * EPT.
-// The keys (entry << 32 | q) are sorted by an ascending bitonic network in registers: position
-// a = t*EPT + r lives in thread t, so a compare-exchange at distance jj < EPT stays in the
-// thread, one with EPT <= jj < 64*EPT crosses lanes of a wave (DPP moves, or a lane shuffle
-// for lanes 16 and 32 apart), and only the three stages with partners in another wave
-// exchange through LDS (spos as scratch). The candidates are then written to spos unsorted
-// and gathered into sorted order.
+// Image-shifted fp32 position of a candidate with shift code `code` (one rounding per axis);
+// the staging and the sorted fill compute it the same way from the same stored coordinates.
+__device__ __forceinline__ float3 shifted_pos(float x, float y, float z, int code,
+                                              const CellGrid& g) {
+  return make_float3(x + (float)(code / 9 - 1) * (float)g.L[0],
+                     y + (float)((code / 3) % 3 - 1) * (float)g.L[1],
+                     z + (float)(code % 3 - 1) * (float)g.L[2]);
+}
+
+// Sorts the block's staged candidates by their entry (j << 5 | shift code; distinct within a
+// stencil) and leaves them in that order in spos[0, total), with their image-shifted
+// positions. On entry, thread t holds candidate q = t + 256 r in sp[r] (r < kPer; the entry's
+// bits in .w) and spos is free; total <= 256 * EPT. The 32-bit entries are sorted by an
+// ascending bitonic network in registers: position a = t*EPT + r lives in thread t, so a
+// compare-exchange at distance jj < EPT stays in the thread, one with EPT <= jj < 64*EPT
+// crosses lanes of a wave (DPP moves, or a lane shuffle for lanes 16 and 32 apart), and only
+// the three stages with partners in another wave exchange through LDS (spos as scratch).
+// Each sorted entry then reads its atom's stored position again (pos[3j..3j+2], mostly an L2
+// hit: the staging has just read it) and shifts it, so only the 4-byte entries travel
+// through the network.
 template <int J, int EPT>
-__device__ __forceinline__ void bitonic_in_thread(uint64_t (&x)[EPT], int base, int k) {
+__device__ __forceinline__ void bitonic_in_thread(uint32_t (&x)[EPT], int base, int k) {
 #pragma unroll
   for (int r = 0; r < EPT; r++)
     if ((r & J) == 0) {
       const bool up = ((base + r) & k) == 0;
-      const uint64_t a = x[r], b = x[r | J];
-      const bool swap = (a > b) == up;
-      x[r] = swap ? b : a;
-      x[r | J] = swap ? a : b;
+      const uint32_t a = x[r], b = x[r | J];
+      const uint32_t lo = min(a, b), hi = max(a, b);
+      x[r] = up ? lo : hi;
+      x[r | J] = up ? hi : lo;
     }
 }
 
@@ -414,25 +425,20 @@ __device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v, int m) {
   }
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = lane_xor_u32((uint32_t)v, m);
-  const uint32_t hi = lane_xor_u32((uint32_t)(v >> 32), m);
-  return ((uint64_t)hi << 32) | lo;
-}
-
 template <int EPT, int kPer>
 __device__ __forceinline__ void sort_staged(float4* spos, const float4 (&sp)[kPer], int total,
-                                            int t) {
+                                            int t, const float* __restrict__ pos,
+                                            const CellGrid& g) {
   static_assert(EPT <= kPer, "every key slot has a staged candidate slot");
   constexpr int N = 256 * EPT;
   const int base = t * EPT;
-  uint64_t x[EPT];
+  uint32_t x[EPT];
 #pragma unroll
   for (int r = 0; r < EPT; r++) {
     const int q = t + 256 * r;
-    x[r] = q < total ? ((uint64_t)__float_as_uint(sp[r].w) << 32) | (uint32_t)q : ~0ull;
+    x[r] = q < total ? __float_as_uint(sp[r].w) : 0xFFFFFFFFu;  // above every entry
   }
-  uint64_t* xbuf = reinterpret_cast<uint64_t*>(spos);  // N * 8 bytes <= half of spos
+  uint32_t* xbuf = reinterpret_cast<uint32_t*>(spos);  // N * 4 bytes <= spos
   // fully unrolled: every stage's distances are compile-time constants
 #pragma unroll
   for (int k = 2; k <= N; k <<= 1) {
@@ -446,18 +452,18 @@ __device__ __forceinline__ void sort_staged(float4* spos, const float4 (&sp)[kPe
 #pragma unroll
         for (int r = 0; r < EPT; r++) {
           const int a = base + r;
-          const uint64_t y = xbuf[a ^ jj];
+          const uint32_t y = xbuf[a ^ jj];
           const bool keep_min = ((a & jj) == 0) == ((a & k) == 0);
-          x[r] = keep_min ? (x[r] < y ? x[r] : y) : (x[r] < y ? y : x[r]);
+          x[r] = keep_min ? min(x[r], y) : max(x[r], y);
         }
       } else if (jj >= EPT) {
         const int m = jj / EPT;  // lane distance (a power of two below 64)
 #pragma unroll
         for (int r = 0; r < EPT; r++) {
           const int a = base + r;
-          const uint64_t y = shfl_xor_u64(x[r], m);
+          const uint32_t y = lane_xor_u32(x[r], m);
           const bool keep_min = ((a & jj) == 0) == ((a & k) == 0);
-          x[r] = keep_min ? (x[r] < y ? x[r] : y) : (x[r] < y ? y : x[r]);
+          x[r] = keep_min ? min(x[r], y) : max(x[r], y);
         }
       } else if (jj == 1) {
         bitonic_in_thread<1, EPT>(x, base, k);
@@ -468,25 +474,23 @@ __device__ __forceinline__ void sort_staged(float4* spos, const float4 (&sp)[kPe
       }
     }
   }
-  __syncthreads();  // the last exchange reads are done
+  // positions of the sorted entries (requested together, then written once the last
+  // exchange reads are done); positions in [total, kCellCap) take filler that the pair loop
+  // never reads
+  float4 v[EPT];
 #pragma unroll
-  for (int r = 0; r < kPer; r++) {
-    const int q = t + 256 * r;
-    if (q < total) spos[q] = sp[r];
+  for (int r = 0; r < EPT; r++) {
+    const uint32_t e = base + r < total ? x[r] : 0u;
+    const int32_t j = (int32_t)(e >> 5);
+    v[r] = make_float4(pos[3 * j], pos[3 * j + 1], pos[3 * j + 2], __uint_as_float(e));
   }
   __syncthreads();
-  // (a native 4-vector keeps the gathered values in registers)
-  typedef float f32x4 __attribute__((ext_vector_type(4)));
-  f32x4* sv4 = reinterpret_cast<f32x4*>(spos);
-  f32x4 v[EPT];
-#pragma unroll
-  for (int r = 0; r < EPT; r++)  // (the clamp only guards the LDS index)
-    v[r] = sv4[base + r < total ? min((uint32_t)x[r], (uint32_t)(total - 1)) : 0u];
-  __syncthreads();
-  // positions in [total, kCellCap) take filler that the pair loop never reads
 #pragma unroll
   for (int r = 0; r < EPT; r++)
-    if (base + r < kCellCap) sv4[base + r] = v[r];
+    if (base + r < kCellCap) {
+      const float3 ps = shifted_pos(v[r].x, v[r].y, v[r].z, (int)(x[r] & 31u), g);
+      spos[base + r] = make_float4(ps.x, ps.y, ps.z, v[r].w);
+    }
 }
 
 // Pair search with LDS-staged cell stencils: one 256-thread block per cell (the second level
@@ -584,17 +588,17 @@ __global__ void __launch_bounds__(256) k_cell_pairs(CellGrid g, double rcs2, flo
       const float4 p = sp[r];
       const int code = vcode[sv[r]];
       const uint32_t entry = ((uint32_t)__float_as_int(p.w) << 5) | (uint32_t)code;
-      // image-shifted position in fp32 (one rounding per axis)
-      const float xs = p.x + (float)(code / 9 - 1) * (float)g.L[0];
-      const float ys = p.y + (float)((code / 3) % 3 - 1) * (float)g.L[1];
-      const float zs = p.z + (float)(code % 3 - 1) * (float)g.L[2];
-      sp[r] = make_float4(xs, ys, zs, __uint_as_float(entry));
-      if (!FILL) spos[q] = sp[r];
+      if (FILL) {  // the sort shifts the positions after sorting the entries
+        sp[r].w = __uint_as_float(entry);
+      } else {
+        const float3 ps = shifted_pos(p.x, p.y, p.z, code, g);
+        spos[q] = make_float4(ps.x, ps.y, ps.z, __uint_as_float(entry));
+      }
     }
   }
   if (FILL) {  // the entries of one stencil are distinct; block-uniform choice
-    if (total <= 1024) sort_staged<4>(spos, sp, total, t);
-    else sort_staged<8>(spos, sp, total, t);
+    if (total <= 1024) sort_staged<4>(spos, sp, total, t, pos, g);
+    else sort_staged<8>(spos, sp, total, t, pos, g);
   }
   __syncthreads();
   // Each wave takes kCellAtoms of the cell's atoms at a time: every staged candidate read
