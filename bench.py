@@ -351,15 +351,15 @@ def large_system(name: str = "salt500k") -> dict:
 
 def _traffic(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
-    (profiles/traffic_<kernel>_<workload>.json), or None when there is none or the kernel
-    sources changed since the counters were taken."""
+    (profiles/traffic_<kernel>_<workload>.json), or None when there is none or the sources
+    it names (all of csrc/ if it names none) changed since the counters were taken."""
     from molecular_dynamics_hilbert_amd import profiling
     path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel, workload))
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("source_digest") != profiling.source_digest():
+    if t.get("source_digest") != profiling.source_digest(t.get("source_files")):
         return None
     return round(t["bytes_per_launch"], 1)
 

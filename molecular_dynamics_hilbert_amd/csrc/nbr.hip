@@ -527,7 +527,9 @@ __global__ void __launch_bounds__(256) k_cell_pairs(CellGrid g, double rcs2, flo
   // counts scalar)
   const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
   const int c = (int)xcd_block(blockIdx.x, gridDim.x);
-  const int32_t a0 = cell_start[c], a1 = cell_start[c + 1];
+  // the cell's atom range, wave-uniform (scalar registers, scalar per-atom conditions)
+  const int32_t a0 = __builtin_amdgcn_readfirstlane(cell_start[c]);
+  const int32_t a1 = __builtin_amdgcn_readfirstlane(cell_start[c + 1]);
   if (a0 == a1) return;  // empty cell (the whole block returns)
   if (t < 64) {
     int32_t sz = 0;
@@ -602,9 +604,13 @@ __global__ void __launch_bounds__(256) k_cell_pairs(CellGrid g, double rcs2, flo
   }
   __syncthreads();
   // Each wave takes kCellAtoms of the cell's atoms at a time: every staged candidate read
-  // from LDS is tested against all of them.
+  // from LDS is tested against all of them. An atom meets itself once among the staged
+  // candidates (its own cell with shift code 13, at fp32 distance exactly 0, so always
+  // near): the count pass subtracts it once per atom, the fill pass drops the lane whose
+  // entry is the atom's own (i << 5 | 13).
   for (int32_t k0 = a0 + wv * kCellAtoms; k0 < a1; k0 += 4 * kCellAtoms) {
     int32_t ia[kCellAtoms];
+    uint32_t eself[kCellAtoms];
     float xf[kCellAtoms][3];
     int count[kCellAtoms];
     int64_t o[kCellAtoms];
@@ -613,28 +619,22 @@ __global__ void __launch_bounds__(256) k_cell_pairs(CellGrid g, double rcs2, flo
       // atoms past the cell's end repeat its first atom (wave-uniform; never written)
       const int32_t i = cell_atoms[k0 + u < a1 ? k0 + u : a0];
       ia[u] = i;
+      eself[u] = ((uint32_t)i << 5) | 13u;
       xf[u][0] = pos[3 * i];
       xf[u][1] = pos[3 * i + 1];
       xf[u][2] = pos[3 * i + 2];
-      count[u] = 0;
+      count[u] = FILL ? 0 : -1;
       o[u] = FILL ? (int64_t)row_ptr[i] : 0;
     }
-    float4 pn = spos[lane < total ? lane : 0];  // the first batch's candidate
-    for (int q0 = 0; q0 < total; q0 += 64) {
+    // one batch of 64 staged candidates (p: this lane's); the next batch's candidate is read
+    // by the caller before this one is tested
+    auto batch = [&](int q0, const float4 p) {
       const int q = q0 + lane;
       const bool ok = q < total;
-      const float4 p = pn;
-      if (q0 + 64 < total) {  // wave-uniform: request the next batch's candidate now
-        const int qn = q + 64;
-        pn = spos[qn < total ? qn : 0];
-      }
       const uint32_t entry = __float_as_uint(p.w);
-      const int32_t j = (int32_t)(entry >> 5);
-      const int code = (int)(entry & 31u);
-      // the decisions as wave masks (one compare each): near in fp32 and the atom itself (same
-      // index, zero shift); the rounding band is checked once per batch
+      // the decisions as wave masks (one compare each): near in fp32, and within the rounding
+      // band of (r_cut+skin)^2 (checked once per batch)
       const uint64_t m_ok = __ballot(ok);
-      const uint64_t m_self = __ballot(code == 13);
       float d2v[kCellAtoms];
       uint64_t m_near[kCellAtoms];
       uint64_t m_band = 0;
@@ -643,11 +643,13 @@ __global__ void __launch_bounds__(256) k_cell_pairs(CellGrid g, double rcs2, flo
         const float dx = p.x - xf[u][0], dy = p.y - xf[u][1], dz = p.z - xf[u][2];
         d2v[u] = __builtin_fmaf(dz, dz, __builtin_fmaf(dy, dy, dx * dx));
         m_near[u] = __ballot(d2v[u] < lo2);
-        m_band |= __ballot(d2v[u] >= lo2) & __ballot(d2v[u] <= hi2);
+        m_band |= __ballot(d2v[u] <= hi2) & ~m_near[u];
       }
       // inside the band the fp64 test decides; one branch per batch keeps its fp64 shift
       // terms (shared by the atoms) out of the common path
       if ((m_band & m_ok) != 0ull) {  // wave-uniform, rare
+        const int32_t j = (int32_t)(entry >> 5);
+        const int code = (int)(entry & 31u);
 #pragma unroll
         for (int u = 0; u < kCellAtoms; u++) {
           if (k0 + u >= a1) break;  // wave-uniform
@@ -661,21 +663,36 @@ __global__ void __launch_bounds__(256) k_cell_pairs(CellGrid g, double rcs2, flo
 #pragma unroll
       for (int u = 0; u < kCellAtoms; u++) {
         // atoms past the cell's end (repeats of its first atom) are never written or counted
-        const uint64_t m = k0 + u < a1 ? m_near[u] & m_ok & ~(m_self & __ballot(j == ia[u]))
-                                       : 0ull;
-        if (FILL && ((m >> lane) & 1ull)) {
-          const int slot = count[u] + (int)__builtin_amdgcn_mbcnt_hi(
-                                          (uint32_t)(m >> 32),
-                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-          if (slot < kMaxRow) col_shift[o[u] + slot] = (uint32_t)j | ((uint32_t)code << 27);
+        uint64_t m = k0 + u < a1 ? m_near[u] & m_ok : 0ull;
+        if (FILL) {
+          m &= ~__ballot(entry == eself[u]);
+          if ((m >> lane) & 1ull) {
+            const int slot = count[u] + (int)__builtin_amdgcn_mbcnt_hi(
+                                            (uint32_t)(m >> 32),
+                                            __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (slot < kMaxRow)
+              col_shift[o[u] + slot] = (entry >> 5) | ((entry & 31u) << 27);
+          }
         }
         count[u] += __popcll(m);
+      }
+    };
+    // batches in pairs, so the prefetched candidate alternates between two registers
+    float4 pa = spos[lane < total ? lane : 0];
+    for (int q0 = 0; q0 < total; q0 += 128) {
+      const int qb = q0 + 64 + lane;
+      const float4 pb = spos[qb < total ? qb : 0];  // (past the end: a filler, masked)
+      batch(q0, pa);
+      if (q0 + 64 < total) {  // wave-uniform
+        const int qa = q0 + 128 + lane;
+        pa = spos[qa < total ? qa : 0];
+        batch(q0 + 64, pb);
       }
     }
     if (!FILL && lane == 0) {
 #pragma unroll
-      for (int u = 0; u < kCellAtoms; u++)
-        if (k0 + u < a1) row_ptr[ia[u]] = count[u];
+      for (int u = 0; u < kCellAtoms; u++)  // (an atom at a non-finite position meets nothing)
+        if (k0 + u < a1) row_ptr[ia[u]] = max(count[u], 0);
     }
   }
 }

@@ -71,9 +71,17 @@ def traffic(fetch_csv: str, write_csv: str, kernel: str, copy_mib: int) -> dict:
     return res
 
 
-def source_digest() -> str:
+# Sources of the energy/forces kernels (the edge kernels and GEMMs whose counters the traffic
+# summaries hold): a change to the rebuild or API sources leaves those counters valid.
+EF_SOURCES = ("model.hip", "tess_common.h")
+NBR_SOURCES = ("nbr.hip", "tess_common.h")  # the rebuild kernels
+
+
+def source_digest(files=None) -> str:
+    """sha256 over csrc/ (or over the named files of csrc/, in sorted order)."""
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(HERE, "csrc"))):
+    names = sorted(files) if files else sorted(os.listdir(os.path.join(HERE, "csrc")))
+    for f in names:
         with open(os.path.join(HERE, "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -85,7 +93,8 @@ def write_summaries(stats_csv: str, fetch_csv: str, write_csv: str, kernel_key: 
     """profiles/<kernel>_<workload>.md (kernel statistics + counter traffic) and
     profiles/traffic_<kernel>_<workload>.json (bytes per launch, source digest)."""
     t = traffic(fetch_csv, write_csv, kernel_name, copy_mib)
-    t["source_digest"] = source_digest()
+    t["source_files"] = list(EF_SOURCES)
+    t["source_digest"] = source_digest(EF_SOURCES)
     t["workload"] = workload
     with open(os.path.join(out_dir, "traffic_%s_%s.json" % (kernel_key, workload)), "w") as f:
         json.dump(t, f, indent=1)
@@ -106,15 +115,15 @@ def write_summaries(stats_csv: str, fetch_csv: str, write_csv: str, kernel_key: 
     tot = sum(float(r["TotalDurationNs"]) for r in rows)
     md += ["", "All launches matching `%s` (every layer): %d calls, average %.1f us." % (
         kernel_name, calls, tot / max(calls, 1) / 1e3)]
-    md += ["", "Launches counted: %d. Source digest: %s." % (t["fetch"]["launches"],
-                                                             t["source_digest"])]
+    md += ["", "Launches counted: %d. Source digest (%s): %s." % (
+        t["fetch"]["launches"], ", ".join(t["source_files"]), t["source_digest"])]
     with open(os.path.join(out_dir, "%s_%s.md" % (kernel_key, workload)), "w") as f:
         f.write("\n".join(md) + "\n")
 
 
-REBUILD_KERNELS = ("k_wrap_key", "k_radix_hist", "k_radix_scatter", "k_scan_partial", "k_scan_sums",
-                   "k_scan_final", "k_permute", "k_cell_count", "k_cell_fill", "k_cell_pairs",
-                   "k_max_row", "k_rev", "k_rev_grouped")
+REBUILD_KERNELS = ("k_wrap_key", "k_radix_hist", "k_radix_scatter", "k_scan_one", "k_scan_partial",
+                   "k_scan_sums", "k_scan_final", "k_permute", "k_cell_fill", "k_cell_pairs",
+                   "k_rev", "k_rev_grouped")
 
 
 def rebuild_md(stats_csv: str, workload: str, command: str, calls_per_rebuild: dict = None) -> str:
@@ -129,7 +138,7 @@ def rebuild_md(stats_csv: str, workload: str, command: str, calls_per_rebuild: d
         out.append("| %s | %s | %.1f | %.1f | %.1f |" % (
             short_name(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3,
             float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
-    out += ["", "Source digest: %s." % source_digest()]
+    out += ["", "Source digest (%s): %s." % (", ".join(NBR_SOURCES), source_digest(NBR_SOURCES))]
     return "\n".join(out) + "\n"
 
 
@@ -157,7 +166,8 @@ def main(argv):
                         cmds, os.path.join(os.path.dirname(HERE), "profiles"))
     elif argv[0] == "traffic":
         t = traffic(argv[1], argv[2], argv[3], int(argv[4]))
-        t["source_digest"] = source_digest()
+        t["source_files"] = list(EF_SOURCES)
+        t["source_digest"] = source_digest(EF_SOURCES)
         with open(argv[5], "w") as f:
             json.dump(t, f, indent=1)
         print(json.dumps(t, indent=1))
