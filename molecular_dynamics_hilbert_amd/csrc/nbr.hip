@@ -1090,14 +1090,12 @@ __global__ void __launch_bounds__(256) k_rev_grouped(int32_t n,
 
 // ---- scan -----------------------------------------------------------------------------
 // Exclusive scan of int32 counts in place. Up to kScanOneMax entries one block of 1024
-// threads does it in one launch (all values loaded first, then four 16,384-entry chunks scanned
-// with a running carry); longer arrays take two launches (tile sums, then each tile adds the
-// sum of the tile sums before it, which it reduces itself), and beyond kScanCarryTiles tiles a
-// third launch scans the tile sums. Optionally the same launches report the largest count and
+// threads does it in one launch (16 entries per thread); longer arrays take two launches
+// (tile sums, then each tile adds the sum of the tile sums before it, which it reduces
+// itself), and beyond kScanCarryTiles tiles a third launch scans the tile sums. Optionally the same launches report the largest count and
 // the 64-bit total of the counts (stats[0], stats[2..3]).
 constexpr int kScanTile = 4096;          // 256 threads x 16 (multi-block tiles)
-constexpr int kScanOneChunk = 16384;     // 1024 threads x 16
-constexpr int kScanOneMax = 4 * kScanOneChunk;
+constexpr int kScanOneMax = 16384;       // 1024 threads x 16
 constexpr int kScanCarryTiles = 4096;
 
 __device__ __forceinline__ int32_t wave_inclusive_scan(int32_t v) {
@@ -1196,37 +1194,25 @@ __device__ __forceinline__ void store16(int32_t* __restrict__ d, int64_t base, i
 __global__ void __launch_bounds__(1024) k_scan_one(int32_t* __restrict__ d, int32_t n,
                                                    int32_t* __restrict__ stats) {
   __shared__ int32_t sh[16];
-  constexpr int kChunks = kScanOneMax / kScanOneChunk;
-  int32_t v[kChunks][16];
-  const int nch = (n + kScanOneChunk - 1) / kScanOneChunk;
-#pragma unroll
-  for (int c = 0; c < kChunks; c++)
-    if (c < nch) load16(d, (int64_t)c * kScanOneChunk + threadIdx.x * 16, n, v[c]);
-  int32_t mx = 0;
+  int32_t v[16];
+  load16(d, threadIdx.x * 16, n, v);
+  int32_t s = 0, mx = 0;
   unsigned long long sm = 0;
-  int32_t carry = 0;
 #pragma unroll
-  for (int c = 0; c < kChunks; c++) {
-    if (c < nch) {
-      int32_t s = 0;
-#pragma unroll
-      for (int k = 0; k < 16; k++) {
-        s += v[c][k];
-        mx = max(mx, v[c][k]);
-        sm += (unsigned long long)(uint32_t)v[c][k];
-      }
-      int32_t tot;
-      int32_t run = block_exclusive_scan<16>(s, sh, &tot) + carry;
-      carry += tot;
-#pragma unroll
-      for (int k = 0; k < 16; k++) {
-        const int32_t x = v[c][k];
-        v[c][k] = run;
-        run += x;
-      }
-      store16(d, (int64_t)c * kScanOneChunk + threadIdx.x * 16, n, v[c]);
-    }
+  for (int k = 0; k < 16; k++) {
+    s += v[k];
+    mx = max(mx, v[k]);
+    sm += (unsigned long long)(uint32_t)v[k];
   }
+  int32_t tot;
+  int32_t run = block_exclusive_scan<16>(s, sh, &tot);
+#pragma unroll
+  for (int k = 0; k < 16; k++) {
+    const int32_t y = v[k];
+    v[k] = run;
+    run += y;
+  }
+  store16(d, threadIdx.x * 16, n, v);
   if (stats) block_stats<16>(mx, sm, stats, false);
 }
 

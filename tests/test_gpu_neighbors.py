@@ -109,6 +109,17 @@ def test_rebuild_tiny_and_ragged_boxes(T, oracle_mod, seed, n, L):
     _check_against_oracle(oracle_mod, box, pos, sp, g)
 
 
+# Row-offset scan lengths n + 1 = 16,384 (the largest one-launch scan) and 16,385 (the
+# two-launch form, a last tile of one entry), at water density
+@pytest.mark.parametrize("n", [16383, 16384])
+def test_rebuild_at_the_scan_size_boundary(T, oracle_mod, n):
+    L = float((n / 0.1) ** (1.0 / 3.0))
+    box, pos, sp = W.random_small_box(n, L, 20 + n % 7)
+    g = _gpu_rebuild(T, box, pos, sp, cap=200 * n)
+    print("n", n, "pairs", g["n_edges"], flush=True)
+    _check_against_oracle(oracle_mod, box, pos, sp, g)
+
+
 def test_rebuild_repeatable_bit_for_bit(T):
     wl = W.load("salt60k")
     a = _gpu_rebuild(T, wl.box, wl.pos, wl.species)
