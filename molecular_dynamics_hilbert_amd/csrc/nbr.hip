@@ -942,7 +942,9 @@ __global__ void __launch_bounds__(256) k_rev_grouped(int32_t n,
   __shared__ uint32_t tkey[kRevSlots];
   __shared__ uint32_t tmask[kRevSlots];
   __shared__ int32_t tbase[kRevSlots];
-  __shared__ __align__(16) uint32_t sc[kRevEntries];  // the group's targets j, entry order
+  // the group's targets j in entry order; after the table pass, each entry's table slot and
+  // group row (slot | row << 16), so the last pass reads them without probing the table
+  __shared__ __align__(16) uint32_t sc[kRevEntries];
   __shared__ __align__(16) uint8_t srow[kRevEntries];  // their rows, offsets from the first
   __shared__ int16_t slist[kRevSlots];                 // occupied table slots
   __shared__ int32_t srp[kRevGroup + 1];
@@ -1007,7 +1009,9 @@ __global__ void __launch_bounds__(256) k_rev_grouped(int32_t n,
         sflag = 1;
         break;
       }
-      atomicOr(&tmask[h], 1u << srow[k]);
+      const uint32_t r = srow[k];
+      atomicOr(&tmask[h], 1u << r);
+      sc[k] = h | (r << 16);  // the entry's slot and row (its target is no longer needed)
     }
     __syncthreads();
     const bool over = sflag != 0;
@@ -1062,17 +1066,15 @@ __global__ void __launch_bounds__(256) k_rev_grouped(int32_t n,
     __syncthreads();
     // 3. every entry's reverse slot, four consecutive entries per thread and store
     for (int k = 4 * t; k < ne; k += 4 * 256) {
-      const uint4 j4 = *reinterpret_cast<const uint4*>(&sc[k]);
-      const uint32_t r4 = *reinterpret_cast<const uint32_t*>(&srow[k]);
-      const uint32_t jj[4] = {j4.x, j4.y, j4.z, j4.w};
+      const uint4 i4 = *reinterpret_cast<const uint4*>(&sc[k]);  // slot | row << 16
+      const uint32_t info[4] = {i4.x, i4.y, i4.z, i4.w};
       int32_t v[4];
 #pragma unroll
       for (int u = 0; u < 4; u++) {
         v[u] = 0;
         if (k + u < ne) {
-          uint32_t h = rev_hash(jj[u]);
-          while (tkey[h] != jj[u]) h = (h + 1) & (kRevSlots - 1);  // present after pass 1
-          const uint32_t below = (1u << ((r4 >> (8 * u)) & 0xFFu)) - 1u;
+          const uint32_t h = info[u] & 0xFFFFu;
+          const uint32_t below = (1u << (info[u] >> 16)) - 1u;
           v[u] = tbase[h] + __popc(tmask[h] & below);
         }
       }
