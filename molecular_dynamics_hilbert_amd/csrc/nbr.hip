@@ -15,6 +15,8 @@
 // off.
 #include "tess_common.h"
 
+#include <cstring>
+
 #pragma clang fp contract(off)
 
 namespace tess {
@@ -1194,7 +1196,8 @@ __device__ __forceinline__ void store16(int32_t* __restrict__ d, int64_t base, i
 }
 
 __global__ void __launch_bounds__(1024) k_scan_one(int32_t* __restrict__ d, int32_t n,
-                                                   int32_t* __restrict__ stats) {
+                                                   int32_t* __restrict__ stats,
+                                                   const int32_t* __restrict__ extra) {
   __shared__ int32_t sh[16];
   int32_t v[16];
   load16(d, threadIdx.x * 16, n, v);
@@ -1215,12 +1218,16 @@ __global__ void __launch_bounds__(1024) k_scan_one(int32_t* __restrict__ d, int3
     run += y;
   }
   store16(d, threadIdx.x * 16, n, v);
-  if (stats) block_stats<16>(mx, sm, stats, false);
+  if (stats) {
+    block_stats<16>(mx, sm, stats, false);
+    if (extra && threadIdx.x == 0) stats[1] = *extra;
+  }
 }
 
 __global__ void __launch_bounds__(256) k_scan_partial(const int32_t* __restrict__ d, int64_t n,
                                                       int32_t* __restrict__ sums,
-                                                      int32_t* __restrict__ stats) {
+                                                      int32_t* __restrict__ stats,
+                                                      const int32_t* __restrict__ extra) {
   int32_t v[16];
   load16(d, (int64_t)blockIdx.x * kScanTile + threadIdx.x * 16, n, v);
   int32_t s = 0, mx = 0;
@@ -1237,7 +1244,10 @@ __global__ void __launch_bounds__(256) k_scan_partial(const int32_t* __restrict_
   if ((threadIdx.x & 63) == 63) sh[threadIdx.x >> 6] = s;
   __syncthreads();
   if (threadIdx.x == 0) sums[blockIdx.x] = sh[0] + sh[1] + sh[2] + sh[3];
-  if (stats) block_stats<4>(mx, sm, stats, true);
+  if (stats) {
+    block_stats<4>(mx, sm, stats, true);
+    if (extra && blockIdx.x == 0 && threadIdx.x == 0) stats[1] = *extra;
+  }
 }
 
 __global__ void __launch_bounds__(256) k_scan_sums(int32_t* __restrict__ sums, int32_t nb) {
@@ -1291,14 +1301,14 @@ inline int32_t grid(int64_t n, int b) { return (int32_t)((n + b - 1) / b); }
 }  // namespace
 
 hipError_t scan_exclusive_i32(int32_t* data, int64_t n, int32_t* partial, hipStream_t s,
-                              int32_t* stats) {
+                              int32_t* stats, const int32_t* extra) {
   if (n <= 0) return hipSuccess;
   if (n <= kScanOneMax) {
-    k_scan_one<<<1, 1024, 0, s>>>(data, (int32_t)n, stats);
+    k_scan_one<<<1, 1024, 0, s>>>(data, (int32_t)n, stats, extra);
     return hipGetLastError();
   }
   const int64_t nb = (n + kScanTile - 1) / kScanTile;
-  k_scan_partial<<<(unsigned)nb, 256, 0, s>>>(data, n, partial, stats);
+  k_scan_partial<<<(unsigned)nb, 256, 0, s>>>(data, n, partial, stats, extra);
   if (nb <= kScanCarryTiles) {
     k_scan_final<true><<<(unsigned)nb, 256, 0, s>>>(data, n, partial);
   } else {
@@ -1409,17 +1419,17 @@ int32_t build_neighbors_impl(int32_t n, const float box[3], float r_cut, float s
                  g, rcs2, lo2, hi2, pos, ws.cell_pos, ws.cell_start, ws.cell_atoms, row_ptr,
                  nullptr));
   TESS_HIP_CHECK(hipGetLastError());
-  // the scan also writes the longest row (misc[0]) and the 64-bit pair total (misc[2..3]):
-  // it adds in 32 bits, so a total beyond the int32 range of row_ptr wraps there, while each
-  // row's count is still the difference of its (wrapped) bounds and the 64-bit sum is exact
-  TESS_HIP_CHECK(scan_exclusive_i32(row_ptr, (int64_t)n + 1, ws.scan_tmp, st, ws.misc));
-  unsigned long long* total = reinterpret_cast<unsigned long long*>(ws.misc + 2);
-  int32_t max_row = 0, bits = 0;
-  unsigned long long pairs = 0;
-  TESS_HIP_CHECK(hipMemcpyAsync(&max_row, ws.misc, sizeof(int32_t), hipMemcpyDeviceToHost, st));
-  TESS_HIP_CHECK(hipMemcpyAsync(&pairs, total, sizeof(pairs), hipMemcpyDeviceToHost, st));
-  TESS_HIP_CHECK(hipMemcpyAsync(&bits, status, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+  // the scan also writes the longest row (misc[0]), a copy of the status word (misc[1]) and
+  // the 64-bit pair total (misc[2..3]), read back with one copy: it adds in 32 bits, so a total
+  // beyond the int32 range of row_ptr wraps there, while each row's count is still the
+  // difference of its (wrapped) bounds and the 64-bit sum is exact
+  TESS_HIP_CHECK(scan_exclusive_i32(row_ptr, (int64_t)n + 1, ws.scan_tmp, st, ws.misc, status));
+  int32_t rb[4] = {0, 0, 0, 0};
+  TESS_HIP_CHECK(hipMemcpyAsync(rb, ws.misc, sizeof(rb), hipMemcpyDeviceToHost, st));
   TESS_HIP_CHECK(hipStreamSynchronize(st));
+  const int32_t max_row = rb[0], bits = rb[1];
+  unsigned long long pairs = 0;
+  std::memcpy(&pairs, rb + 2, sizeof(pairs));
   *n_edges = (int64_t)pairs;
   if (bits) {  // reported here and cleared (a pending bit may come from an earlier pass)
     TESS_HIP_CHECK(hipMemsetAsync(status, 0, sizeof(int32_t), st));

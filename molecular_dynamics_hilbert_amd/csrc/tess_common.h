@@ -236,9 +236,11 @@ __device__ __forceinline__ float wave_max(float v) {
 // Exclusive scan of int32 counts in place, any length (one launch up to 16,384 entries, else
 // two, or three beyond 2^24); `partial` holds ceil(n/4096) entries. With `stats` (zeroed by the
 // caller when n > 16,384) the launches also write the largest count to stats[0] and the
-// 64-bit total of the counts to stats[2..3] (8-byte aligned). Host wrapper in nbr.hip.
+// 64-bit total of the counts to stats[2..3] (8-byte aligned), and with `extra` a copy of
+// *extra to stats[1] (read after the work before the scan on the stream). Host wrapper in
+// nbr.hip.
 hipError_t scan_exclusive_i32(int32_t* data, int64_t n, int32_t* partial, hipStream_t s,
-                              int32_t* stats = nullptr);
+                              int32_t* stats = nullptr, const int32_t* extra = nullptr);
 
 }  // namespace tess
 
