@@ -208,7 +208,7 @@ struct Layout {
   // tess_md_steps scratch
   float* ref_pos;
   int32_t* perm;
-  int32_t* flag;
+  int32_t* flag;    // skin flag: the word after the status word (both read with one copy)
   double* epot;
   double* ke_part;      // kinetic-energy sums, one per block of 256 atoms
   uint32_t* rmin2_bits;  // shortest squared pair distance of the step (float bits)
@@ -225,7 +225,7 @@ Layout layout(char* base, const tess_model_desc* md, int32_t n, int64_t cap) {
   int64_t nn = n > 0 ? n : 1;
   L.ref_pos = cv.take<float>(3 * nn);
   L.perm = cv.take<int32_t>(nn);
-  L.flag = cv.take<int32_t>(64);
+  L.flag = L.status + 1;
   L.epot = cv.take<double>(4);
   L.ke_part = cv.take<double>(gridn(nn, 256));
   L.rmin2_bits = cv.take<uint32_t>(64);
@@ -368,10 +368,10 @@ int32_t md_interval_graph(const tess_model_desc* d, const float* weights, int32_
 // Reads the status word and the skin flag (one synchronisation); returns the status error,
 // else TESS_ERR_SKIN if the flag is set, else TESS_OK. A reported status is cleared.
 int32_t md_sync_check(const Layout& L, hipStream_t st) {
-  int32_t f = 0, bits = 0;
-  TESS_HIP_CHECK(hipMemcpyAsync(&f, L.flag, sizeof(int32_t), hipMemcpyDeviceToHost, st));
-  TESS_HIP_CHECK(hipMemcpyAsync(&bits, L.status, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+  int32_t sf[2] = {0, 0};  // status word, skin flag
+  TESS_HIP_CHECK(hipMemcpyAsync(sf, L.status, sizeof(sf), hipMemcpyDeviceToHost, st));
   TESS_HIP_CHECK(hipStreamSynchronize(st));
+  const int32_t bits = sf[0], f = sf[1];
   if (bits) {
     TESS_HIP_CHECK(hipMemsetAsync(L.status, 0, sizeof(int32_t), st));
     return status_error(bits);
