@@ -942,8 +942,8 @@ __global__ void __launch_bounds__(256) k_rev_grouped(int32_t n,
                                                      const uint32_t* __restrict__ col,
                                                      int32_t* __restrict__ rev) {
   __shared__ uint32_t tkey[kRevSlots];
-  __shared__ uint32_t tmask[kRevSlots];
-  __shared__ int32_t tbase[kRevSlots];
+  // per slot: (search result, mask of the group rows holding the target), read together
+  __shared__ int2 tbm[kRevSlots];
   // the group's targets j in entry order; after the table pass, each entry's table slot and
   // group row (slot | row << 16), so the last pass reads them without probing the table
   __shared__ __align__(16) uint32_t sc[kRevEntries];
@@ -987,7 +987,7 @@ __global__ void __launch_bounds__(256) k_rev_grouped(int32_t n,
         srow[k] = (uint8_t)r;
     for (int k = t; k < kRevSlots; k += 256) {
       tkey[k] = kRevEmpty;
-      tmask[k] = 0u;
+      tbm[k].y = 0;
     }
     if (t == 0) sflag = 0;
     __syncthreads();
@@ -1012,7 +1012,7 @@ __global__ void __launch_bounds__(256) k_rev_grouped(int32_t n,
         break;
       }
       const uint32_t r = srow[k];
-      atomicOr(&tmask[h], 1u << r);
+      atomicOr(reinterpret_cast<uint32_t*>(&tbm[h].y), 1u << r);
       sc[k] = h | (r << 16);  // the entry's slot and row (its target is no longer needed)
     }
     __syncthreads();
@@ -1063,7 +1063,7 @@ __global__ void __launch_bounds__(256) k_rev_grouped(int32_t n,
       lower_bound_runs<2>(col, act, rs, re, (uint32_t)ga << 5, out);
 #pragma unroll
       for (int s2 = 0; s2 < 2; s2++)
-        if (act[s2]) tbase[slot[s2]] = out[s2];
+        if (act[s2]) tbm[slot[s2]].x = out[s2];
     }
     __syncthreads();
     // 3. every entry's reverse slot, four consecutive entries per thread and store
@@ -1077,7 +1077,8 @@ __global__ void __launch_bounds__(256) k_rev_grouped(int32_t n,
         if (k + u < ne) {
           const uint32_t h = info[u] & 0xFFFFu;
           const uint32_t below = (1u << (info[u] >> 16)) - 1u;
-          v[u] = tbase[h] + __popc(tmask[h] & below);
+          const int2 bm = tbm[h];
+          v[u] = bm.x + __popc((uint32_t)bm.y & below);
         }
       }
       if (k + 4 <= ne) {
