@@ -540,7 +540,10 @@ __global__ void k_radial_verdict(int T, const uint32_t* __restrict__ acc,
 // edges, stage one layer's table (98 KB) at a time and interpolate every edge of their range
 // from it. A thread takes 4 consecutive edges at a time, so each output row gets one 16-byte
 // store per thread (a wave writes 1 KB of a row); slots past the active count in the last
-// group get the value at r = 0 (never read).
+// group get the value at r = 0 (never read). Only the paths the layer's edge kernels read are
+// written: in the first layer (input features of degree 0) the paths with sender degree 0
+// (mfirst), in the last layer (only the degree-0 output is used) those with output degree 0
+// (mlast); the other rows of those layers are left as they are and never read.
 constexpr int kRadThreads = 1024;
 constexpr int kRadBlocks = 256;  // one per compute unit (the table fills most of a CU's LDS)
 template <int NP>
@@ -550,7 +553,7 @@ __global__ void __launch_bounds__(kRadThreads) k_edge_radial(
     float* __restrict__ edw, int64_t lstride, int64_t ews, int64_t cap,
     const int32_t* __restrict__ adst, const int32_t* __restrict__ asrc,
     const int32_t* __restrict__ species, const float4* __restrict__ l0tab, int S,
-    float4* __restrict__ es) {
+    float4* __restrict__ es, uint32_t mfirst, uint32_t mlast) {
   __shared__ float4 stab[(kRadKnots + 1) * 6];
   const int64_t n_act = min((int64_t)*arow_n, cap);
   const int64_t ngr = (n_act + 3) / 4;  // groups of 4 edges
@@ -558,6 +561,8 @@ __global__ void __launch_bounds__(kRadThreads) k_edge_radial(
   const int64_t g0 = (int64_t)blockIdx.x * per, g1 = min(g0 + per, ngr);
   const float hk = rc / (float)kRadKnots, ih = (float)kRadKnots / rc;
   for (int t = t_begin; t < t_end; t++) {
+    // paths whose weights the layer's kernels read (first layer: mfirst; last: mlast)
+    const uint32_t pm = t == 0 ? mfirst : (t == t_end - 1 ? mlast : 0xFFFFFFFFu);
     if (t > t_begin) __syncthreads();
     const float4* src = reinterpret_cast<const float4*>(rtab + (int64_t)t * (kRadKnots + 1) * 24);
     for (int k = threadIdx.x; k < (kRadKnots + 1) * 6; k += kRadThreads) stab[k] = src[k];
@@ -594,6 +599,11 @@ __global__ void __launch_bounds__(kRadThreads) k_edge_radial(
       float* pd = edw + t * lstride + a;
 #pragma unroll
       for (int q = 0; q < (NP + 3) / 4; q++) {
+        if (((pm >> (4 * q)) & 15u) == 0u) {  // block-uniform: no path of the group is read
+          pw += 4 * ews;
+          pd += 4 * ews;
+          continue;
+        }
         float wv[4][4], dv[4][4];
 #pragma unroll
         for (int e = 0; e < 4; e++) {
@@ -612,8 +622,10 @@ __global__ void __launch_bounds__(kRadThreads) k_edge_radial(
 #pragma unroll
         for (int c = 0; c < 4; c++) {
           if (4 * q + c < NP) {
-            *reinterpret_cast<float4*>(pw) = make_float4(wv[0][c], wv[1][c], wv[2][c], wv[3][c]);
-            *reinterpret_cast<float4*>(pd) = make_float4(dv[0][c], dv[1][c], dv[2][c], dv[3][c]);
+            if ((pm >> (4 * q + c)) & 1u) {
+              *reinterpret_cast<float4*>(pw) = make_float4(wv[0][c], wv[1][c], wv[2][c], wv[3][c]);
+              *reinterpret_cast<float4*>(pd) = make_float4(dv[0][c], dv[1][c], dv[2][c], dv[3][c]);
+            }
             pw += ews;
             pd += ews;
           }
@@ -767,6 +779,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((TRANS
   // edges per chunk (the adjoint keeps less in registers and runs 4 waves per SIMD)
   constexpr int kChunk = TRANS ? 28 : 32;
   constexpr int DO = OUT0 ? 1 : D;  // output components formed
+  // radial weights that reach the stored coupling entries (the others are neither written
+  // for this layer nor read): column 0 only (first layer) -> sender degree 0; row 0 only
+  // (last layer's forward and adjoint) -> output degree 0
+  constexpr uint32_t WMASK = (L0ONLY && !TRANS) ? paths_from<LMAX>(0)
+                             : (OUT0 || (L0ONLY && TRANS)) ? paths_to<LMAX>(0)
+                                                          : all_paths<LMAX>();
   __shared__ float sA[4][kChunk][DO * DI];
   __shared__ float sAl[4][kChunk][4];
   __shared__ int32_t sJ[4][kChunk];
@@ -834,7 +852,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((TRANS
       pf_geo = ageo[a];
       pf_s4 = es[a];
 #pragma unroll
-      for (int p = 0; p < PP; p++) pf_w[p] = ew[p * ews + a];
+      for (int p = 0; p < PP; p++) pf_w[p] = ((WMASK >> p) & 1u) ? ew[p * ews + a] : 0.0f;
     }
   };
   prefetch(a0);
@@ -872,7 +890,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((TRANS
       sph<LMAX>(sg * geo.x * ir, sg * geo.y * ir, sg * geo.z * ir, Y);
       float w[Dims<LMAX>::P];
 #pragma unroll
-      for (int p = 0; p < Dims<LMAX>::P; p++) w[p] = TRANS ? ew[p * ews + a] : pf_w[p];
+      for (int p = 0; p < Dims<LMAX>::P; p++)
+        w[p] = TRANS ? (((WMASK >> p) & 1u) ? ew[p * ews + a] : 0.0f) : pf_w[p];
       float A[D * D];
       coupling_matrix<LMAX>(w, Y, A);
       // row o of the LDS copy lists the coupling of output component o to every input
@@ -1426,6 +1445,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
   constexpr int dh = C / H;
   constexpr int EPW = 256 / H;               // edges per pass of the block's threads
   constexpr int EPB = kGradPasses * EPW;     // edges per block
+  // radial weights this layer reads: the first layer's input has sender degree 0 only
+  constexpr uint32_t WMASK = L0ONLY ? paths_from<LMAX>(0) : all_paths<LMAX>();
   __shared__ float4 smb[kGradRows * D * C / 4];
   // first layer: h_j = (e_(s_j), 0, ..., 0) depends on the species only, so
   // Abar^h[d3][0] = sum_{c in h} mbar_i[d3][c] e_s[c] is tabulated per staged row and species
@@ -1481,7 +1502,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
     sph<LMAX>(nx, ny, nz, Y);
     float w[P];
 #pragma unroll
-    for (int p = 0; p < P; p++) w[p] = ew[p * ews + a];
+    for (int p = 0; p < P; p++) w[p] = ((WMASK >> p) & 1u) ? ew[p * ews + a] : 0.0f;
     float wb[P], Yb[9];
 #pragma unroll
     for (int p = 0; p < P; p++) wb[p] = 0.0f;
@@ -1523,7 +1544,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
     if (hh == 0) {
       float dEdr = ubar * du;
 #pragma unroll
-      for (int p = 0; p < P; p++) dEdr += wb[p] * edw[p * ews + a];
+      for (int p = 0; p < P; p++)
+        if ((WMASK >> p) & 1u) dEdr += wb[p] * edw[p * ews + a];
       float gy[3];
       sph_vjp<LMAX>(nx, ny, nz, Yb, gy);
       const float ng = nx * gy[0] + ny * gy[1] + nz * gy[2];
@@ -1570,6 +1592,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
   constexpr int NC = dh / 4;
   constexpr int EPW = 256 / H;
   constexpr int EPB = kGradPasses * EPW;
+  // radial weights of the paths into output degree 0 (m_bar has only its l = 0 component)
+  constexpr uint32_t WMASK = paths_to<LMAX>(0);
   __shared__ float4 shj[kGradRows * D * C / 4];
   const int64_t n_act = *arow_n;
   const uint32_t nb_act = (uint32_t)((n_act + EPB - 1) / EPB);
@@ -1604,7 +1628,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
       sph<LMAX>(nx, ny, nz, Y);
       float w[P];
 #pragma unroll
-      for (int p = 0; p < P; p++) w[p] = ew[p * ews + a];
+      for (int p = 0; p < P; p++) w[p] = ((WMASK >> p) & 1u) ? ew[p * ews + a] : 0.0f;
       float wb[P], Yb[9];
 #pragma unroll
       for (int p = 0; p < P; p++) wb[p] = 0.0f;
@@ -1664,7 +1688,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))
       if (hh == 0) {
         float dEdr = ubar * du;
 #pragma unroll
-        for (int p = 0; p < P; p++) dEdr += wb[p] * edw[p * ews + a];
+        for (int p = 0; p < P; p++)
+          if ((WMASK >> p) & 1u) dEdr += wb[p] * edw[p * ews + a];
         float gy[3];
         sph_vjp<LMAX>(nx, ny, nz, Yb, gy);
         const float ng = nx * gy[0] + ny * gy[1] + nz * gy[2];
@@ -1942,7 +1967,8 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     TESS_TIMED("edge_radial", st,
                k_edge_radial<P><<<kRadBlocks, kRadThreads, 0, st>>>(
                    w.arow + n, w.ar, w.rtab, 0, T, rc, w.ew, w.edw, ews * 12, ews, cap,
-                   w.adst, w.asrc, species, w.l0tab, S, w.es));
+                   w.adst, w.asrc, species, w.l0tab, S, w.es, paths_from<LMAX>(0),
+                   paths_to<LMAX>(0)));
   TESS_HIP_CHECK(hipGetLastError());
   // ---------------- forward ----------------
   for (int t = 0; t < T; t++) {

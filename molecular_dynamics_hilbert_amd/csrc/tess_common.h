@@ -116,6 +116,29 @@ __device__ __forceinline__ constexpr const CGTable& cg_table() {
   if constexpr (LMAX == 1) return kCG1; else return kCG2;
 }
 
+// Bit p set for the paths with sender degree l1 == l (paths_from), or with output degree
+// l3 == l (paths_to); all_paths has every bit.
+template <int LMAX>
+constexpr uint32_t paths_from(int l) {
+  const CGTable& T = LMAX == 1 ? kCG1 : kCG2;
+  uint32_t m = 0;
+  for (int p = 0; p < T.P; p++)
+    if (T.l1[p] == l) m |= 1u << p;
+  return m;
+}
+template <int LMAX>
+constexpr uint32_t paths_to(int l) {
+  const CGTable& T = LMAX == 1 ? kCG1 : kCG2;
+  uint32_t m = 0;
+  for (int p = 0; p < T.P; p++)
+    if (T.l3[p] == l) m |= 1u << p;
+  return m;
+}
+template <int LMAX>
+constexpr uint32_t all_paths() {
+  return (1u << Dims<LMAX>::P) - 1u;
+}
+
 // Real spherical harmonics values on a unit vector (float).
 template <int LMAX>
 __device__ __forceinline__ void sph(float x, float y, float z, float* Y) {

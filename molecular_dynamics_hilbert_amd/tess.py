@@ -157,11 +157,13 @@ def _stream():
 
 def workspace(spec, n: int, edge_cap: int, device="cuda") -> torch.Tensor:
     """A workspace of tess_workspace_bytes() bytes whose device status word (its first
-    word) starts at zero."""
+    word) starts at zero and whose other bytes start as 0xFF."""
     nb = workspace_bytes(spec, n, edge_cap)
     if nb < 0:
         raise TessError(ERR_ARG, "tess_workspace_bytes")
-    ws = torch.empty(nb, dtype=torch.uint8, device=device)
+    # every byte but the status word's line starts as 0xFF (a NaN in every float), so a read of
+    # anything the library did not write first shows up in the results
+    ws = torch.full((nb,), 0xFF, dtype=torch.uint8, device=device)
     ws[:256].zero_()
     return ws
 
