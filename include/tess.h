@@ -32,7 +32,8 @@
  *    The next synchronising call on that workspace -- tess_check_status,
  *    tess_build_neighbors or tess_md_steps -- returns TESS_ERR_SPECIES (first),
  *    TESS_ERR_NONFINITE or TESS_ERR_RADIAL and clears the word. A fresh workspace must start with that word zero
- *    (zero-filled memory, or one tess_check_status call). The Tessera abstract reports runs
+ *    (zero-filled memory, or one tess_check_status call); the rest of the workspace may hold
+ *    anything, since the library writes every other value there before reading it. The Tessera abstract reports runs
  *    with no broken bonds or anomalously close pairs; this is the device-side check that a
  *    run has not blown up.
  *  - Supported model shapes (kernels are compiled per shape): n_rbf == 8, n_species <= 16,
