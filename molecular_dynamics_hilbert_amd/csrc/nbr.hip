@@ -1097,8 +1097,10 @@ __global__ void __launch_bounds__(256) k_rev_grouped(int32_t n,
 // Exclusive scan of int32 counts in place. Up to kScanOneMax entries one block of 1024
 // threads does it in one launch (16 entries per thread); longer arrays take two launches
 // (tile sums, then each tile adds the sum of the tile sums before it, which it reduces
-// itself), and beyond kScanCarryTiles tiles a third launch scans the tile sums. Optionally the same launches report the largest count and
-// the 64-bit total of the counts (stats[0], stats[2..3]).
+// itself), and beyond kScanCarryTiles tiles a third launch scans the tile sums. Optionally
+// the same launches report the largest count and the 64-bit total of the counts (stats[0],
+// stats[2..3]) and copy one more word next to them (stats[1]), so that a caller reads all
+// three with one copy.
 constexpr int kScanTile = 4096;          // 256 threads x 16 (multi-block tiles)
 constexpr int kScanOneMax = 16384;       // 1024 threads x 16
 constexpr int kScanCarryTiles = 4096;
