@@ -332,16 +332,12 @@ __global__ void __launch_bounds__(256) k_active_fill(int32_t n, const float* __r
                                                      int32_t* __restrict__ aslot,
                                                      int32_t* __restrict__ slot2act,
                                                      float4* __restrict__ ageo,
-                                                     float* __restrict__ ar,
-                                                     const int32_t* __restrict__ species,
-                                                     const float4* __restrict__ l0tab, int S,
-                                                     float4* __restrict__ es0) {
+                                                     float* __restrict__ ar) {
   int32_t i = blockIdx.x * 4 + (threadIdx.x >> 6);
   int lane = threadIdx.x & 63;
   if (i >= n) return;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int32_t a0 = arow[i];
-  const float4* l0row = l0tab + sp_index(species[i], S) * S;  // this destination's row
   for (int32_t e0 = row_ptr[i]; e0 < row_ptr[i + 1]; e0 += 64) {
     int32_t e = e0 + lane;
     bool ok = e < row_ptr[i + 1];
@@ -362,7 +358,6 @@ __global__ void __launch_bounds__(256) k_active_fill(int32_t n, const float* __r
       ageo[a] = make_float4(r.x, r.y, r.z, rr);
       ar[a] = rr;
       slot2act[e] = a;
-      es0[a] = l0row[sp_index(species[j], S)];  // first-layer logits of the edge
     } else if (ok) {
       slot2act[e] = -1;
     }
@@ -538,9 +533,10 @@ __global__ void k_radial_verdict(int T, const uint32_t* __restrict__ acc,
   if (!(ew <= 1e-6f * mw) || !(ed <= 1e-4f * md)) atomicOr(status, kStatusRadial);
 }
 
-// Radial weights w and dw/dr of layers t_begin..t_end-1 for each active edge from the table,
-// written at [layer][path][edge] (path-major rows of ews floats, ews a multiple of 64). The
-// distances are random, so the table is read from LDS: persistent blocks (one per CU) take contiguous ranges of whole groups of 4
+// Radial weights w and dw/dr of layers t_begin..t_end-1 for each active edge from the table, written at
+// [layer][path][edge] (path-major rows of ews floats, ews a multiple of 64); with l0tab, also
+// the first layer's logits from the species table. The distances are random, so the table is
+// read from LDS: persistent blocks (one per CU) take contiguous ranges of whole groups of 4
 // edges, stage one layer's table (98 KB) at a time and interpolate every edge of their range
 // from it. A thread takes 4 consecutive edges at a time, so each output row gets one 16-byte
 // store per thread (a wave writes 1 KB of a row); slots past the active count in the last
@@ -554,8 +550,10 @@ template <int NP>
 __global__ void __launch_bounds__(kRadThreads) k_edge_radial(
     const int32_t* __restrict__ arow_n, const float* __restrict__ ar,
     const float* __restrict__ rtab, int t_begin, int t_end, float rc, float* __restrict__ ew,
-    float* __restrict__ edw, int64_t lstride, int64_t ews, int64_t cap, uint32_t mfirst,
-    uint32_t mlast) {
+    float* __restrict__ edw, int64_t lstride, int64_t ews, int64_t cap,
+    const int32_t* __restrict__ adst, const int32_t* __restrict__ asrc,
+    const int32_t* __restrict__ species, const float4* __restrict__ l0tab, int S,
+    float4* __restrict__ es, uint32_t mfirst, uint32_t mlast) {
   __shared__ float4 stab[(kRadKnots + 1) * 6];
   const int64_t n_act = min((int64_t)*arow_n, cap);
   const int64_t ngr = (n_act + 3) / 4;  // groups of 4 edges
@@ -630,6 +628,16 @@ __global__ void __launch_bounds__(kRadThreads) k_edge_radial(
             }
             pw += ews;
             pd += ews;
+          }
+        }
+      }
+      if (t == 0 && l0tab) {
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          if (a + e < n_act) {
+            const int si = sp_index(species[adst[a + e]], S);
+            const int sj = sp_index(species[asrc[a + e]], S);
+            es[a + e] = l0tab[si * S + sj];
           }
         }
       }
@@ -1916,10 +1924,6 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
   const int64_t NDC = (int64_t)n * D * C;
   // embedding
   k_embed<<<gridn((int64_t)n * C, 256), 256, 0, st>>>(n, C, D, S, species, emb, w.h, status);
-  // first layer: logits from the per-species table (q and k of the first layer are not needed
-  // anywhere else: the backward stops before dE/dh^0), written per active edge by the
-  // active-edge fill
-  k_l0_logits<C, H><<<1, 256, 0, st>>>(S, emb, lw[0].Wq, lw[0].Wk, w.l0tab);
   // active edges
   const int32_t* rev = rev_in;
   if (cap > 0) {
@@ -1933,8 +1937,7 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     TESS_HIP_CHECK(scan_exclusive_i32(w.arow, (int64_t)n + 1, w.scan_tmp, st));
     k_active_fill<<<gridn(n, 4), 256, 0, st>>>(n, pos, row_ptr, col_shift, box[0], box[1], box[2],
                                                rc * rc, w.arow, w.adst, w.asrc, w.aslot,
-                                               w.slot2act, w.ageo, w.ar, species, w.l0tab, S,
-                                               w.es);
+                                               w.slot2act, w.ageo, w.ar);
     k_active_rev<<<gridn(cap, 256), 256, 0, st>>>(w.arow + n, w.aslot, rev, w.slot2act, w.arev, cap);
     TESS_HIP_CHECK(hipGetLastError());
   } else {
@@ -1955,13 +1958,17 @@ int32_t ef_run(const tess_model_desc& md, const float* weights, int32_t n, const
     TESS_HIP_CHECK(hipGetLastError());
     return TESS_OK;
   };
-  // the radial weights of every layer for each active edge
+  // first layer: logits from the per-species table (q and k of the first layer are not needed
+  // anywhere else: the backward stops before dE/dh^0); then the radial weights of every layer
+  // and the first layer's logits for each active edge
+  k_l0_logits<C, H><<<1, 256, 0, st>>>(S, emb, lw[0].Wq, lw[0].Wk, w.l0tab);
   if (ax) TESS_HIP_CHECK(hipStreamWaitEvent(st, ax->ev[kEvTabDone], 0));
   if (cap > 0)
     TESS_TIMED("edge_radial", st,
                k_edge_radial<P><<<kRadBlocks, kRadThreads, 0, st>>>(
                    w.arow + n, w.ar, w.rtab, 0, T, rc, w.ew, w.edw, ews * 12, ews, cap,
-                   paths_from<LMAX>(0), paths_to<LMAX>(0)));
+                   w.adst, w.asrc, species, w.l0tab, S, w.es, paths_from<LMAX>(0),
+                   paths_to<LMAX>(0)));
   TESS_HIP_CHECK(hipGetLastError());
   // ---------------- forward ----------------
   for (int t = 0; t < T; t++) {
